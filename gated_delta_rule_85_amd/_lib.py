@@ -1,0 +1,118 @@
+"""ctypes binding of libgdr.so (the C ABI declared in include/gdr.h).
+
+Argument marshalling only: every step of the operator runs in the library's
+HIP kernels.  Importing this module fails loudly when the library has not
+been built; there is no fallback.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdr.so")
+
+ABI_VERSION = 1
+CHUNK = 64
+
+OK, EINVAL, ENOTSUP, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
+BF16, F32 = 0, 1
+CP_AUTO, CP_OFF, CP_WARMUP = 0, 1, 2
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+class FwdArgs(ctypes.Structure):
+    """Mirror of gdr_fwd_args."""
+    _fields_ = [
+        ("B", _i64), ("T", _i64), ("H_q", _i64), ("H_v", _i64), ("K", _i64), ("V", _i64),
+        ("n_seq", _i64),
+        ("dtype", _i32), ("out_dtype", _i32), ("scale", ctypes.c_float),
+        ("cp_mode", _i32), ("cp_segment_chunks", _i32), ("cp_warmup_chunks", _i32),
+        ("q", _p), ("k", _p), ("v", _p), ("g", _p), ("beta", _p), ("initial_state", _p),
+        ("cu_seqlens", _p),
+        ("o", _p), ("final_state", _p), ("g_cum", _p), ("A", _p), ("h", _p),
+        ("w_out", _p), ("u_out", _p),
+        ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class BwdArgs(ctypes.Structure):
+    """Mirror of gdr_bwd_args."""
+    _fields_ = [
+        ("B", _i64), ("T", _i64), ("H_q", _i64), ("H_v", _i64), ("K", _i64), ("V", _i64),
+        ("n_seq", _i64),
+        ("dtype", _i32), ("scale", ctypes.c_float),
+        ("q", _p), ("k", _p), ("v", _p), ("g_cum", _p), ("beta", _p), ("A", _p),
+        ("dout", _p), ("dht", _p), ("initial_state", _p), ("cu_seqlens", _p),
+        ("dq", _p), ("dk", _p), ("dv", _p), ("dbeta", _p), ("dg", _p), ("dh0", _p),
+        ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libgdr.so is not built (%s); run `python -m gated_delta_rule_85_amd.build` or "
+            "__graft_entry__.build() first" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.gdr_abi_version.restype = ctypes.c_int
+    lib.gdr_abi_version.argtypes = []
+    lib.gdr_strerror.restype = ctypes.c_char_p
+    lib.gdr_strerror.argtypes = [ctypes.c_int]
+    for name, st in (("gdr_fwd", FwdArgs), ("gdr_bwd", BwdArgs)):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.POINTER(st), _p]
+        fw = getattr(lib, name + "_workspace")
+        fw.restype = ctypes.c_int
+        fw.argtypes = [ctypes.POINTER(st), ctypes.POINTER(ctypes.c_size_t)]
+    if lib.gdr_abi_version() != ABI_VERSION:
+        raise ImportError("libgdr ABI version %d, binding expects %d"
+                          % (lib.gdr_abi_version(), ABI_VERSION))
+    return lib
+
+
+lib = _load()
+
+
+class GdrError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__("%s failed: %s (%d)" % (fn, strerror(code), code))
+        self.code = code
+
+
+def strerror(code):
+    return lib.gdr_strerror(int(code)).decode()
+
+
+def abi_version():
+    return lib.gdr_abi_version()
+
+
+def fwd_workspace(args):
+    n = ctypes.c_size_t(0)
+    rc = lib.gdr_fwd_workspace(ctypes.byref(args), ctypes.byref(n))
+    if rc:
+        raise GdrError("gdr_fwd_workspace", rc)
+    return n.value
+
+
+def fwd(args, stream):
+    rc = lib.gdr_fwd(ctypes.byref(args), _p(stream))
+    if rc:
+        raise GdrError("gdr_fwd", rc)
+
+
+def bwd_workspace(args):
+    n = ctypes.c_size_t(0)
+    rc = lib.gdr_bwd_workspace(ctypes.byref(args), ctypes.byref(n))
+    if rc:
+        raise GdrError("gdr_bwd_workspace", rc)
+    return n.value
+
+
+def bwd(args, stream):
+    rc = lib.gdr_bwd(ctypes.byref(args), _p(stream))
+    if rc:
+        raise GdrError("gdr_bwd", rc)

@@ -1,0 +1,178 @@
+"""PyTorch-facing API of the gfx950 gated delta rule operator.
+
+Names and argument order follow the FlashQLA README ("Usage": the high-level
+``chunk_gated_delta_rule`` and the low-level ``chunk_gated_delta_rule_fwd`` /
+``chunk_gated_delta_rule_bwd``).  PyTorch only allocates device memory and
+supplies the current stream; every step runs in libgdr's HIP kernels.
+
+Output dtype.  ``o`` is returned in float32 by default: for bf16 inputs the
+operator accumulates in fp32 and a bf16 ``o`` would add a rounding of up to
+2^-8 |o| per element (``output_dtype=torch.bfloat16`` selects it).
+"""
+import math
+
+import torch
+
+from . import _lib
+
+_DT = {torch.bfloat16: _lib.BF16, torch.float32: _lib.F32}
+_CP = {"auto": _lib.CP_AUTO, "off": _lib.CP_OFF, "exact": _lib.CP_OFF, "warmup": _lib.CP_WARMUP}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(q, k, v, g, beta, cu_seqlens):
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("expected q, k [B,T,H_q,K] and v [B,T,H_v,V]")
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype, bfloat16 or float32")
+    B, T, Hv = v.shape[0], v.shape[1], v.shape[2]
+    if g.shape != (B, T, Hv) or beta.shape != (B, T, Hv):
+        raise ValueError("g and beta must be [B,T,H_v]")
+    if not q.is_cuda:
+        raise ValueError("inputs must be on the GPU")
+    if cu_seqlens is not None and (B != 1 or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1):
+        raise ValueError("cu_seqlens must be int32 [N+1] with B == 1")
+
+
+def _c(t, dtype=None):
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        t = t.to(dtype)
+    return t.contiguous()
+
+
+def num_chunks(T, B=1, cu_seqlens=None):
+    """Chunk-start state count of the forward's h (host sync with cu_seqlens)."""
+    if cu_seqlens is None:
+        return B * ((T + _lib.CHUNK - 1) // _lib.CHUNK)
+    lens = (cu_seqlens[1:] - cu_seqlens[:-1]).to("cpu", torch.int64)
+    return int(((lens + _lib.CHUNK - 1) // _lib.CHUNK).sum())
+
+
+def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
+                               cu_seqlens=None, output_final_state=True, *,
+                               output_dtype=torch.float32, return_h=True, cp_mode="auto",
+                               cp_segment_chunks=0, cp_warmup_chunks=0, return_wu=False):
+    """Low-level forward.  Returns ``(g_cum, A, o, h, final_state)``.
+
+    g_cum [B,T,H_v] fp32 is the in-chunk cumulative log-gate; A [B,T,H_v,64]
+    fp32 holds, per token, its row of T = (I + A_strict)^{-1} for its chunk;
+    h [1,NT,H_v,K,V] fp32 the chunk-start states (None unless return_h);
+    final_state [N,H_v,K,V] fp32 (None unless output_final_state).  With
+    ``return_wu`` also returns W, U [B,T,H_v,K|V] fp32.
+    """
+    _check(q, k, v, g, beta, cu_seqlens)
+    q, k, v = _c(q), _c(k), _c(v)
+    g, beta = _c(g, torch.float32), _c(beta, torch.float32)
+    B, T, Hq, K = q.shape
+    Hv, V = v.shape[2], v.shape[3]
+    n_seq = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    h0 = _c(initial_state, torch.float32)
+    if h0 is not None and h0.shape != (n_seq, Hv, K, V):
+        raise ValueError("initial_state must be [N,H_v,K,V]")
+    cu = _c(cu_seqlens)
+    o = torch.empty((B, T, Hv, V), dtype=output_dtype, device=dev)
+    g_cum = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
+    A = torch.empty((B, T, Hv, _lib.CHUNK), dtype=torch.float32, device=dev)
+    ht = torch.empty((n_seq, Hv, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    h = None
+    if return_h:
+        h = torch.empty((1 if cu is not None else B, num_chunks(T, 1, cu) if cu is not None
+                         else num_chunks(T), Hv, K, V), dtype=torch.float32, device=dev)
+    w = u = None
+    if return_wu:
+        w = torch.empty((B, T, Hv, K), dtype=torch.float32, device=dev)
+        u = torch.empty((B, T, Hv, V), dtype=torch.float32, device=dev)
+    a = _lib.FwdArgs()
+    a.B, a.T, a.H_q, a.H_v, a.K, a.V, a.n_seq = B, T, Hq, Hv, K, V, n_seq
+    a.dtype = _DT[q.dtype]
+    a.out_dtype = _DT[output_dtype]
+    a.scale = float(scale)
+    a.cp_mode = _CP[cp_mode]
+    a.cp_segment_chunks = int(cp_segment_chunks)
+    a.cp_warmup_chunks = int(cp_warmup_chunks)
+    a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    a.initial_state, a.cu_seqlens = _ptr(h0), _ptr(cu)
+    a.o, a.final_state, a.g_cum, a.A, a.h = _ptr(o), _ptr(ht), _ptr(g_cum), _ptr(A), _ptr(h)
+    a.w_out, a.u_out = _ptr(w), _ptr(u)
+    nbytes = _lib.fwd_workspace(a)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
+    _lib.fwd(a, torch.cuda.current_stream(dev).cuda_stream)
+    if return_wu:
+        return g_cum, A, o, h, ht, w, u
+    return g_cum, A, o, h, ht
+
+
+def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, initial_state=None,
+                               cu_seqlens=None):
+    """Low-level backward.  ``g`` is the forward's g_cum, ``A`` its A.
+    Returns ``(dq, dk, dv, db, dg, dh0)``; dh0 is None without initial_state."""
+    _check(q, k, v, g, beta, cu_seqlens)
+    q, k, v, do = _c(q), _c(k), _c(v), _c(do, q.dtype)
+    g, beta, A = _c(g, torch.float32), _c(beta, torch.float32), _c(A, torch.float32)
+    B, T, Hq, K = q.shape
+    Hv, V = v.shape[2], v.shape[3]
+    n_seq = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    h0 = _c(initial_state, torch.float32)
+    dht = _c(dht, torch.float32)
+    cu = _c(cu_seqlens)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    db = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
+    dg = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
+    dh0 = torch.empty((n_seq, Hv, K, V), dtype=torch.float32, device=dev) if h0 is not None else None
+    a = _lib.BwdArgs()
+    a.B, a.T, a.H_q, a.H_v, a.K, a.V, a.n_seq = B, T, Hq, Hv, K, V, n_seq
+    a.dtype = _DT[q.dtype]
+    a.scale = float(scale)
+    a.q, a.k, a.v, a.g_cum, a.beta, a.A = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A)
+    a.dout, a.dht, a.initial_state, a.cu_seqlens = _ptr(do), _ptr(dht), _ptr(h0), _ptr(cu)
+    a.dq, a.dk, a.dv, a.dbeta, a.dg, a.dh0 = _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(dg), _ptr(dh0)
+    nbytes = _lib.bwd_workspace(a)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
+    _lib.bwd(a, torch.cuda.current_stream(dev).cuda_stream)
+    return dq, dk, dv, db, dg, dh0
+
+
+class _ChunkGDR(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
+                output_dtype):
+        g_cum, A, o, _, ht = chunk_gated_delta_rule_fwd(
+            q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_state=True,
+            output_dtype=output_dtype, return_h=False)
+        ctx.save_for_backward(q, k, v, g_cum, beta, A, initial_state, cu_seqlens)
+        ctx.scale = scale
+        ctx.g_dtype = g.dtype
+        return o, (ht if output_final_state else None)
+
+    @staticmethod
+    def backward(ctx, do, dht):
+        q, k, v, g_cum, beta, A, h0, cu = ctx.saved_tensors
+        dq, dk, dv, db, dg, dh0 = chunk_gated_delta_rule_bwd(
+            q, k, v, g_cum, beta, A, do, dht, ctx.scale, h0, cu)
+        return (dq, dk, dv, dg.to(ctx.g_dtype), db.to(beta.dtype), None, dh0, None, None, None)
+
+
+def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
+                           output_final_state=False, cu_seqlens=None, *,
+                           output_dtype=torch.float32):
+    """High-level differentiable API.  Returns ``(o, final_state)``."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    o, ht = _ChunkGDR.apply(q, k, v, g, beta, scale, initial_state, output_final_state,
+                            cu_seqlens, output_dtype)
+    return o, ht

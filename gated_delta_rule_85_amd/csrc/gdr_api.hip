@@ -1,0 +1,209 @@
+// Host side of the libgdr C ABI: argument validation, workspace sizing, the
+// sequence-split decision and kernel launches.  Declarations and the
+// contract of every entry point are in include/gdr.h.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/gdr.h"
+#include "gdr_kernels.hpp"
+
+using namespace gdr;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct FwdPlan {
+    int64_t n_seq, tokens, nct, nt_ub;  // nct: chunks per sequence bound
+    size_t off_chunk, off_gcum, off_A, total;
+    int seg_chunks, warm_chunks, n_seg;
+    bool split;
+};
+
+int check_dims(int64_t B, int64_t T, int64_t Hq, int64_t Hv, int64_t K, int64_t V, int64_t n_seq,
+               bool varlen, int32_t dtype) {
+    if (B < 1 || T < 0 || Hq < 1 || Hv < 1) return GDR_EINVAL;
+    if (Hv % Hq != 0) return GDR_EINVAL;
+    if (varlen && (B != 1 || n_seq < 1)) return GDR_EINVAL;
+    if (dtype != GDR_BF16 && dtype != GDR_F32) return GDR_ENOTSUP;
+    if ((K != 64 && K != 128) || (V != 64 && V != 128)) return GDR_ENOTSUP;
+    // 32-bit limits of the chunk bookkeeping
+    if (B * T > (int64_t)1 << 31 || (varlen ? n_seq : B) * Hv > (int64_t)1 << 30) return GDR_EINVAL;
+    return GDR_OK;
+}
+
+int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl) {
+    if (!a) return GDR_EINVAL;
+    const bool varlen = a->cu_seqlens != nullptr;
+    int rc = check_dims(a->B, a->T, a->H_q, a->H_v, a->K, a->V, a->n_seq, varlen, a->dtype);
+    if (rc) return rc;
+    if (a->out_dtype != GDR_BF16 && a->out_dtype != GDR_F32) return GDR_ENOTSUP;
+    if (a->cp_mode < GDR_CP_AUTO || a->cp_mode > GDR_CP_WARMUP) return GDR_EINVAL;
+    if (a->cp_segment_chunks < 0 || a->cp_warmup_chunks < 0) return GDR_EINVAL;
+    pl.n_seq = varlen ? a->n_seq : a->B;
+    pl.tokens = a->B * a->T;
+    pl.nct = cdiv(a->T, GDR_CHUNK);
+    pl.nt_ub = varlen ? pl.nct + pl.n_seq : a->B * pl.nct;
+    size_t off = 0;
+    pl.off_chunk = off;
+    if (varlen) off += up(sizeof(int32_t) * (size_t)(pl.n_seq + 1));
+    pl.off_gcum = off;
+    if (!a->g_cum) off += up(sizeof(float) * (size_t)(pl.tokens * a->H_v));
+    pl.off_A = off;
+    if (!a->A) off += up(sizeof(float) * (size_t)(pl.tokens * a->H_v * GDR_CHUNK));
+    pl.total = off;
+    // sequence split ("AutoCP"): the pages' trigger on batch x heads and length
+    const int64_t bh = pl.n_seq * a->H_v;
+    bool split = a->cp_mode == GDR_CP_WARMUP ||
+                 (a->cp_mode == GDR_CP_AUTO && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
+    int L = a->cp_segment_chunks > 0 ? a->cp_segment_chunks
+                                      : (int)ceil(sqrt((double)(pl.nct > 0 ? pl.nct : 1)));
+    if (L < 1) L = 1;
+    if (!split || L >= pl.nct) {
+        split = false;
+        L = (int)pl.nct + 1;
+    }
+    pl.split = split;
+    pl.seg_chunks = L;
+    pl.warm_chunks = a->cp_warmup_chunks > 0 ? a->cp_warmup_chunks : 8;
+    pl.n_seg = split ? (int)cdiv(pl.nct, L) : 1;
+    return GDR_OK;
+}
+
+SeqMap make_map(const gdr_fwd_args *a, const FwdPlan &pl, const int32_t *chunk_off) {
+    SeqMap m;
+    m.cu = a->cu_seqlens;
+    m.chunk_off = chunk_off;
+    m.T = a->T;
+    m.n_seq = (int32_t)pl.n_seq;
+    m.nct = (int32_t)pl.nct;
+    return m;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+const char *gdr_strerror(int code) {
+    switch (code) {
+        case GDR_OK: return "ok";
+        case GDR_EINVAL: return "invalid argument";
+        case GDR_ENOTSUP: return "unsupported size or dtype";
+        case GDR_EWORKSPACE: return "workspace too small";
+        case GDR_ELAUNCH: return "kernel launch failed";
+        default: return "unknown error";
+    }
+}
+
+int gdr_fwd_workspace(const gdr_fwd_args *a, size_t *bytes) {
+    if (!bytes) return GDR_EINVAL;
+    FwdPlan pl;
+    int rc = plan_fwd(a, pl);
+    if (rc) return rc;
+    *bytes = pl.total;
+    return GDR_OK;
+}
+
+int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
+    FwdPlan pl;
+    int rc = plan_fwd(a, pl);
+    if (rc) return rc;
+    if (pl.tokens > 0) {
+        if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o) return GDR_EINVAL;
+        if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->o, 16) ||
+            !aligned(a->g, 4) || !aligned(a->beta, 4))
+            return GDR_EINVAL;
+    }
+    if ((a->A && !aligned(a->A, 16)) || (a->g_cum && !aligned(a->g_cum, 4)) ||
+        (a->h && !aligned(a->h, 16)) || (a->final_state && !aligned(a->final_state, 16)) ||
+        (a->initial_state && !aligned(a->initial_state, 16)) || (a->w_out && !aligned(a->w_out, 16)) ||
+        (a->u_out && !aligned(a->u_out, 16)))
+        return GDR_EINVAL;
+    if (a->workspace_bytes < pl.total || (pl.total > 0 && !a->workspace)) return GDR_EWORKSPACE;
+    if (pl.total > 0 && !aligned(a->workspace, 16)) return GDR_EINVAL;
+
+    char *ws = static_cast<char *>(a->workspace);
+    int32_t *chunk_off = a->cu_seqlens ? reinterpret_cast<int32_t *>(ws + pl.off_chunk) : nullptr;
+    float *g_cum = a->g_cum ? a->g_cum : reinterpret_cast<float *>(ws + pl.off_gcum);
+    float *Tm = a->A ? a->A : reinterpret_cast<float *>(ws + pl.off_A);
+    const Dt dt = a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
+    const Dt ot = a->out_dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
+    const SeqMap sm = make_map(a, pl, chunk_off);
+
+    if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, chunk_off, (int)pl.n_seq, stream) != hipSuccess)
+        return GDR_ELAUNCH;
+    if (pl.tokens > 0) {
+        PrepParams pp;
+        pp.k = a->k;
+        pp.g = a->g;
+        pp.beta = a->beta;
+        pp.g_cum = g_cum;
+        pp.Tm = Tm;
+        pp.sm = sm;
+        pp.Hq = (int)a->H_q;
+        pp.Hv = (int)a->H_v;
+        if (launch_prep(dt, (int)a->K, pp, (int)pl.nt_ub, stream) != hipSuccess) return GDR_ELAUNCH;
+    }
+    ScanParams sp;
+    sp.q = a->q;
+    sp.k = a->k;
+    sp.v = a->v;
+    sp.Tm = Tm;
+    sp.g_cum = g_cum;
+    sp.beta = a->beta;
+    sp.h0 = a->initial_state;
+    sp.o = a->o;
+    sp.hT = a->final_state;
+    sp.hsnap = a->h;
+    sp.sm = sm;
+    sp.Hq = (int)a->H_q;
+    sp.Hv = (int)a->H_v;
+    sp.V = (int)a->V;
+    sp.scale = a->scale;
+    sp.seg_chunks = pl.seg_chunks;
+    sp.warm_chunks = pl.warm_chunks;
+    sp.n_vt = (int)(a->V / scan_vtile(dt, (int)a->K, (int)a->V));
+    sp.n_units = (int)(pl.n_seq * a->H_v);
+    sp.n_seg = pl.n_seg;
+    if (launch_scan_output(dt, ot, (int)a->K, (int)a->V, sp, stream) != hipSuccess) return GDR_ELAUNCH;
+    if ((a->w_out || a->u_out) && pl.tokens > 0) {
+        if (!a->w_out || !a->u_out) return GDR_EINVAL;
+        WUParams wp;
+        wp.k = a->k;
+        wp.v = a->v;
+        wp.Tm = Tm;
+        wp.g_cum = g_cum;
+        wp.beta = a->beta;
+        wp.w = a->w_out;
+        wp.u = a->u_out;
+        wp.sm = sm;
+        wp.Hq = (int)a->H_q;
+        wp.Hv = (int)a->H_v;
+        wp.K = (int)a->K;
+        wp.V = (int)a->V;
+        if (launch_wu(dt, wp, (int)pl.nt_ub, stream) != hipSuccess) return GDR_ELAUNCH;
+    }
+    return GDR_OK;
+}
+
+int gdr_bwd_workspace(const gdr_bwd_args *a, size_t *bytes) {
+    if (!a || !bytes) return GDR_EINVAL;
+    int rc = check_dims(a->B, a->T, a->H_q, a->H_v, a->K, a->V, a->n_seq, a->cu_seqlens != nullptr, a->dtype);
+    if (rc) return rc;
+    *bytes = 0;
+    return GDR_ENOTSUP;
+}
+
+int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
+    (void)stream;
+    size_t b;
+    int rc = gdr_bwd_workspace(a, &b);
+    return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,209 @@
+// Device helpers shared by the gfx950 gated delta rule kernels.
+//
+// MFMA operand convention ("accumulator order").  A 16x16 output tile of a
+// v_mfma_f32_16x16x* instruction lives in lane l as rows 4*(l>>4)+j, j=0..3,
+// of column l&15.  Every operand here uses the same shape for its k index:
+// inside each 16-deep k block, lane l holds the 4 consecutive k values
+// 4*(l>>4) .. 4*(l>>4)+3 of row (A) or column (B) l&15.  Because A and B use
+// the same lane/slot -> k mapping, any such mapping gives the same product,
+// and with this one an accumulator tile of X is, unchanged, the B operand of
+// X (k = X's rows) and the A operand of X^T.  That is what lets the state h,
+// the corrected values U~ and the decayed scores stay in registers between
+// products.
+//
+// Precision.  Inputs q, k, v are exact bf16 values.  fp32 intermediates that
+// feed a product are split into hi = bf16(x) and lo = bf16(x - hi); a product
+// of a split operand with an exact one takes two MFMAs, split x split takes
+// three (hi*hi + hi*lo + lo*hi), which keeps about 16 significant bits.  For
+// fp32 inputs every operand is fp32 and the products use
+// v_mfma_f32_16x16x4_f32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CH = 64;    // chunk length
+constexpr int NTHR = 256; // threads per workgroup (4 waves)
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ int ln16() { return threadIdx.x & 15; }
+__device__ __forceinline__ int lg4() { return (threadIdx.x >> 4) & 3; }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------- operands
+struct OpX { bf16x4 b0, b1; };                    // exact bf16, k blocks 0 and 1
+struct OpS { bf16x4 h0, h1, l0, l1; };            // split fp32, k blocks 0 and 1
+struct OpF { f32x4 b0, b1; };                     // fp32 path
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x4 a0, bf16x4 a1, bf16x4 b0, bf16x4 b1, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat(a0, a1), cat(b0, b1), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma(f32x4 c, const OpX &a, const OpX &b) {
+    return mfma_bf16(a.b0, a.b1, b.b0, b.b1, c);
+}
+__device__ __forceinline__ f32x4 mma(f32x4 c, const OpS &a, const OpX &b) {
+    c = mfma_bf16(a.l0, a.l1, b.b0, b.b1, c);
+    return mfma_bf16(a.h0, a.h1, b.b0, b.b1, c);
+}
+__device__ __forceinline__ f32x4 mma(f32x4 c, const OpX &a, const OpS &b) {
+    c = mfma_bf16(a.b0, a.b1, b.l0, b.l1, c);
+    return mfma_bf16(a.b0, a.b1, b.h0, b.h1, c);
+}
+__device__ __forceinline__ f32x4 mma(f32x4 c, const OpS &a, const OpS &b) {
+    c = mfma_bf16(a.l0, a.l1, b.h0, b.h1, c);
+    c = mfma_bf16(a.h0, a.h1, b.l0, b.l1, c);
+    return mfma_bf16(a.h0, a.h1, b.h0, b.h1, c);
+}
+__device__ __forceinline__ f32x4 mma(f32x4 c, const OpF &a, const OpF &b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b0[j], b.b0[j], c, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b1[j], b.b1[j], c, 0, 0, 0);
+    return c;
+}
+
+// fp32 -> (hi, lo) bf16 pair, round to nearest even
+__device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
+    hi = __builtin_convertvector(x, bf16x4);
+    f32x4 r = x - __builtin_convertvector(hi, f32x4);
+    lo = __builtin_convertvector(r, bf16x4);
+}
+
+// Per-input-type operand policy.
+template <typename In> struct Ops;
+
+template <> struct Ops<bf16> {
+    using X = OpX;  // operand built from input values
+    using S = OpS;  // operand built from fp32 intermediates
+    // 4 consecutive inputs at p0 (k block 0) and p1 (k block 1)
+    static __device__ __forceinline__ X load(const bf16 *p0, const bf16 *p1) {
+        X r;
+        r.b0 = *reinterpret_cast<const bf16x4 *>(p0);
+        r.b1 = *reinterpret_cast<const bf16x4 *>(p1);
+        return r;
+    }
+    static __device__ __forceinline__ S split(f32x4 x0, f32x4 x1) {
+        S r;
+        split4(x0, r.h0, r.l0);
+        split4(x1, r.h1, r.l1);
+        return r;
+    }
+};
+
+template <> struct Ops<float> {
+    using X = OpF;
+    using S = OpF;
+    static __device__ __forceinline__ X load(const float *p0, const float *p1) {
+        X r;
+        r.b0 = *reinterpret_cast<const f32x4 *>(p0);
+        r.b1 = *reinterpret_cast<const f32x4 *>(p1);
+        return r;
+    }
+    static __device__ __forceinline__ S split(f32x4 x0, f32x4 x1) { return S{x0, x1}; }
+};
+
+// split-operand storage in LDS for an fp32 matrix that is read as an A
+// operand (row r, 4 consecutive k).  bf16 path: two bf16 planes; fp32 path:
+// one fp32 plane.
+template <typename In> struct SplitPlane;
+template <> struct SplitPlane<bf16> {
+    bf16 *hi, *lo;
+    __device__ __forceinline__ void put4(int off, f32x4 x) const {
+        bf16x4 h, l;
+        split4(x, h, l);
+        *reinterpret_cast<bf16x4 *>(hi + off) = h;
+        *reinterpret_cast<bf16x4 *>(lo + off) = l;
+    }
+    __device__ __forceinline__ OpS get(int off0, int off1) const {
+        OpS r;
+        r.h0 = *reinterpret_cast<const bf16x4 *>(hi + off0);
+        r.h1 = *reinterpret_cast<const bf16x4 *>(hi + off1);
+        r.l0 = *reinterpret_cast<const bf16x4 *>(lo + off0);
+        r.l1 = *reinterpret_cast<const bf16x4 *>(lo + off1);
+        return r;
+    }
+};
+template <> struct SplitPlane<float> {
+    float *hi, *lo;  // lo unused
+    __device__ __forceinline__ void put4(int off, f32x4 x) const {
+        *reinterpret_cast<f32x4 *>(hi + off) = x;
+    }
+    __device__ __forceinline__ OpF get(int off0, int off1) const {
+        OpF r;
+        r.b0 = *reinterpret_cast<const f32x4 *>(hi + off0);
+        r.b1 = *reinterpret_cast<const f32x4 *>(hi + off1);
+        return r;
+    }
+};
+
+template <typename T> __device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
+
+// 16-byte vector of inputs
+template <typename In> struct Vec16;
+template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int n = 8; };
+template <> struct Vec16<float> { typedef f32x4 type; static constexpr int n = 4; };
+
+// ---------------------------------------------------------------- sequences
+// Packed-token view of a batch.  Without cu_seqlens, sequence j is tokens
+// [j*T, (j+1)*T) and its chunks are j*ceil(T/64) ...; with cu_seqlens the
+// chunk offsets come from a table built on the device (gdr_chunk_offsets).
+struct SeqMap {
+    const int32_t *cu;        // [n_seq+1] or null
+    const int32_t *chunk_off; // [n_seq+1] or null (with cu)
+    int64_t T;                // tokens per sequence without cu
+    int32_t n_seq;
+    int32_t nct;              // chunks per sequence without cu
+
+    __device__ __forceinline__ void bounds(int j, int64_t &bos, int64_t &eos) const {
+        if (cu) {
+            bos = cu[j];
+            eos = cu[j + 1];
+        } else {
+            bos = (int64_t)j * T;
+            eos = bos + T;
+        }
+    }
+    __device__ __forceinline__ int chunk_base(int j) const { return cu ? chunk_off[j] : j * nct; }
+    // global chunk id -> (sequence, chunk in sequence); false past the end
+    __device__ __forceinline__ bool locate(int gid, int &j, int &c) const {
+        if (!cu) {
+            j = gid / nct;
+            c = gid - j * nct;
+            return j < n_seq;
+        }
+        if (gid >= chunk_off[n_seq]) return false;
+        int lo = 0, hi = n_seq - 1;  // largest j with chunk_off[j] <= gid
+        while (lo < hi) {
+            int mid = (lo + hi + 1) >> 1;
+            if (chunk_off[mid] <= gid) lo = mid; else hi = mid - 1;
+        }
+        j = lo;
+        c = gid - chunk_off[j];
+        return true;
+    }
+};
+
+// Workgroup id -> logical work index such that consecutive logical indices
+// run on the same XCD (the hardware deals workgroups to the 8 XCDs round
+// robin, each XCD with its own L2).
+__device__ __forceinline__ int xcd_remap(int id, int nb) {
+    const int xcd = id & 7, pos = id >> 3, per = nb >> 3, rem = nb & 7;
+    return xcd < rem ? xcd * (per + 1) + pos : rem * (per + 1) + (xcd - rem) * per + pos;
+}
+
+__device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+
+}  // namespace gdr

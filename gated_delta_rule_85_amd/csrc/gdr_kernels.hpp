@@ -1,0 +1,56 @@
+// Kernel parameter blocks and host-side launchers of libgdr (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdr_device.hpp"
+
+namespace gdr {
+
+enum class Dt : int { BF16 = 0, F32 = 1 };
+
+// gdr_chunk_prep: per (chunk, q/k head): in-chunk cumulative log-gate,
+// decayed strictly lower beta K K^T, T = (I + A)^{-1}.
+struct PrepParams {
+    const void *k;
+    const float *g, *beta;
+    float *g_cum;  // [tokens, H_v]
+    float *Tm;     // [tokens, H_v, 64]
+    SeqMap sm;
+    int Hq, Hv;
+};
+
+// gdr_scan_output: per (sequence, v-head, V tile, segment): serial scan over
+// chunks with the output of each chunk.
+struct ScanParams {
+    const void *q, *k, *v;
+    const float *Tm, *g_cum, *beta;
+    const float *h0;  // [N, H_v, K, V] or null
+    void *o;          // [tokens, H_v, V]
+    float *hT;        // [N, H_v, K, V] or null
+    float *hsnap;     // [NT, H_v, K, V] or null
+    SeqMap sm;
+    int Hq, Hv, V;
+    float scale;
+    int seg_chunks;   // chunks per segment
+    int warm_chunks;  // warm-up window of segments after the first
+    int n_vt, n_units, n_seg;
+};
+
+// optional materialisation of W = T diag(beta e^gam) K and U = T diag(beta) V
+struct WUParams {
+    const void *k, *v;
+    const float *Tm, *g_cum, *beta;
+    float *w, *u;
+    SeqMap sm;
+    int Hq, Hv, K, V;
+};
+
+hipError_t launch_chunk_offsets(const int32_t *cu, int32_t *chunk_off, int n_seq, hipStream_t s);
+hipError_t launch_prep(Dt dt, int K, const PrepParams &p, int n_chunks_ub, hipStream_t s);
+hipError_t launch_scan_output(Dt dt, Dt out, int K, int V, const ScanParams &p, hipStream_t s);
+hipError_t launch_wu(Dt dt, const WUParams &p, int n_chunks_ub, hipStream_t s);
+int scan_vtile(Dt dt, int K, int V);  // V columns per scan workgroup
+
+}  // namespace gdr

@@ -1,0 +1,250 @@
+// gdr_chunk_prep — the chunk-parallel part of the chunked forward.
+//
+// For one chunk of one q/k head (and each of the v heads sharing it):
+//   gam = in-chunk running sum of the log-gate g          (returned as g_cum)
+//   A   = strictly lower part of diag(beta) (K K^T) * exp(gam_r - gam_i)
+//   T   = (I + A)^{-1}                                     (returned as A)
+// These are the first steps the efeozkan blog lists under "2. Hardware-
+// Friendly Algebraic Reformulation" (computing the A matrix, then W and U);
+// W = T diag(beta e^gam) K and U = T diag(beta) V are not stored: the scan
+// kernel applies T to V - diag(e^gam) K h directly (U - W h in one product).
+//
+// K K^T depends only on the q/k head, so it is formed once per workgroup on
+// MFMA and reused by the H_v/H_q v heads.  The inverse of the unit lower
+// triangular 64x64 matrix is blocked in 16x16 tiles: the four diagonal tiles
+// by forward substitution (one wave, one lane per column), the off-diagonal
+// tiles by T_ab = -D_a sum_{m=b}^{a-1} A_am T_mb on fp32 MFMA, one block
+// diagonal at a time.
+#include "gdr_kernels.hpp"
+
+namespace gdr {
+
+namespace {
+
+constexpr int LDF = 68;  // fp32 64x64 tiles in LDS: row pitch (floats)
+
+// acc += X[16x16] * Y[16x16], X and Y fp32 in LDS with pitch LDF
+__device__ __forceinline__ f32x4 blk_mm(f32x4 acc, const float *X, const float *Y) {
+    const int n = ln16(), g = lg4();
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(X + n * LDF + 4 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], Y[(4 * g + j) * LDF + n], acc, 0, 0, 0);
+    return acc;
+}
+// acc += X[16x16] * Y where Y is an accumulator tile in registers
+__device__ __forceinline__ f32x4 blk_mm_reg(f32x4 acc, const float *X, f32x4 y) {
+    const int n = ln16(), g = lg4();
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(X + n * LDF + 4 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], y[j], acc, 0, 0, 0);
+    return acc;
+}
+
+// T_ab (a > b) from the diagonal inverses and the lower blocks already done
+__device__ __forceinline__ void offdiag_tile(const float *A, float *Tm, int a, int b) {
+    f32x4 P = zero4();
+    for (int m = b; m < a; ++m) P = blk_mm(P, A + 16 * a * LDF + 16 * m, Tm + 16 * m * LDF + 16 * b);
+    const f32x4 R = blk_mm_reg(zero4(), Tm + 16 * a * LDF + 16 * a, P);
+    const int n = ln16(), g = lg4();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Tm[(16 * a + 4 * g + j) * LDF + 16 * b + n] = -R[j];
+}
+
+template <typename In, int KD>
+__global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
+    using O = Ops<In>;
+    using V16 = typename Vec16<In>::type;
+    constexpr int EV = Vec16<In>::n;
+    constexpr int LDK = KD + EV;  // 16-byte row padding
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    In *Ks = reinterpret_cast<In *>(smem);
+    float *S = reinterpret_cast<float *>(smem + sizeof(In) * CH * LDK);
+    float *A = S + CH * LDF;
+    float *Tm = A + CH * LDF;
+    float *gam = Tm + CH * LDF;
+    float *bet = gam + CH;
+
+    const int gid = blockIdx.x, hq = blockIdx.y;
+    int j, c;
+    if (!p.sm.locate(gid, j, c)) return;
+    int64_t bos, eos;
+    p.sm.bounds(j, bos, eos);
+    const int64_t ts = bos + (int64_t)c * CH;
+    const int n = (int)min<int64_t>(CH, eos - ts);
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int G = p.Hv / p.Hq;
+
+    // K rows of the chunk (zero past its end); upper off-diagonal T tiles = 0
+    const In *kp = reinterpret_cast<const In *>(p.k);
+    for (int idx = tid; idx < CH * (KD / EV); idx += NTHR) {
+        const int r = idx / (KD / EV), cv = idx % (KD / EV);
+        V16 val = {};
+        if (r < n) val = *reinterpret_cast<const V16 *>(kp + ((ts + r) * p.Hq + hq) * KD + cv * EV);
+        *reinterpret_cast<V16 *>(Ks + r * LDK + cv * EV) = val;
+    }
+    for (int idx = tid; idx < CH * CH; idx += NTHR) {
+        const int r = idx >> 6, i = idx & 63;
+        if ((i >> 4) > (r >> 4)) Tm[r * LDF + i] = 0.f;
+    }
+    __syncthreads();
+
+    // S = K K^T, the ten tiles on or below the diagonal
+    {
+        const int n16 = ln16(), g = lg4();
+        for (int t = w; t < 10; t += 4) {
+            int tr = 0;
+            while ((tr + 1) * (tr + 2) / 2 <= t) ++tr;
+            const int ti = t - tr * (tr + 1) / 2;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int dp = 0; dp < KD / 32; ++dp) {
+                const In *ar = Ks + (16 * tr + n16) * LDK + 32 * dp + 4 * g;
+                const In *br = Ks + (16 * ti + n16) * LDK + 32 * dp + 4 * g;
+                acc = mma(acc, O::load(ar, ar + 16), O::load(br, br + 16));
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) S[(16 * tr + 4 * g + jj) * LDF + 16 * ti + n16] = acc[jj];
+        }
+    }
+    __syncthreads();
+
+    for (int rr = 0; rr < G; ++rr) {
+        const int hv = hq * G + rr;
+        if (w == 0) {
+            // inclusive running sum of g over the chunk (zero past its end)
+            float x = l < n ? p.g[(ts + l) * p.Hv + hv] : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off, 64);
+                if (l >= off) x += y;
+            }
+            gam[l] = x;
+            bet[l] = l < n ? p.beta[(ts + l) * p.Hv + hv] : 0.f;
+            if (l < n) p.g_cum[(ts + l) * p.Hv + hv] = x;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < CH * CH; idx += NTHR) {
+            const int r = idx >> 6, i = idx & 63;
+            A[r * LDF + i] = i < r ? bet[r] * fast_exp(gam[r] - gam[i]) * S[r * LDF + i] : 0.f;
+        }
+        __syncthreads();
+        if (w == 0) {
+            // diagonal tiles: lane = (tile b, column cc); forward substitution
+            const int b = l >> 4, cc = l & 15;
+            const float *Ab = A + 16 * b * LDF + 16 * b;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float s = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 0; i < r; ++i) s -= Ab[r * LDF + i] * x[i];
+                x[r] = s;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Tm[(16 * b + r) * LDF + 16 * b + cc] = x[r];
+        }
+        __syncthreads();
+        if (w < 3) offdiag_tile(A, Tm, w + 1, w);
+        __syncthreads();
+        if (w < 2) offdiag_tile(A, Tm, w + 2, w);
+        __syncthreads();
+        if (w == 0) offdiag_tile(A, Tm, 3, 0);
+        __syncthreads();
+        for (int idx = tid; idx < CH * 16; idx += NTHR) {
+            const int r = idx >> 4, c4 = idx & 15;
+            if (r < n)
+                *reinterpret_cast<f32x4 *>(p.Tm + ((ts + r) * p.Hv + hv) * CH + 4 * c4) =
+                    *reinterpret_cast<const f32x4 *>(Tm + r * LDF + 4 * c4);
+        }
+        __syncthreads();
+    }
+}
+
+template <typename In, int KD>
+size_t prep_smem() {
+    return sizeof(In) * CH * (KD + Vec16<In>::n) + sizeof(float) * (3 * CH * LDF + 2 * CH);
+}
+
+template <typename In, int KD>
+hipError_t launch_prep_t(const PrepParams &p, int n_chunks_ub, hipStream_t s) {
+    const size_t smem = prep_smem<In, KD>();
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&prep_kernel<In, KD>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    (void)attr;  // a refusal shows up as a launch error below
+    dim3 grid(n_chunks_ub, p.Hq);
+    hipLaunchKernelGGL((prep_kernel<In, KD>), grid, dim3(NTHR), smem, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- W, U
+// Materialises W = T diag(beta e^gam) K and U = T diag(beta) V in fp32 (a
+// check of the algebra; not used by the forward itself).
+template <typename In>
+__global__ __launch_bounds__(NTHR) void wu_kernel(const WUParams p) {
+    const int gid = blockIdx.x, hv = blockIdx.y;
+    int j, c;
+    if (!p.sm.locate(gid, j, c)) return;
+    int64_t bos, eos;
+    p.sm.bounds(j, bos, eos);
+    const int64_t ts = bos + (int64_t)c * CH;
+    const int n = (int)min<int64_t>(CH, eos - ts);
+    const int hq = hv / (p.Hv / p.Hq);
+    const In *kp = reinterpret_cast<const In *>(p.k);
+    const In *vp = reinterpret_cast<const In *>(p.v);
+    for (int idx = threadIdx.x; idx < n * (p.K + p.V); idx += NTHR) {
+        const int r = idx / (p.K + p.V), col = idx % (p.K + p.V);
+        const bool isw = col < p.K;
+        float acc = 0.f;
+        for (int i = 0; i <= r; ++i) {
+            const float t = p.Tm[((ts + r) * p.Hv + hv) * CH + i];
+            const float b = p.beta[(ts + i) * p.Hv + hv];
+            if (isw)
+                acc += t * b * expf(p.g_cum[(ts + i) * p.Hv + hv]) *
+                       to_f32(kp[((ts + i) * p.Hq + hq) * p.K + col]);
+            else
+                acc += t * b * to_f32(vp[((ts + i) * p.Hv + hv) * p.V + col - p.K]);
+        }
+        if (isw)
+            p.w[((ts + r) * p.Hv + hv) * p.K + col] = acc;
+        else
+            p.u[((ts + r) * p.Hv + hv) * p.V + col - p.K] = acc;
+    }
+}
+
+// chunk offsets of packed sequences: chunk_off[j] = sum_{i<j} ceil(len_i/64)
+__global__ void chunk_offsets_kernel(const int32_t *cu, int32_t *off, int n_seq) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        int32_t acc = 0;
+        for (int j = 0; j < n_seq; ++j) {
+            off[j] = acc;
+            acc += (cu[j + 1] - cu[j] + CH - 1) / CH;
+        }
+        off[n_seq] = acc;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_offsets(const int32_t *cu, int32_t *chunk_off, int n_seq, hipStream_t s) {
+    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, s, cu, chunk_off, n_seq);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep(Dt dt, int K, const PrepParams &p, int n_chunks_ub, hipStream_t s) {
+    if (dt == Dt::BF16)
+        return K == 128 ? launch_prep_t<bf16, 128>(p, n_chunks_ub, s) : launch_prep_t<bf16, 64>(p, n_chunks_ub, s);
+    return K == 128 ? launch_prep_t<float, 128>(p, n_chunks_ub, s) : launch_prep_t<float, 64>(p, n_chunks_ub, s);
+}
+
+hipError_t launch_wu(Dt dt, const WUParams &p, int n_chunks_ub, hipStream_t s) {
+    dim3 grid(n_chunks_ub, p.Hv);
+    if (dt == Dt::BF16)
+        hipLaunchKernelGGL(wu_kernel<bf16>, grid, dim3(NTHR), 0, s, p);
+    else
+        hipLaunchKernelGGL(wu_kernel<float>, grid, dim3(NTHR), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace gdr

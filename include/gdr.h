@@ -1,0 +1,151 @@
+/*
+ * gdr.h — C ABI of libgdr, the MI355X (gfx950) gated delta rule operator.
+ *
+ * The operator is the Gated Delta Network chunked prefill that the FlashQLA
+ * pages centre on ("Main functions" on the aiboss88 page; "Introduction" and
+ * "Usage" in the PyPI README).  Per (sequence, v-head) it evaluates
+ *
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = scale * S_t q_t,
+ *
+ * with the state stored as h = S^T (K x V, the README's state shape
+ * [.., H_v, K, V]).  q/k head hq serves v heads hv with hv / (H_v/H_q) == hq.
+ * Evaluation is chunked (64 tokens): an in-chunk cumulative log-gate, the
+ * strictly lower decayed beta*K K^T matrix A, T = (I + A)^{-1}, and a serial
+ * scan over chunks that produces the chunk-start states and the output.
+ *
+ * Argument names and order follow the README's low-level API,
+ *     g, A, o, h, final_state = chunk_gated_delta_rule_fwd(q, k, v, g, beta,
+ *                                   scale, initial_state, cu_seqlens)
+ *     dq, dk, dv, db, dg, dh0 = chunk_gated_delta_rule_bwd(q, k, v, g, beta,
+ *                                   A, do, dht, scale, initial_state, cu_seqlens)
+ * where the forward's returned g is the in-chunk cumulative log-gate and A is
+ * T, one 64-wide row per token.
+ *
+ * Conventions (all entry points):
+ *  - Every pointer in an args struct is a DEVICE pointer unless stated; all
+ *    tensors are contiguous row-major in the layouts given, 16-byte aligned.
+ *  - The caller allocates and owns every buffer, including the workspace.
+ *    The library allocates nothing, holds no state between calls, never
+ *    synchronises the stream and never reads device memory on the host.
+ *    Calls on different streams may run concurrently if their buffers do
+ *    not overlap.
+ *  - Validation happens on the host before any launch.  A non-zero return
+ *    means nothing was launched (GDR_ELAUNCH: a launch failed part way).
+ *  - NaN/Inf inputs are not checked; they propagate.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+#define GDR_CHUNK 64
+
+/* return codes */
+#define GDR_OK 0
+#define GDR_EINVAL -1     /* null required pointer, bad size, misalignment, H_v % H_q != 0, B != 1 with cu_seqlens */
+#define GDR_ENOTSUP -2    /* K or V not in {64, 128}; unsupported dtype */
+#define GDR_EWORKSPACE -3 /* workspace_bytes below what gdr_*_workspace reports */
+#define GDR_ELAUNCH -4    /* a HIP launch failed */
+
+/* element types */
+#define GDR_BF16 0
+#define GDR_F32 1
+
+/* sequence-split ("AutoCP") modes of the forward */
+#define GDR_CP_AUTO 0   /* split when B*H_v <= 40, or B*H_v <= 56 and T >= 8192 */
+#define GDR_CP_OFF 1    /* exact scan, one segment per sequence */
+#define GDR_CP_WARMUP 2 /* always split; each segment warms up from a zero state */
+
+typedef struct {
+    /* sizes.  With cu_seqlens, B must be 1, T is the packed token count and
+       n_seq the number of sequences; otherwise n_seq is ignored (= B). */
+    int64_t B, T, H_q, H_v, K, V, n_seq;
+    int32_t dtype;     /* element type of q, k, v: GDR_BF16 or GDR_F32 */
+    int32_t out_dtype; /* element type of o: GDR_F32 or GDR_BF16 */
+    float scale;       /* output scale, usually K^-1/2 */
+    int32_t cp_mode;           /* GDR_CP_* */
+    int32_t cp_segment_chunks; /* split mode: chunks per segment, 0 = ceil(sqrt(chunks)) */
+    int32_t cp_warmup_chunks;  /* split mode: warm-up window in chunks, 0 = 8 */
+    /* inputs */
+    const void *q;              /* [B,T,H_q,K] dtype */
+    const void *k;              /* [B,T,H_q,K] dtype; each row should have unit L2 norm */
+    const void *v;              /* [B,T,H_v,V] dtype */
+    const float *g;             /* [B,T,H_v] per-token log-decay (<= 0 for decay) */
+    const float *beta;          /* [B,T,H_v] */
+    const float *initial_state; /* [N,H_v,K,V], N = B or n_seq; NULL = zeros */
+    const int32_t *cu_seqlens;  /* [n_seq+1] monotone token offsets, or NULL */
+    /* outputs */
+    void *o;                    /* [B,T,H_v,V] out_dtype */
+    float *final_state;         /* [N,H_v,K,V]; NULL = not wanted */
+    float *g_cum;               /* [B,T,H_v] in-chunk cumulative log-gate; NULL = kept in workspace */
+    float *A;                   /* [B,T,H_v,64] row r of the token's chunk of T = (I+A)^{-1},
+                                   zero past the chunk end; NULL = kept in workspace */
+    float *h;                   /* [NT,H_v,K,V] chunk-start states (NT = sum of ceil(len/64));
+                                   NULL = not written */
+    float *w_out;               /* [B,T,H_v,K] W = T diag(beta e^g_cum) K, NULL = not computed */
+    float *u_out;               /* [B,T,H_v,V] U = T diag(beta) V, NULL = not computed */
+    /* scratch */
+    void *workspace;
+    size_t workspace_bytes;
+} gdr_fwd_args;
+
+typedef struct {
+    int64_t B, T, H_q, H_v, K, V, n_seq;
+    int32_t dtype;    /* element type of q, k, v, do, dq, dk, dv */
+    float scale;
+    const void *q, *k, *v;      /* as in gdr_fwd_args */
+    const float *g_cum;         /* [B,T,H_v] the forward's g_cum */
+    const float *beta;          /* [B,T,H_v] */
+    const float *A;             /* [B,T,H_v,64] the forward's A */
+    const void *dout;           /* [B,T,H_v,V] gradient of o, dtype */
+    const float *dht;           /* [N,H_v,K,V] gradient of final_state; NULL = zeros */
+    const float *initial_state; /* [N,H_v,K,V] or NULL */
+    const int32_t *cu_seqlens;  /* [n_seq+1] or NULL */
+    void *dq, *dk;              /* [B,T,H_q,K] dtype, summed over the v heads of each q/k head */
+    void *dv;                   /* [B,T,H_v,V] dtype */
+    float *dbeta;               /* [B,T,H_v] gradient w.r.t. beta */
+    float *dg;                  /* [B,T,H_v] gradient w.r.t. the raw per-token g */
+    float *dh0;                 /* [N,H_v,K,V]; NULL = not wanted (required to be NULL when
+                                   initial_state is NULL is not enforced: zeros are used) */
+    void *workspace;
+    size_t workspace_bytes;
+} gdr_bwd_args;
+
+/* GDR_ABI_VERSION of the loaded library. */
+int gdr_abi_version(void);
+
+/* Static description of a return code ("ok", "invalid argument", ...). */
+const char *gdr_strerror(int code);
+
+/* Workspace bytes gdr_fwd needs for these sizes and options (pointers are
+   not read).  Returns GDR_OK or a validation error. */
+int gdr_fwd_workspace(const gdr_fwd_args *args, size_t *bytes);
+
+/* Forward chunked prefill on `stream`.  Computes o (and the optional
+   outputs).  Chunks never cross a sequence boundary; the last chunk of a
+   sequence may be partial; an empty sequence copies initial_state to
+   final_state.  In split mode the chunk-start states and the output of
+   segments after the first are the warm-up approximation (exact when the
+   window reaches the start of the sequence). */
+int gdr_fwd(const gdr_fwd_args *args, hipStream_t stream);
+
+/* Workspace bytes gdr_bwd needs. */
+int gdr_bwd_workspace(const gdr_bwd_args *args, size_t *bytes);
+
+/* Backward of the exact forward: gradients of <dout, o> + <dht, final_state>. */
+int gdr_bwd(const gdr_bwd_args *args, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

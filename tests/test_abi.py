@@ -1,0 +1,119 @@
+"""The C ABI of libgdr without a GPU: exports, struct layout, host-side errors.
+
+Only calls that return before any HIP work are made here (version, error
+strings, workspace sizing, argument validation).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from gated_delta_rule_85_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdr_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert {"gdr_fwd", "gdr_bwd", "gdr_fwd_workspace", "gdr_bwd_workspace", "gdr_strerror",
+            "gdr_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(L.lib, n), n
+
+
+def test_version_and_strings(L):
+    assert L.abi_version() == L.ABI_VERSION
+    assert L.strerror(0) == "ok"
+    assert L.strerror(-3) == "workspace too small"
+    assert L.strerror(12345) == "unknown error"
+
+
+def _struct_offsets_from_c(tmp_path, struct, fields):
+    src = tmp_path / "layout.c"
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "gdr.h"', "int main(void){"]
+    lines.append('printf("size %%zu\\n", sizeof(%s));' % struct)
+    for f in fields:
+        lines.append('printf("%s %%zu\\n", offsetof(%s, %s));' % (f, struct, f))
+    lines.append("return 0;}")
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROOT, "include"),
+                    "-I/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    return {k: int(v) for k, v in (l.split() for l in out.splitlines())}
+
+
+@pytest.mark.parametrize("which", ["fwd", "bwd"])
+def test_ctypes_layout_matches_header(L, tmp_path, which):
+    st = L.FwdArgs if which == "fwd" else L.BwdArgs
+    names = [f[0] for f in st._fields_]
+    c = _struct_offsets_from_c(tmp_path, "gdr_%s_args" % which, names)
+    assert c["size"] == ctypes.sizeof(st)
+    for n in names:
+        assert c[n] == getattr(st, n).offset, n
+
+
+def fwd_args(L, **kw):
+    a = L.FwdArgs()
+    a.B, a.T, a.H_q, a.H_v, a.K, a.V, a.n_seq = 1, 256, 2, 4, 128, 128, 0
+    a.dtype, a.out_dtype, a.scale = L.BF16, L.F32, 0.088
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def rc_ws(L, a):
+    n = ctypes.c_size_t(0)
+    return L.lib.gdr_fwd_workspace(ctypes.byref(a), ctypes.byref(n)), n.value
+
+
+def test_workspace_sizes(L):
+    rc, n = rc_ws(L, fwd_args(L))
+    # g_cum and A kept in the workspace when not supplied, 256-byte aligned
+    assert rc == 0 and n == 256 * 4 * 4 + 256 * 4 * 64 * 4
+    rc, n = rc_ws(L, fwd_args(L, g_cum=16, A=16))
+    assert rc == 0 and n == 0
+    rc, n = rc_ws(L, fwd_args(L, g_cum=16, A=16, cu_seqlens=16, n_seq=3))
+    assert rc == 0 and n == 256
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H_v=3), -1),             # H_v % H_q != 0
+    (dict(K=96), -2),              # unsupported head dim
+    (dict(V=32), -2),
+    (dict(dtype=7), -2),
+    (dict(out_dtype=9), -2),
+    (dict(B=0), -1),
+    (dict(T=-1), -1),
+    (dict(cu_seqlens=16, n_seq=0), -1),
+    (dict(cu_seqlens=16, n_seq=2, B=2), -1),
+    (dict(cp_mode=5), -1),
+    (dict(cp_segment_chunks=-1), -1),
+])
+def test_validation_errors(L, kw, code):
+    rc, _ = rc_ws(L, fwd_args(L, **kw))
+    assert rc == code
+    assert L.lib.gdr_fwd(ctypes.byref(fwd_args(L, **kw)), None) == code
+
+
+def test_fwd_host_errors_before_any_launch(L):
+    a = fwd_args(L)  # all pointers null
+    assert L.lib.gdr_fwd(ctypes.byref(a), None) == L.EINVAL
+    a = fwd_args(L, q=16, k=16, v=16, g=16, beta=16, o=16)
+    assert L.lib.gdr_fwd(ctypes.byref(a), None) == L.EWORKSPACE
+    a = fwd_args(L, q=16, k=16, v=16, g=16, beta=16, o=24, workspace=4096, workspace_bytes=1 << 30)
+    assert L.lib.gdr_fwd(ctypes.byref(a), None) == L.EINVAL  # misaligned o
+    with pytest.raises(L.GdrError):
+        L.fwd_workspace(fwd_args(L, K=48))
