@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
 ABI_VERSION = 1
 CHUNK = 64
+FWD_STAGES = 3
 
 OK, EINVAL, ENOTSUP, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
@@ -32,7 +33,7 @@ class FwdArgs(ctypes.Structure):
         ("q", _p), ("k", _p), ("v", _p), ("g", _p), ("beta", _p), ("initial_state", _p),
         ("cu_seqlens", _p),
         ("o", _p), ("final_state", _p), ("g_cum", _p), ("A", _p), ("h", _p),
-        ("w_out", _p), ("u_out", _p),
+        ("w_out", _p), ("u_out", _p), ("events", _p),
         ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
     ]
 

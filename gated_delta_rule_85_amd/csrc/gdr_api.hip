@@ -18,7 +18,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct FwdPlan {
     int64_t n_seq, tokens, nct, nt_ub;  // nct: chunks per sequence bound
-    size_t off_chunk, off_gcum, off_A, total;
+    size_t off_chunk, off_tblk, total;
     int seg_chunks, warm_chunks, n_seg;
     bool split;
 };
@@ -50,10 +50,8 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl) {
     size_t off = 0;
     pl.off_chunk = off;
     if (varlen) off += up(sizeof(int32_t) * (size_t)(pl.n_seq + 1));
-    pl.off_gcum = off;
-    if (!a->g_cum) off += up(sizeof(float) * (size_t)(pl.tokens * a->H_v));
-    pl.off_A = off;
-    if (!a->A) off += up(sizeof(float) * (size_t)(pl.tokens * a->H_v * GDR_CHUNK));
+    pl.off_tblk = off;
+    off += up(tblock_bytes(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32) * (size_t)(pl.nt_ub * a->H_v));
     pl.total = off;
     // sequence split ("AutoCP"): the pages' trigger on batch x heads and length
     const int64_t bh = pl.n_seq * a->H_v;
@@ -129,33 +127,36 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
 
     char *ws = static_cast<char *>(a->workspace);
     int32_t *chunk_off = a->cu_seqlens ? reinterpret_cast<int32_t *>(ws + pl.off_chunk) : nullptr;
-    float *g_cum = a->g_cum ? a->g_cum : reinterpret_cast<float *>(ws + pl.off_gcum);
-    float *Tm = a->A ? a->A : reinterpret_cast<float *>(ws + pl.off_A);
+    char *tblk = ws + pl.off_tblk;
     const Dt dt = a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
     const Dt ot = a->out_dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
     const SeqMap sm = make_map(a, pl, chunk_off);
 
+    auto mark = [&](int i) {
+        return !a->events || hipEventRecord(a->events[i], stream) == hipSuccess;
+    };
     if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, chunk_off, (int)pl.n_seq, stream) != hipSuccess)
         return GDR_ELAUNCH;
+    if (!mark(0)) return GDR_ELAUNCH;
     if (pl.tokens > 0) {
         PrepParams pp;
         pp.k = a->k;
         pp.g = a->g;
         pp.beta = a->beta;
-        pp.g_cum = g_cum;
-        pp.Tm = Tm;
+        pp.g_cum = a->g_cum;
+        pp.Tm = a->A;
+        pp.tblk = tblk;
         pp.sm = sm;
         pp.Hq = (int)a->H_q;
         pp.Hv = (int)a->H_v;
         if (launch_prep(dt, (int)a->K, pp, (int)pl.nt_ub, stream) != hipSuccess) return GDR_ELAUNCH;
     }
+    if (!mark(1) || !mark(2)) return GDR_ELAUNCH;
     ScanParams sp;
     sp.q = a->q;
     sp.k = a->k;
     sp.v = a->v;
-    sp.Tm = Tm;
-    sp.g_cum = g_cum;
-    sp.beta = a->beta;
+    sp.tblk = tblk;
     sp.h0 = a->initial_state;
     sp.o = a->o;
     sp.hT = a->final_state;
@@ -171,13 +172,13 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
     sp.n_units = (int)(pl.n_seq * a->H_v);
     sp.n_seg = pl.n_seg;
     if (launch_scan_output(dt, ot, (int)a->K, (int)a->V, sp, stream) != hipSuccess) return GDR_ELAUNCH;
+    if (!mark(3) || !mark(4)) return GDR_ELAUNCH;
     if ((a->w_out || a->u_out) && pl.tokens > 0) {
         if (!a->w_out || !a->u_out) return GDR_EINVAL;
         WUParams wp;
         wp.k = a->k;
         wp.v = a->v;
-        wp.Tm = Tm;
-        wp.g_cum = g_cum;
+        wp.tblk = tblk;
         wp.beta = a->beta;
         wp.w = a->w_out;
         wp.u = a->u_out;
@@ -188,6 +189,7 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
         wp.V = (int)a->V;
         if (launch_wu(dt, wp, (int)pl.nt_ub, stream) != hipSuccess) return GDR_ELAUNCH;
     }
+    if (!mark(5)) return GDR_ELAUNCH;
     return GDR_OK;
 }
 

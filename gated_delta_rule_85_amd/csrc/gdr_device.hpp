@@ -118,9 +118,22 @@ template <> struct Ops<float> {
 // split-operand storage in LDS for an fp32 matrix that is read as an A
 // operand (row r, 4 consecutive k).  bf16 path: two bf16 planes; fp32 path:
 // one fp32 plane.
+template <typename In> struct SplitPlaneT { typedef bf16 type; };
+template <> struct SplitPlaneT<float> { typedef float type; };
+
 template <typename In> struct SplitPlane;
 template <> struct SplitPlane<bf16> {
     bf16 *hi, *lo;
+    // operand from byte offsets of k block 0 and k block 1 in both planes
+    __device__ __forceinline__ OpS get_bytes(int b0, int b1) const {
+        const char *H = reinterpret_cast<const char *>(hi), *Lo = reinterpret_cast<const char *>(lo);
+        OpS r;
+        r.h0 = *reinterpret_cast<const bf16x4 *>(H + b0);
+        r.h1 = *reinterpret_cast<const bf16x4 *>(H + b1);
+        r.l0 = *reinterpret_cast<const bf16x4 *>(Lo + b0);
+        r.l1 = *reinterpret_cast<const bf16x4 *>(Lo + b1);
+        return r;
+    }
     __device__ __forceinline__ void put4(int off, f32x4 x) const {
         bf16x4 h, l;
         split4(x, h, l);
@@ -138,6 +151,13 @@ template <> struct SplitPlane<bf16> {
 };
 template <> struct SplitPlane<float> {
     float *hi, *lo;  // lo unused
+    __device__ __forceinline__ OpF get_bytes(int b0, int b1) const {
+        const char *H = reinterpret_cast<const char *>(hi);
+        OpF r;
+        r.b0 = *reinterpret_cast<const f32x4 *>(H + b0);
+        r.b1 = *reinterpret_cast<const f32x4 *>(H + b1);
+        return r;
+    }
     __device__ __forceinline__ void put4(int off, f32x4 x) const {
         *reinterpret_cast<f32x4 *>(hi + off) = x;
     }

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "gdr_device.hpp"
+#include "gdr_layout.hpp"
 
 namespace gdr {
 
@@ -15,8 +16,9 @@ enum class Dt : int { BF16 = 0, F32 = 1 };
 struct PrepParams {
     const void *k;
     const float *g, *beta;
-    float *g_cum;  // [tokens, H_v]
-    float *Tm;     // [tokens, H_v, 64]
+    float *g_cum;  // [tokens, H_v] or null
+    float *Tm;     // [tokens, H_v, 64] or null
+    char *tblk;    // [chunks, H_v] T blocks (gdr_layout.hpp)
     SeqMap sm;
     int Hq, Hv;
 };
@@ -25,7 +27,7 @@ struct PrepParams {
 // chunks with the output of each chunk.
 struct ScanParams {
     const void *q, *k, *v;
-    const float *Tm, *g_cum, *beta;
+    const char *tblk;  // [chunks, H_v] T blocks from gdr_chunk_prep
     const float *h0;  // [N, H_v, K, V] or null
     void *o;          // [tokens, H_v, V]
     float *hT;        // [N, H_v, K, V] or null
@@ -41,7 +43,8 @@ struct ScanParams {
 // optional materialisation of W = T diag(beta e^gam) K and U = T diag(beta) V
 struct WUParams {
     const void *k, *v;
-    const float *Tm, *g_cum, *beta;
+    const char *tblk;
+    const float *beta;
     float *w, *u;
     SeqMap sm;
     int Hq, Hv, K, V;
@@ -51,6 +54,7 @@ hipError_t launch_chunk_offsets(const int32_t *cu, int32_t *chunk_off, int n_seq
 hipError_t launch_prep(Dt dt, int K, const PrepParams &p, int n_chunks_ub, hipStream_t s);
 hipError_t launch_scan_output(Dt dt, Dt out, int K, int V, const ScanParams &p, hipStream_t s);
 hipError_t launch_wu(Dt dt, const WUParams &p, int n_chunks_ub, hipStream_t s);
+size_t tblock_bytes(Dt dt);
 int scan_vtile(Dt dt, int K, int V);  // V columns per scan workgroup
 
 }  // namespace gdr

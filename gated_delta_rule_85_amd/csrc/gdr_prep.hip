@@ -8,6 +8,9 @@
 // Friendly Algebraic Reformulation" (computing the A matrix, then W and U);
 // W = T diag(beta e^gam) K and U = T diag(beta) V are not stored: the scan
 // kernel applies T to V - diag(e^gam) K h directly (U - W h in one product).
+// For the scan it writes one T block per (chunk, v head), the LDS image the
+// scan copies in (gdr_layout.hpp): T split into bf16 hi/lo planes (fp32 for
+// fp32 inputs) with swizzled rows, and the chunk's gate scalars.
 //
 // K K^T depends only on the q/k head, so it is formed once per workgroup on
 // MFMA and reused by the H_v/H_q v heads.  The inverse of the unit lower
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
             }
             gam[l] = x;
             bet[l] = l < n ? p.beta[(ts + l) * p.Hv + hv] : 0.f;
-            if (l < n) p.g_cum[(ts + l) * p.Hv + hv] = x;
+            if (l < n && p.g_cum) p.g_cum[(ts + l) * p.Hv + hv] = x;
         }
         __syncthreads();
         for (int idx = tid; idx < CH * CH; idx += NTHR) {
@@ -151,11 +154,45 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
         __syncthreads();
         if (w == 0) offdiag_tile(A, Tm, 3, 0);
         __syncthreads();
-        for (int idx = tid; idx < CH * 16; idx += NTHR) {
-            const int r = idx >> 4, c4 = idx & 15;
-            if (r < n)
-                *reinterpret_cast<f32x4 *>(p.Tm + ((ts + r) * p.Hv + hv) * CH + 4 * c4) =
-                    *reinterpret_cast<const f32x4 *>(Tm + r * LDF + 4 * c4);
+        if (p.Tm) {
+            for (int idx = tid; idx < CH * 16; idx += NTHR) {
+                const int r = idx >> 4, c4 = idx & 15;
+                if (r < n)
+                    *reinterpret_cast<f32x4 *>(p.Tm + ((ts + r) * p.Hv + hv) * CH + 4 * c4) =
+                        *reinterpret_cast<const f32x4 *>(Tm + r * LDF + 4 * c4);
+            }
+        }
+        // T block for the scan: swizzled planes (rows past the chunk end zero) + scalars
+        {
+            using TB = TBlock<In>;
+            using SW = Swz<TB::ROWB>;
+            char *blk = p.tblk + ((int64_t)gid * p.Hv + hv) * TB::BYTES;
+            constexpr int EPC = 16 / (TB::BF ? 2 : 4);  // elements per 16-byte chunk
+            for (int idx = tid; idx < CH * SW::CPR; idx += NTHR) {
+                const int r = idx / SW::CPR, pc = idx % SW::CPR, lc = SW::chunk(r, pc);
+                f32x4 x0 = zero4(), x1 = zero4();
+                if (r < n) {
+                    x0 = *reinterpret_cast<const f32x4 *>(Tm + r * LDF + EPC * lc);
+                    if constexpr (TB::BF) x1 = *reinterpret_cast<const f32x4 *>(Tm + r * LDF + EPC * lc + 4);
+                }
+                if constexpr (TB::BF) {
+                    bf16x4 h0, l0, h1, l1;
+                    split4(x0, h0, l0);
+                    split4(x1, h1, l1);
+                    *reinterpret_cast<bf16x8 *>(blk + r * TB::ROWB + 16 * pc) = cat(h0, h1);
+                    *reinterpret_cast<bf16x8 *>(blk + TB::PLANE + r * TB::ROWB + 16 * pc) = cat(l0, l1);
+                } else {
+                    *reinterpret_cast<f32x4 *>(blk + r * TB::ROWB + 16 * pc) = x0;
+                }
+            }
+            if (tid < CH) {
+                float *sc = reinterpret_cast<float *>(blk + TB::SC);
+                const float gl = gam[n - 1];
+                sc[tid] = gam[tid];
+                sc[CH + tid] = fast_exp(gam[tid]);
+                sc[2 * CH + tid] = fast_exp(gl - gam[tid]);
+                sc[3 * CH + tid] = bet[tid];
+            }
         }
         __syncthreads();
     }
@@ -182,6 +219,18 @@ hipError_t launch_prep_t(const PrepParams &p, int n_chunks_ub, hipStream_t s) {
 // Materialises W = T diag(beta e^gam) K and U = T diag(beta) V in fp32 (a
 // check of the algebra; not used by the forward itself).
 template <typename In>
+__device__ __forceinline__ float tblock_T(const char *blk, int r, int i) {
+    using TB = TBlock<In>;
+    using SW = Swz<TB::ROWB>;
+    const int byte = i * (TB::BF ? 2 : 4);
+    if constexpr (TB::BF)
+        return to_f32(*reinterpret_cast<const bf16 *>(blk + SW::off(r, byte))) +
+               to_f32(*reinterpret_cast<const bf16 *>(blk + TB::PLANE + SW::off(r, byte)));
+    else
+        return *reinterpret_cast<const float *>(blk + SW::off(r, byte));
+}
+
+template <typename In>
 __global__ __launch_bounds__(NTHR) void wu_kernel(const WUParams p) {
     const int gid = blockIdx.x, hv = blockIdx.y;
     int j, c;
@@ -193,16 +242,17 @@ __global__ __launch_bounds__(NTHR) void wu_kernel(const WUParams p) {
     const int hq = hv / (p.Hv / p.Hq);
     const In *kp = reinterpret_cast<const In *>(p.k);
     const In *vp = reinterpret_cast<const In *>(p.v);
+    const char *blk = p.tblk + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES;
+    const float *sc = reinterpret_cast<const float *>(blk + TBlock<In>::SC);
     for (int idx = threadIdx.x; idx < n * (p.K + p.V); idx += NTHR) {
         const int r = idx / (p.K + p.V), col = idx % (p.K + p.V);
         const bool isw = col < p.K;
         float acc = 0.f;
         for (int i = 0; i <= r; ++i) {
-            const float t = p.Tm[((ts + r) * p.Hv + hv) * CH + i];
-            const float b = p.beta[(ts + i) * p.Hv + hv];
+            const float t = tblock_T<In>(blk, r, i);
+            const float b = sc[3 * CH + i];
             if (isw)
-                acc += t * b * expf(p.g_cum[(ts + i) * p.Hv + hv]) *
-                       to_f32(kp[((ts + i) * p.Hq + hq) * p.K + col]);
+                acc += t * b * sc[CH + i] * to_f32(kp[((ts + i) * p.Hq + hq) * p.K + col]);
             else
                 acc += t * b * to_f32(vp[((ts + i) * p.Hv + hv) * p.V + col - p.K]);
         }
@@ -237,6 +287,8 @@ hipError_t launch_prep(Dt dt, int K, const PrepParams &p, int n_chunks_ub, hipSt
         return K == 128 ? launch_prep_t<bf16, 128>(p, n_chunks_ub, s) : launch_prep_t<bf16, 64>(p, n_chunks_ub, s);
     return K == 128 ? launch_prep_t<float, 128>(p, n_chunks_ub, s) : launch_prep_t<float, 64>(p, n_chunks_ub, s);
 }
+
+size_t tblock_bytes(Dt dt) { return dt == Dt::BF16 ? TBlock<bf16>::BYTES : TBlock<float>::BYTES; }
 
 hipError_t launch_wu(Dt dt, const WUParams &p, int n_chunks_ub, hipStream_t s) {
     dim3 grid(n_chunks_ub, p.Hv);

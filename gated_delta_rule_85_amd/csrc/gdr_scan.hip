@@ -1,10 +1,10 @@
 // gdr_scan_output — the serial inter-chunk scan fused with the output.
 //
-// One workgroup owns one (sequence, v-head, block of BV value columns) and
-// walks the chunks of its segment in order, keeping the K x BV slice of the
-// state h in registers (fp32, accumulator order; wave w holds columns
-// [16*NCT*w, 16*NCT*(w+1)) of the block).  For a chunk of n tokens with
-// start state h (the chunked form of the gated delta rule):
+// One workgroup owns one (sequence, v-head, block of 64 value columns) and
+// walks the chunks of its segment in order.  Wave w keeps columns
+// [16w, 16w+16) of the block of the K x V state h in registers (fp32,
+// accumulator order).  For a chunk of n tokens with start state h (the
+// chunked form of the gated delta rule):
 //
 //   X  = beta * (V - diag(e^gam) K h)          (delta-rule target before the
 //                                                in-chunk correction)
@@ -14,9 +14,19 @@
 //   O  = scale (diag(e^gam) Q h + P U~),  P = tril(Q K^T) * exp(gam_r - gam_i)
 //   h' = e^{gam_last} h + K^T (exp(gam_last - gam) * U~)
 //
-// T comes from gdr_chunk_prep.  Columns of h evolve independently, so the
-// value dimension is split across workgroups.  Products with fp32 operands
-// use split-bf16 MFMA (see gdr_device.hpp); accumulation is fp32.
+// T (split into bf16 hi/lo planes) and the gate scalars come from
+// gdr_chunk_prep as one LDS image per (chunk, v head).  Columns of h evolve
+// independently, so waves never exchange state; the four waves share the
+// decayed scores P through LDS (each forms some of its ten 16x16 tiles as
+// K Q^T, whose accumulator layout is P's A operand).  Products with fp32
+// operands use split-bf16 MFMA (gdr_device.hpp); accumulation is fp32.
+//
+// Data movement: K, Q, the V columns and the T block of the next chunk are
+// copied global -> LDS by the waves' direct-to-LDS loads while the current
+// chunk computes (two LDS buffers, bf16 inputs), into XOR-swizzled rows
+// (gdr_layout.hpp).  The K^T operand of the state update and the V columns
+// are read with the gfx950 transposing LDS read.  The output chunk is staged
+// in LDS and written with 16-byte stores during the next chunk.
 //
 // Sequence split (the pages' AutoCP with its sliding-window warm-up): with
 // seg_chunks smaller than the sequence, segment s > 0 starts from a zero
@@ -29,390 +39,417 @@ namespace gdr {
 
 namespace {
 
-template <typename In> struct PlaneT { typedef bf16 type; static constexpr int planes = 2; };
-template <> struct PlaneT<float> { typedef float type; static constexpr int planes = 1; };
+constexpr int BV = 64;  // value columns per workgroup (16 per wave)
 
-template <typename In, int KD, int NCT> struct ScanLayout {
-    static constexpr int BV = 64 * NCT;
-    static constexpr int EV = Vec16<In>::n;
-    static constexpr int LDK = KD + EV;   // K, Q rows
-    static constexpr int LDV = BV + EV;   // V rows
-    typedef typename PlaneT<In>::type P;
-    static constexpr int LDT = CH + 16 / (int)sizeof(P);  // T, P planes
-    static constexpr size_t ks = 0;
-    static constexpr size_t qs = ks + sizeof(In) * CH * LDK;
-    static constexpr size_t vs = qs + sizeof(In) * CH * LDK;
-    static constexpr size_t tp = vs + sizeof(In) * CH * LDV;
-    static constexpr size_t pp = tp + sizeof(P) * CH * LDT * PlaneT<In>::planes;
-    static constexpr size_t sc = pp + sizeof(P) * CH * LDT * PlaneT<In>::planes;
-    static constexpr size_t bytes = sc + sizeof(float) * 4 * CH;
-    // per-thread prefetch counts
-    static constexpr int NK = CH * (KD / EV) / NTHR;
-    static constexpr int NV = CH * (BV / EV) / NTHR;
-    static constexpr int NT = CH * 16 / NTHR;
-    static_assert(NK * NTHR == CH * (KD / EV), "K tiling");
-    static_assert(NV * NTHR == CH * (BV / EV), "V tiling");
-};
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-template <typename In> __device__ __forceinline__ SplitPlane<In> plane(char *base, int ldt) {
-    typedef typename PlaneT<In>::type P;
-    SplitPlane<In> sp;
-    sp.hi = reinterpret_cast<P *>(base);
-    sp.lo = reinterpret_cast<P *>(base) + CH * ldt;
-    return sp;
+// wave-wide copy of 64 x 16 bytes: lane l's source -> lds_base + 16 l
+__device__ __forceinline__ void dma16(const void *src, char *lds_base) {
+    __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// gfx950 transposing LDS read: within each 16-lane group, lane i receives
+// element i%4 of the 8-byte chunks read by source lanes i/4 + 4j, j = 0..3.
+__device__ __forceinline__ bf16x4 lds_tr4(const char *p) {
+    v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
+    return __builtin_bit_cast(bf16x4, v);
 }
 
-// A operand of K^T (rows = key dims d0 + lane, k = tokens 32*ip ..), gathered
-// from the token-major K tile.
-template <typename In>
-__device__ __forceinline__ typename Ops<In>::X gather_kt(const In *Ks, int ldk, int d, int ip) {
-    const int g = lg4();
-    const In *b0 = Ks + (32 * ip + 4 * g) * ldk + d;
-    const In *b1 = b0 + 16 * ldk;
+template <typename In, int KD> struct Cfg {
+    static constexpr bool BF = sizeof(In) == 2;
+    static constexpr int NB = BF ? 2 : 1;          // LDS buffers
+    static constexpr int ES = sizeof(In);
+    static constexpr int EV = 16 / ES;             // elements per 16-byte chunk
+    static constexpr int KROW = KD * ES, VROW = BV * ES;
+    static constexpr int KT = CH * KROW, VT = CH * VROW;
+    using TB = TBlock<In>;
+    static constexpr int OFF_K = 0, OFF_Q = KT, OFF_V = 2 * KT, OFF_T = 2 * KT + VT;
+    static constexpr int BUF = OFF_T + TB::BYTES;
+    static constexpr int PROW = CH * (BF ? 2 : 4);  // score plane row bytes
+    static constexpr int PBYTES = CH * PROW * (BF ? 2 : 1);
+    static constexpr int LDO = BV + 4;
+    static constexpr int NKI = KT / 1024, NVI = VT / 1024, NTI = TB::BYTES / 1024;
+    static_assert(NKI % 4 == 0 && NVI % 4 == 0, "tile copies spread over 4 waves");
+    static constexpr int DT = KD / 16, DP = KD / 32;
+};
+
+// A-operand fragment rows (row0 + lane16, bytes off..off+7 and off+32..) of a swizzled tile
+template <typename In, int ROWB>
+__device__ __forceinline__ typename Ops<In>::X frag(const char *tile, int row, int byte) {
+    using S = Swz<ROWB>;
+    return Ops<In>::load(reinterpret_cast<const In *>(tile + S::off(row, byte)),
+                         reinterpret_cast<const In *>(tile + S::off(row, byte + 16 * sizeof(In))));
+}
+
+// 4 consecutive rows r0+4g..r0+4g+3 of column c0+lane16, as the B operand of
+// an accumulator-ordered tile expects
+template <typename In, int ROWB>
+__device__ __forceinline__ f32x4 rows4(const char *tile, int r0, int c0) {
+    using S = Swz<ROWB>;
+    const int n = ln16(), g = lg4();
+    if constexpr (sizeof(In) == 2) {
+        const bf16x4 v = lds_tr4(tile + S::off(r0 + 4 * g + (n >> 2), 2 * (c0 + 4 * (n & 3))));
+        return __builtin_convertvector(v, f32x4);
+    } else {
+        f32x4 r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            r[j] = *reinterpret_cast<const float *>(tile + S::off(r0 + 4 * g + j, 4 * (c0 + n)));
+        return r;
+    }
+}
+
+// A operand of K^T: rows = key dims d0 + lane16, k = tokens 32 ip .. 32 ip + 31
+template <typename In, int ROWB>
+__device__ __forceinline__ typename Ops<In>::X kt_operand(const char *Ks, int d0, int ip) {
     typename Ops<In>::X r;
     if constexpr (sizeof(In) == 2) {
-        r.b0 = bf16x4{b0[0], b0[ldk], b0[2 * ldk], b0[3 * ldk]};
-        r.b1 = bf16x4{b1[0], b1[ldk], b1[2 * ldk], b1[3 * ldk]};
+        using S = Swz<ROWB>;
+        const int n = ln16(), g = lg4();
+        const int row = 32 * ip + 4 * g + (n >> 2), byte = 2 * (d0 + 4 * (n & 3));
+        r.b0 = lds_tr4(Ks + S::off(row, byte));
+        r.b1 = lds_tr4(Ks + S::off(row + 16, byte));
     } else {
-        r.b0 = f32x4{b0[0], b0[ldk], b0[2 * ldk], b0[3 * ldk]};
-        r.b1 = f32x4{b1[0], b1[ldk], b1[2 * ldk], b1[3 * ldk]};
+        r.b0 = rows4<In, ROWB>(Ks, 32 * ip, d0);
+        r.b1 = rows4<In, ROWB>(Ks, 32 * ip + 16, d0);
     }
     return r;
 }
 
-template <typename T> __device__ __forceinline__ void store_out(T *p, float x);
-template <> __device__ __forceinline__ void store_out<float>(float *p, float x) { *p = x; }
-template <> __device__ __forceinline__ void store_out<bf16>(bf16 *p, float x) { *p = static_cast<bf16>(x); }
+template <typename T> struct OutVec;
+template <> struct OutVec<float> {
+    static __device__ __forceinline__ void put(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
+};
+template <> struct OutVec<bf16> {
+    static __device__ __forceinline__ void put(bf16 *p, f32x4 x) {
+        *reinterpret_cast<bf16x4 *>(p) = __builtin_convertvector(x, bf16x4);
+    }
+};
 
-template <typename In, typename Out, int KD, int NCT>
-__global__ __launch_bounds__(NTHR) void scan_output_kernel(const ScanParams p) {
-    using L = ScanLayout<In, KD, NCT>;
+template <typename In, typename Out, int KD> struct Scan {
+    using C = Cfg<In, KD>;
     using O = Ops<In>;
     using XT = typename O::X;
     using ST = typename O::S;
-    using V16 = typename Vec16<In>::type;
-    constexpr int EV = L::EV, LDK = L::LDK, LDV = L::LDV, LDT = L::LDT, BV = L::BV;
-    constexpr int DT = KD / 16;  // row tiles of the state
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    In *Ks = reinterpret_cast<In *>(smem + L::ks);
-    In *Qs = reinterpret_cast<In *>(smem + L::qs);
-    In *Vs = reinterpret_cast<In *>(smem + L::vs);
-    const SplitPlane<In> Tp = plane<In>(smem + L::tp, LDT);
-    const SplitPlane<In> Pp = plane<In>(smem + L::pp, LDT);
-    float *gam = reinterpret_cast<float *>(smem + L::sc);
-    float *eg = gam + CH, *rr = eg + CH, *bet = rr + CH;
+    using TB = typename C::TB;
+    using SK = Swz<C::KROW>;
+    using SV = Swz<C::VROW>;
+    using ST_ = Swz<TB::ROWB>;
+    using SP = Swz<C::PROW>;
 
-    // ---- work item: (v tile, v head, sequence, segment), XCD-grouped
-    const int wid = xcd_remap(blockIdx.x, gridDim.x);
-    const int vt = wid % p.n_vt;
-    const int rest = wid / p.n_vt;
-    const int unit = rest % p.n_units, seg = rest / p.n_units;
-    const int j = unit / p.Hv, hv = unit % p.Hv;
-    const int G = p.Hv / p.Hq, hq = hv / G;
+    const ScanParams &p;
+    char *buf[2];
+    char *pplane;  // shared score planes (hi, lo)
+    float *Os;     // staged output chunk
+    // work item
+    int vt, unit, j, hv, hq, cb;
     int64_t bos, eos;
-    p.sm.bounds(j, bos, eos);
-    const int N = (int)((eos - bos + CH - 1) / CH);
+    int tid, w, n16, g, colw;
+    const In *qp, *kp, *vp;
+    Out *op;
+    // state slice: h[dt] = rows 16dt+4g+i, column colw+n16
+    f32x4 h[C::DT];
+    // staged output bookkeeping
+    int64_t pend_ts;
+    int pend_n;
+
+    __device__ __forceinline__ Scan(const ScanParams &p_) : p(p_) {}
+
+    // copy chunk c (tokens from ts, n valid) into LDS buffer b
+    __device__ __forceinline__ void issue(int c, char *b) {
+        const int64_t ts = bos + (int64_t)c * CH;
+        const int nm1 = (int)min<int64_t>(CH, eos - ts) - 1;
+        const int l = lane_id();
+#pragma unroll
+        for (int s = 0; s < C::NKI / 4; ++s) {
+            const int i = w + 4 * s, byte = i * 1024 + 16 * l;
+            const int r = byte / C::KROW, lc = SK::chunk(r, (byte % C::KROW) / 16);
+            const int64_t row = (ts + min(r, nm1)) * p.Hq + hq;
+            dma16(kp + row * KD + lc * C::EV, b + C::OFF_K + i * 1024);
+            dma16(qp + row * KD + lc * C::EV, b + C::OFF_Q + i * 1024);
+        }
+#pragma unroll
+        for (int s = 0; s < C::NVI / 4; ++s) {
+            const int i = w + 4 * s, byte = i * 1024 + 16 * l;
+            const int r = byte / C::VROW, lc = SV::chunk(r, (byte % C::VROW) / 16);
+            dma16(vp + ((ts + min(r, nm1)) * p.Hv + hv) * p.V + vt * BV + lc * C::EV, b + C::OFF_V + i * 1024);
+        }
+        const char *blk = p.tblk + ((int64_t)(cb + c) * p.Hv + hv) * TB::BYTES;
+        for (int i = w; i < C::NTI; i += 4) dma16(blk + i * 1024 + 16 * l, b + C::OFF_T + i * 1024);
+    }
+
+    __device__ __forceinline__ void flush() {
+        if (pend_ts < 0) return;
+#pragma unroll
+        for (int s = 0; s < CH * (BV / 4) / NTHR; ++s) {
+            const int idx = tid + NTHR * s, r = idx / (BV / 4), c4 = idx % (BV / 4);
+            if (r < pend_n)
+                OutVec<Out>::put(op + ((pend_ts + r) * p.Hv + hv) * p.V + vt * BV + 4 * c4,
+                                 *reinterpret_cast<const f32x4 *>(Os + r * C::LDO + 4 * c4));
+        }
+        pend_ts = -1;
+    }
+
+    // one chunk; LDS buffer `b` holds it and every wave has passed the barrier after it landed
+    __device__ __forceinline__ void step(int c, const char *b, const bool EMIT) {
+        const char *Ks = b + C::OFF_K, *Qs = b + C::OFF_Q, *Vs = b + C::OFF_V, *Tb = b + C::OFF_T;
+        const float *sc = reinterpret_cast<const float *>(Tb + TB::SC);
+        const float *gam = sc, *eg = sc + CH, *rr = sc + 2 * CH, *bet = sc + 3 * CH;
+        const int64_t ts = bos + (int64_t)c * CH;
+        const int n = (int)min<int64_t>(CH, eos - ts);
+
+        // decayed causal scores: this wave's share of the ten tiles (tr >= ti)
+        if (EMIT) {
+            const int t0 = w == 0 ? 0 : w == 1 ? 3 : w == 2 ? 6 : 8;
+            const int t1 = w == 0 ? 3 : w == 1 ? 6 : w == 2 ? 8 : 10;
+            for (int t = t0; t < t1; ++t) {
+                const int tr = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+                const int ti = t - tr * (tr + 1) / 2;
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int dp = 0; dp < C::DP; ++dp)
+                    acc = mma(acc, frag<In, C::KROW>(Ks, 16 * ti + n16, (32 * dp + 4 * g) * C::ES),
+                              frag<In, C::KROW>(Qs, 16 * tr + n16, (32 * dp + 4 * g) * C::ES));
+                // acc[jj] = P[r][i], r = 16 tr + n16, i = 16 ti + 4g + jj
+                const int r = 16 * tr + n16;
+                const float gr = gam[r];
+                const f32x4 gi = *reinterpret_cast<const f32x4 *>(gam + 16 * ti + 4 * g);
+                f32x4 v;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    v[jj] = (ti < tr || 4 * g + jj <= n16) ? acc[jj] * fast_exp(gr - gi[jj]) : 0.f;
+                const int off = SP::off(r, (16 * ti + 4 * g) * (C::BF ? 2 : 4));
+                if constexpr (C::BF) {
+                    bf16x4 hi, lo;
+                    split4(v, hi, lo);
+                    *reinterpret_cast<bf16x4 *>(pplane + off) = hi;
+                    *reinterpret_cast<bf16x4 *>(pplane + CH * C::PROW + off) = lo;
+                } else {
+                    *reinterpret_cast<f32x4 *>(pplane + off) = v;
+                }
+            }
+            if (p.hsnap) {
+                float *hs = p.hsnap + ((int64_t)(cb + c) * p.Hv + hv) * (int64_t)KD * p.V;
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) hs[(16 * dt + 4 * g + i) * p.V + colw + n16] = h[dt][i];
+            }
+        }
+
+        // K h (chain) and Q h (output) for this wave's columns
+        f32x4 kh[4], qh[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) kh[rt] = qh[rt] = zero4();
+#pragma unroll
+        for (int dp = 0; dp < C::DP; ++dp) {
+            const ST hb = O::split(h[2 * dp], h[2 * dp + 1]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                kh[rt] = mma(kh[rt], frag<In, C::KROW>(Ks, 16 * rt + n16, (32 * dp + 4 * g) * C::ES), hb);
+                if (EMIT)
+                    qh[rt] = mma(qh[rt], frag<In, C::KROW>(Qs, 16 * rt + n16, (32 * dp + 4 * g) * C::ES), hb);
+            }
+        }
+        // X = beta (V - e^gam K h), as the split B operand (k = tokens)
+        ST xs0, xs1;
+        {
+            f32x4 x[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const f32x4 vv = rows4<In, C::VROW>(Vs, 16 * rt, w * 16);
+                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bet + 16 * rt + 4 * g);
+                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(eg + 16 * rt + 4 * g);
+                x[rt] = b4 * (vv - e4 * kh[rt]);
+            }
+            xs0 = O::split(x[0], x[1]);
+            xs1 = O::split(x[2], x[3]);
+        }
+        // U~ = T X  (T unit lower triangular, zero rows past the chunk end)
+        f32x4 ut[4];
+        {
+            SplitPlane<In> tp;
+            tp.hi = reinterpret_cast<typename SplitPlaneT<In>::type *>(const_cast<char *>(Tb));
+            tp.lo = reinterpret_cast<typename SplitPlaneT<In>::type *>(const_cast<char *>(Tb) + TB::PLANE);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                ut[rt] = zero4();
+#pragma unroll
+                for (int ip = 0; ip <= rt / 2; ++ip) {
+                    const int row = 16 * rt + n16, byte = (32 * ip + 4 * g) * (C::BF ? 2 : 4);
+                    const int o0 = ST_::off(row, byte), o1 = ST_::off(row, byte + 16 * (C::BF ? 2 : 4));
+                    ut[rt] = mma(ut[rt], tp.get_bytes(o0, o1), ip == 0 ? xs0 : xs1);
+                }
+            }
+        }
+        __syncthreads();  // score planes complete
+        if (EMIT) {
+            const ST us0 = O::split(ut[0], ut[1]);
+            const ST us1 = O::split(ut[2], ut[3]);
+            SplitPlane<In> pp;
+            pp.hi = reinterpret_cast<typename SplitPlaneT<In>::type *>(pplane);
+            pp.lo = reinterpret_cast<typename SplitPlaneT<In>::type *>(pplane + CH * C::PROW);
+            const int EB = C::BF ? 2 : 4;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(eg + 16 * rt + 4 * g);
+                f32x4 acc = e4 * qh[rt];
+#pragma unroll
+                for (int ip = 0; ip <= rt / 2; ++ip) {
+                    const int row = 16 * rt + n16, byte = (32 * ip + 4 * g) * EB;
+                    acc = mma(acc, pp.get_bytes(SP::off(row, byte), SP::off(row, byte + 16 * EB)),
+                              ip == 0 ? us0 : us1);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Os[(16 * rt + 4 * g + i) * C::LDO + w * 16 + n16] = p.scale * acc[i];
+            }
+            pend_ts = ts;
+            pend_n = n;
+        }
+        // h' = e^{gam_last} h + K^T (exp(gam_last - gam) U~)
+        {
+            f32x4 y[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) y[rt] = *reinterpret_cast<const f32x4 *>(rr + 16 * rt + 4 * g) * ut[rt];
+            const ST rus0 = O::split(y[0], y[1]);
+            const ST rus1 = O::split(y[2], y[3]);
+            const float ec = eg[CH - 1];
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) {
+                h[dt] *= ec;
+                h[dt] = mma(h[dt], kt_operand<In, C::KROW>(Ks, 16 * dt, 0), rus0);
+                h[dt] = mma(h[dt], kt_operand<In, C::KROW>(Ks, 16 * dt, 1), rus1);
+            }
+        }
+    }
+
+    // chunk c from buffer `cur`; chunk c+1 (if any) copied into `nxt` meanwhile
+    template <int CUR>
+    __device__ __forceinline__ void run(int c, int c_begin, int c_end) {
+        char *cur = buf[C::NB == 2 ? CUR : 0];
+        char *nxt = buf[C::NB == 2 ? 1 - CUR : 0];
+        if constexpr (C::NB == 1) {
+            issue(c, cur);
+            flush();
+            wait_dma();
+            __syncthreads();
+        } else {
+            if (c + 1 < c_end) issue(c + 1, nxt);
+            flush();
+        }
+        step(c, cur, c >= c_begin);
+        if constexpr (C::NB == 2) wait_dma();
+        __syncthreads();  // chunk c done with `cur`, staged output complete, chunk c+1 landed
+    }
+};
+
+template <typename In, typename Out, int KD>
+__global__ __launch_bounds__(NTHR) void scan_output_kernel(const ScanParams p) {
+    using C = Cfg<In, KD>;
+    __shared__ __attribute__((aligned(16))) char buf0[C::BUF];
+    __shared__ __attribute__((aligned(16))) char buf1[C::NB == 2 ? C::BUF : 16];
+    __shared__ __attribute__((aligned(16))) char pplane[C::PBYTES];
+    __shared__ __attribute__((aligned(16))) float Os[CH * C::LDO];
+
+    Scan<In, Out, KD> S(p);
+    S.buf[0] = buf0;
+    S.buf[1] = buf1;
+    S.pplane = pplane;
+    S.Os = Os;
+
+    // work item: (v tile, v head, sequence, segment), XCD-grouped
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    S.vt = wid % p.n_vt;
+    const int rest = wid / p.n_vt;
+    S.unit = rest % p.n_units;
+    const int seg = rest / p.n_units;
+    S.j = S.unit / p.Hv;
+    S.hv = S.unit % p.Hv;
+    S.hq = S.hv / (p.Hv / p.Hq);
+    p.sm.bounds(S.j, S.bos, S.eos);
+    const int N = (int)((S.eos - S.bos + CH - 1) / CH);
     const int c_begin = seg * p.seg_chunks;
     if (c_begin >= N && !(N == 0 && seg == 0)) return;
     const int c_end = min(N, c_begin + p.seg_chunks);
     const int w_begin = seg == 0 ? 0 : max(0, c_begin - p.warm_chunks);
 
-    const int tid = threadIdx.x, w = wave_id(), n16 = ln16(), g = lg4();
-    const In *qp = reinterpret_cast<const In *>(p.q);
-    const In *kp = reinterpret_cast<const In *>(p.k);
-    const In *vp = reinterpret_cast<const In *>(p.v);
+    S.tid = threadIdx.x;
+    S.w = wave_id();
+    S.n16 = ln16();
+    S.g = lg4();
+    S.colw = S.vt * BV + S.w * 16;
+    S.qp = reinterpret_cast<const In *>(p.q);
+    S.kp = reinterpret_cast<const In *>(p.k);
+    S.vp = reinterpret_cast<const In *>(p.v);
+    S.op = reinterpret_cast<Out *>(p.o);
+    S.cb = p.sm.chunk_base(S.j);
+    S.pend_ts = -1;
+    S.pend_n = 0;
     const int64_t KV = (int64_t)KD * p.V;
-    const int colw = vt * BV + w * 16 * NCT;  // first value column of this wave
-
-    // ---- state slice in accumulator order: h[dt][ct] = rows 16dt+4g+i, column colw+16ct+n16
-    f32x4 h[DT][NCT];
     {
         const bool from_h0 = (w_begin == 0) && p.h0 != nullptr;
-        const float *h0 = from_h0 ? p.h0 + (int64_t)unit * KV : nullptr;
+        const float *h0 = from_h0 ? p.h0 + (int64_t)S.unit * KV : nullptr;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    h[dt][ct][i] = from_h0 ? h0[(16 * dt + 4 * g + i) * p.V + colw + 16 * ct + n16] : 0.f;
+            for (int i = 0; i < 4; ++i)
+                S.h[dt][i] = from_h0 ? h0[(16 * dt + 4 * S.g + i) * p.V + S.colw + S.n16] : 0.f;
     }
-    // never-written tiles of P above the diagonal pairs
+    // score-plane tiles above the diagonal pairs, (0,1) and (2,3), are read as zero and never written
     {
-        typedef typename PlaneT<In>::type PT;
-        for (int idx = tid; idx < 2 * 16 * 16; idx += NTHR) {
-            const int t = idx >> 8, r = (idx >> 4) & 15, i = idx & 15;
-            const int off = (32 * t + r) * LDT + 32 * t + 16 + i;
-            Pp.hi[off] = PT(0.f);
-            if constexpr (PlaneT<In>::planes == 2) Pp.lo[off] = PT(0.f);
-        }
-    }
-
-    // ---- prefetch registers (next chunk)
-    V16 kr[L::NK], qr[L::NK], vr[L::NV];
-    f32x4 tr[L::NT];
-    float gr = 0.f, glast = 0.f, br = 0.f;
-    int pf_n = 0;
-    auto prefetch = [&](int c) {
-        const int64_t ts = bos + (int64_t)c * CH;
-        const int n = (int)min<int64_t>(CH, eos - ts);
-        pf_n = n;
-#pragma unroll
-        for (int s = 0; s < L::NK; ++s) {
-            const int idx = tid + NTHR * s, r = idx / (KD / EV), cv = idx % (KD / EV);
-            kr[s] = V16{};
-            qr[s] = V16{};
-            if (r < n) {
-                kr[s] = *reinterpret_cast<const V16 *>(kp + ((ts + r) * p.Hq + hq) * KD + cv * EV);
-                qr[s] = *reinterpret_cast<const V16 *>(qp + ((ts + r) * p.Hq + hq) * KD + cv * EV);
+        using SP = Swz<C::PROW>;
+        constexpr int EB = C::BF ? 2 : 4;
+        for (int idx = threadIdx.x; idx < 2 * 16 * 16; idx += NTHR) {
+            const int t = idx >> 8, r = 32 * t + ((idx >> 4) & 15), i = 32 * t + 16 + (idx & 15);
+            const int off = SP::off(r, i * EB);
+            if constexpr (C::BF) {
+                *reinterpret_cast<bf16 *>(pplane + off) = bf16(0.f);
+                *reinterpret_cast<bf16 *>(pplane + CH * C::PROW + off) = bf16(0.f);
+            } else {
+                *reinterpret_cast<float *>(pplane + off) = 0.f;
             }
         }
-#pragma unroll
-        for (int s = 0; s < L::NV; ++s) {
-            const int idx = tid + NTHR * s, r = idx / (BV / EV), cv = idx % (BV / EV);
-            vr[s] = V16{};
-            if (r < n) vr[s] = *reinterpret_cast<const V16 *>(vp + ((ts + r) * p.Hv + hv) * p.V + vt * BV + cv * EV);
-        }
-#pragma unroll
-        for (int s = 0; s < L::NT; ++s) {
-            const int idx = tid + NTHR * s, r = idx >> 4, c4 = idx & 15;
-            tr[s] = zero4();
-            if (r < n) tr[s] = *reinterpret_cast<const f32x4 *>(p.Tm + ((ts + r) * p.Hv + hv) * CH + 4 * c4);
-        }
-        if (tid < CH) {
-            const int r = min(tid, n - 1);
-            gr = p.g_cum[(ts + r) * p.Hv + hv];
-            glast = p.g_cum[(ts + n - 1) * p.Hv + hv];
-            br = tid < n ? p.beta[(ts + tid) * p.Hv + hv] : 0.f;
-        }
-    };
-    auto commit = [&]() {
-#pragma unroll
-        for (int s = 0; s < L::NK; ++s) {
-            const int idx = tid + NTHR * s, r = idx / (KD / EV), cv = idx % (KD / EV);
-            *reinterpret_cast<V16 *>(Ks + r * LDK + cv * EV) = kr[s];
-            *reinterpret_cast<V16 *>(Qs + r * LDK + cv * EV) = qr[s];
-        }
-#pragma unroll
-        for (int s = 0; s < L::NV; ++s) {
-            const int idx = tid + NTHR * s, r = idx / (BV / EV), cv = idx % (BV / EV);
-            *reinterpret_cast<V16 *>(Vs + r * LDV + cv * EV) = vr[s];
-        }
-#pragma unroll
-        for (int s = 0; s < L::NT; ++s) {
-            const int idx = tid + NTHR * s, r = idx >> 4, c4 = idx & 15;
-            Tp.put4(r * LDT + 4 * c4, tr[s]);
-        }
-        if (tid < CH) {
-            gam[tid] = gr;
-            eg[tid] = fast_exp(gr);
-            rr[tid] = fast_exp(glast - gr);
-            bet[tid] = br;
-        }
-    };
-
-    if (w_begin < c_end) prefetch(w_begin);
-    const int cb = p.sm.chunk_base(j);
-    for (int c = w_begin; c < c_end; ++c) {
-        const bool emit = c >= c_begin;
-        const int64_t ts = bos + (int64_t)c * CH;
-        __syncthreads();  // previous chunk done with LDS
-        commit();
-        const int n = pf_n;
-        if (c + 1 < c_end) prefetch(c + 1);
+    }
+    wait_dma();  // initial-state loads done before the copy engine counts start
+    if constexpr (C::NB == 2) {
+        if (w_begin < c_end) S.issue(w_begin, buf0);
+        wait_dma();
         __syncthreads();
-
-        if (emit && p.hsnap) {
-            float *hs = p.hsnap + ((int64_t)(cb + c) * p.Hv + hv) * KV;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        hs[(16 * dt + 4 * g + i) * p.V + colw + 16 * ct + n16] = h[dt][ct][i];
-        }
-        // P = tril(Q K^T) * exp(gam_r - gam_i): ten tiles spread over the waves
-        if (emit) {
-            const int t0 = w == 0 ? 0 : w == 1 ? 3 : w == 2 ? 6 : 8;
-            const int t1 = w == 0 ? 3 : w == 1 ? 6 : w == 2 ? 8 : 10;
-            for (int t = t0; t < t1; ++t) {
-                int trow = 0;
-                while ((trow + 1) * (trow + 2) / 2 <= t) ++trow;
-                const int ti = t - trow * (trow + 1) / 2;
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int dp = 0; dp < KD / 32; ++dp) {
-                    const In *ar = Ks + (16 * ti + n16) * LDK + 32 * dp + 4 * g;
-                    const In *brw = Qs + (16 * trow + n16) * LDK + 32 * dp + 4 * g;
-                    acc = mma(acc, O::load(ar, ar + 16), O::load(brw, brw + 16));
-                }
-                // acc[jj] = (K Q^T)[i][r] = P[r][i], i = 16ti+4g+jj, r = 16trow+n16
-                const int r = 16 * trow + n16;
-                f32x4 pv;
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int i = 16 * ti + 4 * g + jj;
-                    pv[jj] = i <= r ? acc[jj] * fast_exp(gam[r] - gam[i]) : 0.f;
-                }
-                Pp.put4(r * LDT + 16 * ti + 4 * g, pv);
-            }
-        }
-
-        // split state as B operand (k = key dims)
-        ST hsb[DT / 2][NCT];
-#pragma unroll
-        for (int dp = 0; dp < DT / 2; ++dp)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) hsb[dp][ct] = O::split(h[2 * dp][ct], h[2 * dp + 1][ct]);
-
-        // K h and Q h over the chunk's 64 rows
-        f32x4 kh[4][NCT], qh[4][NCT];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                kh[rt][ct] = zero4();
-                qh[rt][ct] = zero4();
-            }
-#pragma unroll
-            for (int dp = 0; dp < DT / 2; ++dp) {
-                const In *ar = Ks + (16 * rt + n16) * LDK + 32 * dp + 4 * g;
-                const XT a = O::load(ar, ar + 16);
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) kh[rt][ct] = mma(kh[rt][ct], a, hsb[dp][ct]);
-                if (emit) {
-                    const In *aq = Qs + (16 * rt + n16) * LDK + 32 * dp + 4 * g;
-                    const XT b = O::load(aq, aq + 16);
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) qh[rt][ct] = mma(qh[rt][ct], b, hsb[dp][ct]);
-                }
-            }
-        }
-        // X = beta (V - e^gam K h), split as B operand (k = tokens)
-        ST xs[2][NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const int col = w * 16 * NCT + 16 * ct + n16;
-            f32x4 x[4];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * rt + 4 * g + i;
-                    x[rt][i] = bet[row] * (to_f32(Vs[row * LDV + col]) - eg[row] * kh[rt][ct][i]);
-                }
-            xs[0][ct] = O::split(x[0], x[1]);
-            xs[1][ct] = O::split(x[2], x[3]);
-        }
-        // U~ = T X  (T unit lower triangular: row tile rt uses k pairs <= rt/2)
-        f32x4 ut[4][NCT];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) ut[rt][ct] = zero4();
-#pragma unroll
-            for (int ip = 0; ip <= rt / 2; ++ip) {
-                const int off = (16 * rt + n16) * LDT + 32 * ip + 4 * g;
-                const ST a = Tp.get(off, off + 16);
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) ut[rt][ct] = mma(ut[rt][ct], a, xs[ip][ct]);
-            }
-        }
-        __syncthreads();  // P tiles visible
-        if (emit) {
-            ST us[2][NCT];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                us[0][ct] = O::split(ut[0][ct], ut[1][ct]);
-                us[1][ct] = O::split(ut[2][ct], ut[3][ct]);
-            }
-            Out *op = reinterpret_cast<Out *>(p.o);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                f32x4 acc[NCT];
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[ct][i] = eg[16 * rt + 4 * g + i] * qh[rt][ct][i];
-#pragma unroll
-                for (int ip = 0; ip <= rt / 2; ++ip) {
-                    const int off = (16 * rt + n16) * LDT + 32 * ip + 4 * g;
-                    const ST a = Pp.get(off, off + 16);
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) acc[ct] = mma(acc[ct], a, us[ip][ct]);
-                }
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = 16 * rt + 4 * g + i;
-                        if (row < n)
-                            store_out(op + ((ts + row) * p.Hv + hv) * p.V + colw + 16 * ct + n16,
-                                      p.scale * acc[ct][i]);
-                    }
-            }
-        }
-        // h' = e^{gam_last} h + K^T (exp(gam_last - gam) U~)
-        {
-            ST rus[2][NCT];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                f32x4 y[4];
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) y[rt][i] = rr[16 * rt + 4 * g + i] * ut[rt][ct][i];
-                rus[0][ct] = O::split(y[0], y[1]);
-                rus[1][ct] = O::split(y[2], y[3]);
-            }
-            const float ec = eg[CH - 1];
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) h[dt][ct] *= ec;
-#pragma unroll
-                for (int ip = 0; ip < 2; ++ip) {
-                    const XT a = gather_kt<In>(Ks, LDK, 16 * dt + n16, ip);
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) h[dt][ct] = mma(h[dt][ct], a, rus[ip][ct]);
-                }
-            }
-        }
     }
+    for (int c = w_begin; c < c_end; c += 2) {
+        S.template run<0>(c, c_begin, c_end);
+        if (c + 1 < c_end) S.template run<1>(c + 1, c_begin, c_end);
+    }
+    S.flush();
     if (c_end == N && p.hT) {
-        float *hT = p.hT + (int64_t)unit * KV;
+        float *hT = p.hT + (int64_t)S.unit * KV;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    hT[(16 * dt + 4 * g + i) * p.V + colw + 16 * ct + n16] = h[dt][ct][i];
+            for (int i = 0; i < 4; ++i) hT[(16 * dt + 4 * S.g + i) * p.V + S.colw + S.n16] = S.h[dt][i];
     }
 }
 
-template <typename In, typename Out, int KD, int NCT>
+template <typename In, typename Out, int KD>
 hipError_t launch_scan_t(const ScanParams &p, hipStream_t s) {
-    using L = ScanLayout<In, KD, NCT>;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&scan_output_kernel<In, Out, KD, NCT>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
-    (void)attr;  // a refusal shows up as a launch error below
     const int nb = p.n_vt * p.n_units * p.n_seg;
-    hipLaunchKernelGGL((scan_output_kernel<In, Out, KD, NCT>), dim3(nb), dim3(NTHR), L::bytes, s, p);
+    hipLaunchKernelGGL((scan_output_kernel<In, Out, KD>), dim3(nb), dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
 
 template <typename In, typename Out>
 hipError_t launch_scan_k(int K, const ScanParams &p, hipStream_t s) {
-    if (K == 128) return launch_scan_t<In, Out, 128, 1>(p, s);
-    return launch_scan_t<In, Out, 64, 1>(p, s);
+    if (K == 128) return launch_scan_t<In, Out, 128>(p, s);
+    return launch_scan_t<In, Out, 64>(p, s);
 }
 
 }  // namespace
 
-int scan_vtile(Dt, int, int V) { return V < 64 ? V : 64; }
+int scan_vtile(Dt, int, int) { return BV; }
 
 hipError_t launch_scan_output(Dt dt, Dt out, int K, int V, const ScanParams &p, hipStream_t s) {
     (void)V;

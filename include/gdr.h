@@ -48,6 +48,7 @@ extern "C" {
 
 #define GDR_ABI_VERSION 1
 #define GDR_CHUNK 64
+#define GDR_FWD_STAGES 3
 
 /* return codes */
 #define GDR_OK 0
@@ -93,6 +94,10 @@ typedef struct {
                                    NULL = not written */
     float *w_out;               /* [B,T,H_v,K] W = T diag(beta e^g_cum) K, NULL = not computed */
     float *u_out;               /* [B,T,H_v,V] U = T diag(beta) V, NULL = not computed */
+    /* timing hook: NULL, or a HOST array of 2*GDR_FWD_STAGES events that are
+       recorded on the stream before and after each stage (chunk prep, scan
+       with output, W/U); a stage that does not run records both at once */
+    hipEvent_t *events;
     /* scratch */
     void *workspace;
     size_t workspace_bytes;
