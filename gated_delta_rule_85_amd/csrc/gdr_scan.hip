@@ -71,9 +71,8 @@ template <typename In, int KD> struct Cfg {
     static constexpr int BUF = OFF_T + TB::BYTES;
     static constexpr int PROW = CH * (BF ? 2 : 4);  // score plane row bytes
     static constexpr int PBYTES = CH * PROW * (BF ? 2 : 1);
-    static constexpr int LDO = BV + 4;
     static constexpr int NKI = KT / 1024, NVI = VT / 1024, NTI = TB::BYTES / 1024;
-    static_assert(NKI % 4 == 0 && NVI % 4 == 0, "tile copies spread over 4 waves");
+    static_assert(NKI % 2 == 0 && NVI % 2 == 0, "tile copies spread over 2 waves");
     static constexpr int DT = KD / 16, DP = KD / 32;
 };
 
@@ -144,7 +143,6 @@ template <typename In, typename Out, int KD> struct Scan {
     const ScanParams &p;
     char *buf[2];
     char *pplane;  // shared score planes (hi, lo)
-    float *Os;     // staged output chunk
     // work item
     int vt, unit, j, hv, hq, cb;
     int64_t bos, eos;
@@ -153,49 +151,82 @@ template <typename In, typename Out, int KD> struct Scan {
     Out *op;
     // state slice: h[dt] = rows 16dt+4g+i, column colw+n16
     f32x4 h[C::DT];
-    // staged output bookkeeping
+    // pending output bookkeeping
     int64_t pend_ts;
     int pend_n;
 
     __device__ __forceinline__ Scan(const ScanParams &p_) : p(p_) {}
 
-    // copy chunk c (tokens from ts, n valid) into LDS buffer b
+    // Waves 0-1 issue the chunk copies (spreading them keeps each copy wave's
+    // vmcnt wait short); every wave stores its own output columns.
+    static constexpr int NCW = 2;  // copy waves
+    // per-lane parts of the copies (fixed for the whole scan): row of the tile
+    // this lane fills in each of its copies and the byte offset of its 16-byte
+    // chunk inside that row
+    int krow[C::NKI / NCW], kchk[C::NKI / NCW], vrow[C::NVI / NCW], vchk[C::NVI / NCW];
+
+    __device__ __forceinline__ void setup_copies() {
+        const int l = lane_id();
+        const int cw = w < NCW ? w : 0;
+#pragma unroll
+        for (int s = 0; s < C::NKI / NCW; ++s) {
+            const int byte = (cw + NCW * s) * 1024 + 16 * l, r = byte / C::KROW;
+            krow[s] = r;
+            kchk[s] = 16 * SK::chunk(r, (byte % C::KROW) / 16);
+        }
+#pragma unroll
+        for (int s = 0; s < C::NVI / NCW; ++s) {
+            const int byte = (cw + NCW * s) * 1024 + 16 * l, r = byte / C::VROW;
+            vrow[s] = r;
+            vchk[s] = 16 * SV::chunk(r, (byte % C::VROW) / 16);
+        }
+    }
+
+    // copy chunk c into LDS buffer b (rows past the chunk end repeat its last row)
     __device__ __forceinline__ void issue(int c, char *b) {
+        if (w >= NCW) return;
         const int64_t ts = bos + (int64_t)c * CH;
         const int nm1 = (int)min<int64_t>(CH, eos - ts) - 1;
         const int l = lane_id();
+        const int krs = p.Hq * KD * C::ES, vrs = p.Hv * p.V * C::ES;  // row strides (bytes)
+        const char *kb = reinterpret_cast<const char *>(kp + (ts * p.Hq + hq) * KD);
+        const char *qb = reinterpret_cast<const char *>(qp + (ts * p.Hq + hq) * KD);
+        const char *vb = reinterpret_cast<const char *>(vp + (ts * p.Hv + hv) * p.V + vt * BV);
 #pragma unroll
-        for (int s = 0; s < C::NKI / 4; ++s) {
-            const int i = w + 4 * s, byte = i * 1024 + 16 * l;
-            const int r = byte / C::KROW, lc = SK::chunk(r, (byte % C::KROW) / 16);
-            const int64_t row = (ts + min(r, nm1)) * p.Hq + hq;
-            dma16(kp + row * KD + lc * C::EV, b + C::OFF_K + i * 1024);
-            dma16(qp + row * KD + lc * C::EV, b + C::OFF_Q + i * 1024);
+        for (int s = 0; s < C::NKI / NCW; ++s) {
+            const uint32_t off = (uint32_t)(min(krow[s], nm1) * krs + kchk[s]);
+            const int i = w + NCW * s;
+            dma16(kb + off, b + C::OFF_K + i * 1024);
+            dma16(qb + off, b + C::OFF_Q + i * 1024);
         }
 #pragma unroll
-        for (int s = 0; s < C::NVI / 4; ++s) {
-            const int i = w + 4 * s, byte = i * 1024 + 16 * l;
-            const int r = byte / C::VROW, lc = SV::chunk(r, (byte % C::VROW) / 16);
-            dma16(vp + ((ts + min(r, nm1)) * p.Hv + hv) * p.V + vt * BV + lc * C::EV, b + C::OFF_V + i * 1024);
+        for (int s = 0; s < C::NVI / NCW; ++s) {
+            const uint32_t off = (uint32_t)(min(vrow[s], nm1) * vrs + vchk[s]);
+            dma16(vb + off, b + C::OFF_V + (w + NCW * s) * 1024);
         }
         const char *blk = p.tblk + ((int64_t)(cb + c) * p.Hv + hv) * TB::BYTES;
-        for (int i = w; i < C::NTI; i += 4) dma16(blk + i * 1024 + 16 * l, b + C::OFF_T + i * 1024);
+        for (int i = w; i < C::NTI; i += NCW) dma16(blk + i * 1024 + 16 * l, b + C::OFF_T + i * 1024);
     }
 
-    __device__ __forceinline__ void flush() {
+    // output of the previous chunk, held in registers as O^T tiles: pend_o[rt]
+    // holds o[token 16 rt + lane16][columns colw + 4g .. colw + 4g + 3]
+    f32x4 pend_o[4];
+
+    __device__ __forceinline__ void store_pending() {
         if (pend_ts < 0) return;
+        Out *ob = op + (pend_ts * p.Hv + hv) * p.V + colw + 4 * g;
+        const int rstride = p.Hv * p.V;
 #pragma unroll
-        for (int s = 0; s < CH * (BV / 4) / NTHR; ++s) {
-            const int idx = tid + NTHR * s, r = idx / (BV / 4), c4 = idx % (BV / 4);
-            if (r < pend_n)
-                OutVec<Out>::put(op + ((pend_ts + r) * p.Hv + hv) * p.V + vt * BV + 4 * c4,
-                                 *reinterpret_cast<const f32x4 *>(Os + r * C::LDO + 4 * c4));
+        for (int rt = 0; rt < 4; ++rt) {
+            const int tok = 16 * rt + n16;
+            if (tok < pend_n) OutVec<Out>::put(ob + (uint32_t)(tok * rstride), pend_o[rt]);
         }
         pend_ts = -1;
     }
 
     // one chunk; LDS buffer `b` holds it and every wave has passed the barrier after it landed
-    __device__ __forceinline__ void step(int c, const char *b, const bool EMIT) {
+    template <bool EMIT>
+    __device__ __forceinline__ void step(int c, const char *b) {
         const char *Ks = b + C::OFF_K, *Qs = b + C::OFF_Q, *Vs = b + C::OFF_V, *Tb = b + C::OFF_T;
         const float *sc = reinterpret_cast<const float *>(Tb + TB::SC);
         const float *gam = sc, *eg = sc + CH, *rr = sc + 2 * CH, *bet = sc + 3 * CH;
@@ -203,10 +234,12 @@ template <typename In, typename Out, int KD> struct Scan {
         const int n = (int)min<int64_t>(CH, eos - ts);
 
         // decayed causal scores: this wave's share of the ten tiles (tr >= ti)
-        if (EMIT) {
-            const int t0 = w == 0 ? 0 : w == 1 ? 3 : w == 2 ? 6 : 8;
-            const int t1 = w == 0 ? 3 : w == 1 ? 6 : w == 2 ? 8 : 10;
-            for (int t = t0; t < t1; ++t) {
+        if constexpr (EMIT) {
+            // wave w forms tiles w, w + 4 and (waves 0, 1) w + 8 of the ten
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const int t = w + 4 * k;
+                if (t >= 10) break;
                 const int tr = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
                 const int ti = t - tr * (tr + 1) / 2;
                 f32x4 acc = zero4();
@@ -251,8 +284,8 @@ template <typename In, typename Out, int KD> struct Scan {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 kh[rt] = mma(kh[rt], frag<In, C::KROW>(Ks, 16 * rt + n16, (32 * dp + 4 * g) * C::ES), hb);
-                if (EMIT)
-                    qh[rt] = mma(qh[rt], frag<In, C::KROW>(Qs, 16 * rt + n16, (32 * dp + 4 * g) * C::ES), hb);
+                if constexpr (EMIT)  // (Q h)^T tile: lane (token, g) holds 4 output columns
+                    qh[rt] = mma(qh[rt], hb, frag<In, C::KROW>(Qs, 16 * rt + n16, (32 * dp + 4 * g) * C::ES));
             }
         }
         // X = beta (V - e^gam K h), as the split B operand (k = tokens)
@@ -287,7 +320,9 @@ template <typename In, typename Out, int KD> struct Scan {
             }
         }
         __syncthreads();  // score planes complete
-        if (EMIT) {
+        if constexpr (EMIT) {
+            // O^T = (Q h)^T diag(e^gam) + U~^T P^T; the split U~ serves as the A operand of U~^T
+            // and the P fragments as the B operand of P^T
             const ST us0 = O::split(ut[0], ut[1]);
             const ST us1 = O::split(ut[2], ut[3]);
             SplitPlane<In> pp;
@@ -296,16 +331,14 @@ template <typename In, typename Out, int KD> struct Scan {
             const int EB = C::BF ? 2 : 4;
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(eg + 16 * rt + 4 * g);
-                f32x4 acc = e4 * qh[rt];
+                f32x4 acc = eg[16 * rt + n16] * qh[rt];
 #pragma unroll
                 for (int ip = 0; ip <= rt / 2; ++ip) {
                     const int row = 16 * rt + n16, byte = (32 * ip + 4 * g) * EB;
-                    acc = mma(acc, pp.get_bytes(SP::off(row, byte), SP::off(row, byte + 16 * EB)),
-                              ip == 0 ? us0 : us1);
+                    acc = mma(acc, ip == 0 ? us0 : us1,
+                              pp.get_bytes(SP::off(row, byte), SP::off(row, byte + 16 * EB)));
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Os[(16 * rt + 4 * g + i) * C::LDO + w * 16 + n16] = p.scale * acc[i];
+                pend_o[rt] = p.scale * acc;
             }
             pend_ts = ts;
             pend_n = n;
@@ -334,16 +367,19 @@ template <typename In, typename Out, int KD> struct Scan {
         char *nxt = buf[C::NB == 2 ? 1 - CUR : 0];
         if constexpr (C::NB == 1) {
             issue(c, cur);
-            flush();
-            wait_dma();
+            store_pending();
+            if (w < NCW) wait_dma();
             __syncthreads();
         } else {
             if (c + 1 < c_end) issue(c + 1, nxt);
-            flush();
+            store_pending();
         }
-        step(c, cur, c >= c_begin);
-        if constexpr (C::NB == 2) wait_dma();
-        __syncthreads();  // chunk c done with `cur`, staged output complete, chunk c+1 landed
+        if (c >= c_begin)
+            step<true>(c, cur);
+        else
+            step<false>(c, cur);
+        if (C::NB == 2 && w < NCW) wait_dma();
+        __syncthreads();  // chunk c done with `cur`, chunk c+1 landed
     }
 };
 
@@ -353,13 +389,11 @@ __global__ __launch_bounds__(NTHR) void scan_output_kernel(const ScanParams p) {
     __shared__ __attribute__((aligned(16))) char buf0[C::BUF];
     __shared__ __attribute__((aligned(16))) char buf1[C::NB == 2 ? C::BUF : 16];
     __shared__ __attribute__((aligned(16))) char pplane[C::PBYTES];
-    __shared__ __attribute__((aligned(16))) float Os[CH * C::LDO];
 
     Scan<In, Out, KD> S(p);
     S.buf[0] = buf0;
     S.buf[1] = buf1;
     S.pplane = pplane;
-    S.Os = Os;
 
     // work item: (v tile, v head, sequence, segment), XCD-grouped
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -378,7 +412,7 @@ __global__ __launch_bounds__(NTHR) void scan_output_kernel(const ScanParams p) {
     const int w_begin = seg == 0 ? 0 : max(0, c_begin - p.warm_chunks);
 
     S.tid = threadIdx.x;
-    S.w = wave_id();
+    S.w = __builtin_amdgcn_readfirstlane(wave_id());
     S.n16 = ln16();
     S.g = lg4();
     S.colw = S.vt * BV + S.w * 16;
@@ -389,6 +423,7 @@ __global__ __launch_bounds__(NTHR) void scan_output_kernel(const ScanParams p) {
     S.cb = p.sm.chunk_base(S.j);
     S.pend_ts = -1;
     S.pend_n = 0;
+    S.setup_copies();
     const int64_t KV = (int64_t)KD * p.V;
     {
         const bool from_h0 = (w_begin == 0) && p.h0 != nullptr;
@@ -424,7 +459,7 @@ __global__ __launch_bounds__(NTHR) void scan_output_kernel(const ScanParams p) {
         S.template run<0>(c, c_begin, c_end);
         if (c + 1 < c_end) S.template run<1>(c + 1, c_begin, c_end);
     }
-    S.flush();
+    S.store_pending();
     if (c_end == N && p.hT) {
         float *hT = p.hT + (int64_t)S.unit * KV;
 #pragma unroll
