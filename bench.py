@@ -3,7 +3,8 @@
 
 One step is one gdr_fwd call (gdr_chunk_prep + the fused scan/output kernel)
 over the full-width prefill shard: B=4, T=4096, H_q=16, H_v=32, K=V=128,
-bf16 q/k/v, fp32 g/beta/initial and final state, fp32 o.  Inputs are seeded
+bf16 q/k/v, fp32 g/beta/initial and final state, fp32 o (inference forward:
+the A and g_cum tensors a backward would need are not written).  Inputs are seeded
 synthetic tensors already resident in HBM; W untimed warm-up steps, then K
 timed steps between stream synchronisations.  Each step records HIP events
 around each kernel on the library's stream; the dominant kernel's average
@@ -31,20 +32,24 @@ F_TRI = 139264                  # algorithmic flop per token per v head (C=64, K
 STAGES = ("gdr_chunk_prep", "gdr_scan_output", "gdr_wu")
 
 
+TBLOCK = 17408  # bytes of one (chunk, v head) T block: T hi/lo planes + gate scalars
+
+
 def algorithmic_bytes(cfg, out_bytes=4):
-    """Bytes each kernel must move once per launch (every tensor it reads or
-    writes, counted once; q/k shared by the v heads of a group)."""
+    """Bytes each kernel must move once per launch in this design (every
+    tensor it reads or writes counted once; q/k shared by the v heads of a
+    group; one T block per chunk and v head between the two kernels)."""
     B, T, Hq, Hv, K, V = cfg["B"], cfg["T"], cfg["Hq"], cfg["Hv"], cfg["K"], cfg["V"]
     e = 2 if cfg["dtype"] == "bf16" else 4
     tok = B * T
     qk = tok * Hq * K * e
     vv = tok * Hv * V * e
     gate = tok * Hv * 4
-    Tm = tok * Hv * 64 * 4
+    blocks = B * ((T + 63) // 64) * Hv * TBLOCK
     state = B * Hv * K * V * 4
     o = tok * Hv * V * out_bytes
-    prep = qk + 2 * gate + gate + Tm          # k, g, beta -> g_cum, T
-    scan = 2 * qk + vv + Tm + 2 * gate + o + (2 * state if cfg.get("h0") else state)
+    prep = qk + 2 * gate + blocks                  # k, g, beta -> T blocks
+    scan = 2 * qk + vv + blocks + o + (2 * state if cfg.get("h0") else state)
     return {"gdr_chunk_prep": prep, "gdr_scan_output": scan}
 
 
@@ -58,12 +63,13 @@ def source_hash():
 
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
+    was taken on the current kernel sources; else None.  The summary's last
+    line is a JSON object with source_hash and bytes_per_launch."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (kernel, workload))
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        t = json.load(f)
+        t = json.loads(f.read().strip().splitlines()[-1])
     if t.get("source_hash") != source_hash():
         return None
     return t.get("bytes_per_launch")
@@ -105,6 +111,8 @@ def main():
     ap.add_argument("--workload", default="prefill_shard")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this operator has no multi-GPU path here "
@@ -132,8 +140,6 @@ def main():
     n_seq = B if cu is None else cu.numel() - 1
     o = torch.empty((B, T, Hv, V), dtype=torch.float32, device=dev)
     ht = torch.empty((n_seq, Hv, K, V), dtype=torch.float32, device=dev)
-    g_cum = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
-    A = torch.empty((B, T, Hv, 64), dtype=torch.float32, device=dev)
 
     a = _lib.FwdArgs()
     a.B, a.T, a.H_q, a.H_v, a.K, a.V, a.n_seq = B, T, Hq, Hv, K, V, n_seq
@@ -144,7 +150,8 @@ def main():
     a.q, a.k, a.v, a.g, a.beta = q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr()
     a.initial_state = None if h0 is None else h0.data_ptr()
     a.cu_seqlens = None if cu is None else cu.data_ptr()
-    a.o, a.final_state, a.g_cum, a.A = o.data_ptr(), ht.data_ptr(), g_cum.data_ptr(), A.data_ptr()
+    # inference forward: o and the final state (the backward's A and g_cum are not written)
+    a.o, a.final_state = o.data_ptr(), ht.data_ptr()
     nbytes = _lib.fwd_workspace(a)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
@@ -166,6 +173,12 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     a.events = None
     for _ in range(args.warmup):
         _lib.fwd(a, sh)

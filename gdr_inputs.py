@@ -21,7 +21,7 @@ import math
 import numpy as np
 
 # name -> shape/dtype recipe.  "lens" means packed variable-length sequences.
-CONFIGS = {
+WORKLOADS = {
     "tiny_fp32": dict(B=1, T=256, Hq=2, Hv=2, K=64, V=64, dtype="fp32", h0=False),
     "prefill_shard": dict(B=4, T=4096, Hq=16, Hv=32, K=128, V=128, dtype="bf16", h0=True),
     "small_head_long": dict(B=1, T=32768, Hq=4, Hv=8, K=128, V=128, dtype="bf16", h0=False),
@@ -30,7 +30,7 @@ CONFIGS = {
     "training": dict(B=8, T=4096, Hq=32, Hv=64, K=128, V=128, dtype="bf16", h0=True,
                      grads=True),
 }
-CONFIG_ORDER = ["tiny_fp32", "prefill_shard", "small_head_long", "varlen", "training"]
+WORKLOAD_ORDER = ["tiny_fp32", "prefill_shard", "small_head_long", "varlen", "training"]
 
 
 def round_bf16(x):
@@ -61,12 +61,12 @@ def varlen_lengths(rng, nseq, lo, hi, max_padded, chunk=64):
 
 
 def make_inputs(shape, seed=0, grads=None, h0=None):
-    """Draw one problem.  ``shape`` is a CONFIGS key or a dict with the same keys
+    """Draw one problem.  ``shape`` is a WORKLOADS key or a dict with the same keys
     (B, T or nseq/lens, Hq, Hv, K, V, dtype).  Returns a dict of numpy arrays:
     q, k [B,T,Hq,K]; v [B,T,Hv,V]; g, beta [B,T,Hv]; initial_state
     [N,Hv,K,V] or None; cu_seqlens int32 or None; do, dht when grads; plus
     scale = 1/sqrt(K) and the recipe."""
-    cfg = dict(CONFIGS[shape]) if isinstance(shape, str) else dict(shape)
+    cfg = dict(WORKLOADS[shape]) if isinstance(shape, str) else dict(shape)
     rng = np.random.default_rng(seed)
     cu = None
     if "lens" in cfg or "nseq" in cfg:

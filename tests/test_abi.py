@@ -79,14 +79,21 @@ def rc_ws(L, a):
     return L.lib.gdr_fwd_workspace(ctypes.byref(a), ctypes.byref(n)), n.value
 
 
+TBLOCK = 17408  # one (chunk, v head) T block: bf16 hi/lo planes of T + gate scalars
+
+
 def test_workspace_sizes(L):
+    # T=256: 4 chunks x 4 v heads of T blocks
     rc, n = rc_ws(L, fwd_args(L))
-    # g_cum and A kept in the workspace when not supplied, 256-byte aligned
-    assert rc == 0 and n == 256 * 4 * 4 + 256 * 4 * 64 * 4
+    assert rc == 0 and n == 4 * 4 * TBLOCK
     rc, n = rc_ws(L, fwd_args(L, g_cum=16, A=16))
-    assert rc == 0 and n == 0
-    rc, n = rc_ws(L, fwd_args(L, g_cum=16, A=16, cu_seqlens=16, n_seq=3))
-    assert rc == 0 and n == 256
+    assert rc == 0 and n == 4 * 4 * TBLOCK
+    # packed sequences: chunk-offset table (256-byte aligned) + blocks for up to
+    # ceil(T/64) + n_seq chunks
+    rc, n = rc_ws(L, fwd_args(L, cu_seqlens=16, n_seq=3))
+    assert rc == 0 and n == 256 + (4 + 3) * 4 * TBLOCK
+    rc, n = rc_ws(L, fwd_args(L, dtype=L.F32, K=64, V=64))
+    assert rc == 0 and n == 4 * 4 * TBLOCK
 
 
 @pytest.mark.parametrize("kw,code", [

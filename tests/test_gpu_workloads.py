@@ -1,0 +1,102 @@
+"""GPU parity on the full-size workloads (sampled units) and the sequence split.
+
+Every launch covers the whole workload; the fp64 oracle recomputes whole
+(sequence, q/k-head group) units, exact because units are independent.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gdr_inputs import make_inputs
+from gpu_helpers import host, rel, run_fwd, slice_units
+
+pytestmark = pytest.mark.gpu
+
+
+def test_varlen_packed_batch_full_size():
+    """16 packed sequences (61,412 tokens, seed-0 lengths), H_q=16, H_v=32,
+    K=V=128, bf16, zero initial states, per-sequence final states."""
+    x = make_inputs("varlen", seed=0)
+    g_cum, A, o, h, ht = run_fwd(x, return_h=False)
+    o, ht = host(o), host(ht)
+    for hq in (0, 9):
+        y, hs = slice_units(x, 0, hq)
+        r = oracle.fwd(y["q"], y["k"], y["v"], y["g"], y["beta"], y["scale"],
+                       cu_seqlens=y["cu_seqlens"])
+        eo, eh = rel(o[:, :, hs], r["o"]), rel(ht[:, hs], r["final_state"])
+        print("hq=%d o %.3g final %.3g" % (hq, eo, eh), flush=True)
+        assert eo <= 2e-2 and eh <= 2e-2
+
+
+def test_training_shape_forward_full_size():
+    """B=8, T=4096, H_q=32, H_v=64, K=V=128, bf16 with initial state (forward part)."""
+    x = make_inputs("training", seed=0, grads=False)
+    g_cum, A, o, h, ht = run_fwd(x, return_h=False)
+    o, ht = host(o), host(ht)
+    for b, hq in ((0, 0), (7, 31)):
+        y, hs = slice_units(x, b, hq)
+        r = oracle.fwd(y["q"], y["k"], y["v"], y["g"], y["beta"], y["scale"], y["initial_state"])
+        eo, eh = rel(o[b:b + 1, :, hs], r["o"]), rel(ht[b:b + 1, hs], r["final_state"])
+        print("b=%d hq=%d o %.3g final %.3g" % (b, hq, eo, eh), flush=True)
+        assert eo <= 2e-2 and eh <= 2e-2
+
+
+@pytest.fixture(scope="module")
+def long_seq():
+    """B=1, T=32768, H_q=4, H_v=8, K=V=128, bf16: 512 chunks per head."""
+    return make_inputs("small_head_long", seed=0)
+
+
+def test_long_sequence_exact_scan(long_seq):
+    x = long_seq
+    o = host(run_fwd(x, return_h=False, cp_mode="off")[2])
+    r = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"])
+    e = rel(o, r["o"])
+    print("exact o %.3g" % e, flush=True)
+    assert e <= 2e-2
+
+
+@pytest.mark.parametrize("wm", [6, 7, 8])
+def test_long_sequence_warmup_split(long_seq, wm):
+    """Segments of L = ceil(sqrt(512)) = 23 chunks, each warmed up over wm chunks
+    from a zero state; compared with the oracle of the same split (the bar), and
+    the split's own deviation from the exact result reported separately."""
+    x = long_seq
+    L = 23
+    _, _, o, _, ht = run_fwd(x, return_h=False, cp_mode="warmup", cp_segment_chunks=L,
+                             cp_warmup_chunks=wm)
+    o, ht = host(o), host(ht)
+    rs = oracle.fwd_split(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], L, wm)
+    re = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"])
+    e_split, e_final = rel(o, rs["o"]), rel(ht, rs["final_state"])
+    e_vs_exact = rel(o, re["o"])
+    e_method = rel(rs["o"], re["o"])
+    print("wm=%d gpu-vs-split %.3g final %.3g | gpu-vs-exact %.3g | split-vs-exact (fp64) %.3g"
+          % (wm, e_split, e_final, e_vs_exact, e_method), flush=True)
+    assert e_split <= 2e-2 and e_final <= 2e-2
+    assert e_vs_exact <= 2e-2  # decaying gates: the split meets the same bar
+
+
+def test_auto_mode_splits_the_long_sequence(long_seq):
+    """AutoCP: B*H_v = 8 <= 40 selects the split with L = ceil(sqrt(N)), Wm = 8."""
+    x = long_seq
+    auto = host(run_fwd(x, return_h=False, cp_mode="auto")[2])
+    forced = host(run_fwd(x, return_h=False, cp_mode="warmup", cp_segment_chunks=23,
+                          cp_warmup_chunks=8)[2])
+    assert np.array_equal(auto, forced)
+
+
+@pytest.mark.parametrize("scale_g", [0.03, 0.01])
+def test_weak_decay_split_diagnostic(scale_g):
+    """Weak gates (g scaled down): the warm-up error becomes visible.  Reported,
+    and the GPU must still match the oracle of the same split."""
+    x = make_inputs(dict(B=1, T=64 * 48, Hq=1, Hv=2, K=128, V=128, dtype="bf16", h0=False), seed=0)
+    x["g"] = (x["g"] * scale_g).astype(np.float32)
+    L, wm = 7, 8
+    o = host(run_fwd(x, return_h=False, cp_mode="warmup", cp_segment_chunks=L,
+                     cp_warmup_chunks=wm)[2])
+    rs = oracle.fwd_split(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], L, wm)
+    re = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"])
+    print("g x %.2f: split-vs-exact (fp64) %.3g, gpu-vs-split %.3g"
+          % (scale_g, rel(rs["o"], re["o"]), rel(o, rs["o"])), flush=True)
+    assert rel(o, rs["o"]) <= 2e-2
