@@ -43,7 +43,7 @@ class BwdArgs(ctypes.Structure):
     _fields_ = [
         ("B", _i64), ("T", _i64), ("H_q", _i64), ("H_v", _i64), ("K", _i64), ("V", _i64),
         ("n_seq", _i64),
-        ("dtype", _i32), ("scale", ctypes.c_float),
+        ("dtype", _i32), ("grad_dtype", _i32), ("scale", ctypes.c_float),
         ("q", _p), ("k", _p), ("v", _p), ("g_cum", _p), ("beta", _p), ("A", _p),
         ("dout", _p), ("dht", _p), ("initial_state", _p), ("cu_seqlens", _p),
         ("dq", _p), ("dk", _p), ("dv", _p), ("dbeta", _p), ("dg", _p), ("dh0", _p),

@@ -112,9 +112,12 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
 
 
 def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, initial_state=None,
-                               cu_seqlens=None):
+                               cu_seqlens=None, *, grad_dtype=None):
     """Low-level backward.  ``g`` is the forward's g_cum, ``A`` its A.
-    Returns ``(dq, dk, dv, db, dg, dh0)``; dh0 is None without initial_state."""
+    Returns ``(dq, dk, dv, db, dg, dh0)``; dh0 is None without initial_state.
+    dq, dk, dv come in ``grad_dtype`` (default: the dtype of q), db, dg, dh0 in
+    float32.  The gradients are accumulated in fp32; a bf16 dq/dk/dv adds one
+    rounding of up to 2^-9 |x| per element."""
     _check(q, k, v, g, beta, cu_seqlens)
     q, k, v, do = _c(q), _c(k), _c(v), _c(do, q.dtype)
     g, beta, A = _c(g, torch.float32), _c(beta, torch.float32), _c(A, torch.float32)
@@ -127,15 +130,17 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
     h0 = _c(initial_state, torch.float32)
     dht = _c(dht, torch.float32)
     cu = _c(cu_seqlens)
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
+    gdt = q.dtype if grad_dtype is None else grad_dtype
+    dq = torch.empty(q.shape, dtype=gdt, device=dev)
+    dk = torch.empty(k.shape, dtype=gdt, device=dev)
+    dv = torch.empty(v.shape, dtype=gdt, device=dev)
     db = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
     dg = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
     dh0 = torch.empty((n_seq, Hv, K, V), dtype=torch.float32, device=dev) if h0 is not None else None
     a = _lib.BwdArgs()
     a.B, a.T, a.H_q, a.H_v, a.K, a.V, a.n_seq = B, T, Hq, Hv, K, V, n_seq
     a.dtype = _DT[q.dtype]
+    a.grad_dtype = _DT[gdt]
     a.scale = float(scale)
     a.q, a.k, a.v, a.g_cum, a.beta, a.A = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A)
     a.dout, a.dht, a.initial_state, a.cu_seqlens = _ptr(do), _ptr(dht), _ptr(h0), _ptr(cu)
@@ -150,10 +155,13 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
 class _ChunkGDR(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
-                output_dtype):
+                output_dtype, cp_mode):
+        # the backward differentiates the exact scan: no sequence split when training
+        if any(ctx.needs_input_grad):
+            cp_mode = "off"
         g_cum, A, o, _, ht = chunk_gated_delta_rule_fwd(
             q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_state=True,
-            output_dtype=output_dtype, return_h=False)
+            output_dtype=output_dtype, return_h=False, cp_mode=cp_mode)
         ctx.save_for_backward(q, k, v, g_cum, beta, A, initial_state, cu_seqlens)
         ctx.scale = scale
         ctx.g_dtype = g.dtype
@@ -164,15 +172,20 @@ class _ChunkGDR(torch.autograd.Function):
         q, k, v, g_cum, beta, A, h0, cu = ctx.saved_tensors
         dq, dk, dv, db, dg, dh0 = chunk_gated_delta_rule_bwd(
             q, k, v, g_cum, beta, A, do, dht, ctx.scale, h0, cu)
-        return (dq, dk, dv, dg.to(ctx.g_dtype), db.to(beta.dtype), None, dh0, None, None, None)
+        return (dq, dk, dv, dg.to(ctx.g_dtype), db.to(beta.dtype), None, dh0, None, None, None,
+                None)
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
                            output_final_state=False, cu_seqlens=None, *,
-                           output_dtype=torch.float32):
-    """High-level differentiable API.  Returns ``(o, final_state)``."""
+                           output_dtype=torch.float32, cp_mode="auto"):
+    """High-level differentiable API.  Returns ``(o, final_state)``.
+
+    Without gradients the forward may split long sequences (``cp_mode``);
+    when any input requires a gradient it runs the exact scan, which is what
+    the backward differentiates."""
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     o, ht = _ChunkGDR.apply(q, k, v, g, beta, scale, initial_state, output_final_state,
-                            cu_seqlens, output_dtype)
+                            cu_seqlens, output_dtype, cp_mode)
     return o, ht

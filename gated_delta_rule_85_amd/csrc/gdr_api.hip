@@ -71,6 +71,36 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl) {
     return GDR_OK;
 }
 
+struct BwdPlan {
+    int64_t n_seq, tokens, nct, nt_ub;
+    size_t off_chunk, off_tblk, off_hs, off_dhs, total;
+};
+
+// workspace: [chunk offsets] | T blocks | chunk-start states | chunk-end state gradients
+int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl) {
+    if (!a) return GDR_EINVAL;
+    const bool varlen = a->cu_seqlens != nullptr;
+    int rc = check_dims(a->B, a->T, a->H_q, a->H_v, a->K, a->V, a->n_seq, varlen, a->dtype);
+    if (rc) return rc;
+    if (a->grad_dtype != GDR_BF16 && a->grad_dtype != GDR_F32) return GDR_ENOTSUP;
+    pl.n_seq = varlen ? a->n_seq : a->B;
+    pl.tokens = a->B * a->T;
+    pl.nct = cdiv(a->T, GDR_CHUNK);
+    pl.nt_ub = varlen ? pl.nct + pl.n_seq : a->B * pl.nct;
+    const size_t nb = (size_t)(pl.nt_ub * a->H_v);
+    size_t off = 0;
+    pl.off_chunk = off;
+    if (varlen) off += up(sizeof(int32_t) * (size_t)(pl.n_seq + 1));
+    pl.off_tblk = off;
+    off += up(tblock_bytes(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32) * nb);
+    pl.off_hs = off;
+    off += up(sizeof(float) * nb * (size_t)(a->K * a->V));
+    pl.off_dhs = off;
+    off += up(sizeof(float) * nb * (size_t)(a->K * a->V));
+    pl.total = pl.tokens > 0 ? off : pl.off_tblk;
+    return GDR_OK;
+}
+
 SeqMap make_map(const gdr_fwd_args *a, const FwdPlan &pl, const int32_t *chunk_off) {
     SeqMap m;
     m.cu = a->cu_seqlens;
@@ -194,18 +224,98 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
 }
 
 int gdr_bwd_workspace(const gdr_bwd_args *a, size_t *bytes) {
-    if (!a || !bytes) return GDR_EINVAL;
-    int rc = check_dims(a->B, a->T, a->H_q, a->H_v, a->K, a->V, a->n_seq, a->cu_seqlens != nullptr, a->dtype);
+    if (!bytes) return GDR_EINVAL;
+    BwdPlan pl;
+    int rc = plan_bwd(a, pl);
     if (rc) return rc;
-    *bytes = 0;
-    return GDR_ENOTSUP;
+    *bytes = pl.total;
+    return GDR_OK;
 }
 
 int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
-    (void)stream;
-    size_t b;
-    int rc = gdr_bwd_workspace(a, &b);
-    return rc;
+    BwdPlan pl;
+    int rc = plan_bwd(a, pl);
+    if (rc) return rc;
+    if (pl.tokens > 0) {
+        if (!a->q || !a->k || !a->v || !a->g_cum || !a->beta || !a->A || !a->dout || !a->dq || !a->dk ||
+            !a->dv || !a->dbeta || !a->dg)
+            return GDR_EINVAL;
+        if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->dout, 16) ||
+            !aligned(a->A, 16) || !aligned(a->dq, 16) || !aligned(a->dk, 16) || !aligned(a->dv, 16) ||
+            !aligned(a->g_cum, 4) || !aligned(a->beta, 4) || !aligned(a->dbeta, 4) || !aligned(a->dg, 4))
+            return GDR_EINVAL;
+    }
+    if ((a->dht && !aligned(a->dht, 16)) || (a->initial_state && !aligned(a->initial_state, 16)) ||
+        (a->dh0 && !aligned(a->dh0, 16)))
+        return GDR_EINVAL;
+    if (a->workspace_bytes < pl.total || (pl.total > 0 && !a->workspace)) return GDR_EWORKSPACE;
+    if (pl.total > 0 && !aligned(a->workspace, 16)) return GDR_EINVAL;
+
+    char *ws = static_cast<char *>(a->workspace);
+    int32_t *chunk_off = a->cu_seqlens ? reinterpret_cast<int32_t *>(ws + pl.off_chunk) : nullptr;
+    const Dt dt = a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
+    SeqMap sm;
+    sm.cu = a->cu_seqlens;
+    sm.chunk_off = chunk_off;
+    sm.T = a->T;
+    sm.n_seq = (int32_t)pl.n_seq;
+    sm.nct = (int32_t)pl.nct;
+    const int n_units = (int)(pl.n_seq * a->H_v);
+
+    BwdParams bp;
+    bp.q = a->q;
+    bp.k = a->k;
+    bp.v = a->v;
+    bp.dout = a->dout;
+    bp.g_cum = a->g_cum;
+    bp.beta = a->beta;
+    bp.A = a->A;
+    bp.dht = a->dht;
+    bp.tblk = ws + pl.off_tblk;
+    bp.hs = reinterpret_cast<float *>(ws + pl.off_hs);
+    bp.dhs = reinterpret_cast<float *>(ws + pl.off_dhs);
+    bp.dq = a->dq;
+    bp.dk = a->dk;
+    bp.dv = a->dv;
+    bp.dbeta = a->dbeta;
+    bp.dg = a->dg;
+    bp.dh0 = a->dh0;
+    bp.sm = sm;
+    bp.Hq = (int)a->H_q;
+    bp.Hv = (int)a->H_v;
+    bp.V = (int)a->V;
+    bp.scale = a->scale;
+
+    if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, chunk_off, (int)pl.n_seq, stream) != hipSuccess)
+        return GDR_ELAUNCH;
+    if (pl.tokens > 0) {
+        if (launch_tblocks(dt, bp, (int)pl.nt_ub, stream) != hipSuccess) return GDR_ELAUNCH;
+        // chunk-start states: the exact forward scan without its output
+        ScanParams sp;
+        sp.q = a->q;
+        sp.k = a->k;
+        sp.v = a->v;
+        sp.tblk = bp.tblk;
+        sp.h0 = a->initial_state;
+        sp.o = nullptr;
+        sp.hT = nullptr;
+        sp.hsnap = reinterpret_cast<float *>(ws + pl.off_hs);
+        sp.sm = sm;
+        sp.Hq = (int)a->H_q;
+        sp.Hv = (int)a->H_v;
+        sp.V = (int)a->V;
+        sp.scale = a->scale;
+        sp.seg_chunks = (int)pl.nct + 1;
+        sp.warm_chunks = 0;
+        sp.n_vt = (int)(a->V / scan_vtile(dt, (int)a->K, (int)a->V));
+        sp.n_units = n_units;
+        sp.n_seg = 1;
+        if (launch_scan_states(dt, (int)a->K, sp, stream) != hipSuccess) return GDR_ELAUNCH;
+    }
+    const Dt gt = a->grad_dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
+    if (launch_bwd(dt, gt, (int)a->K, bp, pl.tokens > 0 ? (int)pl.nt_ub : 0, n_units, stream) != hipSuccess)
+        return GDR_ELAUNCH;
+    return GDR_OK;
 }
 
 }  // extern "C"

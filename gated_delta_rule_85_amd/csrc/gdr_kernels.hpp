@@ -50,10 +50,30 @@ struct WUParams {
     int Hq, Hv, K, V;
 };
 
+// backward: per (chunk, q/k head) local gradients after a reverse scan over
+// chunks per (sequence, v head, 64 value columns)
+struct BwdParams {
+    const void *q, *k, *v, *dout;
+    const float *g_cum, *beta, *A;
+    const float *dht;  // [N, H_v, K, V] or null
+    char *tblk;        // [chunks, H_v] T blocks rebuilt from A
+    const float *hs;   // [NT, H_v, K, V] chunk-start states
+    float *dhs;        // [NT, H_v, K, V] gradient of each chunk's end state
+    void *dq, *dk, *dv;
+    float *dbeta, *dg;
+    float *dh0;        // [N, H_v, K, V] or null
+    SeqMap sm;
+    int Hq, Hv, V;
+    float scale;
+};
+
 hipError_t launch_chunk_offsets(const int32_t *cu, int32_t *chunk_off, int n_seq, hipStream_t s);
 hipError_t launch_prep(Dt dt, int K, const PrepParams &p, int n_chunks_ub, hipStream_t s);
 hipError_t launch_scan_output(Dt dt, Dt out, int K, int V, const ScanParams &p, hipStream_t s);
 hipError_t launch_wu(Dt dt, const WUParams &p, int n_chunks_ub, hipStream_t s);
+hipError_t launch_scan_states(Dt dt, int K, const ScanParams &p, hipStream_t s);
+hipError_t launch_tblocks(Dt dt, const BwdParams &p, int n_chunks_ub, hipStream_t s);
+hipError_t launch_bwd(Dt dt, Dt gt, int K, const BwdParams &p, int n_chunks_ub, int n_units, hipStream_t s);
 size_t tblock_bytes(Dt dt);
 int scan_vtile(Dt dt, int K, int V);  // V columns per scan workgroup
 

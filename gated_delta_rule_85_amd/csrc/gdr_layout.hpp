@@ -40,4 +40,45 @@ template <typename In> struct TBlock {
     static_assert(BYTES % 1024 == 0, "block copied in 1 KB wave transfers");
 };
 
+// Write one T block from an fp32 row-major T (row r, column i at T[r * ld + i])
+// and the chunk's 64 gate values (gam padded with its last value, bet zero
+// past the chunk end); rows r >= n are written as zero.  All threads of the
+// workgroup take part; gam/bet/T are read, never written.
+template <typename In>
+__device__ __forceinline__ void write_tblock(char *blk, const float *T, int ld, const float *gam,
+                                             const float *bet, int n, int tid, int nthr) {
+    using TB = TBlock<In>;
+    using SW = Swz<TB::ROWB>;
+    constexpr int EPC = 16 / (TB::BF ? 2 : 4);  // elements per 16-byte chunk
+    for (int idx = tid; idx < CH * SW::CPR; idx += nthr) {
+        const int r = idx / SW::CPR, pc = idx % SW::CPR, lc = SW::chunk(r, pc);
+        f32x4 x0 = zero4(), x1 = zero4();
+        if (r < n) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x0[e] = T[r * ld + EPC * lc + e];
+            if constexpr (TB::BF) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x1[e] = T[r * ld + EPC * lc + 4 + e];
+            }
+        }
+        if constexpr (TB::BF) {
+            bf16x4 h0, l0, h1, l1;
+            split4(x0, h0, l0);
+            split4(x1, h1, l1);
+            *reinterpret_cast<bf16x8 *>(blk + r * TB::ROWB + 16 * pc) = cat(h0, h1);
+            *reinterpret_cast<bf16x8 *>(blk + TB::PLANE + r * TB::ROWB + 16 * pc) = cat(l0, l1);
+        } else {
+            *reinterpret_cast<f32x4 *>(blk + r * TB::ROWB + 16 * pc) = x0;
+        }
+    }
+    if (tid < CH) {
+        float *sc = reinterpret_cast<float *>(blk + TB::SC);
+        const float gl = gam[n - 1];
+        sc[tid] = gam[tid];
+        sc[CH + tid] = fast_exp(gam[tid]);
+        sc[2 * CH + tid] = fast_exp(gl - gam[tid]);
+        sc[3 * CH + tid] = bet[tid];
+    }
+}
+
 }  // namespace gdr

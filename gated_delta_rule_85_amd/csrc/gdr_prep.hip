@@ -163,37 +163,8 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
             }
         }
         // T block for the scan: swizzled planes (rows past the chunk end zero) + scalars
-        {
-            using TB = TBlock<In>;
-            using SW = Swz<TB::ROWB>;
-            char *blk = p.tblk + ((int64_t)gid * p.Hv + hv) * TB::BYTES;
-            constexpr int EPC = 16 / (TB::BF ? 2 : 4);  // elements per 16-byte chunk
-            for (int idx = tid; idx < CH * SW::CPR; idx += NTHR) {
-                const int r = idx / SW::CPR, pc = idx % SW::CPR, lc = SW::chunk(r, pc);
-                f32x4 x0 = zero4(), x1 = zero4();
-                if (r < n) {
-                    x0 = *reinterpret_cast<const f32x4 *>(Tm + r * LDF + EPC * lc);
-                    if constexpr (TB::BF) x1 = *reinterpret_cast<const f32x4 *>(Tm + r * LDF + EPC * lc + 4);
-                }
-                if constexpr (TB::BF) {
-                    bf16x4 h0, l0, h1, l1;
-                    split4(x0, h0, l0);
-                    split4(x1, h1, l1);
-                    *reinterpret_cast<bf16x8 *>(blk + r * TB::ROWB + 16 * pc) = cat(h0, h1);
-                    *reinterpret_cast<bf16x8 *>(blk + TB::PLANE + r * TB::ROWB + 16 * pc) = cat(l0, l1);
-                } else {
-                    *reinterpret_cast<f32x4 *>(blk + r * TB::ROWB + 16 * pc) = x0;
-                }
-            }
-            if (tid < CH) {
-                float *sc = reinterpret_cast<float *>(blk + TB::SC);
-                const float gl = gam[n - 1];
-                sc[tid] = gam[tid];
-                sc[CH + tid] = fast_exp(gam[tid]);
-                sc[2 * CH + tid] = fast_exp(gl - gam[tid]);
-                sc[3 * CH + tid] = bet[tid];
-            }
-        }
+        write_tblock<In>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, Tm, LDF, gam, bet, n,
+                         tid, NTHR);
         __syncthreads();
     }
 }

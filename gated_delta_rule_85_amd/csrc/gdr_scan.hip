@@ -225,7 +225,7 @@ template <typename In, typename Out, int KD> struct Scan {
     }
 
     // one chunk; LDS buffer `b` holds it and every wave has passed the barrier after it landed
-    template <bool EMIT>
+    template <bool EMIT, bool SNAP>
     __device__ __forceinline__ void step(int c, const char *b) {
         const char *Ks = b + C::OFF_K, *Qs = b + C::OFF_Q, *Vs = b + C::OFF_V, *Tb = b + C::OFF_T;
         const float *sc = reinterpret_cast<const float *>(Tb + TB::SC);
@@ -265,6 +265,8 @@ template <typename In, typename Out, int KD> struct Scan {
                     *reinterpret_cast<f32x4 *>(pplane + off) = v;
                 }
             }
+        }
+        if constexpr (SNAP) {
             if (p.hsnap) {
                 float *hs = p.hsnap + ((int64_t)(cb + c) * p.Hv + hv) * (int64_t)KD * p.V;
 #pragma unroll
@@ -361,7 +363,7 @@ template <typename In, typename Out, int KD> struct Scan {
     }
 
     // chunk c from buffer `cur`; chunk c+1 (if any) copied into `nxt` meanwhile
-    template <int CUR>
+    template <int CUR, bool STATES>
     __device__ __forceinline__ void run(int c, int c_begin, int c_end) {
         char *cur = buf[C::NB == 2 ? CUR : 0];
         char *nxt = buf[C::NB == 2 ? 1 - CUR : 0];
@@ -374,16 +376,19 @@ template <typename In, typename Out, int KD> struct Scan {
             if (c + 1 < c_end) issue(c + 1, nxt);
             store_pending();
         }
-        if (c >= c_begin)
-            step<true>(c, cur);
+        if constexpr (STATES)
+            step<false, true>(c, cur);
+        else if (c >= c_begin)
+            step<true, true>(c, cur);
         else
-            step<false>(c, cur);
+            step<false, false>(c, cur);
         if (C::NB == 2 && w < NCW) wait_dma();
         __syncthreads();  // chunk c done with `cur`, chunk c+1 landed
     }
 };
 
-template <typename In, typename Out, int KD>
+// STATES: chunk-start states only (no scores, no output), for the backward
+template <typename In, typename Out, int KD, bool STATES>
 __global__ __launch_bounds__(NTHR) void scan_output_kernel(const ScanParams p) {
     using C = Cfg<In, KD>;
     __shared__ __attribute__((aligned(16))) char buf0[C::BUF];
@@ -456,8 +461,8 @@ __global__ __launch_bounds__(NTHR) void scan_output_kernel(const ScanParams p) {
         __syncthreads();
     }
     for (int c = w_begin; c < c_end; c += 2) {
-        S.template run<0>(c, c_begin, c_end);
-        if (c + 1 < c_end) S.template run<1>(c + 1, c_begin, c_end);
+        S.template run<0, STATES>(c, c_begin, c_end);
+        if (c + 1 < c_end) S.template run<1, STATES>(c + 1, c_begin, c_end);
     }
     S.store_pending();
     if (c_end == N && p.hT) {
@@ -469,17 +474,17 @@ __global__ __launch_bounds__(NTHR) void scan_output_kernel(const ScanParams p) {
     }
 }
 
-template <typename In, typename Out, int KD>
+template <typename In, typename Out, int KD, bool STATES>
 hipError_t launch_scan_t(const ScanParams &p, hipStream_t s) {
     const int nb = p.n_vt * p.n_units * p.n_seg;
-    hipLaunchKernelGGL((scan_output_kernel<In, Out, KD>), dim3(nb), dim3(NTHR), 0, s, p);
+    hipLaunchKernelGGL((scan_output_kernel<In, Out, KD, STATES>), dim3(nb), dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
 
-template <typename In, typename Out>
+template <typename In, typename Out, bool STATES = false>
 hipError_t launch_scan_k(int K, const ScanParams &p, hipStream_t s) {
-    if (K == 128) return launch_scan_t<In, Out, 128>(p, s);
-    return launch_scan_t<In, Out, 64>(p, s);
+    if (K == 128) return launch_scan_t<In, Out, 128, STATES>(p, s);
+    return launch_scan_t<In, Out, 64, STATES>(p, s);
 }
 
 }  // namespace
@@ -491,6 +496,11 @@ hipError_t launch_scan_output(Dt dt, Dt out, int K, int V, const ScanParams &p, 
     if (dt == Dt::BF16)
         return out == Dt::F32 ? launch_scan_k<bf16, float>(K, p, s) : launch_scan_k<bf16, bf16>(K, p, s);
     return out == Dt::F32 ? launch_scan_k<float, float>(K, p, s) : launch_scan_k<float, bf16>(K, p, s);
+}
+
+hipError_t launch_scan_states(Dt dt, int K, const ScanParams &p, hipStream_t s) {
+    if (dt == Dt::BF16) return launch_scan_k<bf16, float, true>(K, p, s);
+    return launch_scan_k<float, float, true>(K, p, s);
 }
 
 }  // namespace gdr

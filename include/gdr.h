@@ -105,7 +105,8 @@ typedef struct {
 
 typedef struct {
     int64_t B, T, H_q, H_v, K, V, n_seq;
-    int32_t dtype;    /* element type of q, k, v, do, dq, dk, dv */
+    int32_t dtype;      /* element type of q, k, v, do */
+    int32_t grad_dtype; /* element type of dq, dk, dv: GDR_BF16 or GDR_F32 */
     float scale;
     const void *q, *k, *v;      /* as in gdr_fwd_args */
     const float *g_cum;         /* [B,T,H_v] the forward's g_cum */
@@ -115,12 +116,12 @@ typedef struct {
     const float *dht;           /* [N,H_v,K,V] gradient of final_state; NULL = zeros */
     const float *initial_state; /* [N,H_v,K,V] or NULL */
     const int32_t *cu_seqlens;  /* [n_seq+1] or NULL */
-    void *dq, *dk;              /* [B,T,H_q,K] dtype, summed over the v heads of each q/k head */
-    void *dv;                   /* [B,T,H_v,V] dtype */
+    void *dq, *dk;              /* [B,T,H_q,K] grad_dtype, summed over the v heads of each q/k head */
+    void *dv;                   /* [B,T,H_v,V] grad_dtype */
     float *dbeta;               /* [B,T,H_v] gradient w.r.t. beta */
     float *dg;                  /* [B,T,H_v] gradient w.r.t. the raw per-token g */
-    float *dh0;                 /* [N,H_v,K,V]; NULL = not wanted (required to be NULL when
-                                   initial_state is NULL is not enforced: zeros are used) */
+    float *dh0;                 /* [N,H_v,K,V] gradient of initial_state (NULL initial_state
+                                   means zeros); NULL = not wanted */
     void *workspace;
     size_t workspace_bytes;
 } gdr_bwd_args;
@@ -143,10 +144,18 @@ int gdr_fwd_workspace(const gdr_fwd_args *args, size_t *bytes);
    window reaches the start of the sequence). */
 int gdr_fwd(const gdr_fwd_args *args, hipStream_t stream);
 
-/* Workspace bytes gdr_bwd needs. */
+/* Workspace bytes gdr_bwd needs for these sizes (pointers are not read):
+   T blocks, the chunk-start states and the chunk-end state gradients,
+   4 K V bytes each per (chunk, v head).  Returns GDR_OK or a validation
+   error. */
 int gdr_bwd_workspace(const gdr_bwd_args *args, size_t *bytes);
 
-/* Backward of the exact forward: gradients of <dout, o> + <dht, final_state>. */
+/* Backward of the exact forward (GDR_CP_OFF) on `stream`: gradients of
+   <dout, o> + <dht, final_state> for an fp32 o, with respect to q, k, v,
+   beta, the raw per-token g and initial_state.  g_cum and A must be what
+   gdr_fwd returned for the same inputs.  The chunk-start states are
+   recomputed, not read.  dq and dk are written in full (rows of every
+   token); every output is overwritten, none accumulated into. */
 int gdr_bwd(const gdr_bwd_args *args, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -124,3 +124,40 @@ def test_fwd_host_errors_before_any_launch(L):
     assert L.lib.gdr_fwd(ctypes.byref(a), None) == L.EINVAL  # misaligned o
     with pytest.raises(L.GdrError):
         L.fwd_workspace(fwd_args(L, K=48))
+
+
+def bwd_args(L, **kw):
+    a = L.BwdArgs()
+    a.B, a.T, a.H_q, a.H_v, a.K, a.V, a.n_seq = 1, 256, 2, 4, 128, 128, 0
+    a.dtype, a.scale = L.BF16, 0.088
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_bwd_workspace_sizes(L):
+    # T blocks + chunk-start states + chunk-end state gradients, per (chunk, v head)
+    per = TBLOCK + 2 * 4 * 128 * 128
+    assert L.bwd_workspace(bwd_args(L)) == 4 * 4 * per
+    assert L.bwd_workspace(bwd_args(L, cu_seqlens=16, n_seq=3)) == 256 + (4 + 3) * 4 * per
+    assert L.bwd_workspace(bwd_args(L, T=0)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H_v=3), -1), (dict(K=96), -2), (dict(dtype=7), -2), (dict(grad_dtype=9), -2),
+    (dict(B=0), -1),
+    (dict(cu_seqlens=16, n_seq=2, B=2), -1),
+])
+def test_bwd_validation_errors(L, kw, code):
+    n = ctypes.c_size_t(0)
+    assert L.lib.gdr_bwd_workspace(ctypes.byref(bwd_args(L, **kw)), ctypes.byref(n)) == code
+    assert L.lib.gdr_bwd(ctypes.byref(bwd_args(L, **kw)), None) == code
+
+
+def test_bwd_host_errors_before_any_launch(L):
+    assert L.lib.gdr_bwd(ctypes.byref(bwd_args(L)), None) == L.EINVAL  # null pointers
+    full = dict(q=16, k=16, v=16, g_cum=16, beta=16, A=16, dout=16, dq=16, dk=16, dv=16,
+                dbeta=16, dg=16)
+    assert L.lib.gdr_bwd(ctypes.byref(bwd_args(L, **full)), None) == L.EWORKSPACE
+    bad = dict(full, dq=24, workspace=4096, workspace_bytes=1 << 34)
+    assert L.lib.gdr_bwd(ctypes.byref(bwd_args(L, **bad)), None) == L.EINVAL

@@ -1,0 +1,160 @@
+"""GPU parity of the backward (HIP kernels through the C ABI) against the fp64 oracle.
+
+The backward takes the forward's g_cum and A (as the README's low-level API
+does) and the raw q, k, v, beta, do, dht, initial state; the oracle
+differentiates the token recurrence from the raw inputs alone.  Metric per
+gradient: max |gpu - oracle| / rms(oracle), bar 1e-4 for fp32 inputs and
+2e-2 for bf16 inputs, with dq, dk, dv requested in fp32 (dbeta, dg, dh0 are
+always fp32).  A bf16 dq/dk/dv adds one rounding per element, which the
+max/rms metric cannot absorb where the gradient is heavy-tailed (the last
+token of a sequence takes dht directly), so bf16 gradients are checked
+element-wise against |gpu - oracle| <= 2^-8 |oracle| + 1e-3 rms(oracle).
+The full training shape is checked on whole (sequence, q/k head group)
+units, which the oracle computes exactly on their own.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gdr_inputs import make_inputs
+from gpu_helpers import dev, gpu_inputs, host, rel, slice_units, tol
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dbeta", "dg", "dh0")
+
+
+def run_bwd(x, with_dht=True, grad_dtype=torch.float32):
+    from gated_delta_rule_85_amd import chunk_gated_delta_rule_bwd, chunk_gated_delta_rule_fwd
+    d = gpu_inputs(x)
+    dt = d["q"].dtype
+    g_cum, A, _, _, _ = chunk_gated_delta_rule_fwd(
+        d["q"], d["k"], d["v"], d["g"], d["beta"], x["scale"], d["initial_state"],
+        d["cu_seqlens"], output_final_state=False, return_h=False, cp_mode="off")
+    do = dev(x["do"], dt)
+    dht = dev(x["dht"]) if with_dht else None
+    out = chunk_gated_delta_rule_bwd(d["q"], d["k"], d["v"], g_cum, d["beta"], A, do, dht,
+                                     x["scale"], d["initial_state"], d["cu_seqlens"],
+                                     grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return dict(zip(NAMES, out))
+
+
+def ora_bwd(x, with_dht=True):
+    return oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], x["scale"],
+                      initial_state=x["initial_state"], dht=x["dht"] if with_dht else None,
+                      cu_seqlens=x["cu_seqlens"])
+
+
+def compare(x, got, ref, t=None, names=NAMES):
+    t = tol(x) if t is None else t
+    errs = {}
+    for n in names:
+        if got.get(n) is None:
+            continue
+        errs[n] = rel(host(got[n]), ref[n])
+    print({k: "%.3g" % v for k, v in errs.items()}, flush=True)
+    for n, e in errs.items():
+        assert e <= t, (n, e)
+    return errs
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=1, T=256, Hq=2, Hv=2, K=64, V=64, dtype="fp32", h0=True),
+    dict(B=3, T=77, Hq=1, Hv=2, K=64, V=64, dtype="fp32", h0=True),
+    dict(B=1, T=190, Hq=1, Hv=3, K=128, V=128, dtype="fp32", h0=True),
+    dict(B=2, T=300, Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True),
+    dict(B=1, T=200, Hq=1, Hv=1, K=64, V=128, dtype="bf16", h0=True),
+    dict(B=1, T=130, Hq=2, Hv=2, K=128, V=64, dtype="bf16", h0=False),
+])
+def test_small_ragged(shape):
+    """Every element of every gradient; several chunks and a ragged tail."""
+    x = make_inputs(shape, seed=2, grads=True)
+    print(shape, flush=True)
+    compare(x, run_bwd(x), ora_bwd(x))
+
+
+def check_rounded(got, ref, names=("dq", "dk", "dv")):
+    """bf16 gradients: within one bf16 rounding of the exact value plus 1e-3 rms."""
+    for n in names:
+        a, b = host(got[n]), ref[n]
+        bound = 2.0 ** -8 * np.abs(b) + 1e-3 * np.sqrt(np.mean(b * b))
+        worst = float(np.max(np.abs(a - b) / bound))
+        print(n, "worst/bound %.3g" % worst, flush=True)
+        assert worst <= 1.0, (n, worst)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=2, T=300, Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True),
+    dict(B=1, T=130, Hq=2, Hv=2, K=64, V=64, dtype="bf16", h0=False),
+])
+def test_bf16_gradients_within_rounding(shape):
+    """The README's default: dq, dk, dv in the input dtype."""
+    x = make_inputs(shape, seed=2, grads=True)
+    got, ref = run_bwd(x, grad_dtype=torch.bfloat16), ora_bwd(x)
+    assert got["dq"].dtype == torch.bfloat16
+    check_rounded(got, ref)
+    compare(x, got, ref, names=("dbeta", "dg", "dh0"))
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65])
+def test_short_sequences(T):
+    x = make_inputs(dict(B=2, T=T, Hq=1, Hv=2, K=64, V=64, dtype="fp32", h0=True), seed=3,
+                    grads=True)
+    compare(x, run_bwd(x), ora_bwd(x))
+
+
+def test_without_final_state_gradient():
+    """dht = None is a zero gradient of the final state."""
+    x = make_inputs(dict(B=2, T=150, Hq=2, Hv=4, K=64, V=64, dtype="fp32", h0=True), seed=4,
+                    grads=True)
+    compare(x, run_bwd(x, with_dht=False), ora_bwd(x, with_dht=False))
+
+
+def test_varlen_with_empty_sequence():
+    """Packed sequences, one of them empty: its dh0 is dht, nothing else is touched."""
+    x = make_inputs(dict(lens=[70, 0, 129, 5, 64], Hq=2, Hv=4, K=128, V=64, dtype="bf16",
+                         h0=True), seed=5, grads=True)
+    got, ref = run_bwd(x), ora_bwd(x)
+    compare(x, got, ref)
+    assert np.array_equal(host(got["dh0"])[1], x["dht"][1].astype(np.float64))
+
+
+def test_autograd_function_matches_low_level():
+    """chunk_gated_delta_rule(...).backward() routes to the same kernels."""
+    from gated_delta_rule_85_amd import chunk_gated_delta_rule
+    x = make_inputs(dict(B=1, T=200, Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True), seed=6,
+                    grads=True)
+    d = gpu_inputs(x)
+    leaves = {n: d[n].clone().requires_grad_(True) for n in ("q", "k", "v", "g", "beta",
+                                                             "initial_state")}
+    o, ht = chunk_gated_delta_rule(leaves["q"], leaves["k"], leaves["v"], leaves["g"],
+                                   leaves["beta"], x["scale"], leaves["initial_state"],
+                                   output_final_state=True)
+    loss = (o * dev(x["do"])).sum() + (ht * dev(x["dht"])).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    ref = ora_bwd(x)
+    got = dict(dq=leaves["q"].grad, dk=leaves["k"].grad, dv=leaves["v"].grad,
+               dbeta=leaves["beta"].grad, dg=leaves["g"].grad, dh0=leaves["initial_state"].grad)
+    assert got["dq"].dtype == torch.bfloat16
+    check_rounded(got, ref)
+    compare(x, got, ref, names=("dbeta", "dg", "dh0"))
+
+
+def test_training_shape_full_size_sampled_units():
+    """B=8, T=4096, H_q=32, H_v=64, K=V=128, bf16: the whole backward on the GPU,
+    four (sequence, q/k head) units against the oracle."""
+    x = make_inputs("training", seed=0)
+    got = run_bwd(x)
+    for b, hq in [(0, 0), (3, 17), (5, 9), (7, 31)]:
+        y, hs = slice_units(x, b, hq)
+        y["do"] = x["do"][b:b + 1, :, hs]
+        y["dht"] = x["dht"][b:b + 1, hs]
+        ref = ora_bwd(y)
+        sub = dict(dq=got["dq"][b:b + 1, :, hq:hq + 1], dk=got["dk"][b:b + 1, :, hq:hq + 1],
+                   dv=got["dv"][b:b + 1, :, hs], dbeta=got["dbeta"][b:b + 1, :, hs],
+                   dg=got["dg"][b:b + 1, :, hs], dh0=got["dh0"][b:b + 1, hs])
+        print((b, hq), end=" ")
+        compare(y, sub, ref)
