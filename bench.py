@@ -11,6 +11,11 @@ around each kernel on the library's stream; the dominant kernel's average
 duration gives the roofline entry.  The fp64 CPU oracle is timed on a bounded
 sample of the same workload for the cpu_baseline entry.
 
+``--workload training`` instead times one training step of the operator:
+gdr_fwd (exact scan, writing the g_cum and A the backward needs) followed by
+gdr_bwd (dq, dk, dv in bf16; dbeta, dg, dh0 in fp32) at B=8, T=4096,
+H_q=32, H_v=64, K=V=128, with upstream gradients do and dht.
+
 Prints one JSON line.
 """
 import argparse
@@ -53,6 +58,28 @@ def algorithmic_bytes(cfg, out_bytes=4):
     return {"gdr_chunk_prep": prep, "gdr_scan_output": scan}
 
 
+BWD_STAGES = ("gdr_bwd_tblocks", "gdr_bwd_states", "gdr_bwd_scan", "gdr_bwd_local")
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
+
+
+def bwd_algorithmic_flops(cfg):
+    """Flops each backward kernel must do per launch: the dense products of
+    the chunked adjoint at C=64 (counted once per (chunk, v head); K K^T once
+    per (chunk, q/k head)), not what the tiling recomputes."""
+    B, T, Hq, Hv, K, V = cfg["B"], cfg["T"], cfg["Hq"], cfg["Hv"], cfg["K"], cfg["V"]
+    C = 64
+    units = B * ((T + C - 1) // C) * Hv
+    cc_k, cc_v, ckv = 2 * C * C * K, 2 * C * C * V, 2 * C * K * V
+    # reverse scan: P, K dh', P^T dO, T^T dU, Q^T(e dO), K^T(b e dX)
+    scan = units * (cc_k + ckv + 2 * cc_v + 2 * ckv)
+    # local: P, Kh, Qh, K dh', T X, P^T dO, T^T dU, dO U^T, dU X^T, three K x V
+    # products into dq/dk, T^T dT T^T, and (dP*Gam) K, (dP*Gam)^T Q, dS K
+    local = units * (cc_k + 3 * ckv + 5 * cc_v + 3 * ckv + 2 * 2 * C ** 3 + 3 * cc_k) \
+        + B * ((T + C - 1) // C) * Hq * cc_k
+    states = units * (2 * ckv + cc_v)  # K h, T X, K^T U
+    return {"gdr_bwd_scan": scan, "gdr_bwd_local": local, "gdr_bwd_states": states}
+
+
 def source_hash():
     h = hashlib.sha256()
     for f in ("gdr_scan.hip", "gdr_prep.hip", "gdr_device.hpp"):
@@ -75,9 +102,9 @@ def measured_traffic(kernel, workload):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(x, seconds):
-    """Time the fp64 oracle on whole sequences of the workload until about
-    `seconds` of CPU time have been spent."""
+def cpu_baseline(x, seconds, train=False):
+    """Time the fp64 oracle (forward, plus backward when `train`) on whole
+    sequences of the workload until about `seconds` of CPU time have been spent."""
     import numpy as np
 
     import oracle
@@ -93,21 +120,68 @@ def cpu_baseline(x, seconds):
             np.ascontiguousarray(x["initial_state"][b:b + 1], dtype=np.float64)
         t0 = time.perf_counter()
         oracle.fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], x["scale"], h0)
+        if train:
+            oracle.bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], x["do"][b:b + 1],
+                       x["scale"], initial_state=h0, dht=x["dht"][b:b + 1])
         elapsed += time.perf_counter() - t0
         threads = oracle.last_threads()
         done += 1
         if elapsed >= seconds:
             break
     return {"value": done * T / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d sequences (all %d v heads, T=%d) in %.1f s" %
-                      (done, B, x["v"].shape[2], T, elapsed)}
+            "sample": "%d of %d sequences (all %d v heads, T=%d)%s in %.1f s" %
+                      (done, B, x["v"].shape[2], T, ", forward + backward" if train else "",
+                       elapsed)}
+
+
+class Events:
+    """HIP events handed to the library's timing hooks, one array per step."""
+
+    def __init__(self, steps, n):
+        self.hip = hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+        hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.n = n
+        self.arrays = []
+        for _ in range(steps):
+            arr = (ctypes.c_void_p * n)()
+            for i in range(n):
+                e = ctypes.c_void_p()
+                if hip.hipEventCreate(ctypes.byref(e)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                arr[i] = e.value
+            self.arrays.append(arr)
+
+    def ptr(self, step):
+        return ctypes.addressof(self.arrays[step])
+
+    def stage_ms(self, names):
+        """Average duration of stage s (events 2s, 2s+1) over the steps."""
+        f = ctypes.c_float()
+        out = {}
+        for s, name in enumerate(names):
+            tot = 0.0
+            for arr in self.arrays:
+                if self.hip.hipEventElapsedTime(ctypes.byref(f), arr[2 * s], arr[2 * s + 1]) != 0:
+                    raise RuntimeError("hipEventElapsedTime failed")
+                tot += f.value
+            out[name] = tot / len(self.arrays)
+        return out
+
+    def close(self):
+        for arr in self.arrays:
+            for i in range(self.n):
+                self.hip.hipEventDestroy(arr[i])
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 100; 20 for the training step)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 10; 3)")
     ap.add_argument("--workload", default="prefill_shard")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
@@ -127,6 +201,9 @@ def main():
 
     x = make_inputs(args.workload, seed=0)
     cfg = x["cfg"]
+    train = bool(cfg.get("grads"))
+    steps = args.steps if args.steps is not None else (20 if train else 100)
+    warmup = args.warmup if args.warmup is not None else (3 if train else 10)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dt = torch.bfloat16 if x["dtype"] == "bf16" else torch.float32
@@ -140,37 +217,53 @@ def main():
     n_seq = B if cu is None else cu.numel() - 1
     o = torch.empty((B, T, Hv, V), dtype=torch.float32, device=dev)
     ht = torch.empty((n_seq, Hv, K, V), dtype=torch.float32, device=dev)
+    keep = []  # device buffers that must outlive the timed loop
 
     a = _lib.FwdArgs()
     a.B, a.T, a.H_q, a.H_v, a.K, a.V, a.n_seq = B, T, Hq, Hv, K, V, n_seq
     a.dtype = _lib.BF16 if dt == torch.bfloat16 else _lib.F32
     a.out_dtype = _lib.F32
     a.scale = float(x["scale"])
-    a.cp_mode = _lib.CP_AUTO
+    a.cp_mode = _lib.CP_OFF if train else _lib.CP_AUTO
     a.q, a.k, a.v, a.g, a.beta = q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr()
     a.initial_state = None if h0 is None else h0.data_ptr()
     a.cu_seqlens = None if cu is None else cu.data_ptr()
-    # inference forward: o and the final state (the backward's A and g_cum are not written)
     a.o, a.final_state = o.data_ptr(), ht.data_ptr()
+    if train:  # the forward keeps what the backward reads
+        g_cum = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
+        A = torch.empty((B, T, Hv, 64), dtype=torch.float32, device=dev)
+        keep += [g_cum, A]
+        a.g_cum, a.A = g_cum.data_ptr(), A.data_ptr()
     nbytes = _lib.fwd_workspace(a)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
 
-    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
-    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-    nev = 2 * _lib.FWD_STAGES
-    ev_arrays = []
-    for _ in range(args.steps):
-        arr = (ctypes.c_void_p * nev)()
-        for i in range(nev):
-            e = ctypes.c_void_p()
-            if hip.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
-            arr[i] = e.value
-        ev_arrays.append(arr)
+    bw = None
+    if train:
+        do, dht = put(x["do"], dt), put(x["dht"])
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        db = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
+        dg = torch.empty_like(db)
+        dh0 = torch.empty((n_seq, Hv, K, V), dtype=torch.float32, device=dev)
+        keep += [do, dht, dq, dk, dv, db, dg, dh0]
+        bw = _lib.BwdArgs()
+        bw.B, bw.T, bw.H_q, bw.H_v, bw.K, bw.V, bw.n_seq = B, T, Hq, Hv, K, V, n_seq
+        bw.dtype = bw.grad_dtype = a.dtype
+        bw.scale = a.scale
+        bw.q, bw.k, bw.v, bw.beta = a.q, a.k, a.v, a.beta
+        bw.g_cum, bw.A = a.g_cum, a.A
+        bw.dout, bw.dht, bw.initial_state, bw.cu_seqlens = do.data_ptr(), dht.data_ptr(), \
+            a.initial_state, a.cu_seqlens
+        bw.dq, bw.dk, bw.dv, bw.dbeta, bw.dg = dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), \
+            db.data_ptr(), dg.data_ptr()
+        bw.dh0 = dh0.data_ptr()
+        nb = _lib.bwd_workspace(bw)
+        wsb = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        keep.append(wsb)
+        bw.workspace, bw.workspace_bytes = wsb.data_ptr(), nb
 
+    ev_f = Events(steps, 2 * _lib.FWD_STAGES)
+    ev_b = Events(steps, 2 * _lib.BWD_STAGES) if train else None
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
     if args.copy_mib:
@@ -179,60 +272,72 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    a.events = None
-    for _ in range(args.warmup):
+
+    def step(i=None):
+        a.events = None if i is None else ev_f.ptr(i)
         _lib.fwd(a, sh)
+        if bw is not None:
+            bw.events = None if i is None else ev_b.ptr(i)
+            _lib.bwd(bw, sh)
+
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     start.record(stream)
-    for i in range(args.steps):
-        a.events = ctypes.addressof(ev_arrays[i])
-        _lib.fwd(a, sh)
+    for i in range(steps):
+        step(i)
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms = start.elapsed_time(end) / args.steps
+    ms = start.elapsed_time(end) / steps
 
-    stage_ms = {}
-    f = ctypes.c_float()
-    for s, name in enumerate(STAGES):
-        tot = 0.0
-        for arr in ev_arrays:
-            if hip.hipEventElapsedTime(ctypes.byref(f), arr[2 * s], arr[2 * s + 1]) != 0:
-                raise RuntimeError("hipEventElapsedTime failed")
-            tot += f.value
-        stage_ms[name] = tot / args.steps
-    for arr in ev_arrays:
-        for i in range(nev):
-            hip.hipEventDestroy(arr[i])
+    stage_ms = ev_f.stage_ms(STAGES)
+    ev_f.close()
+    if train:
+        stage_ms.update(ev_b.stage_ms(BWD_STAGES))
+        ev_b.close()
 
     tokens = B * T
     value = tokens / (ms * 1e-3)
     tflops = F_TRI * tokens * Hv / (ms * 1e-3) / 1e12
-    ab = algorithmic_bytes(dict(cfg, B=B, T=T), out_bytes=4)
-    dom = max(ab, key=lambda kname: stage_ms[kname])
-    achieved = ab[dom] / (stage_ms[dom] * 1e-3) / 1e9
-    traffic = measured_traffic(dom, args.workload)
+    wl = "%s: B=%d T=%d H_q=%d H_v=%d K=%d V=%d, %s q/k/v, fp32 g/beta/state/o" % (
+        args.workload, B, T, Hq, Hv, K, V, x["dtype"])
     rec = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "metric": METRIC if not train else
+        "GDN chunked fwd+bwd (training step) tokens/s, H_v=%d K=V=%d T=%d" % (Hv, K, T),
+        "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if dt == torch.bfloat16 else "f32", "data": "synthetic",
-        "config": {"workload": "%s: B=%d T=%d H_q=%d H_v=%d K=%d V=%d, %s q/k/v, fp32 g/beta/state/o"
-                               % (args.workload, B, T, Hq, Hv, K, V, x["dtype"]),
+        "config": {"workload": wl + (", fwd (exact) + bwd, bf16 dq/dk/dv" if train else ""),
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
-        "tflops_algorithmic": tflops,
-        "mfma_bf16_peak_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
         "kernel_ms": stage_ms,
-        "wall_ms_per_step": t_wall * 1e3 / args.steps,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes": ab[dom]},
+        "wall_ms_per_step": t_wall * 1e3 / steps,
     }
+    if not train:
+        ab = algorithmic_bytes(dict(cfg, B=B, T=T), out_bytes=4)
+        dom = max(ab, key=lambda kname: stage_ms[kname])
+        achieved = ab[dom] / (stage_ms[dom] * 1e-3) / 1e9
+        rec["tflops_algorithmic"] = tflops
+        rec["mfma_bf16_peak_frac"] = tflops / MFMA_BF16_PEAK_TFLOPS
+        rec["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": achieved,
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                           "traffic": measured_traffic(dom, args.workload),
+                           "algorithmic_bytes": ab[dom]}
+    else:
+        af = bwd_algorithmic_flops(dict(cfg, B=B, T=T))
+        dom = max(af, key=lambda kname: stage_ms[kname])
+        achieved = af[dom] / (stage_ms[dom] * 1e-3) / 1e12
+        # the backward kernels run their products on fp32 MFMA (v_mfma_f32_16x16x4_f32)
+        rec["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": achieved,
+                           "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "traffic": None,
+                           "algorithmic_flops": af[dom]}
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds, train)
     print(json.dumps(rec), flush=True)
 
 

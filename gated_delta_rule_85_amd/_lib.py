@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libgdr.so")
 ABI_VERSION = 1
 CHUNK = 64
 FWD_STAGES = 3
+BWD_STAGES = 4
 
 OK, EINVAL, ENOTSUP, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
@@ -47,7 +48,7 @@ class BwdArgs(ctypes.Structure):
         ("q", _p), ("k", _p), ("v", _p), ("g_cum", _p), ("beta", _p), ("A", _p),
         ("dout", _p), ("dht", _p), ("initial_state", _p), ("cu_seqlens", _p),
         ("dq", _p), ("dk", _p), ("dv", _p), ("dbeta", _p), ("dg", _p), ("dh0", _p),
-        ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
+        ("events", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 

@@ -286,10 +286,15 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
     bp.V = (int)a->V;
     bp.scale = a->scale;
 
+    auto mark = [&](int i) {
+        return !a->events || hipEventRecord(a->events[i], stream) == hipSuccess;
+    };
     if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, chunk_off, (int)pl.n_seq, stream) != hipSuccess)
         return GDR_ELAUNCH;
+    if (!mark(0)) return GDR_ELAUNCH;
+    if (pl.tokens > 0 && launch_tblocks(dt, bp, (int)pl.nt_ub, stream) != hipSuccess) return GDR_ELAUNCH;
+    if (!mark(1) || !mark(2)) return GDR_ELAUNCH;
     if (pl.tokens > 0) {
-        if (launch_tblocks(dt, bp, (int)pl.nt_ub, stream) != hipSuccess) return GDR_ELAUNCH;
         // chunk-start states: the exact forward scan without its output
         ScanParams sp;
         sp.q = a->q;
@@ -312,8 +317,10 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
         sp.n_seg = 1;
         if (launch_scan_states(dt, (int)a->K, sp, stream) != hipSuccess) return GDR_ELAUNCH;
     }
+    if (!mark(3) || !mark(4)) return GDR_ELAUNCH;
     const Dt gt = a->grad_dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
-    if (launch_bwd(dt, gt, (int)a->K, bp, pl.tokens > 0 ? (int)pl.nt_ub : 0, n_units, stream) != hipSuccess)
+    const hipEvent_t *ev = a->events ? a->events + 5 : nullptr;  // reverse scan end, local start/end
+    if (launch_bwd(dt, gt, (int)a->K, bp, pl.tokens > 0 ? (int)pl.nt_ub : 0, n_units, ev, stream) != hipSuccess)
         return GDR_ELAUNCH;
     return GDR_OK;
 }

@@ -521,18 +521,25 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(const BwdParams p) {
 }
 
 template <typename In, typename Gt, int KD>
-hipError_t launch_bwd_t(const BwdParams &p, int n_chunks_ub, int n_units, hipStream_t s) {
+hipError_t launch_bwd_t(const BwdParams &p, int n_chunks_ub, int n_units, const hipEvent_t *ev, hipStream_t s) {
     hipLaunchKernelGGL((bwd_scan_kernel<In, KD>), dim3(n_units * (p.V / 64)), dim3(NTHR), 0, s, p, n_units);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || n_chunks_ub == 0) return e;
-    hipLaunchKernelGGL((bwd_local_kernel<In, Gt, KD>), dim3(n_chunks_ub, p.Hq), dim3(NTHR), 0, s, p);
-    return hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ev && ((e = hipEventRecord(ev[0], s)) != hipSuccess || (e = hipEventRecord(ev[1], s)) != hipSuccess))
+        return e;
+    if (n_chunks_ub > 0) {
+        hipLaunchKernelGGL((bwd_local_kernel<In, Gt, KD>), dim3(n_chunks_ub, p.Hq), dim3(NTHR), 0, s, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (ev) e = hipEventRecord(ev[2], s);
+    return e;
 }
 
 template <typename In, typename Gt>
-hipError_t launch_bwd_k(int K, const BwdParams &p, int n_chunks_ub, int n_units, hipStream_t s) {
-    return K == 128 ? launch_bwd_t<In, Gt, 128>(p, n_chunks_ub, n_units, s)
-                    : launch_bwd_t<In, Gt, 64>(p, n_chunks_ub, n_units, s);
+hipError_t launch_bwd_k(int K, const BwdParams &p, int n_chunks_ub, int n_units, const hipEvent_t *ev,
+                        hipStream_t s) {
+    return K == 128 ? launch_bwd_t<In, Gt, 128>(p, n_chunks_ub, n_units, ev, s)
+                    : launch_bwd_t<In, Gt, 64>(p, n_chunks_ub, n_units, ev, s);
 }
 
 }  // namespace
@@ -546,12 +553,13 @@ hipError_t launch_tblocks(Dt dt, const BwdParams &p, int n_chunks_ub, hipStream_
     return hipGetLastError();
 }
 
-hipError_t launch_bwd(Dt dt, Dt gt, int K, const BwdParams &p, int n_chunks_ub, int n_units, hipStream_t s) {
+hipError_t launch_bwd(Dt dt, Dt gt, int K, const BwdParams &p, int n_chunks_ub, int n_units,
+                      const hipEvent_t *ev, hipStream_t s) {
     if (dt == Dt::BF16)
-        return gt == Dt::BF16 ? launch_bwd_k<bf16, bf16>(K, p, n_chunks_ub, n_units, s)
-                              : launch_bwd_k<bf16, float>(K, p, n_chunks_ub, n_units, s);
-    return gt == Dt::BF16 ? launch_bwd_k<float, bf16>(K, p, n_chunks_ub, n_units, s)
-                          : launch_bwd_k<float, float>(K, p, n_chunks_ub, n_units, s);
+        return gt == Dt::BF16 ? launch_bwd_k<bf16, bf16>(K, p, n_chunks_ub, n_units, ev, s)
+                              : launch_bwd_k<bf16, float>(K, p, n_chunks_ub, n_units, ev, s);
+    return gt == Dt::BF16 ? launch_bwd_k<float, bf16>(K, p, n_chunks_ub, n_units, ev, s)
+                          : launch_bwd_k<float, float>(K, p, n_chunks_ub, n_units, ev, s);
 }
 
 }  // namespace gdr

@@ -49,6 +49,7 @@ extern "C" {
 #define GDR_ABI_VERSION 1
 #define GDR_CHUNK 64
 #define GDR_FWD_STAGES 3
+#define GDR_BWD_STAGES 4
 
 /* return codes */
 #define GDR_OK 0
@@ -122,6 +123,10 @@ typedef struct {
     float *dg;                  /* [B,T,H_v] gradient w.r.t. the raw per-token g */
     float *dh0;                 /* [N,H_v,K,V] gradient of initial_state (NULL initial_state
                                    means zeros); NULL = not wanted */
+    /* timing hook: NULL, or a HOST array of 2*GDR_BWD_STAGES events recorded
+       before and after each stage (T-block rebuild, chunk-start state
+       recompute, reverse scan, chunk-local gradients) */
+    hipEvent_t *events;
     void *workspace;
     size_t workspace_bytes;
 } gdr_bwd_args;
