@@ -20,7 +20,7 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I" + os.path.join(ROOT, "include")]
-SOURCES = ["gdr_api.hip", "gdr_prep.hip", "gdr_scan.hip", "gdr_bwd.hip"]
+SOURCES = ["gdr_api.hip", "gdr_prep.hip", "gdr_scan.hip", "gdr_bwd.hip", "gdr_bwd_mfma.hip"]
 
 
 def _compile(src):

@@ -522,8 +522,13 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(const BwdParams p) {
 
 template <typename In, typename Gt, int KD>
 hipError_t launch_bwd_t(const BwdParams &p, int n_chunks_ub, int n_units, const hipEvent_t *ev, hipStream_t s) {
-    hipLaunchKernelGGL((bwd_scan_kernel<In, KD>), dim3(n_units * (p.V / 64)), dim3(NTHR), 0, s, p, n_units);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if constexpr (sizeof(In) == 2) {
+        e = launch_bwd_scan_bf16(KD, p, n_units, s);
+    } else {
+        hipLaunchKernelGGL((bwd_scan_kernel<In, KD>), dim3(n_units * (p.V / 64)), dim3(NTHR), 0, s, p, n_units);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
     if (ev && ((e = hipEventRecord(ev[0], s)) != hipSuccess || (e = hipEventRecord(ev[1], s)) != hipSuccess))
         return e;

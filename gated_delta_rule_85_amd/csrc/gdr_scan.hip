@@ -34,30 +34,13 @@
 // state when that window reaches chunk 0) and runs the scan without output
 // over the window before its own chunks.
 #include "gdr_kernels.hpp"
+#include "gdr_lds.hpp"
 
 namespace gdr {
 
 namespace {
 
 constexpr int BV = 64;  // value columns per workgroup (16 per wave)
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// wave-wide copy of 64 x 16 bytes: lane l's source -> lds_base + 16 l
-__device__ __forceinline__ void dma16(const void *src, char *lds_base) {
-    __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
-
-// gfx950 transposing LDS read: within each 16-lane group, lane i receives
-// element i%4 of the 8-byte chunks read by source lanes i/4 + 4j, j = 0..3.
-__device__ __forceinline__ bf16x4 lds_tr4(const char *p) {
-    v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
-    return __builtin_bit_cast(bf16x4, v);
-}
 
 template <typename In, int KD> struct Cfg {
     static constexpr bool BF = sizeof(In) == 2;
@@ -75,49 +58,6 @@ template <typename In, int KD> struct Cfg {
     static_assert(NKI % 2 == 0 && NVI % 2 == 0, "tile copies spread over 2 waves");
     static constexpr int DT = KD / 16, DP = KD / 32;
 };
-
-// A-operand fragment rows (row0 + lane16, bytes off..off+7 and off+32..) of a swizzled tile
-template <typename In, int ROWB>
-__device__ __forceinline__ typename Ops<In>::X frag(const char *tile, int row, int byte) {
-    using S = Swz<ROWB>;
-    return Ops<In>::load(reinterpret_cast<const In *>(tile + S::off(row, byte)),
-                         reinterpret_cast<const In *>(tile + S::off(row, byte + 16 * sizeof(In))));
-}
-
-// 4 consecutive rows r0+4g..r0+4g+3 of column c0+lane16, as the B operand of
-// an accumulator-ordered tile expects
-template <typename In, int ROWB>
-__device__ __forceinline__ f32x4 rows4(const char *tile, int r0, int c0) {
-    using S = Swz<ROWB>;
-    const int n = ln16(), g = lg4();
-    if constexpr (sizeof(In) == 2) {
-        const bf16x4 v = lds_tr4(tile + S::off(r0 + 4 * g + (n >> 2), 2 * (c0 + 4 * (n & 3))));
-        return __builtin_convertvector(v, f32x4);
-    } else {
-        f32x4 r;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            r[j] = *reinterpret_cast<const float *>(tile + S::off(r0 + 4 * g + j, 4 * (c0 + n)));
-        return r;
-    }
-}
-
-// A operand of K^T: rows = key dims d0 + lane16, k = tokens 32 ip .. 32 ip + 31
-template <typename In, int ROWB>
-__device__ __forceinline__ typename Ops<In>::X kt_operand(const char *Ks, int d0, int ip) {
-    typename Ops<In>::X r;
-    if constexpr (sizeof(In) == 2) {
-        using S = Swz<ROWB>;
-        const int n = ln16(), g = lg4();
-        const int row = 32 * ip + 4 * g + (n >> 2), byte = 2 * (d0 + 4 * (n & 3));
-        r.b0 = lds_tr4(Ks + S::off(row, byte));
-        r.b1 = lds_tr4(Ks + S::off(row + 16, byte));
-    } else {
-        r.b0 = rows4<In, ROWB>(Ks, 32 * ip, d0);
-        r.b1 = rows4<In, ROWB>(Ks, 32 * ip + 16, d0);
-    }
-    return r;
-}
 
 template <typename T> struct OutVec;
 template <> struct OutVec<float> {
