@@ -18,14 +18,18 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I" + os.path.join(ROOT, "include")]
-SOURCES = ["gdr_api.hip", "gdr_prep.hip", "gdr_scan.hip", "gdr_bwd.hip", "gdr_bwd_mfma.hip"]
+# MFMA operands and results in VGPRs rather than AGPRs (fewer copies in the
+# scan's register-resident loops); the backward's LDS-fed kernels are left to
+# the default allocation, which the option crashes on.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+SOURCES = {"gdr_api.hip": VGPR_FORM, "gdr_prep.hip": VGPR_FORM, "gdr_scan.hip": VGPR_FORM,
+           "gdr_bwd.hip": VGPR_FORM, "gdr_bwd_mfma.hip": []}
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + SOURCES[src] + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

@@ -533,8 +533,13 @@ hipError_t launch_bwd_t(const BwdParams &p, int n_chunks_ub, int n_units, const 
     if (ev && ((e = hipEventRecord(ev[0], s)) != hipSuccess || (e = hipEventRecord(ev[1], s)) != hipSuccess))
         return e;
     if (n_chunks_ub > 0) {
-        hipLaunchKernelGGL((bwd_local_kernel<In, Gt, KD>), dim3(n_chunks_ub, p.Hq), dim3(NTHR), 0, s, p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if constexpr (sizeof(In) == 2) {
+            e = launch_bwd_local_bf16(sizeof(Gt) == 2 ? Dt::BF16 : Dt::F32, KD, p, n_chunks_ub, s);
+        } else {
+            hipLaunchKernelGGL((bwd_local_kernel<In, Gt, KD>), dim3(n_chunks_ub, p.Hq), dim3(NTHR), 0, s, p);
+            e = hipGetLastError();
+        }
+        if (e != hipSuccess) return e;
     }
     if (ev) e = hipEventRecord(ev[2], s);
     return e;

@@ -77,6 +77,7 @@ hipError_t launch_tblocks(Dt dt, const BwdParams &p, int n_chunks_ub, hipStream_
 hipError_t launch_bwd(Dt dt, Dt gt, int K, const BwdParams &p, int n_chunks_ub, int n_units,
                       const hipEvent_t *ev, hipStream_t s);
 hipError_t launch_bwd_scan_bf16(int K, const BwdParams &p, int n_units, hipStream_t s);
+hipError_t launch_bwd_local_bf16(Dt gt, int K, const BwdParams &p, int n_chunks_ub, hipStream_t s);
 size_t tblock_bytes(Dt dt);
 int scan_vtile(Dt dt, int K, int V);  // V columns per scan workgroup
 
