@@ -160,7 +160,6 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
     constexpr int KROW = KD * 2, DROW = 64 * 2, PROW = 64 * 2, PPLANE = CH * PROW;
     constexpr int DT = KD / 16, DP = KD / 32;
     using TB = TBlock<bf16>;
-    using SP = Swz<PROW>;
     __shared__ __attribute__((aligned(16))) char Ks[CH * KROW];
     __shared__ __attribute__((aligned(16))) char Qs[CH * KROW];
     __shared__ __attribute__((aligned(16))) char Ds[CH * DROW];
@@ -283,26 +282,34 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
 // ------------------------------------------------------- chunk-local terms
 // One workgroup per (chunk, q/k head); its v heads in turn, the value
 // dimension in blocks of 64 columns.  In a block, wave w first works on
-// columns 16 w .. 16 w + 15 with tokens on the rows (K h, Q h, K dh', X,
-// U~ = T X, dU~, dX = T^T dU~, dv), then writes U~, dU~, X and
-// -diag(beta e) dX to LDS as split planes; the products over the value
-// dimension (dP, dT and the value parts of dq, dk) are then accumulated on
-// the tiles each wave owns: column strip w of the 64 x 64 matrices and key
-// tiles w, w + 4 of the 64 x K ones.  After the value blocks, the 64 x 64
-// stage forms dP * Gam, T^T dT T^T, dA, dS and the gate-gradient sums, and
-// dq, dk take their score and K K^T terms; dq, dk add up over the v heads.
+// columns 16 w .. 16 w + 15 with tokens on the rows: K h and K dh' (h, dh'
+// staged through LDS in 64-row halves as split planes), X, U~ = T X,
+// dU~ = diag(r) K dh' + s P^T dO, dX = T^T dU~ and dv; it writes U~ and dX
+// to LDS as split planes.  Then the products over the value dimension are
+// accumulated on the tiles each wave owns: column strip w of
+// dP = s dO U~^T and dA = -dX U~^T (= -T^T dT T^T with dT = dU~ X^T), and
+// key tiles w, w + 4 of dO h^T, U~ dh'^T, dX h^T for dq and dk.  Row sums
+// over the value dimension come from the same tiles where possible
+// (sum_c dO.(Q h) = sum_d Q.(dO h^T) and alike).  After the value blocks
+// the 64 x 64 stage forms dP * Gam and dS = diag(beta)(dA * Gam) with the
+// gate-gradient sums, and dq, dk take their score and K K^T terms; dq, dk
+// add up over the v heads of the q/k head.
 template <typename Gt, int KD>
 __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
     constexpr int KROW = KD * 2, VROW = 128, PROW = 128, PPL = CH * PROW;
-    constexpr int DP = KD / 32, TD = KD / 64;
-    constexpr int NQ = 7;  // row sums: dO.Qh, dX.Kh, U~.Kdh', dX.Y, of dP*P, of dA*A, dbeta through A
+    constexpr int DP = KD / 32, TD = KD / 64, NH = KD / 64;  // 64-row halves of h
+    constexpr int NQ = 7;
+    // row sums: 0 Q.(dO h^T), 1 K.(dX h^T), 2 K.(U~ dh'^T), 3 dX.V, 4 dP*P, 5 dA*A, 6 dbeta via A
     using TB = TBlock<bf16>;
+    using S128 = Swz<128>;
     __shared__ __attribute__((aligned(16))) char Ks[CH * KROW];
     __shared__ __attribute__((aligned(16))) char Qs[CH * KROW];
     __shared__ __attribute__((aligned(16))) char Tb[TB::BYTES];
     __shared__ __attribute__((aligned(16))) char Pt[2 * PPL];
     __shared__ __attribute__((aligned(16))) char Ds[CH * VROW];
-    __shared__ __attribute__((aligned(16))) char Wm[4][2 * PPL];
+    __shared__ __attribute__((aligned(16))) char Vs[CH * VROW];
+    __shared__ __attribute__((aligned(16))) char Wm[2][2 * PPL];  // U~, dX; later dP * Gam, dS
+    __shared__ __attribute__((aligned(16))) char Hs[2][2 * PPL];  // h, dh' rows of one half
     __shared__ float rs[NQ][4][CH];
     __shared__ float cs[2][CH];
     __shared__ float red[4];
@@ -315,15 +322,15 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
     const int64_t ts = bos + (int64_t)c * CH;
     const int n = (int)min<int64_t>(CH, eos - ts);
     const int G = p.Hv / p.Hq;
-    const int w = __builtin_amdgcn_readfirstlane(wave_id()), n16 = ln16(), g = lg4();
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(wave_id()), n16 = ln16(), g = lg4();
     const int V = p.V;
     const int64_t KV = (int64_t)KD * V;
     const char *kp = reinterpret_cast<const char *>(p.k), *qp = reinterpret_cast<const char *>(p.q);
-    const bf16 *vp = reinterpret_cast<const bf16 *>(p.v);
-    const char *dop = reinterpret_cast<const char *>(p.dout);
+    const char *vpc = reinterpret_cast<const char *>(p.v), *dop = reinterpret_cast<const char *>(p.dout);
     Gt *dvp = reinterpret_cast<Gt *>(p.dv);
     const float *sc = reinterpret_cast<const float *>(Tb + TB::SC);
     const float *gam = sc, *eg = sc + CH, *rr = sc + 2 * CH, *bet = sc + 3 * CH;
+    const int ci = 16 * w + n16;  // this lane's column in a 64-wide strip
 
     copy_tile<KROW>(Ks, kp + (ts * p.Hq + hq) * KROW, (int64_t)p.Hq * KROW, n - 1, w);
     copy_tile<KROW>(Qs, qp + (ts * p.Hq + hq) * KROW, (int64_t)p.Hq * KROW, n - 1, w);
@@ -336,69 +343,79 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
 
     for (int gi = 0; gi < G; ++gi) {
         const int hv = hq * G + gi;
+        const int64_t hoff = ((int64_t)gid * p.Hv + hv) * KV;
         __syncthreads();  // the previous v head is done with every LDS array
         copy_flat(Tb, p.tblk + ((int64_t)gid * p.Hv + hv) * TB::BYTES, TB::BYTES, w);
         wait_dma();
         __syncthreads();
         scores_t<KD>(Pt, Qs, Ks, gam, n, w);
 
-        f32x4 dPa[4], dTa[4];
+        f32x4 dPa[4], dAa[4];
 #pragma unroll
-        for (int tr = 0; tr < 4; ++tr) dPa[tr] = dTa[tr] = zero4();
-        float rsum[4][4];
+        for (int tr = 0; tr < 4; ++tr) dPa[tr] = dAa[tr] = zero4();
+        float rsum[NQ - 3][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < NQ - 3; ++q)
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) rsum[q][rt] = 0.f;
         float dec = 0.f;
-        const int64_t hoff = ((int64_t)gid * p.Hv + hv) * KV;
+
+        // stage rows [64 hf, 64 hf + 64) of the h and dh' block (columns vb ..) as split planes
+        auto stage = [&](int hf, int vb, bool dot) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int idx = tid + NTHR * it, row = idx >> 4, c4 = idx & 15;
+                const int64_t o = hoff + (int64_t)(64 * hf + row) * V + vb + 4 * c4;
+                const f32x4 hx = *reinterpret_cast<const f32x4 *>(p.hs + o);
+                const f32x4 dx = *reinterpret_cast<const f32x4 *>(p.dhs + o);
+                if (dot) dec += hx[0] * dx[0] + hx[1] * dx[1] + hx[2] * dx[2] + hx[3] * dx[3];
+                bf16x4 hh, hl, dh, dl;
+                split4(hx, hh, hl);
+                split4(dx, dh, dl);
+                const int off = S128::off(row, 8 * c4);
+                *reinterpret_cast<bf16x4 *>(Hs[0] + off) = hh;
+                *reinterpret_cast<bf16x4 *>(Hs[0] + PPL + off) = hl;
+                *reinterpret_cast<bf16x4 *>(Hs[1] + off) = dh;
+                *reinterpret_cast<bf16x4 *>(Hs[1] + PPL + off) = dl;
+            }
+        };
 
         for (int vb = 0; vb < V; vb += 64) {
-            __syncthreads();  // the previous block is done with Ds and Wm; scores complete
+            __syncthreads();  // the previous block is done with Ds, Vs, Wm, Hs; scores complete
             copy_tile<VROW>(Ds, dop + ((ts * p.Hv + hv) * V + vb) * 2, (int64_t)p.Hv * V * 2, n - 1, w);
-            const int colg = vb + 16 * w + n16;
-            // K h, K dh' for this wave's columns (h, dh' in accumulator order from HBM)
+            copy_tile<VROW>(Vs, vpc + ((ts * p.Hv + hv) * V + vb) * 2, (int64_t)p.Hv * V * 2, n - 1, w);
+            // K h, K dh' for this wave's columns, over the halves of the key dimension
             f32x4 kh[4], kd[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) kh[rt] = kd[rt] = zero4();
 #pragma unroll 1
-            for (int dp = 0; dp < DP; ++dp) {
-                f32x4 h0, h1, d0, d1;
+            for (int hf = 0; hf < NH; ++hf) {
+                if (hf > 0) __syncthreads();
+                stage(hf, vb, true);
+                __syncthreads();
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t o0 = hoff + (int64_t)(32 * dp + 4 * g + i) * V + colg, o1 = o0 + 16 * V;
-                    h0[i] = p.hs[o0];
-                    h1[i] = p.hs[o1];
-                    d0[i] = p.dhs[o0];
-                    d1[i] = p.dhs[o1];
-                }
+                for (int ip = 0; ip < 2; ++ip) {
+                    const OpS hb = kt_s<128>(Hs[0], PPL, 16 * w, ip), db = kt_s<128>(Hs[1], PPL, 16 * w, ip);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dec += h0[i] * d0[i] + h1[i] * d1[i];
-                const OpS hb = Ops<bf16>::split(h0, h1), db = Ops<bf16>::split(d0, d1);
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    const OpX kf = frag<bf16, KROW>(Ks, 16 * rt + n16, (32 * dp + 4 * g) * 2);
-                    kh[rt] = mma(kh[rt], kf, hb);
-                    kd[rt] = mma(kd[rt], kf, db);
+                    for (int rt = 0; rt < 4; ++rt) {
+                        const OpX kf = frag<bf16, KROW>(Ks, 16 * rt + n16, (64 * hf + 32 * ip + 4 * g) * 2);
+                        kh[rt] = mma(kh[rt], kf, hb);
+                        kd[rt] = mma(kd[rt], kf, db);
+                    }
                 }
             }
-            // Y = V - diag(e) K h, X = diag(beta) Y
-            f32x4 y[4], x[4];
+            wait_dma();
+            __syncthreads();  // dO and V blocks landed
+            // X = diag(beta) (V - diag(e) K h)
+            f32x4 x[4], vv[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const int r0 = 16 * rt + 4 * g;
                 const f32x4 e4 = *reinterpret_cast<const f32x4 *>(eg + r0);
                 const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bet + r0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tok = r0 + i;
-                    const float vv = tok < n ? float(vp[((ts + tok) * p.Hv + hv) * V + colg]) : 0.f;
-                    y[rt][i] = vv - e4[i] * kh[rt][i];
-                }
-                x[rt] = b4 * y[rt];
+                vv[rt] = rows4<bf16, VROW>(Vs, 16 * rt, 16 * w);
+                x[rt] = b4 * (vv[rt] - e4 * kh[rt]);
             }
-            wait_dma();
-            __syncthreads();  // dO block landed
             const OpS xs0 = Ops<bf16>::split(x[0], x[1]), xs1 = Ops<bf16>::split(x[2], x[3]);
             // U~ = T X (T lower triangular)
             f32x4 u[4];
@@ -424,171 +441,115 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
             }
             // dX = T^T dU~
             const OpS dus0 = Ops<bf16>::split(du[0], du[1]), dus1 = Ops<bf16>::split(du[2], du[3]);
-            f32x4 dx[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                dx[rt] = zero4();
+                f32x4 dx = zero4();
 #pragma unroll
                 for (int ip = rt / 2; ip < 2; ++ip)
-                    dx[rt] = mma(dx[rt], kt_s<TB::ROWB>(Tb, TB::PLANE, 16 * rt, ip), ip == 0 ? dus0 : dus1);
-            }
-            // dv = diag(beta) dX; row sums; U~, dU~, X, -diag(beta e) dX to LDS
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
+                    dx = mma(dx, kt_s<TB::ROWB>(Tb, TB::PLANE, 16 * rt, ip), ip == 0 ? dus0 : dus1);
                 const int r0 = 16 * rt + 4 * g;
-                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(eg + r0);
                 const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bet + r0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tok = r0 + i;
-                    if (tok < n) dvp[((ts + tok) * p.Hv + hv) * V + colg] = Gt(b4[i] * dx[rt][i]);
+                    if (tok < n) dvp[((ts + tok) * p.Hv + hv) * V + vb + ci] = Gt(b4[i] * dx[i]);
+                    put_s(Wm[0], PPL, tok, ci, u[rt][i]);
+                    put_s(Wm[1], PPL, tok, ci, dx[i]);
                 }
-                rsum[1][rt] += rowsum16(dx[rt] * kh[rt]);
-                rsum[3][rt] += rowsum16(dx[rt] * y[rt]);
-                const f32x4 sdx = -(b4 * e4) * dx[rt];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    put_s(Wm[0], PPL, r0 + i, 16 * w + n16, u[rt][i]);
-                    put_s(Wm[1], PPL, r0 + i, 16 * w + n16, du[rt][i]);
-                    put_s(Wm[2], PPL, r0 + i, 16 * w + n16, x[rt][i]);
-                    put_s(Wm[3], PPL, r0 + i, 16 * w + n16, sdx[i]);
-                }
+                rsum[3][rt] += rowsum16(dx * vv[rt]);
             }
-            __syncthreads();
-            // products over this block's 64 value columns (two k blocks of 32)
-#pragma unroll 1
+            __syncthreads();  // U~, dX planes complete; Hs holds the last half
+            // dP += dO U~^T, dA -= dX U~^T on strip w (two k blocks of 32 value columns)
+#pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const int kbyte = (32 * kb + 4 * g) * 2;
-                const OpS ub = frag_s<PROW>(Wm[0], PPL, 16 * w + n16, kbyte);  // U~^T, tokens of strip w
-                const OpS xb = frag_s<PROW>(Wm[2], PPL, 16 * w + n16, kbyte);  // X^T
+                const OpS ub = frag_s<PROW>(Wm[0], PPL, ci, kbyte);  // U~^T for the tokens of strip w
 #pragma unroll
                 for (int tr = 0; tr < 4; ++tr) {
                     dPa[tr] = mma(dPa[tr], frag<bf16, VROW>(Ds, 16 * tr + n16, kbyte), ub);
-                    dTa[tr] = mma(dTa[tr], frag_s<PROW>(Wm[1], PPL, 16 * tr + n16, kbyte), xb);
+                    dAa[tr] = mma(dAa[tr], frag_s<PROW>(Wm[1], PPL, 16 * tr + n16, kbyte), ub);
                 }
             }
-            // value parts of dq, dk: s diag(e) dO h^T and diag(r) U~ dh'^T (row scales applied
-            // per block), - diag(beta e) dX h^T (scale already in the plane).  The row sums
-            // of dO * (Q h) and U~ * (K dh') are those of Q * (dO h^T) and K * (U~ dh'^T).
-            f32x4 sq[4], sk[4];
+            // value parts of dq, dk on key tiles w + 4 s (the half holding them, last half first)
 #pragma unroll
-            for (int tr = 0; tr < 4; ++tr) sq[tr] = sk[tr] = zero4();
+            for (int s = TD - 1; s >= 0; --s) {
+                if (s != NH - 1) {
+                    __syncthreads();  // every wave is done with the staged half
+                    stage(s, vb, false);
+                    __syncthreads();
+                }
+                f32x4 aQ[4], aKa[4], aKe[4];
 #pragma unroll
-            for (int s = 0; s < TD; ++s) {
-                const int td = w + 4 * s;
-                f32x4 aQ[4], aKa[4];
+                for (int tr = 0; tr < 4; ++tr) aQ[tr] = aKa[tr] = aKe[tr] = zero4();
 #pragma unroll
-                for (int tr = 0; tr < 4; ++tr) aQ[tr] = aKa[tr] = zero4();
-#pragma unroll 1
                 for (int kb = 0; kb < 2; ++kb) {
                     const int kbyte = (32 * kb + 4 * g) * 2;
-                    // h^T, dh'^T: rows d = 16 td + lane16, value columns vb + 32 kb + 4 g ..
-                    const int64_t o = hoff + (int64_t)(16 * td + n16) * V + vb + 32 * kb + 4 * g;
-                    const OpS hT = Ops<bf16>::split(*reinterpret_cast<const f32x4 *>(p.hs + o),
-                                                    *reinterpret_cast<const f32x4 *>(p.hs + o + 16));
-                    const OpS dhT = Ops<bf16>::split(*reinterpret_cast<const f32x4 *>(p.dhs + o),
-                                                     *reinterpret_cast<const f32x4 *>(p.dhs + o + 16));
+                    const OpS hT = frag_s<128>(Hs[0], PPL, ci, kbyte);   // h^T: rows d = 64 s + 16 w + lane16
+                    const OpS dhT = frag_s<128>(Hs[1], PPL, ci, kbyte);
 #pragma unroll
                     for (int tr = 0; tr < 4; ++tr) {
                         aQ[tr] = mma(aQ[tr], frag<bf16, VROW>(Ds, 16 * tr + n16, kbyte), hT);
                         aKa[tr] = mma(aKa[tr], frag_s<PROW>(Wm[0], PPL, 16 * tr + n16, kbyte), dhT);
-                        dkt[s][tr] = mma(dkt[s][tr], frag_s<PROW>(Wm[3], PPL, 16 * tr + n16, kbyte), hT);
+                        aKe[tr] = mma(aKe[tr], frag_s<PROW>(Wm[1], PPL, 16 * tr + n16, kbyte), hT);
                     }
                 }
+                const int td = w + 4 * s;
 #pragma unroll
                 for (int tr = 0; tr < 4; ++tr) {
-                    const f32x4 e4 = *reinterpret_cast<const f32x4 *>(eg + 16 * tr + 4 * g);
-                    const f32x4 r4 = *reinterpret_cast<const f32x4 *>(rr + 16 * tr + 4 * g);
+                    const int r0 = 16 * tr + 4 * g;
+                    const f32x4 e4 = *reinterpret_cast<const f32x4 *>(eg + r0);
+                    const f32x4 r4 = *reinterpret_cast<const f32x4 *>(rr + r0);
+                    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bet + r0);
                     dqt[s][tr] += (p.scale * e4) * aQ[tr];
-                    dkt[s][tr] += r4 * aKa[tr];
-                    sq[tr] += rows4<bf16, KROW>(Qs, 16 * tr, 16 * td) * aQ[tr];
-                    sk[tr] += rows4<bf16, KROW>(Ks, 16 * tr, 16 * td) * aKa[tr];
+                    dkt[s][tr] += r4 * aKa[tr] - (b4 * e4) * aKe[tr];
+                    const f32x4 q4 = rows4<bf16, KROW>(Qs, 16 * tr, 16 * td);
+                    const f32x4 k4 = rows4<bf16, KROW>(Ks, 16 * tr, 16 * td);
+                    rsum[0][tr] += rowsum16(q4 * aQ[tr]);
+                    rsum[1][tr] += rowsum16(k4 * aKe[tr]);
+                    rsum[2][tr] += rowsum16(k4 * aKa[tr]);
                 }
-            }
-#pragma unroll
-            for (int tr = 0; tr < 4; ++tr) {
-                rsum[0][tr] += rowsum16(sq[tr]);
-                rsum[2][tr] += rowsum16(sk[tr]);
             }
         }
         const int rtok = 4 * g + (n16 >> 2);  // token (within a 16-row tile) of this lane's row sums
         if ((n16 & 3) == 0) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < NQ - 3; ++q)
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) rs[q][w][16 * rt + rtok] = rsum[q][rt];
         }
         dec = sum_wave(dec);
         if (lane_id() == 0) red[w] = dec;
         __syncthreads();  // every wave is done with the block planes
-        // W1 = dP * Gam on i <= r < n (Wm[0]); sums of dP * P; M1 = T^T dT (Wm[1]); S = K K^T strip
-        const int ci = 16 * w + n16;  // this lane's column of the strips
-        float zac = 0.f, zar[4];
+        // dP * Gam on i <= r < n (Wm[0]) and sums of dP * P; dS = diag(beta) (dA * Gam) on i < r
+        // (Wm[1]) and sums of dA * A, with A = diag(beta) (K K^T * Gam)
+        float zac = 0.f, zbc = 0.f, zar[4], zbr[4], dbr[4];
 #pragma unroll
         for (int tr = 0; tr < 4; ++tr) {
-            f32x4 za;
+            f32x4 sS = zero4();
+#pragma unroll
+            for (int dp = 0; dp < DP; ++dp)
+                sS = mma(sS, frag<bf16, KROW>(Ks, 16 * tr + n16, (32 * dp + 4 * g) * 2),
+                         frag<bf16, KROW>(Ks, ci, (32 * dp + 4 * g) * 2));
+            f32x4 za, zb, dbv;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * tr + 4 * g + i;
                 const float dpv = p.scale * dPa[tr][i];
-                const float w1 = (ci <= r && r < n) ? dpv * fast_exp(gam[r] - gam[ci]) : 0.f;
-                put_s(Wm[0], PPL, r, ci, w1);
+                const float G_ = ci <= r ? fast_exp(gam[r] - gam[ci]) : 0.f;
+                put_s(Wm[0], PPL, r, ci, r < n ? dpv * G_ : 0.f);
                 za[i] = ci <= r ? dpv * get_s(Pt, PPL, ci, r) : 0.f;  // P^T below its diagonal is not stored
+                const float da = ci < r ? -dAa[tr][i] : 0.f;
+                dbv[i] = da * sS[i] * G_;
+                zb[i] = bet[r] * dbv[i];
+                put_s(Wm[1], PPL, r, ci, bet[r] * da * G_);
                 zac += za[i];
-            }
-            zar[tr] = rowsum16(za);
-        }
-        zac = sum_groups(zac);
-        {
-            const OpS dts0 = Ops<bf16>::split(dTa[0], dTa[1]), dts1 = Ops<bf16>::split(dTa[2], dTa[3]);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                f32x4 m = zero4();
-#pragma unroll
-                for (int ip = rt / 2; ip < 2; ++ip)
-                    m = mma(m, kt_s<TB::ROWB>(Tb, TB::PLANE, 16 * rt, ip), ip == 0 ? dts0 : dts1);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) put_s(Wm[1], PPL, 16 * rt + 4 * g + i, ci, m[i]);
-            }
-        }
-        f32x4 sS[4];
-#pragma unroll
-        for (int tr = 0; tr < 4; ++tr) {
-            sS[tr] = zero4();
-#pragma unroll
-            for (int dp = 0; dp < DP; ++dp)
-                sS[tr] = mma(sS[tr], frag<bf16, KROW>(Ks, 16 * tr + n16, (32 * dp + 4 * g) * 2),
-                             frag<bf16, KROW>(Ks, 16 * w + n16, (32 * dp + 4 * g) * 2));
-        }
-        __syncthreads();
-        // dA = -(M1 T^T) on i < r; dS = diag(beta) (dA * Gam) (Wm[2]); sums of dA * A; dbeta through A
-        float zbc = 0.f, zbr[4], dbr[4];
-#pragma unroll
-        for (int tr = 0; tr < 4; ++tr) {
-            f32x4 a = zero4();
-#pragma unroll
-            for (int ip = 0; ip <= w / 2; ++ip)
-                a = mma(a, frag_s<PROW>(Wm[1], PPL, 16 * tr + n16, (32 * ip + 4 * g) * 2),
-                        frag_s<TB::ROWB>(Tb, TB::PLANE, ci, (32 * ip + 4 * g) * 2));
-            f32x4 zb, dbv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * tr + 4 * g + i;
-                float dsv = 0.f;
-                zb[i] = dbv[i] = 0.f;
-                if (ci < r) {
-                    const float G_ = fast_exp(gam[r] - gam[ci]);
-                    const float da = -a[i];
-                    dbv[i] = da * sS[tr][i] * G_;
-                    zb[i] = bet[r] * dbv[i];
-                    dsv = bet[r] * da * G_;
-                }
-                put_s(Wm[2], PPL, r, ci, dsv);
                 zbc += zb[i];
             }
+            zar[tr] = rowsum16(za);
             zbr[tr] = rowsum16(zb);
             dbr[tr] = rowsum16(dbv);
         }
+        zac = sum_groups(zac);
         zbc = sum_groups(zbc);
         if ((n16 & 3) == 0) {
 #pragma unroll
@@ -603,7 +564,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
             cs[1][ci] = zbc;
         }
         __syncthreads();
-        // dq += W1 K ;  dk += W1^T Q + dS K + dS^T K
+        // dq += (dP * Gam) K ;  dk += (dP * Gam)^T Q + dS K + dS^T K
 #pragma unroll
         for (int s = 0; s < TD; ++s) {
             const int td = w + 4 * s;
@@ -617,11 +578,11 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
                     if (ip <= tr / 2) {
                         const int kbyte = (32 * ip + 4 * g) * 2;
                         dqt[s][tr] = mma(dqt[s][tr], frag_s<PROW>(Wm[0], PPL, 16 * tr + n16, kbyte), kb);
-                        dkt[s][tr] = mma(dkt[s][tr], frag_s<PROW>(Wm[2], PPL, 16 * tr + n16, kbyte), kb);
+                        dkt[s][tr] = mma(dkt[s][tr], frag_s<PROW>(Wm[1], PPL, 16 * tr + n16, kbyte), kb);
                     }
                     if (ip >= tr / 2) {
                         dkt[s][tr] = mma(dkt[s][tr], kt_s<PROW>(Wm[0], PPL, 16 * tr, ip), ip == 0 ? q0 : q1);
-                        dkt[s][tr] = mma(dkt[s][tr], kt_s<PROW>(Wm[2], PPL, 16 * tr, ip), kb);
+                        dkt[s][tr] = mma(dkt[s][tr], kt_s<PROW>(Wm[1], PPL, 16 * tr, ip), kb);
                     }
                 }
             }
@@ -631,20 +592,12 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
             const int r = lane_id();
             float x = 0.f, rd = 0.f;
             if (r < n) {
-                float dea = 0.f, dkh = 0.f, drv = 0.f, dbx = 0.f, zr = 0.f, zb = 0.f, dba = 0.f;
+                float q[NQ];
 #pragma unroll
-                for (int ww = 0; ww < 4; ++ww) {
-                    dea += rs[0][ww][r];
-                    dkh += rs[1][ww][r];
-                    drv += rs[2][ww][r];
-                    dbx += rs[3][ww][r];
-                    zr += rs[4][ww][r];
-                    zb += rs[5][ww][r];
-                    dba += rs[6][ww][r];
-                }
-                rd = rr[r] * drv;
-                x = eg[r] * (p.scale * dea - bet[r] * dkh) + (zr - cs[0][r]) + (zb - cs[1][r]) - rd;
-                p.dbeta[(ts + r) * p.Hv + hv] = dbx + dba;
+                for (int k = 0; k < NQ; ++k) q[k] = rs[k][0][r] + rs[k][1][r] + rs[k][2][r] + rs[k][3][r];
+                rd = rr[r] * q[2];
+                x = eg[r] * (p.scale * q[0] - bet[r] * q[1]) + (q[4] - cs[0][r]) + (q[5] - cs[1][r]) - rd;
+                p.dbeta[(ts + r) * p.Hv + hv] = q[3] - eg[r] * q[1] + q[6];
             }
             const float tot = sum_wave(rd);
             if (r == n - 1) x += eg[r] * (red[0] + red[1] + red[2] + red[3]) + tot;
