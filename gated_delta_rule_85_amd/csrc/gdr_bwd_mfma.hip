@@ -42,13 +42,13 @@ __device__ __forceinline__ OpS kt_s(const char *hi, int plane, int c0, int ip) {
 // ROWB bytes each) into a swizzled LDS tile, rows past nm1 repeating row nm1;
 // 1 KB pieces spread over the waves
 template <int ROWB>
-__device__ __forceinline__ void copy_tile(char *dst, const char *src, int64_t stride, int nm1, int w) {
+__device__ __forceinline__ void copy_tile(char *dst, const char *src, int stride, int nm1, int w) {
     using S = Swz<ROWB>;
     constexpr int PIECES = CH * ROWB / 1024;
     const int l = lane_id();
     for (int i = w; i < PIECES; i += NTHR / 64) {
         const int b = i * 1024 + 16 * l, r = b / ROWB, pc = (b % ROWB) / 16;
-        dma16(src + min(r, nm1) * stride + 16 * S::chunk(r, pc), dst + i * 1024);
+        dma16(src + (uint32_t)(min(r, nm1) * stride + 16 * S::chunk(r, pc)), dst + i * 1024);
     }
 }
 __device__ __forceinline__ void copy_flat(char *dst, const char *src, int bytes, int w) {
@@ -195,16 +195,16 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
         const int64_t ts = bos + (int64_t)c * CH;
         const int n = (int)min<int64_t>(CH, eos - ts);
         __syncthreads();  // the previous chunk is done with every tile
-        copy_tile<KROW>(Ks, kp + (ts * p.Hq + hq) * KROW, (int64_t)p.Hq * KROW, n - 1, w);
-        copy_tile<KROW>(Qs, qp + (ts * p.Hq + hq) * KROW, (int64_t)p.Hq * KROW, n - 1, w);
-        copy_tile<DROW>(Ds, dop + ((ts * p.Hv + hv) * p.V + vt * 64) * 2, (int64_t)p.Hv * p.V * 2, n - 1, w);
+        copy_tile<KROW>(Ks, kp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
+        copy_tile<KROW>(Qs, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
+        copy_tile<DROW>(Ds, dop + ((ts * p.Hv + hv) * p.V + vt * 64) * 2, p.Hv * p.V * 2, n - 1, w);
         copy_flat(Tb, p.tblk + ((int64_t)(cb + c) * p.Hv + hv) * TB::BYTES, TB::BYTES, w);
         {  // gradient of this chunk's end state, for the chunk-local stage
             float *o = p.dhs + ((int64_t)(cb + c) * p.Hv + hv) * KV;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[(16 * dt + 4 * g + i) * p.V + col] = dh[dt][i];
+                for (int i = 0; i < 4; ++i) o[(uint32_t)((16 * dt + 4 * g + i) * p.V + col)] = dh[dt][i];
         }
         wait_dma();
         __syncthreads();
@@ -332,8 +332,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
     const float *gam = sc, *eg = sc + CH, *rr = sc + 2 * CH, *bet = sc + 3 * CH;
     const int ci = 16 * w + n16;  // this lane's column in a 64-wide strip
 
-    copy_tile<KROW>(Ks, kp + (ts * p.Hq + hq) * KROW, (int64_t)p.Hq * KROW, n - 1, w);
-    copy_tile<KROW>(Qs, qp + (ts * p.Hq + hq) * KROW, (int64_t)p.Hq * KROW, n - 1, w);
+    copy_tile<KROW>(Ks, kp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
+    copy_tile<KROW>(Qs, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
     zero_lower_pt(Pt);
     f32x4 dqt[TD][4], dkt[TD][4];  // dq, dk tiles (key tile w + 4 s, token tile tr)
 #pragma unroll
@@ -344,6 +344,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
     for (int gi = 0; gi < G; ++gi) {
         const int hv = hq * G + gi;
         const int64_t hoff = ((int64_t)gid * p.Hv + hv) * KV;
+        const float *hsb = p.hs + hoff, *dhsb = p.dhs + hoff;      // this (chunk, v head)'s states
+        Gt *dvb = dvp + (ts * p.Hv + hv) * V;                      // row tok at tok * Hv * V
         __syncthreads();  // the previous v head is done with every LDS array
         copy_flat(Tb, p.tblk + ((int64_t)gid * p.Hv + hv) * TB::BYTES, TB::BYTES, w);
         wait_dma();
@@ -365,9 +367,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
                 const int idx = tid + NTHR * it, row = idx >> 4, c4 = idx & 15;
-                const int64_t o = hoff + (int64_t)(64 * hf + row) * V + vb + 4 * c4;
-                const f32x4 hx = *reinterpret_cast<const f32x4 *>(p.hs + o);
-                const f32x4 dx = *reinterpret_cast<const f32x4 *>(p.dhs + o);
+                const uint32_t o = (uint32_t)((64 * hf + row) * V + vb + 4 * c4);
+                const f32x4 hx = *reinterpret_cast<const f32x4 *>(hsb + o);
+                const f32x4 dx = *reinterpret_cast<const f32x4 *>(dhsb + o);
                 if (dot) dec += hx[0] * dx[0] + hx[1] * dx[1] + hx[2] * dx[2] + hx[3] * dx[3];
                 bf16x4 hh, hl, dh, dl;
                 split4(hx, hh, hl);
@@ -382,8 +384,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
 
         for (int vb = 0; vb < V; vb += 64) {
             __syncthreads();  // the previous block is done with Ds, Vs, Wm, Hs; scores complete
-            copy_tile<VROW>(Ds, dop + ((ts * p.Hv + hv) * V + vb) * 2, (int64_t)p.Hv * V * 2, n - 1, w);
-            copy_tile<VROW>(Vs, vpc + ((ts * p.Hv + hv) * V + vb) * 2, (int64_t)p.Hv * V * 2, n - 1, w);
+            copy_tile<VROW>(Ds, dop + ((ts * p.Hv + hv) * V + vb) * 2, p.Hv * V * 2, n - 1, w);
+            copy_tile<VROW>(Vs, vpc + ((ts * p.Hv + hv) * V + vb) * 2, p.Hv * V * 2, n - 1, w);
             // K h, K dh' for this wave's columns, over the halves of the key dimension
             f32x4 kh[4], kd[4];
 #pragma unroll
@@ -452,7 +454,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tok = r0 + i;
-                    if (tok < n) dvp[((ts + tok) * p.Hv + hv) * V + vb + ci] = Gt(b4[i] * dx[i]);
+                    if (tok < n) dvb[(uint32_t)(tok * p.Hv * V + vb + ci)] = Gt(b4[i] * dx[i]);
                     put_s(Wm[0], PPL, tok, ci, u[rt][i]);
                     put_s(Wm[1], PPL, tok, ci, dx[i]);
                 }
@@ -597,7 +599,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
                 for (int k = 0; k < NQ; ++k) q[k] = rs[k][0][r] + rs[k][1][r] + rs[k][2][r] + rs[k][3][r];
                 rd = rr[r] * q[2];
                 x = eg[r] * (p.scale * q[0] - bet[r] * q[1]) + (q[4] - cs[0][r]) + (q[5] - cs[1][r]) - rd;
-                p.dbeta[(ts + r) * p.Hv + hv] = q[3] - eg[r] * q[1] + q[6];
+                p.dbeta[ts * p.Hv + (uint32_t)(r * p.Hv + hv)] = q[3] - eg[r] * q[1] + q[6];
             }
             const float tot = sum_wave(rd);
             if (r == n - 1) x += eg[r] * (red[0] + red[1] + red[2] + red[3]) + tot;
@@ -606,10 +608,11 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
                 const float yv = __shfl_down(x, off, 64);
                 if (r + off < 64) x += yv;
             }
-            if (r < n) p.dg[(ts + r) * p.Hv + hv] = x;
+            if (r < n) p.dg[ts * p.Hv + (uint32_t)(r * p.Hv + hv)] = x;
         }
     }
-    Gt *dq = reinterpret_cast<Gt *>(p.dq), *dk = reinterpret_cast<Gt *>(p.dk);
+    Gt *dq = reinterpret_cast<Gt *>(p.dq) + (ts * p.Hq + hq) * KD;
+    Gt *dk = reinterpret_cast<Gt *>(p.dk) + (ts * p.Hq + hq) * KD;
 #pragma unroll
     for (int s = 0; s < TD; ++s)
 #pragma unroll
@@ -618,7 +621,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
             for (int i = 0; i < 4; ++i) {
                 const int tok = 16 * tr + 4 * g + i;
                 if (tok < n) {
-                    const int64_t o = ((ts + tok) * p.Hq + hq) * KD + 16 * (w + 4 * s) + n16;
+                    const uint32_t o = (uint32_t)(tok * p.Hq * KD + 16 * (w + 4 * s) + n16);
                     dq[o] = Gt(dqt[s][tr][i]);
                     dk[o] = Gt(dkt[s][tr][i]);
                 }
