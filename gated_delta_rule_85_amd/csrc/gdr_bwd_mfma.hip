@@ -38,22 +38,12 @@ __device__ __forceinline__ OpS kt_s(const char *hi, int plane, int c0, int ip) {
     return r;
 }
 
-// copy the 64 rows of a row-major global tile (row r at src + r * stride,
-// ROWB bytes each) into a swizzled LDS tile, rows past nm1 repeating row nm1;
-// 1 KB pieces spread over the waves
 template <int ROWB>
 __device__ __forceinline__ void copy_tile(char *dst, const char *src, int stride, int nm1, int w) {
-    using S = Swz<ROWB>;
-    constexpr int PIECES = CH * ROWB / 1024;
-    const int l = lane_id();
-    for (int i = w; i < PIECES; i += NTHR / 64) {
-        const int b = i * 1024 + 16 * l, r = b / ROWB, pc = (b % ROWB) / 16;
-        dma16(src + (uint32_t)(min(r, nm1) * stride + 16 * S::chunk(r, pc)), dst + i * 1024);
-    }
+    copy_rows<ROWB>(dst, src, stride, nm1, w, NTHR / 64);
 }
 __device__ __forceinline__ void copy_flat(char *dst, const char *src, int bytes, int w) {
-    const int l = lane_id();
-    for (int i = w; i < bytes / 1024; i += NTHR / 64) dma16(src + i * 1024 + 16 * l, dst + i * 1024);
+    copy_bytes(dst, src, bytes, w, NTHR / 64);
 }
 
 // upper-triangle 16x16 tiles (tr <= ti) of a 64 x 64 matrix, t = 0..9

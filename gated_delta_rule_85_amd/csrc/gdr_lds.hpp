@@ -33,6 +33,25 @@ __device__ __forceinline__ bf16x4 lds_tr4(const char *p) {
     return __builtin_bit_cast(bf16x4, v);
 }
 
+// Copy the 64 rows of a row-major global tile (row r at src + r * stride,
+// ROWB bytes each) into a swizzled LDS tile, rows past nm1 repeating row nm1.
+// The 1 KB pieces are spread over nw waves; this wave is number wi of them.
+template <int ROWB>
+__device__ __forceinline__ void copy_rows(char *dst, const char *src, int stride, int nm1, int wi, int nw) {
+    using S = Swz<ROWB>;
+    constexpr int PIECES = CH * ROWB / 1024;
+    const int l = lane_id();
+    for (int i = wi; i < PIECES; i += nw) {
+        const int b = i * 1024 + 16 * l, r = b / ROWB, pc = (b % ROWB) / 16;
+        dma16(src + (uint32_t)(min(r, nm1) * stride + 16 * S::chunk(r, pc)), dst + i * 1024);
+    }
+}
+// Copy `bytes` (a multiple of 1 KB) verbatim, pieces spread as above.
+__device__ __forceinline__ void copy_bytes(char *dst, const char *src, int bytes, int wi, int nw) {
+    const int l = lane_id();
+    for (int i = wi; i < bytes / 1024; i += nw) dma16(src + i * 1024 + 16 * l, dst + i * 1024);
+}
+
 // A-operand fragment rows (row0 + lane16, bytes off..off+7 and off+32..) of a swizzled tile
 template <typename In, int ROWB>
 __device__ __forceinline__ typename Ops<In>::X frag(const char *tile, int row, int byte) {

@@ -175,10 +175,10 @@ template <typename In, typename Out, int KD> struct Scan {
 
         // decayed causal scores: this wave's share of the ten tiles (tr >= ti)
         if constexpr (EMIT) {
-            // wave w forms tiles w, w + 4 and (waves 0, 1) w + 8 of the ten
+            // the ten tiles over the waves: 3 each for waves 2, 3, 2 each for the copy waves 0, 1
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
-                const int t = w + 4 * k;
+                const int t = 4 * k + ((w + 2) & 3);
                 if (t >= 10) break;
                 const int tr = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
                 const int ti = t - tr * (tr + 1) / 2;
