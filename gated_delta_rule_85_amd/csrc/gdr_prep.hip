@@ -60,11 +60,13 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
     using V16 = typename Vec16<In>::type;
     constexpr int EV = Vec16<In>::n;
     constexpr int LDK = KD + EV;  // 16-byte row padding
+    // K (until S = K K^T is in registers), then A, share the first region
+    constexpr int KBYTES = sizeof(In) * CH * LDK, ABYTES = sizeof(float) * CH * LDF;
+    constexpr int R0 = KBYTES > ABYTES ? KBYTES : ABYTES;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     In *Ks = reinterpret_cast<In *>(smem);
-    float *S = reinterpret_cast<float *>(smem + sizeof(In) * CH * LDK);
-    float *A = S + CH * LDF;
-    float *Tm = A + CH * LDF;
+    float *A = reinterpret_cast<float *>(smem);
+    float *Tm = reinterpret_cast<float *>(smem + R0);
     float *gam = Tm + CH * LDF;
     float *bet = gam + CH;
 
@@ -92,25 +94,27 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
     }
     __syncthreads();
 
-    // S = K K^T, the ten tiles on or below the diagonal
-    {
-        const int n16 = ln16(), g = lg4();
-        for (int t = w; t < 10; t += 4) {
-            int tr = 0;
-            while ((tr + 1) * (tr + 2) / 2 <= t) ++tr;
-            const int ti = t - tr * (tr + 1) / 2;
-            f32x4 acc = zero4();
+    // S = K K^T, the ten tiles on or below the diagonal, kept in registers:
+    // wave w holds tiles w, w + 4 and (waves 0, 1) w + 8
+    const int n16 = ln16(), g = lg4();
+    f32x4 sS[3];
+    int str[3], sti[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int t = w + 4 * k;
+        str[k] = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        sti[k] = t - str[k] * (str[k] + 1) / 2;
+        sS[k] = zero4();
+        if (t < 10) {
 #pragma unroll
             for (int dp = 0; dp < KD / 32; ++dp) {
-                const In *ar = Ks + (16 * tr + n16) * LDK + 32 * dp + 4 * g;
-                const In *br = Ks + (16 * ti + n16) * LDK + 32 * dp + 4 * g;
-                acc = mma(acc, O::load(ar, ar + 16), O::load(br, br + 16));
+                const In *ar = Ks + (16 * str[k] + n16) * LDK + 32 * dp + 4 * g;
+                const In *br = Ks + (16 * sti[k] + n16) * LDK + 32 * dp + 4 * g;
+                sS[k] = mma(sS[k], O::load(ar, ar + 16), O::load(br, br + 16));
             }
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) S[(16 * tr + 4 * g + jj) * LDF + 16 * ti + n16] = acc[jj];
         }
     }
-    __syncthreads();
+    __syncthreads();  // K is no longer read: its region becomes A
 
     for (int rr = 0; rr < G; ++rr) {
         const int hv = hq * G + rr;
@@ -127,9 +131,16 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
             if (l < n && p.g_cum) p.g_cum[(ts + l) * p.Hv + hv] = x;
         }
         __syncthreads();
-        for (int idx = tid; idx < CH * CH; idx += NTHR) {
-            const int r = idx >> 6, i = idx & 63;
-            A[r * LDF + i] = i < r ? bet[r] * fast_exp(gam[r] - gam[i]) * S[r * LDF + i] : 0.f;
+        // A = diag(beta) S * exp(gam_r - gam_i) below the diagonal, from the S tiles in registers
+        // (entries on and above the diagonal of a diagonal tile are never read)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            if (w + 4 * k >= 10) break;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = 16 * str[k] + 4 * g + jj, i = 16 * sti[k] + n16;
+                A[r * LDF + i] = i < r ? bet[r] * fast_exp(gam[r] - gam[i]) * sS[k][jj] : 0.f;
+            }
         }
         __syncthreads();
         if (w == 0) {
@@ -171,7 +182,8 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
 
 template <typename In, int KD>
 size_t prep_smem() {
-    return sizeof(In) * CH * (KD + Vec16<In>::n) + sizeof(float) * (3 * CH * LDF + 2 * CH);
+    const size_t kb = sizeof(In) * CH * (KD + Vec16<In>::n), ab = sizeof(float) * CH * LDF;
+    return (kb > ab ? kb : ab) + sizeof(float) * (CH * LDF + 2 * CH);
 }
 
 template <typename In, int KD>
