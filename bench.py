@@ -80,9 +80,14 @@ def bwd_algorithmic_flops(cfg):
     return {"gdr_bwd_scan": scan, "gdr_bwd_local": local, "gdr_bwd_states": states}
 
 
+# sources of the forward kernels: a traffic summary counts only if taken on these
+FWD_SOURCES = ("gdr_scan.hip", "gdr_prep.hip", "gdr_device.hpp", "gdr_layout.hpp", "gdr_lds.hpp",
+               "gdr_kernels.hpp")
+
+
 def source_hash():
     h = hashlib.sha256()
-    for f in ("gdr_scan.hip", "gdr_prep.hip", "gdr_device.hpp"):
+    for f in FWD_SOURCES:
         with open(os.path.join(ROOT, "gated_delta_rule_85_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
