@@ -102,28 +102,16 @@ __device__ __forceinline__ void zero_lower_pt(char *Pt) {
 // Sums over the 16 lanes of each lane group of the 4 values of an
 // accumulator-ordered tile: lane (n, g) returns the sum for row 4 g + ((n >> 2) & 3).
 __device__ __forceinline__ float rowsum16(f32x4 v) {
-    const int n = ln16();
-    const bool b3 = (n >> 3) & 1, b2 = (n >> 2) & 1;
-    float k0 = b3 ? v[2] : v[0], k1 = b3 ? v[3] : v[1];
-    const float s0 = b3 ? v[0] : v[2], s1 = b3 ? v[1] : v[3];
-    k0 += __shfl_xor(s0, 8, 64);
-    k1 += __shfl_xor(s1, 8, 64);
-    float k = b2 ? k1 : k0;
-    k += __shfl_xor(b2 ? k0 : k1, 4, 64);
-    k += __shfl_xor(k, 2, 64);
-    k += __shfl_xor(k, 1, 64);
-    return k;
+    const int t = (ln16() >> 2) & 3;
+    const float s0 = row_sum16(v[0]), s1 = row_sum16(v[1]), s2 = row_sum16(v[2]), s3 = row_sum16(v[3]);
+    return t == 0 ? s0 : t == 1 ? s1 : t == 2 ? s2 : s3;
 }
 // sum over the 4 lane groups
 __device__ __forceinline__ float sum_groups(float v) {
     v += __shfl_xor(v, 16, 64);
     return v + __shfl_xor(v, 32, 64);
 }
-__device__ __forceinline__ float sum_wave(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
+__device__ __forceinline__ float sum_wave(float v) { return sum_groups(row_sum16(v)); }
 
 // one fp32 value as a hi/lo pair at (row, col) of split planes with 64 columns
 __device__ __forceinline__ void put_s(char *hi, int plane, int row, int col, float v) {

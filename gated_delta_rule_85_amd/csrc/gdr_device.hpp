@@ -226,4 +226,19 @@ __device__ __forceinline__ int xcd_remap(int id, int nb) {
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 
+// ------------------------------------------------------------ lane sums
+// DPP lane moves within a row of 16 lanes (VALU, no LDS round trip)
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// sum over the 16 lanes of each row: quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    v += dpp_mov<0x140>(v);
+    return v;
+}
+
 }  // namespace gdr
