@@ -158,3 +158,18 @@ def test_training_shape_full_size_sampled_units():
                    dg=got["dg"][b:b + 1, :, hs], dh0=got["dh0"][b:b + 1, hs])
         print((b, hq), end=" ")
         compare(y, sub, ref)
+
+
+def test_varlen_mixed_lengths_bf16():
+    """Packed batch with lengths from 1 to ~2.3k tokens (ragged tails, single-token
+    and empty sequences), the GQA shape of the workloads; every gradient element."""
+    x = make_inputs(dict(lens=[2300, 1, 0, 700, 129, 64, 1500], Hq=2, Hv=4, K=128, V=128,
+                         dtype="bf16", h0=True), seed=7, grads=True)
+    compare(x, run_bwd(x), ora_bwd(x))
+
+
+def test_fp32_inputs_longer_sequence():
+    """fp32 inputs (fp32-MFMA kernels) over 1000 tokens with K = V = 128."""
+    x = make_inputs(dict(B=1, T=1000, Hq=1, Hv=2, K=128, V=128, dtype="fp32", h0=True), seed=8,
+                    grads=True)
+    compare(x, run_bwd(x), ora_bwd(x))
