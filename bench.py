@@ -107,6 +107,31 @@ def measured_traffic(kernel, workload):
     return t.get("bytes_per_launch")
 
 
+def cpu_single_core(x, train=False):
+    """The oracle on one host core over the first sequence's first 4 v heads
+    (and their q/k heads), in tokens/s for the whole workload's head count."""
+    import numpy as np
+
+    import oracle
+    Hq, Hv = x["q"].shape[2], x["v"].shape[2]
+    G = Hv // Hq
+    hv = min(4, Hv)
+    hq = max(1, hv // G)
+    sl = {n: np.ascontiguousarray(x[n][0:1, :, :hq if n in ("q", "k") else hv], dtype=np.float64)
+          for n in ("q", "k", "v", "g", "beta")}
+    h0 = None if x["initial_state"] is None else \
+        np.ascontiguousarray(x["initial_state"][0:1, :hv], dtype=np.float64)
+    T = x["q"].shape[1]
+    t0 = time.perf_counter()
+    oracle.fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], x["scale"], h0, nthreads=1)
+    if train:
+        oracle.bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], x["do"][0:1, :, :hv],
+                   x["scale"], initial_state=h0, dht=x["dht"][0:1, :hv], nthreads=1)
+    el = time.perf_counter() - t0
+    return {"value": T * hv / Hv / el, "unit": "tokens/s", "cores": 1,
+            "sample": "1 sequence (T=%d), %d of %d v heads, in %.1f s" % (T, hv, Hv, el)}
+
+
 def cpu_baseline(x, seconds, train=False):
     """Time the fp64 oracle (forward, plus backward when `train`) on whole
     sequences of the workload until about `seconds` of CPU time have been spent."""
@@ -190,6 +215,8 @@ def main():
     ap.add_argument("--workload", default="prefill_shard")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cold", type=int, default=10,
+                    help="extra steps timed after a 1 GiB cache scrub (median reported)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -299,11 +326,35 @@ def main():
     t_wall = time.perf_counter() - t_wall
     ms = start.elapsed_time(end) / steps
 
+    # per-step durations (first stage event to last) for the median
+    f = ctypes.c_float()
+    per_step = []
+    for arr in (ev_b.arrays if train else ev_f.arrays):
+        first = ev_f.arrays[len(per_step)][0]
+        if ev_f.hip.hipEventElapsedTime(ctypes.byref(f), first, arr[-1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        per_step.append(f.value)
+    median_ms = sorted(per_step)[len(per_step) // 2]
     stage_ms = ev_f.stage_ms(STAGES)
     ev_f.close()
     if train:
         stage_ms.update(ev_b.stage_ms(BWD_STAGES))
         ev_b.close()
+
+    # cold: every step after a 1 GiB write that evicts L2 and the MALL (not part of value)
+    cold = []
+    if args.cold:
+        scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(args.cold):
+            scrub.fill_(1.0)
+            c0.record(stream)
+            step()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(c0.elapsed_time(c1))
+        del scrub
 
     tokens = B * T
     value = tokens / (ms * 1e-3)
@@ -320,8 +371,11 @@ def main():
         "config": {"workload": wl + (", fwd (exact) + bwd, bf16 dq/dk/dv" if train else ""),
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "kernel_ms": stage_ms,
+        "median_step_ms": median_ms,
         "wall_ms_per_step": t_wall * 1e3 / steps,
     }
+    if cold:
+        rec["cold_step_ms"] = sorted(cold)[len(cold) // 2]
     if not train:
         ab = algorithmic_bytes(dict(cfg, B=B, T=T), out_bytes=4)
         dom = max(ab, key=lambda kname: stage_ms[kname])
@@ -336,13 +390,15 @@ def main():
         af = bwd_algorithmic_flops(dict(cfg, B=B, T=T))
         dom = max(af, key=lambda kname: stage_ms[kname])
         achieved = af[dom] / (stage_ms[dom] * 1e-3) / 1e12
-        # the backward kernels run their products on fp32 MFMA (v_mfma_f32_16x16x4_f32)
+        # bf16 inputs: the backward's products run on bf16 MFMA (split fp32 operands);
+        # fp32 inputs: on fp32 MFMA (v_mfma_f32_16x16x4_f32)
+        peak = MFMA_BF16_PEAK_TFLOPS if dt == torch.bfloat16 else FP32_MFMA_PEAK_TFLOPS
         rec["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": achieved,
-                           "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "traffic": None,
-                           "algorithmic_flops": af[dom]}
+                           "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                           "traffic": None, "algorithmic_flops": af[dom]}
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds, train)
+        rec["cpu_single_core"] = cpu_single_core(x, train)
     print(json.dumps(rec), flush=True)
 
 
