@@ -231,6 +231,22 @@ __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
+template <int CTRL, int ROWS> __device__ __forceinline__ float dpp_mov_rows(float v) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
+}
+// inclusive prefix sum over the 64 lanes: row_shr 1, 2, 4, 8 within each row of
+// 16 (lanes without a source add 0), then row_bcast15 into rows 1 and 3 and
+// row_bcast31 into rows 2 and 3
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp_mov<0x111>(x);
+    x += dpp_mov<0x112>(x);
+    x += dpp_mov<0x114>(x);
+    x += dpp_mov<0x118>(x);
+    x += dpp_mov_rows<0x142, 0xA>(x);
+    x += dpp_mov_rows<0x143, 0xC>(x);
+    return x;
+}
 // sum over the 16 lanes of each row: quad_perm [1,0,3,2], quad_perm [2,3,0,1],
 // row_half_mirror, row_mirror
 __device__ __forceinline__ float row_sum16(float v) {

@@ -120,12 +120,7 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
         const int hv = hq * G + rr;
         if (w == 0) {
             // inclusive running sum of g over the chunk (zero past its end)
-            float x = l < n ? p.g[(ts + l) * p.Hv + hv] : 0.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off, 64);
-                if (l >= off) x += y;
-            }
+            const float x = wave_prefix_sum(l < n ? p.g[(ts + l) * p.Hv + hv] : 0.f);
             gam[l] = x;
             bet[l] = l < n ? p.beta[(ts + l) * p.Hv + hv] : 0.f;
             if (l < n && p.g_cum) p.g_cum[(ts + l) * p.Hv + hv] = x;
