@@ -113,18 +113,15 @@ __device__ __forceinline__ float sum_groups(float v) {
 }
 __device__ __forceinline__ float sum_wave(float v) { return sum_groups(row_sum16(v)); }
 
-// one fp32 value as a hi/lo pair at (row, col) of split planes with 64 columns
-__device__ __forceinline__ void put_s(char *hi, int plane, int row, int col, float v) {
+// four consecutive fp32 values (columns col .. col + 3 of one row) as hi/lo rows of
+// split planes with 64 columns
+__device__ __forceinline__ void put4_s(char *hi, int plane, int row, int col, f32x4 v) {
     const int off = Swz<128>::off(row, 2 * col);
-    const bf16 h = bf16(v);
-    *reinterpret_cast<bf16 *>(hi + off) = h;
-    *reinterpret_cast<bf16 *>(hi + plane + off) = bf16(v - float(h));
+    bf16x4 h, l;
+    split4(v, h, l);
+    *reinterpret_cast<bf16x4 *>(hi + off) = h;
+    *reinterpret_cast<bf16x4 *>(hi + plane + off) = l;
 }
-__device__ __forceinline__ float get_s(const char *hi, int plane, int row, int col) {
-    const int off = Swz<128>::off(row, 2 * col);
-    return float(*reinterpret_cast<const bf16 *>(hi + off)) + float(*reinterpret_cast<const bf16 *>(hi + plane + off));
-}
-
 // ------------------------------------------------------------- reverse scan
 // One workgroup per (sequence, v head, 64 value columns); wave w owns
 // columns 16 w .. 16 w + 15 and keeps its K x 16 slice of dh in registers
@@ -333,11 +330,10 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
         f32x4 dPa[4], dAa[4];
 #pragma unroll
         for (int tr = 0; tr < 4; ++tr) dPa[tr] = dAa[tr] = zero4();
-        float rsum[NQ - 3][4];
+        float rsum[3][4];  // row sums in the rowsum16 layout (token 16 rt + 4 g + (lane16 >> 2))
+        float rs3[4];      // dX.V partial over this lane's 4 columns (token 16 rt + lane16)
 #pragma unroll
-        for (int q = 0; q < NQ - 3; ++q)
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) rsum[q][rt] = 0.f;
+        for (int rt = 0; rt < 4; ++rt) rsum[0][rt] = rsum[1][rt] = rsum[2][rt] = rs3[rt] = 0.f;
         float dec = 0.f;
 
         // stage rows [64 hf, 64 hf + 64) of the h and dh' block (columns vb ..) as split planes
@@ -397,21 +393,13 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
                 x[rt] = b4 * (vv[rt] - e4 * kh[rt]);
             }
             const OpS xs0 = Ops<bf16>::split(x[0], x[1]), xs1 = Ops<bf16>::split(x[2], x[3]);
-            // U~ = T X (T lower triangular)
-            f32x4 u[4];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                u[rt] = zero4();
-#pragma unroll
-                for (int ip = 0; ip <= rt / 2; ++ip)
-                    u[rt] = mma(u[rt], frag_s<TB::ROWB>(Tb, TB::PLANE, 16 * rt + n16, (32 * ip + 4 * g) * 2),
-                                ip == 0 ? xs0 : xs1);
-            }
-            // dU~ = diag(r) K dh' + s P^T dO
+            // U~ and dX transposed (rows = this wave's 16 value columns, columns = tokens):
+            // lane (token 16 rt + lane16, g) then holds columns 16 w + 4 g .. + 3 of its token,
+            // which it writes as one row piece.  U~^T = X^T T^T (T lower triangular).
             const OpX dob0 = kt_operand<bf16, VROW>(Ds, 16 * w, 0), dob1 = kt_operand<bf16, VROW>(Ds, 16 * w, 1);
             f32x4 du[4];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
+            for (int rt = 0; rt < 4; ++rt) {  // dU~ = diag(r) K dh' + s P^T dO (tokens on the rows)
                 f32x4 pd = zero4();
 #pragma unroll
                 for (int ip = rt / 2; ip < 2; ++ip)
@@ -419,24 +407,31 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
                 const f32x4 r4 = *reinterpret_cast<const f32x4 *>(rr + 16 * rt + 4 * g);
                 du[rt] = r4 * kd[rt] + p.scale * pd;
             }
-            // dX = T^T dU~
             const OpS dus0 = Ops<bf16>::split(du[0], du[1]), dus1 = Ops<bf16>::split(du[2], du[3]);
+            const int c4 = 16 * w + 4 * g;  // first of this lane's 4 value columns in the block
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                f32x4 dx = zero4();
+                const int tok = 16 * rt + n16;
+                f32x4 ut = zero4(), dxt = zero4();
 #pragma unroll
-                for (int ip = rt / 2; ip < 2; ++ip)
-                    dx = mma(dx, kt_s<TB::ROWB>(Tb, TB::PLANE, 16 * rt, ip), ip == 0 ? dus0 : dus1);
-                const int r0 = 16 * rt + 4 * g;
-                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bet + r0);
+                for (int ip = 0; ip <= rt / 2; ++ip)
+                    ut = mma(ut, ip == 0 ? xs0 : xs1, frag_s<TB::ROWB>(Tb, TB::PLANE, tok, (32 * ip + 4 * g) * 2));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tok = r0 + i;
-                    if (tok < n) dvb[(uint32_t)(tok * p.Hv * V + vb + ci)] = Gt(b4[i] * dx[i]);
-                    put_s(Wm[0], PPL, tok, ci, u[rt][i]);
-                    put_s(Wm[1], PPL, tok, ci, dx[i]);
+                for (int ip = rt / 2; ip < 2; ++ip)  // dX^T = dU~^T T (T^T upper triangular)
+                    dxt = mma(dxt, ip == 0 ? dus0 : dus1, kt_s<TB::ROWB>(Tb, TB::PLANE, 16 * rt, ip));
+                put4_s(Wm[0], PPL, tok, c4, ut);
+                put4_s(Wm[1], PPL, tok, c4, dxt);
+                if (tok < n) {
+                    const f32x4 dvv = bet[tok] * dxt;
+                    Gt *o = dvb + (uint32_t)(tok * p.Hv * V + vb + c4);
+                    if constexpr (sizeof(Gt) == 2)
+                        *reinterpret_cast<bf16x4 *>(o) = __builtin_convertvector(dvv, bf16x4);
+                    else
+                        *reinterpret_cast<f32x4 *>(o) = dvv;
                 }
-                rsum[3][rt] += rowsum16(dx * vv[rt]);
+                const f32x4 v4 = __builtin_convertvector(
+                    *reinterpret_cast<const bf16x4 *>(Vs + Swz<VROW>::off(tok, 2 * c4)), f32x4);
+                rs3[rt] += dxt[0] * v4[0] + dxt[1] * v4[1] + dxt[2] * v4[2] + dxt[3] * v4[3];
             }
             __syncthreads();  // U~, dX planes complete; Hs holds the last half
             // dP += dO U~^T, dA -= dX U~^T on strip w (two k blocks of 32 value columns)
@@ -446,8 +441,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
                 const OpS ub = frag_s<PROW>(Wm[0], PPL, ci, kbyte);  // U~^T for the tokens of strip w
 #pragma unroll
                 for (int tr = 0; tr < 4; ++tr) {
-                    dPa[tr] = mma(dPa[tr], frag<bf16, VROW>(Ds, 16 * tr + n16, kbyte), ub);
-                    dAa[tr] = mma(dAa[tr], frag_s<PROW>(Wm[1], PPL, 16 * tr + n16, kbyte), ub);
+                    // transposed: lane (token 16 tr + lane16, g) holds tokens i = 16 w + 4 g ..
+                    dPa[tr] = mma(dPa[tr], ub, frag<bf16, VROW>(Ds, 16 * tr + n16, kbyte));
+                    dAa[tr] = mma(dAa[tr], ub, frag_s<PROW>(Wm[1], PPL, 16 * tr + n16, kbyte));
                 }
             }
             // value parts of dq, dk on key tiles w + 4 s (the half holding them, last half first)
@@ -490,58 +486,73 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
                 }
             }
         }
-        const int rtok = 4 * g + (n16 >> 2);  // token (within a 16-row tile) of this lane's row sums
+        const int rtok = 4 * g + (n16 >> 2);  // token (within a 16-row tile) of the rowsum16 sums
         if ((n16 & 3) == 0) {
 #pragma unroll
-            for (int q = 0; q < NQ - 3; ++q)
+            for (int q = 0; q < 3; ++q)
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) rs[q][w][16 * rt + rtok] = rsum[q][rt];
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const float t = sum_groups(rs3[rt]);
+            if (g == 0) rs[3][w][16 * rt + n16] = t;
         }
         dec = sum_wave(dec);
         if (lane_id() == 0) red[w] = dec;
         __syncthreads();  // every wave is done with the block planes
         // dP * Gam on i <= r < n (Wm[0]) and sums of dP * P; dS = diag(beta) (dA * Gam) on i < r
-        // (Wm[1]) and sums of dA * A, with A = diag(beta) (K K^T * Gam)
-        float zac = 0.f, zbc = 0.f, zar[4], zbr[4], dbr[4];
+        // (Wm[1]) and sums of dA * A, with A = diag(beta) (K K^T * Gam).  Lane (token
+        // r = 16 tr + lane16, g) holds columns i = 16 w + 4 g .. + 3 of row r.
+        const int i0 = 16 * w + 4 * g;
+        f32x4 zac = zero4(), zbc = zero4();  // column sums, summed over the token tiles
 #pragma unroll
         for (int tr = 0; tr < 4; ++tr) {
-            f32x4 sS = zero4();
+            const int r = 16 * tr + n16;
+            f32x4 sS = zero4();  // S[r][i] (S = K K^T is symmetric)
 #pragma unroll
             for (int dp = 0; dp < DP; ++dp)
-                sS = mma(sS, frag<bf16, KROW>(Ks, 16 * tr + n16, (32 * dp + 4 * g) * 2),
-                         frag<bf16, KROW>(Ks, ci, (32 * dp + 4 * g) * 2));
-            f32x4 za, zb, dbv;
+                sS = mma(sS, frag<bf16, KROW>(Ks, 16 * w + n16, (32 * dp + 4 * g) * 2),
+                         frag<bf16, KROW>(Ks, r, (32 * dp + 4 * g) * 2));
+            // P[r][i] = P^T[i][r]: four rows of P^T at column r (only i <= r is stored)
+            const f32x4 pr = rows4<bf16, 128>(Pt, 16 * w, 16 * tr) + rows4<bf16, 128>(Pt + PPL, 16 * w, 16 * tr);
+            const float gr = gam[r], br = bet[r];
+            const f32x4 gi = *reinterpret_cast<const f32x4 *>(gam + i0);
+            f32x4 w1, ds, za, zb;
+            float dba = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * tr + 4 * g + i;
-                const float dpv = p.scale * dPa[tr][i];
-                const float G_ = ci <= r ? fast_exp(gam[r] - gam[ci]) : 0.f;
-                put_s(Wm[0], PPL, r, ci, r < n ? dpv * G_ : 0.f);
-                za[i] = ci <= r ? dpv * get_s(Pt, PPL, ci, r) : 0.f;  // P^T below its diagonal is not stored
-                const float da = ci < r ? -dAa[tr][i] : 0.f;
-                dbv[i] = da * sS[i] * G_;
-                zb[i] = bet[r] * dbv[i];
-                put_s(Wm[1], PPL, r, ci, bet[r] * da * G_);
-                zac += za[i];
-                zbc += zb[i];
+            for (int j = 0; j < 4; ++j) {
+                const int i = i0 + j;
+                const float dpv = p.scale * dPa[tr][j];
+                const float G_ = i <= r ? fast_exp(gr - gi[j]) : 0.f;
+                w1[j] = r < n ? dpv * G_ : 0.f;
+                za[j] = i <= r ? dpv * pr[j] : 0.f;
+                const float da = i < r ? -dAa[tr][j] : 0.f;
+                const float dbv = da * sS[j] * G_;
+                dba += dbv;
+                zb[j] = br * dbv;
+                ds[j] = br * da * G_;
             }
-            zar[tr] = rowsum16(za);
-            zbr[tr] = rowsum16(zb);
-            dbr[tr] = rowsum16(dbv);
+            put4_s(Wm[0], PPL, r, i0, w1);
+            put4_s(Wm[1], PPL, r, i0, ds);
+            zac += za;
+            zbc += zb;
+            const float zrow = sum_groups(za[0] + za[1] + za[2] + za[3]);
+            const float zbrow = sum_groups(zb[0] + zb[1] + zb[2] + zb[3]);
+            dba = sum_groups(dba);
+            if (g == 0) {
+                rs[4][w][r] = zrow;
+                rs[5][w][r] = zbrow;
+                rs[6][w][r] = dba;
+            }
         }
-        zac = sum_groups(zac);
-        zbc = sum_groups(zbc);
-        if ((n16 & 3) == 0) {
 #pragma unroll
-            for (int tr = 0; tr < 4; ++tr) {
-                rs[4][w][16 * tr + rtok] = zar[tr];
-                rs[5][w][16 * tr + rtok] = zbr[tr];
-                rs[6][w][16 * tr + rtok] = dbr[tr];
+        for (int j = 0; j < 4; ++j) {
+            const float za_c = row_sum16(zac[j]), zb_c = row_sum16(zbc[j]);
+            if (n16 == 0) {
+                cs[0][i0 + j] = za_c;
+                cs[1][i0 + j] = zb_c;
             }
-        }
-        if (g == 0) {
-            cs[0][ci] = zac;
-            cs[1][ci] = zbc;
         }
         __syncthreads();
         // dq += (dP * Gam) K ;  dk += (dP * Gam)^T Q + dS K + dS^T K
