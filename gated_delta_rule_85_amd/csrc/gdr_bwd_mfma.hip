@@ -99,13 +99,6 @@ __device__ __forceinline__ void zero_lower_pt(char *Pt) {
     }
 }
 
-// Sums over the 16 lanes of each lane group of the 4 values of an
-// accumulator-ordered tile: lane (n, g) returns the sum for row 4 g + ((n >> 2) & 3).
-__device__ __forceinline__ float rowsum16(f32x4 v) {
-    const int t = (ln16() >> 2) & 3;
-    const float s0 = row_sum16(v[0]), s1 = row_sum16(v[1]), s2 = row_sum16(v[2]), s3 = row_sum16(v[3]);
-    return t == 0 ? s0 : t == 1 ? s1 : t == 2 ? s2 : s3;
-}
 // sum over the 4 lane groups
 __device__ __forceinline__ float sum_groups(float v) {
     v += __shfl_xor(v, 16, 64);
@@ -330,7 +323,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
         f32x4 dPa[4], dAa[4];
 #pragma unroll
         for (int tr = 0; tr < 4; ++tr) dPa[tr] = dAa[tr] = zero4();
-        float rsum[3][4];  // row sums in the rowsum16 layout (token 16 rt + 4 g + (lane16 >> 2))
+        float rsum[3][4];  // partial row sums over this lane's 4 keys (token 16 rt + lane16)
         float rs3[4];      // dX.V partial over this lane's 4 columns (token 16 rt + lane16)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) rsum[0][rt] = rsum[1][rt] = rsum[2][rt] = rs3[rt] = 0.f;
@@ -454,49 +447,50 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
                     stage(s, vb, false);
                     __syncthreads();
                 }
+                // transposed tiles: lane (token 16 tr + lane16, g) holds keys 16 td + 4 g .. + 3
                 f32x4 aQ[4], aKa[4], aKe[4];
 #pragma unroll
                 for (int tr = 0; tr < 4; ++tr) aQ[tr] = aKa[tr] = aKe[tr] = zero4();
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const int kbyte = (32 * kb + 4 * g) * 2;
-                    const OpS hT = frag_s<128>(Hs[0], PPL, ci, kbyte);   // h^T: rows d = 64 s + 16 w + lane16
+                    const OpS hT = frag_s<128>(Hs[0], PPL, ci, kbyte);   // rows d = 64 s + 16 w + lane16 of h
                     const OpS dhT = frag_s<128>(Hs[1], PPL, ci, kbyte);
 #pragma unroll
                     for (int tr = 0; tr < 4; ++tr) {
-                        aQ[tr] = mma(aQ[tr], frag<bf16, VROW>(Ds, 16 * tr + n16, kbyte), hT);
-                        aKa[tr] = mma(aKa[tr], frag_s<PROW>(Wm[0], PPL, 16 * tr + n16, kbyte), dhT);
-                        aKe[tr] = mma(aKe[tr], frag_s<PROW>(Wm[1], PPL, 16 * tr + n16, kbyte), hT);
+                        aQ[tr] = mma(aQ[tr], hT, frag<bf16, VROW>(Ds, 16 * tr + n16, kbyte));
+                        aKa[tr] = mma(aKa[tr], dhT, frag_s<PROW>(Wm[0], PPL, 16 * tr + n16, kbyte));
+                        aKe[tr] = mma(aKe[tr], hT, frag_s<PROW>(Wm[1], PPL, 16 * tr + n16, kbyte));
                     }
                 }
                 const int td = w + 4 * s;
 #pragma unroll
                 for (int tr = 0; tr < 4; ++tr) {
-                    const int r0 = 16 * tr + 4 * g;
-                    const f32x4 e4 = *reinterpret_cast<const f32x4 *>(eg + r0);
-                    const f32x4 r4 = *reinterpret_cast<const f32x4 *>(rr + r0);
-                    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bet + r0);
-                    dqt[s][tr] += (p.scale * e4) * aQ[tr];
-                    dkt[s][tr] += r4 * aKa[tr] - (b4 * e4) * aKe[tr];
-                    const f32x4 q4 = rows4<bf16, KROW>(Qs, 16 * tr, 16 * td);
-                    const f32x4 k4 = rows4<bf16, KROW>(Ks, 16 * tr, 16 * td);
-                    rsum[0][tr] += rowsum16(q4 * aQ[tr]);
-                    rsum[1][tr] += rowsum16(k4 * aKe[tr]);
-                    rsum[2][tr] += rowsum16(k4 * aKa[tr]);
+                    const int r = 16 * tr + n16;
+                    const float er = eg[r];
+                    dqt[s][tr] += (p.scale * er) * aQ[tr];
+                    dkt[s][tr] += rr[r] * aKa[tr] - (bet[r] * er) * aKe[tr];
+                    const f32x4 q4 = __builtin_convertvector(
+                        *reinterpret_cast<const bf16x4 *>(Qs + Swz<KROW>::off(r, 2 * (16 * td + 4 * g))), f32x4);
+                    const f32x4 k4 = __builtin_convertvector(
+                        *reinterpret_cast<const bf16x4 *>(Ks + Swz<KROW>::off(r, 2 * (16 * td + 4 * g))), f32x4);
+                    const f32x4 a = q4 * aQ[tr], b = k4 * aKe[tr], cc = k4 * aKa[tr];
+                    rsum[0][tr] += a[0] + a[1] + a[2] + a[3];
+                    rsum[1][tr] += b[0] + b[1] + b[2] + b[3];
+                    rsum[2][tr] += cc[0] + cc[1] + cc[2] + cc[3];
                 }
             }
         }
-        const int rtok = 4 * g + (n16 >> 2);  // token (within a 16-row tile) of the rowsum16 sums
-        if ((n16 & 3) == 0) {
-#pragma unroll
-            for (int q = 0; q < 3; ++q)
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) rs[q][w][16 * rt + rtok] = rsum[q][rt];
-        }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            const float t = sum_groups(rs3[rt]);
-            if (g == 0) rs[3][w][16 * rt + n16] = t;
+            const float t0 = sum_groups(rsum[0][rt]), t1 = sum_groups(rsum[1][rt]);
+            const float t2 = sum_groups(rsum[2][rt]), t3 = sum_groups(rs3[rt]);
+            if (g == 0) {
+                rs[0][w][16 * rt + n16] = t0;
+                rs[1][w][16 * rt + n16] = t1;
+                rs[2][w][16 * rt + n16] = t2;
+                rs[3][w][16 * rt + n16] = t3;
+            }
         }
         dec = sum_wave(dec);
         if (lane_id() == 0) red[w] = dec;
@@ -566,14 +560,15 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
 #pragma unroll
                 for (int ip = 0; ip < 2; ++ip) {
                     const OpX &kb = ip == 0 ? k0 : k1;
+                    // transposed: K^T, Q^T as the A operands
                     if (ip <= tr / 2) {
                         const int kbyte = (32 * ip + 4 * g) * 2;
-                        dqt[s][tr] = mma(dqt[s][tr], frag_s<PROW>(Wm[0], PPL, 16 * tr + n16, kbyte), kb);
-                        dkt[s][tr] = mma(dkt[s][tr], frag_s<PROW>(Wm[1], PPL, 16 * tr + n16, kbyte), kb);
+                        dqt[s][tr] = mma(dqt[s][tr], kb, frag_s<PROW>(Wm[0], PPL, 16 * tr + n16, kbyte));
+                        dkt[s][tr] = mma(dkt[s][tr], kb, frag_s<PROW>(Wm[1], PPL, 16 * tr + n16, kbyte));
                     }
                     if (ip >= tr / 2) {
-                        dkt[s][tr] = mma(dkt[s][tr], kt_s<PROW>(Wm[0], PPL, 16 * tr, ip), ip == 0 ? q0 : q1);
-                        dkt[s][tr] = mma(dkt[s][tr], kt_s<PROW>(Wm[1], PPL, 16 * tr, ip), kb);
+                        dkt[s][tr] = mma(dkt[s][tr], ip == 0 ? q0 : q1, kt_s<PROW>(Wm[0], PPL, 16 * tr, ip));
+                        dkt[s][tr] = mma(dkt[s][tr], kb, kt_s<PROW>(Wm[1], PPL, 16 * tr, ip));
                     }
                 }
             }
@@ -605,16 +600,19 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
 #pragma unroll
     for (int s = 0; s < TD; ++s)
 #pragma unroll
-        for (int tr = 0; tr < 4; ++tr)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = 16 * tr + 4 * g + i;
-                if (tok < n) {
-                    const uint32_t o = (uint32_t)(tok * p.Hq * KD + 16 * (w + 4 * s) + n16);
-                    dq[o] = Gt(dqt[s][tr][i]);
-                    dk[o] = Gt(dkt[s][tr][i]);
+        for (int tr = 0; tr < 4; ++tr) {
+            const int tok = 16 * tr + n16;
+            if (tok < n) {  // keys 16 (w + 4 s) + 4 g .. + 3 of the token
+                const uint32_t o = (uint32_t)(tok * p.Hq * KD + 16 * (w + 4 * s) + 4 * g);
+                if constexpr (sizeof(Gt) == 2) {
+                    *reinterpret_cast<bf16x4 *>(dq + o) = __builtin_convertvector(dqt[s][tr], bf16x4);
+                    *reinterpret_cast<bf16x4 *>(dk + o) = __builtin_convertvector(dkt[s][tr], bf16x4);
+                } else {
+                    *reinterpret_cast<f32x4 *>(dq + o) = dqt[s][tr];
+                    *reinterpret_cast<f32x4 *>(dk + o) = dkt[s][tr];
                 }
             }
+        }
 }
 
 }  // namespace
