@@ -191,6 +191,7 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
     sp.o = a->o;
     sp.hT = a->final_state;
     sp.hsnap = a->h;
+    sp.hsnap_split = 0;
     sp.sm = sm;
     sp.Hq = (int)a->H_q;
     sp.Hv = (int)a->H_v;
@@ -305,6 +306,7 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
         sp.o = nullptr;
         sp.hT = nullptr;
         sp.hsnap = reinterpret_cast<float *>(ws + pl.off_hs);
+        sp.hsnap_split = dt == Dt::BF16;  // the bf16 backward kernels copy split planes straight to LDS
         sp.sm = sm;
         sp.Hq = (int)a->H_q;
         sp.Hv = (int)a->H_v;

@@ -167,12 +167,17 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
         copy_tile<KROW>(Qs, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
         copy_tile<DROW>(Ds, dop + ((ts * p.Hv + hv) * p.V + vt * 64) * 2, p.Hv * p.V * 2, n - 1, w);
         copy_flat(Tb, p.tblk + ((int64_t)(cb + c) * p.Hv + hv) * TB::BYTES, TB::BYTES, w);
-        {  // gradient of this chunk's end state, for the chunk-local stage
-            float *o = p.dhs + ((int64_t)(cb + c) * p.Hv + hv) * KV;
+        {  // gradient of this chunk's end state, for the chunk-local stage: hi, lo planes of dh'^T
+            char *o = reinterpret_cast<char *>(p.dhs + ((int64_t)(cb + c) * p.Hv + hv) * KV);
+            const int plane = KD * p.V * 2;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[(uint32_t)((16 * dt + 4 * g + i) * p.V + col)] = dh[dt][i];
+            for (int dt = 0; dt < DT; ++dt) {
+                bf16x4 hi, lo;
+                split4(dh[dt], hi, lo);
+                const uint32_t off = (uint32_t)((col * KD + 16 * dt + 4 * g) * 2);
+                *reinterpret_cast<bf16x4 *>(o + off) = hi;
+                *reinterpret_cast<bf16x4 *>(o + plane + off) = lo;
+            }
         }
         wait_dma();
         __syncthreads();
@@ -312,7 +317,10 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
     for (int gi = 0; gi < G; ++gi) {
         const int hv = hq * G + gi;
         const int64_t hoff = ((int64_t)gid * p.Hv + hv) * KV;
-        const float *hsb = p.hs + hoff, *dhsb = p.dhs + hoff;      // this (chunk, v head)'s states
+        // this (chunk, v head)'s states and end-state gradients: hi, lo planes of h^T, dh'^T [V][K]
+        const char *hsb = reinterpret_cast<const char *>(p.hs + hoff);
+        const char *dhsb = reinterpret_cast<const char *>(p.dhs + hoff);
+        const int splane = KD * V * 2;
         Gt *dvb = dvp + (ts * p.Hv + hv) * V;                      // row tok at tok * Hv * V
         __syncthreads();  // the previous v head is done with every LDS array
         copy_flat(Tb, p.tblk + ((int64_t)gid * p.Hv + hv) * TB::BYTES, TB::BYTES, w);
@@ -329,23 +337,27 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
         for (int rt = 0; rt < 4; ++rt) rsum[0][rt] = rsum[1][rt] = rsum[2][rt] = rs3[rt] = 0.f;
         float dec = 0.f;
 
-        // stage rows [64 hf, 64 hf + 64) of the h and dh' block (columns vb ..) as split planes
+        // stage keys [64 hf, 64 hf + 64) of the value block vb of h^T and dh'^T (split planes,
+        // rows = value columns) by direct copies; with `dot`, add this thread's share of <dh', h>
         auto stage = [&](int hf, int vb, bool dot) {
+            const int src = (vb * KD + 64 * hf) * 2;
+            copy_rows<128>(Hs[0], hsb + src, KD * 2, 63, w, 4);
+            copy_rows<128>(Hs[0] + PPL, hsb + splane + src, KD * 2, 63, w, 4);
+            copy_rows<128>(Hs[1], dhsb + src, KD * 2, 63, w, 4);
+            copy_rows<128>(Hs[1] + PPL, dhsb + splane + src, KD * 2, 63, w, 4);
+            wait_dma();
+            __syncthreads();
+            if (dot) {
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const int idx = tid + NTHR * it, row = idx >> 4, c4 = idx & 15;
-                const uint32_t o = (uint32_t)((64 * hf + row) * V + vb + 4 * c4);
-                const f32x4 hx = *reinterpret_cast<const f32x4 *>(hsb + o);
-                const f32x4 dx = *reinterpret_cast<const f32x4 *>(dhsb + o);
-                if (dot) dec += hx[0] * dx[0] + hx[1] * dx[1] + hx[2] * dx[2] + hx[3] * dx[3];
-                bf16x4 hh, hl, dh, dl;
-                split4(hx, hh, hl);
-                split4(dx, dh, dl);
-                const int off = S128::off(row, 8 * c4);
-                *reinterpret_cast<bf16x4 *>(Hs[0] + off) = hh;
-                *reinterpret_cast<bf16x4 *>(Hs[0] + PPL + off) = hl;
-                *reinterpret_cast<bf16x4 *>(Hs[1] + off) = dh;
-                *reinterpret_cast<bf16x4 *>(Hs[1] + PPL + off) = dl;
+                for (int it = 0; it < 4; ++it) {
+                    const int idx = tid + NTHR * it, row = idx >> 4, c4 = idx & 15;
+                    const int off = S128::off(row, 8 * c4);
+                    auto ld = [&](const char *pl) {
+                        return __builtin_convertvector(*reinterpret_cast<const bf16x4 *>(pl + off), f32x4);
+                    };
+                    const f32x4 hx = ld(Hs[0]) + ld(Hs[0] + PPL), dx = ld(Hs[1]) + ld(Hs[1] + PPL);
+                    dec += hx[0] * dx[0] + hx[1] * dx[1] + hx[2] * dx[2] + hx[3] * dx[3];
+                }
             }
         };
 
@@ -359,12 +371,13 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
             for (int rt = 0; rt < 4; ++rt) kh[rt] = kd[rt] = zero4();
 #pragma unroll 1
             for (int hf = 0; hf < NH; ++hf) {
-                if (hf > 0) __syncthreads();
+                if (hf > 0) __syncthreads();  // every wave is done with the previous half
                 stage(hf, vb, true);
-                __syncthreads();
 #pragma unroll
                 for (int ip = 0; ip < 2; ++ip) {
-                    const OpS hb = kt_s<128>(Hs[0], PPL, 16 * w, ip), db = kt_s<128>(Hs[1], PPL, 16 * w, ip);
+                    // B operands of h, dh' (k = keys 64 hf + 32 ip .., column 16 w + lane16)
+                    const OpS hb = frag_s<128>(Hs[0], PPL, 16 * w + n16, (32 * ip + 4 * g) * 2);
+                    const OpS db = frag_s<128>(Hs[1], PPL, 16 * w + n16, (32 * ip + 4 * g) * 2);
 #pragma unroll
                     for (int rt = 0; rt < 4; ++rt) {
                         const OpX kf = frag<bf16, KROW>(Ks, 16 * rt + n16, (64 * hf + 32 * ip + 4 * g) * 2);
@@ -445,7 +458,6 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
                 if (s != NH - 1) {
                     __syncthreads();  // every wave is done with the staged half
                     stage(s, vb, false);
-                    __syncthreads();
                 }
                 // transposed tiles: lane (token 16 tr + lane16, g) holds keys 16 td + 4 g .. + 3
                 f32x4 aQ[4], aKa[4], aKe[4];
@@ -454,8 +466,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const int kbyte = (32 * kb + 4 * g) * 2;
-                    const OpS hT = frag_s<128>(Hs[0], PPL, ci, kbyte);   // rows d = 64 s + 16 w + lane16 of h
-                    const OpS dhT = frag_s<128>(Hs[1], PPL, ci, kbyte);
+                    // A operands of h, dh' (rows = keys 64 s + 16 w + lane16, k = value columns 32 kb ..)
+                    const OpS hT = kt_s<128>(Hs[0], PPL, 16 * w, kb);
+                    const OpS dhT = kt_s<128>(Hs[1], PPL, 16 * w, kb);
 #pragma unroll
                     for (int tr = 0; tr < 4; ++tr) {
                         aQ[tr] = mma(aQ[tr], hT, frag<bf16, VROW>(Ds, 16 * tr + n16, kbyte));

@@ -32,6 +32,8 @@ struct ScanParams {
     void *o;          // [tokens, H_v, V]
     float *hT;        // [N, H_v, K, V] or null
     float *hsnap;     // [NT, H_v, K, V] or null
+    int hsnap_split;  // bf16 inputs only: hsnap holds, per (chunk, v head), bf16 hi then lo
+                      // planes of the transposed state [V][K] (4 bytes per element)
     SeqMap sm;
     int Hq, Hv, V;
     float scale;
@@ -57,8 +59,8 @@ struct BwdParams {
     const float *g_cum, *beta, *A;
     const float *dht;  // [N, H_v, K, V] or null
     char *tblk;        // [chunks, H_v] T blocks rebuilt from A
-    const float *hs;   // [NT, H_v, K, V] chunk-start states
-    float *dhs;        // [NT, H_v, K, V] gradient of each chunk's end state
+    const float *hs;   // [NT, H_v, K, V] chunk-start states (bf16 inputs: split planes, as hsnap_split)
+    float *dhs;        // [NT, H_v, K, V] gradient of each chunk's end state (same layout as hs)
     void *dq, *dk, *dv;
     float *dbeta, *dg;
     float *dh0;        // [N, H_v, K, V] or null

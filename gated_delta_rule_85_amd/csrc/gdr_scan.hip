@@ -209,10 +209,23 @@ template <typename In, typename Out, int KD> struct Scan {
         if constexpr (SNAP) {
             if (p.hsnap) {
                 float *hs = p.hsnap + ((int64_t)(cb + c) * p.Hv + hv) * (int64_t)KD * p.V;
+                if (C::BF && p.hsnap_split) {  // hi, lo planes of h^T: this lane's 4 keys at its column
+                    char *hb = reinterpret_cast<char *>(hs);
+                    const int plane = KD * p.V * 2;
 #pragma unroll
-                for (int dt = 0; dt < C::DT; ++dt)
+                    for (int dt = 0; dt < C::DT; ++dt) {
+                        bf16x4 hi, lo;
+                        split4(h[dt], hi, lo);
+                        const uint32_t off = (uint32_t)(((colw + n16) * KD + 16 * dt + 4 * g) * 2);
+                        *reinterpret_cast<bf16x4 *>(hb + off) = hi;
+                        *reinterpret_cast<bf16x4 *>(hb + plane + off) = lo;
+                    }
+                } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) hs[(16 * dt + 4 * g + i) * p.V + colw + n16] = h[dt][i];
+                    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) hs[(16 * dt + 4 * g + i) * p.V + colw + n16] = h[dt][i];
+                }
             }
         }
 
