@@ -76,10 +76,18 @@ __device__ __forceinline__ f32x4 mma(f32x4 c, const OpF &a, const OpF &b) {
 }
 
 // fp32 -> (hi, lo) bf16 pair, round to nearest even
+// (each hi pair is one packed conversion; the fp32 value of its halves is a
+// shift and a mask of that word)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
-    hi = __builtin_convertvector(x, bf16x4);
-    f32x4 r = x - __builtin_convertvector(hi, f32x4);
-    lo = __builtin_convertvector(r, bf16x4);
+    const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2));
+    const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2));
+    const f32x4 hf = {__builtin_bit_cast(float, a << 16), __builtin_bit_cast(float, a & 0xffff0000u),
+                      __builtin_bit_cast(float, b << 16), __builtin_bit_cast(float, b & 0xffff0000u)};
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    hi = __builtin_bit_cast(bf16x4, (u32x2{a, b}));
+    lo = __builtin_convertvector(x - hf, bf16x4);
 }
 
 // Per-input-type operand policy.
@@ -134,6 +142,17 @@ template <> struct SplitPlane<bf16> {
         r.l1 = *reinterpret_cast<const bf16x4 *>(Lo + b1);
         return r;
     }
+    // operand of 8 consecutive elements at byte o0 (16-byte aligned) of both planes
+    __device__ __forceinline__ OpS get8(int o0, int) const {
+        const bf16x8 h = *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(hi) + o0);
+        const bf16x8 l = *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(lo) + o0);
+        OpS r;
+        r.h0 = __builtin_shufflevector(h, h, 0, 1, 2, 3);
+        r.h1 = __builtin_shufflevector(h, h, 4, 5, 6, 7);
+        r.l0 = __builtin_shufflevector(l, l, 0, 1, 2, 3);
+        r.l1 = __builtin_shufflevector(l, l, 4, 5, 6, 7);
+        return r;
+    }
     __device__ __forceinline__ void put4(int off, f32x4 x) const {
         bf16x4 h, l;
         split4(x, h, l);
@@ -158,6 +177,8 @@ template <> struct SplitPlane<float> {
         r.b1 = *reinterpret_cast<const f32x4 *>(H + b1);
         return r;
     }
+    // operand of 8 consecutive elements: bytes o0 .. o0+15 and o1 .. o1+15
+    __device__ __forceinline__ OpF get8(int o0, int o1) const { return get_bytes(o0, o1); }
     __device__ __forceinline__ void put4(int off, f32x4 x) const {
         *reinterpret_cast<f32x4 *>(hi + off) = x;
     }

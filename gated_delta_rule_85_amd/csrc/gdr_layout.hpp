@@ -1,8 +1,8 @@
 // LDS images shared by gdr_chunk_prep (writer) and gdr_scan_output (reader).
 //
 // Tiles in LDS are row-major with their 16-byte chunks XOR-swizzled by row:
-// physical chunk p of row r holds logical chunk p ^ (r mod S), S = min(16,
-// chunks per row).  Sixteen consecutive rows read at one column (the MFMA
+// physical chunk p of row r holds logical chunk p ^ (key(r) mod S), S =
+// min(16, chunks per row), key(r) = r unless stated.  Sixteen consecutive rows read at one column (the MFMA
 // operand pattern) then fall into different banks, and a wave's direct
 // global->LDS copy (64 lanes x 16 bytes, lane l -> base + 16 l) can still
 // fill whole rows in order.
@@ -19,15 +19,37 @@
 
 namespace gdr {
 
-template <int ROWB> struct Swz {
+// Row keys of the XOR swizzle (physical chunk p of row r holds logical chunk
+// p ^ key(r), mod S).  KeyRow suits tiles read as 16 consecutive rows.  The
+// scan also reads tiles in the slot order of gdr_lds.hpp (rows b + 8q + i,
+// q, i = 0..3) and reads K transposed, so its keys mix in higher row bits;
+// they were chosen with a model of the 64-bank LDS that serves a 16-byte read
+// 16 lanes per pass and an 8-byte read 32 lanes per pass.
+struct KeyRow {
+    static __device__ __forceinline__ int key(int r) { return r; }
+};
+// K and Q tiles (256-byte rows): bit 2 of the key is row bits 2 ^ 4 ^ 0
+struct KeyKQ {
+    static __device__ __forceinline__ int key(int r) { return r ^ ((((r >> 4) ^ r) & 1) << 2); }
+};
+// T blocks read by the scan (128-byte rows): key bits are row bits 1, 3, 4
+struct KeyT {
+    static __device__ __forceinline__ int key(int r) { return ((r >> 1) & 1) | ((r >> 2) & 6); }
+};
+// V tiles and score planes (128-byte rows): key bits are row bits 2, 1, 3
+struct KeyVP {
+    static __device__ __forceinline__ int key(int r) { return ((r >> 2) & 1) | (r & 2) | ((r >> 1) & 4); }
+};
+
+template <int ROWB, typename KEY = KeyRow> struct Swz {
     static constexpr int CPR = ROWB / 16;
     static constexpr int S = CPR < 16 ? CPR : 16;
     // byte offset of (row, byte-in-row) in the swizzled tile
     static __device__ __forceinline__ int off(int row, int byte) {
-        return row * ROWB + ((((byte >> 4) ^ (row & (S - 1)))) << 4) + (byte & 15);
+        return row * ROWB + ((((byte >> 4) ^ (KEY::key(row) & (S - 1)))) << 4) + (byte & 15);
     }
     // logical chunk held by physical chunk p of row r (an involution)
-    static __device__ __forceinline__ int chunk(int row, int p) { return p ^ (row & (S - 1)); }
+    static __device__ __forceinline__ int chunk(int row, int p) { return p ^ (KEY::key(row) & (S - 1)); }
 };
 
 template <typename In> struct TBlock {
@@ -39,16 +61,19 @@ template <typename In> struct TBlock {
     static constexpr int BYTES = SC + 4 * CH * 4;
     static_assert(BYTES % 1024 == 0, "block copied in 1 KB wave transfers");
 };
+// swizzle of the T blocks gdr_chunk_prep writes for the scan (the backward's
+// blocks keep KeyRow)
+template <typename In> using SwzTF = Swz<TBlock<In>::ROWB, KeyT>;
+
 
 // Write one T block from an fp32 row-major T (row r, column i at T[r * ld + i])
 // and the chunk's 64 gate values (gam padded with its last value, bet zero
 // past the chunk end); rows r >= n are written as zero.  All threads of the
 // workgroup take part; gam/bet/T are read, never written.
-template <typename In>
+template <typename In, typename SW = Swz<TBlock<In>::ROWB>>
 __device__ __forceinline__ void write_tblock(char *blk, const float *T, int ld, const float *gam,
                                              const float *bet, int n, int tid, int nthr) {
     using TB = TBlock<In>;
-    using SW = Swz<TB::ROWB>;
     constexpr int EPC = 16 / (TB::BF ? 2 : 4);  // elements per 16-byte chunk
     for (int idx = tid; idx < CH * SW::CPR; idx += nthr) {
         const int r = idx / SW::CPR, pc = idx % SW::CPR, lc = SW::chunk(r, pc);

@@ -95,4 +95,69 @@ __device__ __forceinline__ typename Ops<In>::X kt_operand(const char *Ks, int d0
     return r;
 }
 
+// ------------------------------------------------- contiguous-slot operands
+// The slot -> k map of an operand may be any map shared by A and B.  With
+// "slot j (0..7) of lane group g is k = 8g + j" inside each 32-deep k block,
+// a lane's operand is 8 consecutive elements of a row: one 16-byte LDS read
+// (bf16).  A pair of accumulator tiles (t0, t0+1) used as such an operand has
+// to hold k = 8g + i in tile t0 and 8g + 4 + i in tile t0+1 at row 4g + i, so
+// the rows of tile t of a 64-row block are taken in the order
+//   row 4g + i of tile t  <->  index slot_base(t, g) + i.
+__device__ __forceinline__ int slot_base(int t, int g) { return 32 * (t >> 1) + 4 * (t & 1) + 8 * g; }
+// index held by A-operand row n (0..15) of tile t in that order
+__device__ __forceinline__ int slot_row(int t, int n) { return slot_base(t, n >> 2) + (n & 3); }
+
+// A operand (row `row`, k = 8 consecutive elements from byte `byte`, which is
+// a multiple of 16) of a row-major tile with swizzle S
+template <typename In, typename S>
+__device__ __forceinline__ typename Ops<In>::X frag8(const char *tile, int row, int byte) {
+    typename Ops<In>::X r;
+    if constexpr (sizeof(In) == 2) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8 *>(tile + S::off(row, byte));
+        r.b0 = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+        r.b1 = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+    } else {
+        r.b0 = *reinterpret_cast<const f32x4 *>(tile + S::off(row, byte));
+        r.b1 = *reinterpret_cast<const f32x4 *>(tile + S::off(row, byte + 16));
+    }
+    return r;
+}
+
+// rows rb + j (j = 0..3; rb may differ per lane group) of column c0 + lane16,
+// as the B operand of an accumulator tile expects
+template <typename In, typename S>
+__device__ __forceinline__ f32x4 rows4b(const char *tile, int rb, int c0) {
+    const int n = ln16();
+    if constexpr (sizeof(In) == 2) {
+        const bf16x4 v = lds_tr4(tile + S::off(rb + (n >> 2), 2 * (c0 + 4 * (n & 3))));
+        return __builtin_convertvector(v, f32x4);
+    } else {
+        f32x4 r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = *reinterpret_cast<const float *>(tile + S::off(rb + j, 4 * (c0 + n)));
+        return r;
+    }
+}
+
+// A operand of M^T in contiguous slots: row n of the 16-row tile is column
+// c0 + cstep * (n / 4) + n % 4 of M, k = rows r0 + 8g + j (j = 0..7) of M.
+template <typename In, typename S>
+__device__ __forceinline__ typename Ops<In>::X kt8(const char *M, int r0, int c0, int cstep) {
+    typename Ops<In>::X r;
+    const int n = ln16(), g = lg4();
+    if constexpr (sizeof(In) == 2) {
+        const int row = r0 + 8 * g + (n >> 2), byte = 2 * (c0 + cstep * (n & 3));
+        r.b0 = lds_tr4(M + S::off(row, byte));
+        r.b1 = lds_tr4(M + S::off(row + 4, byte));
+    } else {
+        const int col = c0 + cstep * (n >> 2) + (n & 3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            r.b0[j] = *reinterpret_cast<const float *>(M + S::off(r0 + 8 * g + j, 4 * col));
+            r.b1[j] = *reinterpret_cast<const float *>(M + S::off(r0 + 8 * g + 4 + j, 4 * col));
+        }
+    }
+    return r;
+}
+
 }  // namespace gdr

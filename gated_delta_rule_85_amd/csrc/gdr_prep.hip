@@ -169,7 +169,7 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
             }
         }
         // T block for the scan: swizzled planes (rows past the chunk end zero) + scalars
-        write_tblock<In>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, Tm, LDF, gam, bet, n,
+        write_tblock<In, SwzTF<In>>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, Tm, LDF, gam, bet, n,
                          tid, NTHR);
         __syncthreads();
     }
@@ -199,7 +199,7 @@ hipError_t launch_prep_t(const PrepParams &p, int n_chunks_ub, hipStream_t s) {
 template <typename In>
 __device__ __forceinline__ float tblock_T(const char *blk, int r, int i) {
     using TB = TBlock<In>;
-    using SW = Swz<TB::ROWB>;
+    using SW = SwzTF<In>;
     const int byte = i * (TB::BF ? 2 : 4);
     if constexpr (TB::BF)
         return to_f32(*reinterpret_cast<const bf16 *>(blk + SW::off(r, byte))) +

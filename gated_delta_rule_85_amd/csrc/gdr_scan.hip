@@ -33,6 +33,8 @@
 // state warm_chunks chunks before its first chunk (from the true initial
 // state when that window reaches chunk 0) and runs the scan without output
 // over the window before its own chunks.
+#include <type_traits>
+
 #include "gdr_kernels.hpp"
 #include "gdr_lds.hpp"
 
@@ -69,16 +71,17 @@ template <> struct OutVec<bf16> {
     }
 };
 
-template <typename In, typename Out, int KD> struct Scan {
+// STATES: the backward's states pass, which reads the backward's T blocks
+template <typename In, typename Out, int KD, bool STATES> struct Scan {
     using C = Cfg<In, KD>;
     using O = Ops<In>;
     using XT = typename O::X;
     using ST = typename O::S;
     using TB = typename C::TB;
-    using SK = Swz<C::KROW>;
-    using SV = Swz<C::VROW>;
-    using ST_ = Swz<TB::ROWB>;
-    using SP = Swz<C::PROW>;
+    using SK = Swz<C::KROW, KeyKQ>;
+    using SV = Swz<C::VROW, KeyVP>;
+    using ST_ = typename std::conditional<STATES, Swz<TB::ROWB>, SwzTF<In>>::type;
+    using SP = Swz<C::PROW, KeyVP>;
 
     const ScanParams &p;
     char *buf[2];
@@ -89,7 +92,9 @@ template <typename In, typename Out, int KD> struct Scan {
     int tid, w, n16, g, colw;
     const In *qp, *kp, *vp;
     Out *op;
-    // state slice: h[dt] = rows 16dt+4g+i, column colw+n16
+    // state slice: h[dt][i] = key slot_base(dt, g) + i, column colw + n16, so that a
+    // tile pair is a contiguous-slot operand (gdr_lds.hpp); the K h, X and U~ tiles
+    // take their tokens in the same order, the score and output tiles in natural order
     f32x4 h[C::DT];
     // pending output bookkeeping
     int64_t pend_ts;
@@ -185,8 +190,8 @@ template <typename In, typename Out, int KD> struct Scan {
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int dp = 0; dp < C::DP; ++dp)
-                    acc = mma(acc, frag<In, C::KROW>(Ks, 16 * ti + n16, (32 * dp + 4 * g) * C::ES),
-                              frag<In, C::KROW>(Qs, 16 * tr + n16, (32 * dp + 4 * g) * C::ES));
+                    acc = mma(acc, frag8<In, SK>(Ks, 16 * ti + n16, (32 * dp + 8 * g) * C::ES),
+                              frag8<In, SK>(Qs, 16 * tr + n16, (32 * dp + 8 * g) * C::ES));
                 // acc[jj] = P[r][i], r = 16 tr + n16, i = 16 ti + 4g + jj
                 const int r = 16 * tr + n16;
                 const float gr = gam[r];
@@ -216,7 +221,7 @@ template <typename In, typename Out, int KD> struct Scan {
                     for (int dt = 0; dt < C::DT; ++dt) {
                         bf16x4 hi, lo;
                         split4(h[dt], hi, lo);
-                        const uint32_t off = (uint32_t)(((colw + n16) * KD + 16 * dt + 4 * g) * 2);
+                        const uint32_t off = (uint32_t)(((colw + n16) * KD + slot_base(dt, g)) * 2);
                         *reinterpret_cast<bf16x4 *>(hb + off) = hi;
                         *reinterpret_cast<bf16x4 *>(hb + plane + off) = lo;
                     }
@@ -224,7 +229,7 @@ template <typename In, typename Out, int KD> struct Scan {
 #pragma unroll
                     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) hs[(16 * dt + 4 * g + i) * p.V + colw + n16] = h[dt][i];
+                        for (int i = 0; i < 4; ++i) hs[(slot_base(dt, g) + i) * p.V + colw + n16] = h[dt][i];
                 }
             }
         }
@@ -238,9 +243,9 @@ template <typename In, typename Out, int KD> struct Scan {
             const ST hb = O::split(h[2 * dp], h[2 * dp + 1]);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                kh[rt] = mma(kh[rt], frag<In, C::KROW>(Ks, 16 * rt + n16, (32 * dp + 4 * g) * C::ES), hb);
+                kh[rt] = mma(kh[rt], frag8<In, SK>(Ks, slot_row(rt, n16), (32 * dp + 8 * g) * C::ES), hb);
                 if constexpr (EMIT)  // (Q h)^T tile: lane (token, g) holds 4 output columns
-                    qh[rt] = mma(qh[rt], hb, frag<In, C::KROW>(Qs, 16 * rt + n16, (32 * dp + 4 * g) * C::ES));
+                    qh[rt] = mma(qh[rt], hb, frag8<In, SK>(Qs, 16 * rt + n16, (32 * dp + 8 * g) * C::ES));
             }
         }
         // X = beta (V - e^gam K h), as the split B operand (k = tokens)
@@ -249,9 +254,10 @@ template <typename In, typename Out, int KD> struct Scan {
             f32x4 x[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                const f32x4 vv = rows4<In, C::VROW>(Vs, 16 * rt, w * 16);
-                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bet + 16 * rt + 4 * g);
-                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(eg + 16 * rt + 4 * g);
+                const int tb = slot_base(rt, g);
+                const f32x4 vv = rows4b<In, SV>(Vs, tb, w * 16);
+                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bet + tb);
+                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(eg + tb);
                 x[rt] = b4 * (vv - e4 * kh[rt]);
             }
             xs0 = O::split(x[0], x[1]);
@@ -268,9 +274,9 @@ template <typename In, typename Out, int KD> struct Scan {
                 ut[rt] = zero4();
 #pragma unroll
                 for (int ip = 0; ip <= rt / 2; ++ip) {
-                    const int row = 16 * rt + n16, byte = (32 * ip + 4 * g) * (C::BF ? 2 : 4);
-                    const int o0 = ST_::off(row, byte), o1 = ST_::off(row, byte + 16 * (C::BF ? 2 : 4));
-                    ut[rt] = mma(ut[rt], tp.get_bytes(o0, o1), ip == 0 ? xs0 : xs1);
+                    const int row = slot_row(rt, n16), byte = (32 * ip + 8 * g) * (C::BF ? 2 : 4);
+                    const int o0 = ST_::off(row, byte), o1 = ST_::off(row, byte + 16);
+                    ut[rt] = mma(ut[rt], tp.get8(o0, o1), ip == 0 ? xs0 : xs1);
                 }
             }
         }
@@ -289,9 +295,8 @@ template <typename In, typename Out, int KD> struct Scan {
                 f32x4 acc = eg[16 * rt + n16] * qh[rt];
 #pragma unroll
                 for (int ip = 0; ip <= rt / 2; ++ip) {
-                    const int row = 16 * rt + n16, byte = (32 * ip + 4 * g) * EB;
-                    acc = mma(acc, ip == 0 ? us0 : us1,
-                              pp.get_bytes(SP::off(row, byte), SP::off(row, byte + 16 * EB)));
+                    const int row = 16 * rt + n16, byte = (32 * ip + 8 * g) * EB;
+                    acc = mma(acc, ip == 0 ? us0 : us1, pp.get8(SP::off(row, byte), SP::off(row, byte + 16)));
                 }
                 pend_o[rt] = p.scale * acc;
             }
@@ -302,21 +307,22 @@ template <typename In, typename Out, int KD> struct Scan {
         {
             f32x4 y[4];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) y[rt] = *reinterpret_cast<const f32x4 *>(rr + 16 * rt + 4 * g) * ut[rt];
+            for (int rt = 0; rt < 4; ++rt) y[rt] = *reinterpret_cast<const f32x4 *>(rr + slot_base(rt, g)) * ut[rt];
             const ST rus0 = O::split(y[0], y[1]);
             const ST rus1 = O::split(y[2], y[3]);
             const float ec = eg[CH - 1];
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt) {
                 h[dt] *= ec;
-                h[dt] = mma(h[dt], kt_operand<In, C::KROW>(Ks, 16 * dt, 0), rus0);
-                h[dt] = mma(h[dt], kt_operand<In, C::KROW>(Ks, 16 * dt, 1), rus1);
+                const int c0 = 32 * (dt >> 1) + 4 * (dt & 1);
+                h[dt] = mma(h[dt], kt8<In, SK>(Ks, 0, c0, 8), rus0);
+                h[dt] = mma(h[dt], kt8<In, SK>(Ks, 32, c0, 8), rus1);
             }
         }
     }
 
     // chunk c from buffer `cur`; chunk c+1 (if any) copied into `nxt` meanwhile
-    template <int CUR, bool STATES>
+    template <int CUR>
     __device__ __forceinline__ void run(int c, int c_begin, int c_end) {
         char *cur = buf[C::NB == 2 ? CUR : 0];
         char *nxt = buf[C::NB == 2 ? 1 - CUR : 0];
@@ -342,13 +348,13 @@ template <typename In, typename Out, int KD> struct Scan {
 
 // STATES: chunk-start states only (no scores, no output), for the backward
 template <typename In, typename Out, int KD, bool STATES>
-__global__ __launch_bounds__(NTHR) void scan_output_kernel(const ScanParams p) {
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_output_kernel(const ScanParams p) {
     using C = Cfg<In, KD>;
     __shared__ __attribute__((aligned(16))) char buf0[C::BUF];
     __shared__ __attribute__((aligned(16))) char buf1[C::NB == 2 ? C::BUF : 16];
     __shared__ __attribute__((aligned(16))) char pplane[C::PBYTES];
 
-    Scan<In, Out, KD> S(p);
+    Scan<In, Out, KD, STATES> S(p);
     S.buf[0] = buf0;
     S.buf[1] = buf1;
     S.pplane = pplane;
@@ -390,11 +396,11 @@ __global__ __launch_bounds__(NTHR) void scan_output_kernel(const ScanParams p) {
         for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                S.h[dt][i] = from_h0 ? h0[(16 * dt + 4 * S.g + i) * p.V + S.colw + S.n16] : 0.f;
+                S.h[dt][i] = from_h0 ? h0[(slot_base(dt, S.g) + i) * p.V + S.colw + S.n16] : 0.f;
     }
     // score-plane tiles above the diagonal pairs, (0,1) and (2,3), are read as zero and never written
     {
-        using SP = Swz<C::PROW>;
+        using SP = typename Scan<In, Out, KD, STATES>::SP;
         constexpr int EB = C::BF ? 2 : 4;
         for (int idx = threadIdx.x; idx < 2 * 16 * 16; idx += NTHR) {
             const int t = idx >> 8, r = 32 * t + ((idx >> 4) & 15), i = 32 * t + 16 + (idx & 15);
@@ -414,8 +420,8 @@ __global__ __launch_bounds__(NTHR) void scan_output_kernel(const ScanParams p) {
         __syncthreads();
     }
     for (int c = w_begin; c < c_end; c += 2) {
-        S.template run<0, STATES>(c, c_begin, c_end);
-        if (c + 1 < c_end) S.template run<1, STATES>(c + 1, c_begin, c_end);
+        S.template run<0>(c, c_begin, c_end);
+        if (c + 1 < c_end) S.template run<1>(c + 1, c_begin, c_end);
     }
     S.store_pending();
     if (c_end == N && p.hT) {
@@ -423,7 +429,7 @@ __global__ __launch_bounds__(NTHR) void scan_output_kernel(const ScanParams p) {
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) hT[(16 * dt + 4 * S.g + i) * p.V + S.colw + S.n16] = S.h[dt][i];
+            for (int i = 0; i < 4; ++i) hT[(slot_base(dt, S.g) + i) * p.V + S.colw + S.n16] = S.h[dt][i];
     }
 }
 
