@@ -23,12 +23,13 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
 # scan's register-resident loops); the backward's LDS-fed kernels are left to
 # the default allocation, which the option crashes on.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-# The scan runs one wave per SIMD, so nothing hides an LDS read's latency but
+# The scans run one wave per SIMD, so nothing hides an LDS read's latency but
 # the wave's own later instructions: the ILP-seeking scheduler issues the
 # operand reads well ahead of their MFMAs (the default one waits on each).
+# (The backward's chunk-local kernel spills under it and keeps the default.)
 ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 SOURCES = {"gdr_api.hip": VGPR_FORM, "gdr_prep.hip": VGPR_FORM, "gdr_scan.hip": VGPR_FORM + ILP,
-           "gdr_bwd.hip": VGPR_FORM, "gdr_bwd_mfma.hip": []}
+           "gdr_bwd.hip": VGPR_FORM, "gdr_bwd_scan.hip": ILP, "gdr_bwd_mfma.hip": []}
 
 
 def _compile(src):

@@ -1,0 +1,165 @@
+// Reverse state scan of the backward for bf16 inputs on bf16 MFMA.
+//
+// Part of the backward described in gdr_bwd_mfma.hip (the same split-bf16
+// arithmetic); it sits in a file of its own because it is compiled with the
+// ILP-seeking scheduler (one wave per SIMD: operand reads must be issued well
+// ahead of their MFMAs).
+#include "gdr_bwd_ops.hpp"
+
+namespace gdr {
+
+namespace {
+
+using namespace bwd;
+
+// ------------------------------------------------------------- reverse scan
+// One workgroup per (sequence, v head, 64 value columns); wave w owns
+// columns 16 w .. 16 w + 15 and keeps its K x 16 slice of dh in registers
+// (accumulator order: dh[dt] = rows 16 dt + 4 g + i, column 16 w + lane16).
+// Per chunk, from the end: the transposed decayed scores P^T (upper
+// triangular, shared split planes), then per wave
+//   dU~ = diag(r) K dh' + s P^T dO,  dX = T^T dU~,
+//   dh  = e_last dh' + Q^T diag(s e) dO - K^T diag(beta e) dX.
+template <int KD>
+__global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_units) {
+    constexpr int KROW = KD * 2, DROW = 64 * 2, PROW = 64 * 2, PPLANE = CH * PROW;
+    constexpr int DT = KD / 16, DP = KD / 32;
+    using TB = TBlock<bf16>;
+    __shared__ __attribute__((aligned(16))) char Ks[CH * KROW];
+    __shared__ __attribute__((aligned(16))) char Qs[CH * KROW];
+    __shared__ __attribute__((aligned(16))) char Ds[CH * DROW];
+    __shared__ __attribute__((aligned(16))) char Tb[TB::BYTES];
+    __shared__ __attribute__((aligned(16))) char Pt[2 * PPLANE];
+
+    const int nvt = p.V / 64;
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int vt = wid % nvt, unit = wid / nvt;
+    if (unit >= n_units) return;
+    const int j = unit / p.Hv, hv = unit % p.Hv, hq = hv / (p.Hv / p.Hq);
+    const int w = __builtin_amdgcn_readfirstlane(wave_id()), n16 = ln16(), g = lg4();
+    const int col = vt * 64 + 16 * w + n16;
+    int64_t bos, eos;
+    p.sm.bounds(j, bos, eos);
+    const int N = (int)((eos - bos + CH - 1) / CH);
+    const int cb = p.sm.chunk_base(j);
+    const int64_t KV = (int64_t)KD * p.V;
+    const char *kp = reinterpret_cast<const char *>(p.k), *qp = reinterpret_cast<const char *>(p.q);
+    const char *dop = reinterpret_cast<const char *>(p.dout);
+    const float *sc = reinterpret_cast<const float *>(Tb + TB::SC);
+    const float *eg = sc + CH, *rr = sc + 2 * CH, *bet = sc + 3 * CH;
+
+    f32x4 dh[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dh[dt][i] = p.dht ? p.dht[unit * KV + (16 * dt + 4 * g + i) * p.V + col] : 0.f;
+    zero_lower_pt(Pt);
+
+    for (int c = N - 1; c >= 0; --c) {
+        const int64_t ts = bos + (int64_t)c * CH;
+        const int n = (int)min<int64_t>(CH, eos - ts);
+        __syncthreads();  // the previous chunk is done with every tile
+        copy_tile<KROW>(Ks, kp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
+        copy_tile<KROW>(Qs, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
+        copy_tile<DROW>(Ds, dop + ((ts * p.Hv + hv) * p.V + vt * 64) * 2, p.Hv * p.V * 2, n - 1, w);
+        copy_flat(Tb, p.tblk + ((int64_t)(cb + c) * p.Hv + hv) * TB::BYTES, TB::BYTES, w);
+        {  // gradient of this chunk's end state, for the chunk-local stage: hi, lo planes of dh'^T
+            char *o = reinterpret_cast<char *>(p.dhs + ((int64_t)(cb + c) * p.Hv + hv) * KV);
+            const int plane = KD * p.V * 2;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                bf16x4 hi, lo;
+                split4(dh[dt], hi, lo);
+                const uint32_t off = (uint32_t)((col * KD + 16 * dt + 4 * g) * 2);
+                *reinterpret_cast<bf16x4 *>(o + off) = hi;
+                *reinterpret_cast<bf16x4 *>(o + plane + off) = lo;
+            }
+        }
+        wait_dma();
+        __syncthreads();
+        scores_t<KD>(Pt, Qs, Ks, sc, n, w);
+        __syncthreads();
+        // dU~ = diag(r) K dh' + s P^T dO  (rows = tokens, this wave's columns)
+        f32x4 du[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) du[rt] = zero4();
+#pragma unroll
+        for (int dp = 0; dp < DP; ++dp) {
+            const OpS hb = Ops<bf16>::split(dh[2 * dp], dh[2 * dp + 1]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                du[rt] = mma(du[rt], frag<bf16, KROW>(Ks, 16 * rt + n16, (32 * dp + 4 * g) * 2), hb);
+        }
+        const OpX dob0 = kt_operand<bf16, DROW>(Ds, 16 * w, 0), dob1 = kt_operand<bf16, DROW>(Ds, 16 * w, 1);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 pd = zero4();
+#pragma unroll
+            for (int ip = rt / 2; ip < 2; ++ip)
+                pd = mma(pd, frag_s<PROW>(Pt, PPLANE, 16 * rt + n16, (32 * ip + 4 * g) * 2), ip == 0 ? dob0 : dob1);
+            const f32x4 r4 = *reinterpret_cast<const f32x4 *>(rr + 16 * rt + 4 * g);
+            du[rt] = r4 * du[rt] + p.scale * pd;
+        }
+        // dX = T^T dU~ (T^T upper triangular)
+        const OpS dus0 = Ops<bf16>::split(du[0], du[1]), dus1 = Ops<bf16>::split(du[2], du[3]);
+        f32x4 dx[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            dx[rt] = zero4();
+#pragma unroll
+            for (int ip = rt / 2; ip < 2; ++ip)
+                dx[rt] = mma(dx[rt], kt_s<TB::ROWB>(Tb, TB::PLANE, 16 * rt, ip), ip == 0 ? dus0 : dus1);
+        }
+        // dh = e_last dh' + Q^T diag(s e) dO - K^T diag(beta e) dX
+        OpS edo[2], bdx[2];
+        {
+            f32x4 y[4], z[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int r0 = 16 * rt + 4 * g;
+                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(eg + r0);
+                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bet + r0);
+                const f32x4 d4 = rows4<bf16, DROW>(Ds, 16 * rt, 16 * w);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[rt][i] = r0 + i < n ? p.scale * e4[i] * d4[i] : 0.f;
+                z[rt] = -(b4 * e4) * dx[rt];
+            }
+            edo[0] = Ops<bf16>::split(y[0], y[1]);
+            edo[1] = Ops<bf16>::split(y[2], y[3]);
+            bdx[0] = Ops<bf16>::split(z[0], z[1]);
+            bdx[1] = Ops<bf16>::split(z[2], z[3]);
+        }
+        const float el = eg[CH - 1];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            dh[dt] *= el;
+#pragma unroll
+            for (int ip = 0; ip < 2; ++ip) {
+                dh[dt] = mma(dh[dt], kt_operand<bf16, KROW>(Qs, 16 * dt, ip), edo[ip]);
+                dh[dt] = mma(dh[dt], kt_operand<bf16, KROW>(Ks, 16 * dt, ip), bdx[ip]);
+            }
+        }
+    }
+    if (p.dh0) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p.dh0[unit * KV + (16 * dt + 4 * g + i) * p.V + col] = dh[dt][i];
+    }
+}
+
+
+}  // namespace
+
+hipError_t launch_bwd_scan_bf16(int K, const BwdParams &p, int n_units, hipStream_t s) {
+    const dim3 grid(n_units * (p.V / 64));
+    if (K == 128)
+        hipLaunchKernelGGL((bwd_scan_bf16<128>), grid, dim3(NTHR), 0, s, p, n_units);
+    else
+        hipLaunchKernelGGL((bwd_scan_bf16<64>), grid, dim3(NTHR), 0, s, p, n_units);
+    return hipGetLastError();
+}
+
+
+}  // namespace gdr
