@@ -20,9 +20,13 @@ typedef __attribute__((address_space(1))) void glb_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// wave-wide copy of 64 x 16 bytes: lane l's source -> lds_base + 16 l
+// wave-wide copy of 64 x 16 bytes: lane l's source -> lds_base + 16 l.  The
+// LDS address is taken from the low 32 bits of the generic pointer (its
+// offset in the LDS aperture) rather than by a pointer cast, whose null check
+// the compiler cannot always select.
 __device__ __forceinline__ void dma16(const void *src, char *lds_base) {
-    __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)lds_base, 16, 0, 0);
+    lds_void *d = (lds_void *)(uintptr_t)(uint32_t)(uintptr_t)lds_base;
+    __builtin_amdgcn_global_load_lds((glb_void *)src, d, 16, 0, 0);
 }
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
