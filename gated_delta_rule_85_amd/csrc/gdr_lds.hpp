@@ -30,6 +30,14 @@ __device__ __forceinline__ void dma16(const void *src, char *lds_base) {
 }
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
+// Workgroup barrier that orders LDS accesses only: __syncthreads() also waits
+// for every global load and store the wave has in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // gfx950 transposing LDS read: within each 16-lane group, lane i receives
 // element i%4 of the 8-byte chunks read by source lanes i/4 + 4j, j = 0..3.
 __device__ __forceinline__ bf16x4 lds_tr4(const char *p) {

@@ -19,6 +19,7 @@
 // tiles by T_ab = -D_a sum_{m=b}^{a-1} A_am T_mb on fp32 MFMA, one block
 // diagonal at a time.
 #include "gdr_kernels.hpp"
+#include "gdr_lds.hpp"
 
 namespace gdr {
 
@@ -80,13 +81,38 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
     const int tid = threadIdx.x, w = wave_id(), l = lane_id();
     const int G = p.Hv / p.Hq;
 
+    // wave 0 holds the log-gate and beta of the v head being processed, one token
+    // per lane; each head's pair is loaded one head ahead, the first before the
+    // K tile, so their latency overlaps other work
+    float g_nx = 0.f, b_nx = 0.f;
+    if (w == 0 && l < n) {
+        g_nx = p.g[(ts + l) * p.Hv + hq * G];
+        b_nx = p.beta[(ts + l) * p.Hv + hq * G];
+    }
+
     // K rows of the chunk (zero past its end); upper off-diagonal T tiles = 0
     const In *kp = reinterpret_cast<const In *>(p.k);
-    for (int idx = tid; idx < CH * (KD / EV); idx += NTHR) {
-        const int r = idx / (KD / EV), cv = idx % (KD / EV);
-        V16 val = {};
-        if (r < n) val = *reinterpret_cast<const V16 *>(kp + ((ts + r) * p.Hq + hq) * KD + cv * EV);
-        *reinterpret_cast<V16 *>(Ks + r * LDK + cv * EV) = val;
+    {
+        // all of this thread's loads first, then the LDS writes (one memory round trip)
+        constexpr int PER = CH * (KD / EV) / NTHR;
+        static_assert(CH * (KD / EV) % NTHR == 0, "K tile pieces spread evenly");
+        V16 val[PER];
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int idx = tid + it * NTHR, r = idx / (KD / EV), cv = idx % (KD / EV);
+            // rows past the chunk end read its last row (no branch around the
+            // load, which would make the compiler wait on it) and are zeroed
+            const int rr = min(r, n - 1);
+            val[it] = *reinterpret_cast<const V16 *>(kp + ((ts + rr) * p.Hq + hq) * KD + cv * EV);
+        }
+#pragma unroll
+        for (int it = 0; it < PER; ++it)
+            if ((tid + it * NTHR) / (KD / EV) >= n) val[it] = V16{};
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int idx = tid + it * NTHR, r = idx / (KD / EV), cv = idx % (KD / EV);
+            *reinterpret_cast<V16 *>(Ks + r * LDK + cv * EV) = val[it];
+        }
     }
     for (int idx = tid; idx < CH * CH; idx += NTHR) {
         const int r = idx >> 6, i = idx & 63;
@@ -120,10 +146,14 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
         const int hv = hq * G + rr;
         if (w == 0) {
             // inclusive running sum of g over the chunk (zero past its end)
-            const float x = wave_prefix_sum(l < n ? p.g[(ts + l) * p.Hv + hv] : 0.f);
+            const float x = wave_prefix_sum(g_nx);
             gam[l] = x;
-            bet[l] = l < n ? p.beta[(ts + l) * p.Hv + hv] : 0.f;
+            bet[l] = b_nx;
             if (l < n && p.g_cum) p.g_cum[(ts + l) * p.Hv + hv] = x;
+            if (rr + 1 < G && l < n) {
+                g_nx = p.g[(ts + l) * p.Hv + hv + 1];
+                b_nx = p.beta[(ts + l) * p.Hv + hv + 1];
+            }
         }
         __syncthreads();
         // A = diag(beta) S * exp(gam_r - gam_i) below the diagonal, from the S tiles in registers
@@ -171,7 +201,7 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
         // T block for the scan: swizzled planes (rows past the chunk end zero) + scalars
         write_tblock<In, SwzTF<In>>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, Tm, LDF, gam, bet, n,
                          tid, NTHR);
-        __syncthreads();
+        lds_barrier();  // Tm, A, gam, bet free again; the block's stores drain meanwhile
     }
 }
 
