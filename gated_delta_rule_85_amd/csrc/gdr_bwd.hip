@@ -109,11 +109,24 @@ __device__ __forceinline__ void load_gates(const BwdParams &p, int64_t ts, int n
     }
 }
 
-// T rows of one (chunk, v head), zero past the chunk end
+// T rows of one (chunk, v head), zero past the chunk end.  Every load is
+// issued before the first LDS write (rows past the end read the last row and
+// are zeroed), so the tile costs one memory round trip.
 __device__ __forceinline__ void load_T(const BwdParams &p, int64_t ts, int n, int hv, float *Tf) {
-    for (int idx = threadIdx.x; idx < CH * CH; idx += NTHR) {
-        const int r = idx >> 6, i = idx & 63;
-        Tf[r * LF + i] = r < n ? p.A[((ts + r) * p.Hv + hv) * CH + i] : 0.f;
+    constexpr int PER = CH * CH / 4 / NTHR;
+    static_assert(CH * CH / 4 % NTHR == 0, "16-byte pieces spread evenly");
+    f32x4 v[PER];
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        const int idx = threadIdx.x + it * NTHR, r = idx >> 4, c4 = idx & 15;
+        v[it] = *reinterpret_cast<const f32x4 *>(p.A + ((ts + min(r, n - 1)) * p.Hv + hv) * CH + 4 * c4);
+    }
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        const int idx = threadIdx.x + it * NTHR, r = idx >> 4, c4 = idx & 15;
+        const f32x4 x = r < n ? v[it] : zero4();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Tf[r * LF + 4 * c4 + e] = x[e];  // (odd pitch: scalar LDS writes)
     }
 }
 
