@@ -5,10 +5,13 @@ One step is one gdr_fwd call (gdr_chunk_prep + the fused scan/output kernel)
 over the full-width prefill shard: B=4, T=4096, H_q=16, H_v=32, K=V=128,
 bf16 q/k/v, fp32 g/beta/initial and final state, fp32 o (inference forward:
 the A and g_cum tensors a backward would need are not written).  Inputs are seeded
-synthetic tensors already resident in HBM; W untimed warm-up steps, then K
-timed steps between stream synchronisations.  Each step records HIP events
-around each kernel on the library's stream; the dominant kernel's average
-duration gives the roofline entry.  The fp64 CPU oracle is timed on a bounded
+synthetic tensors already resident in HBM; W untimed warm-up steps, a
+breakdown pass (up to 20 steps recording HIP events around every kernel:
+kernel_ms, breakdown_step_ms and the dominant kernel), then K timed steps between
+stream synchronisations, in which only the dominant kernel's two events are
+recorded (on the library's stream; each event record costs the stream a few
+microseconds).  That kernel's average duration over the timed steps gives the
+roofline entry.  The fp64 CPU oracle is timed on a bounded
 sample of the same workload for the cpu_baseline entry.
 
 ``--workload training`` instead times one training step of the operator:
@@ -165,9 +168,11 @@ def cpu_baseline(x, seconds, train=False):
 
 
 class Events:
-    """HIP events handed to the library's timing hooks, one array per step."""
+    """HIP events handed to the library's timing hooks, one array per step.
+    With `keep`, only those entries hold events; the others are NULL, which
+    the library skips (each record costs the stream a few microseconds)."""
 
-    def __init__(self, steps, n):
+    def __init__(self, steps, n, keep=None):
         self.hip = hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
         hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
@@ -178,6 +183,8 @@ class Events:
         for _ in range(steps):
             arr = (ctypes.c_void_p * n)()
             for i in range(n):
+                if keep is not None and i not in keep:
+                    continue
                 e = ctypes.c_void_p()
                 if hip.hipEventCreate(ctypes.byref(e)) != 0:
                     raise RuntimeError("hipEventCreate failed")
@@ -187,11 +194,13 @@ class Events:
     def ptr(self, step):
         return ctypes.addressof(self.arrays[step])
 
-    def stage_ms(self, names):
+    def stage_ms(self, names, only=None):
         """Average duration of stage s (events 2s, 2s+1) over the steps."""
         f = ctypes.c_float()
         out = {}
         for s, name in enumerate(names):
+            if only is not None and name != only:
+                continue
             tot = 0.0
             for arr in self.arrays:
                 if self.hip.hipEventElapsedTime(ctypes.byref(f), arr[2 * s], arr[2 * s + 1]) != 0:
@@ -203,7 +212,8 @@ class Events:
     def close(self):
         for arr in self.arrays:
             for i in range(self.n):
-                self.hip.hipEventDestroy(arr[i])
+                if arr[i]:
+                    self.hip.hipEventDestroy(arr[i])
 
 
 def main():
@@ -294,8 +304,6 @@ def main():
         keep.append(wsb)
         bw.workspace, bw.workspace_bytes = wsb.data_ptr(), nb
 
-    ev_f = Events(steps, 2 * _lib.FWD_STAGES)
-    ev_b = Events(steps, 2 * _lib.BWD_STAGES) if train else None
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
     if args.copy_mib:
@@ -305,15 +313,51 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    evs = {"f": None, "b": None}
+
     def step(i=None):
-        a.events = None if i is None else ev_f.ptr(i)
+        a.events = None if i is None or evs["f"] is None else evs["f"].ptr(i)
         _lib.fwd(a, sh)
         if bw is not None:
-            bw.events = None if i is None else ev_b.ptr(i)
+            bw.events = None if i is None or evs["b"] is None else evs["b"].ptr(i)
             _lib.bwd(bw, sh)
 
     for _ in range(warmup):
         step()
+    torch.cuda.synchronize()
+
+    # stage breakdown (every stage's events; not part of the timed region): per-stage
+    # averages, the median step and the dominant kernel
+    nbk = min(steps, 20)
+    evs["f"] = Events(nbk, 2 * _lib.FWD_STAGES)
+    evs["b"] = Events(nbk, 2 * _lib.BWD_STAGES) if train else None
+    for i in range(nbk):
+        step(i)
+    torch.cuda.synchronize()
+    f = ctypes.c_float()
+    per_step = []
+    for i in range(nbk):
+        first = evs["f"].arrays[i][0]
+        last = (evs["b"] if train else evs["f"]).arrays[i][-1]
+        if evs["f"].hip.hipEventElapsedTime(ctypes.byref(f), first, last) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        per_step.append(f.value)
+    median_ms = sorted(per_step)[len(per_step) // 2]
+    stage_ms = evs["f"].stage_ms(STAGES)
+    evs["f"].close()
+    if train:
+        stage_ms.update(evs["b"].stage_ms(BWD_STAGES))
+        evs["b"].close()
+    model = bwd_algorithmic_flops(dict(cfg, B=B, T=T)) if train else \
+        algorithmic_bytes(dict(cfg, B=B, T=T), out_bytes=4)
+    dom = max(model, key=lambda kname: stage_ms[kname])
+
+    # timed region: K steps; only the dominant kernel's two events are recorded
+    # (on the library's stream), for the roofline
+    in_bwd = dom in BWD_STAGES
+    si = (BWD_STAGES if in_bwd else STAGES).index(dom)
+    ev_dom = Events(steps, 2 * (_lib.BWD_STAGES if in_bwd else _lib.FWD_STAGES), keep={2 * si, 2 * si + 1})
+    evs["f"], evs["b"] = (None, ev_dom) if in_bwd else (ev_dom, None)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -325,21 +369,9 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = start.elapsed_time(end) / steps
-
-    # per-step durations (first stage event to last) for the median
-    f = ctypes.c_float()
-    per_step = []
-    for arr in (ev_b.arrays if train else ev_f.arrays):
-        first = ev_f.arrays[len(per_step)][0]
-        if ev_f.hip.hipEventElapsedTime(ctypes.byref(f), first, arr[-1]) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
-        per_step.append(f.value)
-    median_ms = sorted(per_step)[len(per_step) // 2]
-    stage_ms = ev_f.stage_ms(STAGES)
-    ev_f.close()
-    if train:
-        stage_ms.update(ev_b.stage_ms(BWD_STAGES))
-        ev_b.close()
+    dom_ms = ev_dom.stage_ms(BWD_STAGES if in_bwd else STAGES, only=dom)[dom]
+    ev_dom.close()
+    evs["f"] = evs["b"] = None
 
     # cold: every step after a 1 GiB write that evicts L2 and the MALL (not part of value)
     cold = []
@@ -371,15 +403,14 @@ def main():
         "config": {"workload": wl + (", fwd (exact) + bwd, bf16 dq/dk/dv" if train else ""),
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "kernel_ms": stage_ms,
-        "median_step_ms": median_ms,
+        "breakdown_step_ms": median_ms,  # median step of the breakdown pass (every event recorded)
         "wall_ms_per_step": t_wall * 1e3 / steps,
     }
     if cold:
         rec["cold_step_ms"] = sorted(cold)[len(cold) // 2]
     if not train:
-        ab = algorithmic_bytes(dict(cfg, B=B, T=T), out_bytes=4)
-        dom = max(ab, key=lambda kname: stage_ms[kname])
-        achieved = ab[dom] / (stage_ms[dom] * 1e-3) / 1e9
+        ab = model
+        achieved = ab[dom] / (dom_ms * 1e-3) / 1e9
         rec["tflops_algorithmic"] = tflops
         rec["mfma_bf16_peak_frac"] = tflops / MFMA_BF16_PEAK_TFLOPS
         rec["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": achieved,
@@ -387,9 +418,8 @@ def main():
                            "traffic": measured_traffic(dom, args.workload),
                            "algorithmic_bytes": ab[dom]}
     else:
-        af = bwd_algorithmic_flops(dict(cfg, B=B, T=T))
-        dom = max(af, key=lambda kname: stage_ms[kname])
-        achieved = af[dom] / (stage_ms[dom] * 1e-3) / 1e12
+        af = model
+        achieved = af[dom] / (dom_ms * 1e-3) / 1e12
         # bf16 inputs: the backward's products run on bf16 MFMA (split fp32 operands);
         # fp32 inputs: on fp32 MFMA (v_mfma_f32_16x16x4_f32)
         peak = MFMA_BF16_PEAK_TFLOPS if dt == torch.bfloat16 else FP32_MFMA_PEAK_TFLOPS

@@ -163,7 +163,7 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
     const SeqMap sm = make_map(a, pl, chunk_off);
 
     auto mark = [&](int i) {
-        return !a->events || hipEventRecord(a->events[i], stream) == hipSuccess;
+        return !a->events || !a->events[i] || hipEventRecord(a->events[i], stream) == hipSuccess;
     };
     if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, chunk_off, (int)pl.n_seq, stream) != hipSuccess)
         return GDR_ELAUNCH;
@@ -288,7 +288,7 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
     bp.scale = a->scale;
 
     auto mark = [&](int i) {
-        return !a->events || hipEventRecord(a->events[i], stream) == hipSuccess;
+        return !a->events || !a->events[i] || hipEventRecord(a->events[i], stream) == hipSuccess;
     };
     if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, chunk_off, (int)pl.n_seq, stream) != hipSuccess)
         return GDR_ELAUNCH;

@@ -543,8 +543,8 @@ hipError_t launch_bwd_t(const BwdParams &p, int n_chunks_ub, int n_units, const 
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
-    if (ev && ((e = hipEventRecord(ev[0], s)) != hipSuccess || (e = hipEventRecord(ev[1], s)) != hipSuccess))
-        return e;
+    if (ev && ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
+    if (ev && ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return e;
     if (n_chunks_ub > 0) {
         if constexpr (sizeof(In) == 2) {
             e = launch_bwd_local_bf16(sizeof(Gt) == 2 ? Dt::BF16 : Dt::F32, KD, p, n_chunks_ub, s);
@@ -554,7 +554,7 @@ hipError_t launch_bwd_t(const BwdParams &p, int n_chunks_ub, int n_units, const 
         }
         if (e != hipSuccess) return e;
     }
-    if (ev) e = hipEventRecord(ev[2], s);
+    if (ev && ev[2]) e = hipEventRecord(ev[2], s);
     return e;
 }
 

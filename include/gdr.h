@@ -97,7 +97,9 @@ typedef struct {
     float *u_out;               /* [B,T,H_v,V] U = T diag(beta) V, NULL = not computed */
     /* timing hook: NULL, or a HOST array of 2*GDR_FWD_STAGES events that are
        recorded on the stream before and after each stage (chunk prep, scan
-       with output, W/U); a stage that does not run records both at once */
+       with output, W/U); a stage that does not run records both at once.  A
+       NULL entry is skipped (each record costs the stream a few microseconds,
+       so a caller timing one stage passes only that stage's pair) */
     hipEvent_t *events;
     /* scratch */
     void *workspace;
@@ -125,7 +127,8 @@ typedef struct {
                                    means zeros); NULL = not wanted */
     /* timing hook: NULL, or a HOST array of 2*GDR_BWD_STAGES events recorded
        before and after each stage (T-block rebuild, chunk-start state
-       recompute, reverse scan, chunk-local gradients) */
+       recompute, reverse scan, chunk-local gradients); NULL entries are
+       skipped */
     hipEvent_t *events;
     void *workspace;
     size_t workspace_bytes;
