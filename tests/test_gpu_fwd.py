@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from gdr_inputs import make_inputs
-from gpu_helpers import host, rel, run_fwd, slice_units, tol
+from gpu_helpers import gpu_inputs, host, rel, run_fwd, slice_units, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -112,3 +112,45 @@ def test_run_to_run_bitwise_determinism():
     for ta, tb in zip(a, b):
         if ta is not None:
             assert torch.equal(ta, tb)
+
+
+def test_timing_events_with_null_entries():
+    """The events hook records only the non-NULL entries (here the scan's pair)
+    and changes no result."""
+    import ctypes
+    from gated_delta_rule_85_amd import _lib
+    x = make_inputs(dict(B=1, T=200, Hq=1, Hv=2, K=64, V=64, dtype="bf16", h0=True), seed=6)
+    ref = run_fwd(x, return_h=False, cp_mode="off")
+    d = gpu_inputs(x)
+    B, T, Hq, K = d["q"].shape
+    Hv, V = d["v"].shape[2], d["v"].shape[3]
+    o = torch.empty((B, T, Hv, V), device="cuda")
+    ht = torch.empty((B, Hv, K, V), device="cuda")
+    gc = torch.empty((B, T, Hv), device="cuda")
+    A = torch.empty((B, T, Hv, 64), device="cuda")
+    a = _lib.FwdArgs()
+    a.B, a.T, a.H_q, a.H_v, a.K, a.V, a.n_seq = B, T, Hq, Hv, K, V, B
+    a.dtype, a.out_dtype, a.scale, a.cp_mode = _lib.BF16, _lib.F32, float(x["scale"]), _lib.CP_OFF
+    a.q, a.k, a.v = d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr()
+    a.g, a.beta, a.initial_state = d["g"].data_ptr(), d["beta"].data_ptr(), d["initial_state"].data_ptr()
+    a.o, a.final_state, a.g_cum, a.A = o.data_ptr(), ht.data_ptr(), gc.data_ptr(), A.data_ptr()
+    ws = torch.empty(max(_lib.fwd_workspace(a), 1), dtype=torch.uint8, device="cuda")
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    arr = (ctypes.c_void_p * (2 * _lib.FWD_STAGES))()
+    for i in (2, 3):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        arr[i] = e.value
+    a.events = ctypes.addressof(arr)
+    _lib.fwd(a, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    f = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(f), arr[2], arr[3]) == 0 and f.value > 0.0
+    for i in (2, 3):
+        hip.hipEventDestroy(arr[i])
+    assert torch.equal(o, ref[2]) and torch.equal(ht, ref[4])
+    assert torch.equal(gc, ref[0]) and torch.equal(A, ref[1])
