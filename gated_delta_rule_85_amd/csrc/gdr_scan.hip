@@ -214,16 +214,17 @@ template <typename In, typename Out, int KD, bool STATES> struct Scan {
         if constexpr (SNAP) {
             if (p.hsnap) {
                 float *hs = p.hsnap + ((int64_t)(cb + c) * p.Hv + hv) * (int64_t)KD * p.V;
-                if (C::BF && p.hsnap_split) {  // hi, lo planes of h^T: this lane's 4 keys at its column
+                if (C::BF && p.hsnap_split) {  // hi, lo planes of h^T: this lane's 8 keys at its column
                     char *hb = reinterpret_cast<char *>(hs);
                     const int plane = KD * p.V * 2;
 #pragma unroll
-                    for (int dt = 0; dt < C::DT; ++dt) {
-                        bf16x4 hi, lo;
-                        split4(h[dt], hi, lo);
-                        const uint32_t off = (uint32_t)(((colw + n16) * KD + slot_base(dt, g)) * 2);
-                        *reinterpret_cast<bf16x4 *>(hb + off) = hi;
-                        *reinterpret_cast<bf16x4 *>(hb + plane + off) = lo;
+                    for (int dp = 0; dp < C::DP; ++dp) {  // tiles 2dp, 2dp + 1 hold keys 32dp + 8g .. + 7
+                        bf16x4 hi0, lo0, hi1, lo1;
+                        split4(h[2 * dp], hi0, lo0);
+                        split4(h[2 * dp + 1], hi1, lo1);
+                        const uint32_t off = (uint32_t)(((colw + n16) * KD + slot_base(2 * dp, g)) * 2);
+                        *reinterpret_cast<bf16x8 *>(hb + off) = cat(hi0, hi1);
+                        *reinterpret_cast<bf16x8 *>(hb + plane + off) = cat(lo0, lo1);
                     }
                 } else {
 #pragma unroll
