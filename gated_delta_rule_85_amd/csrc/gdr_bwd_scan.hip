@@ -15,11 +15,25 @@ using namespace bwd;
 // ------------------------------------------------------------- reverse scan
 // One workgroup per (sequence, v head, 64 value columns); wave w owns
 // columns 16 w .. 16 w + 15 and keeps its K x 16 slice of dh in registers
-// (accumulator order: dh[dt] = rows 16 dt + 4 g + i, column 16 w + lane16).
+// (dh[dt] = keys slot_base(dt, g) + i, column 16 w + lane16).
 // Per chunk, from the end: the transposed decayed scores P^T (upper
 // triangular, shared split planes), then per wave
 //   dU~ = diag(r) K dh' + s P^T dO,  dX = T^T dU~,
 //   dh  = e_last dh' + Q^T diag(s e) dO - K^T diag(beta e) dX.
+// A operand of M^T for a K x V tile in the contiguous-slot key order: row n is
+// key c0 + 8 (n / 4) + n % 4, k = tokens 32 ip + 4g + j and 32 ip + 16 + 4g + j
+// (the accumulator order of the token tiles it multiplies)
+template <int ROWB>
+__device__ __forceinline__ OpX kt_keys(const char *M, int c0, int ip) {
+    using S = Swz<ROWB>;
+    const int n = ln16(), g = lg4();
+    const int row = 32 * ip + 4 * g + (n >> 2), byte = 2 * (c0 + 8 * (n & 3));
+    OpX r;
+    r.b0 = lds_tr4(M + S::off(row, byte));
+    r.b1 = lds_tr4(M + S::off(row + 16, byte));
+    return r;
+}
+
 template <int KD>
 __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_units) {
     constexpr int KROW = KD * 2, DROW = 64 * 2, PROW = 64 * 2, PPLANE = CH * PROW;
@@ -48,12 +62,13 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
     const float *sc = reinterpret_cast<const float *>(Tb + TB::SC);
     const float *eg = sc + CH, *rr = sc + 2 * CH, *bet = sc + 3 * CH;
 
+    // dh[dt][i] = key slot_base(dt, g) + i (the contiguous-slot order of gdr_lds.hpp), column col
     f32x4 dh[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            dh[dt][i] = p.dht ? p.dht[unit * KV + (16 * dt + 4 * g + i) * p.V + col] : 0.f;
+            dh[dt][i] = p.dht ? p.dht[unit * KV + (slot_base(dt, g) + i) * p.V + col] : 0.f;
     zero_lower_pt(Pt);
 
     for (int c = N - 1; c >= 0; --c) {
@@ -68,12 +83,13 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
             char *o = reinterpret_cast<char *>(p.dhs + ((int64_t)(cb + c) * p.Hv + hv) * KV);
             const int plane = KD * p.V * 2;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                bf16x4 hi, lo;
-                split4(dh[dt], hi, lo);
-                const uint32_t off = (uint32_t)((col * KD + 16 * dt + 4 * g) * 2);
-                *reinterpret_cast<bf16x4 *>(o + off) = hi;
-                *reinterpret_cast<bf16x4 *>(o + plane + off) = lo;
+            for (int dp = 0; dp < DP; ++dp) {  // tiles 2dp, 2dp + 1: keys 32dp + 8g .. + 7
+                bf16x4 hi0, lo0, hi1, lo1;
+                split4(dh[2 * dp], hi0, lo0);
+                split4(dh[2 * dp + 1], hi1, lo1);
+                const uint32_t off = (uint32_t)((col * KD + slot_base(2 * dp, g)) * 2);
+                *reinterpret_cast<bf16x8 *>(o + off) = cat(hi0, hi1);
+                *reinterpret_cast<bf16x8 *>(o + plane + off) = cat(lo0, lo1);
             }
         }
         wait_dma();
@@ -89,7 +105,7 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
             const OpS hb = Ops<bf16>::split(dh[2 * dp], dh[2 * dp + 1]);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
-                du[rt] = mma(du[rt], frag<bf16, KROW>(Ks, 16 * rt + n16, (32 * dp + 4 * g) * 2), hb);
+                du[rt] = mma(du[rt], frag8<bf16, Swz<KROW>>(Ks, 16 * rt + n16, (32 * dp + 8 * g) * 2), hb);
         }
         const OpX dob0 = kt_operand<bf16, DROW>(Ds, 16 * w, 0), dob1 = kt_operand<bf16, DROW>(Ds, 16 * w, 1);
 #pragma unroll
@@ -134,10 +150,11 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             dh[dt] *= el;
+            const int c0 = 32 * (dt >> 1) + 4 * (dt & 1);  // rows of tile dt: keys c0 + 8m + i
 #pragma unroll
             for (int ip = 0; ip < 2; ++ip) {
-                dh[dt] = mma(dh[dt], kt_operand<bf16, KROW>(Qs, 16 * dt, ip), edo[ip]);
-                dh[dt] = mma(dh[dt], kt_operand<bf16, KROW>(Ks, 16 * dt, ip), bdx[ip]);
+                dh[dt] = mma(dh[dt], kt_keys<KROW>(Qs, c0, ip), edo[ip]);
+                dh[dt] = mma(dh[dt], kt_keys<KROW>(Ks, c0, ip), bdx[ip]);
             }
         }
     }
@@ -145,7 +162,7 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p.dh0[unit * KV + (16 * dt + 4 * g + i) * p.V + col] = dh[dt][i];
+            for (int i = 0; i < 4; ++i) p.dh0[unit * KV + (slot_base(dt, g) + i) * p.V + col] = dh[dt][i];
     }
 }
 
