@@ -55,7 +55,7 @@ class BwdArgs(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            "libgdr.so is not built (%s); run `python -m gated_delta_rule_85_amd.build` or "
+            "libgdr.so is not built (%s); run `python gated_delta_rule_85_amd/build.py` or "
             "__graft_entry__.build() first" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     lib.gdr_abi_version.restype = ctypes.c_int
