@@ -180,11 +180,12 @@ template <typename In, typename Out, int KD, bool STATES> struct Scan {
 
         // decayed causal scores: this wave's share of the ten tiles (tr >= ti)
         if constexpr (EMIT) {
-            // the ten tiles over the waves: 3 each for waves 2, 3, 2 each for the copy waves 0, 1
+            // the ten tiles go to waves 2 and 3, five each: waves 0 and 1 issue the
+            // copies of the next chunk meanwhile
 #pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                const int t = 4 * k + ((w + 2) & 3);
-                if (t >= 10) break;
+            for (int k = 0; k < 5; ++k) {
+                if (w < NCW) break;
+                const int t = 2 * k + (w - NCW);
                 const int tr = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
                 const int ti = t - tr * (tr + 1) / 2;
                 f32x4 acc = zero4();
@@ -227,10 +228,16 @@ template <typename In, typename Out, int KD, bool STATES> struct Scan {
                         *reinterpret_cast<bf16x8 *>(hb + plane + off) = cat(lo0, lo1);
                     }
                 } else {
+                    // row stride made opaque per chunk: otherwise the 32 per-lane
+                    // addresses are hoisted out of the chunk loop and held in registers
+                    int rs = p.V;
+                    asm volatile("" : "+s"(rs));
+                    float *hl = hs + 8 * g * rs + colw + n16;
 #pragma unroll
                     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) hs[(slot_base(dt, g) + i) * p.V + colw + n16] = h[dt][i];
+                        for (int i = 0; i < 4; ++i)
+                            hl[(uint32_t)((32 * (dt >> 1) + 4 * (dt & 1) + i) * rs)] = h[dt][i];
                 }
             }
         }
