@@ -288,29 +288,6 @@ template <typename In, typename Out, int KD, bool STATES> struct Scan {
                 }
             }
         }
-        __syncthreads();  // score planes complete
-        if constexpr (EMIT) {
-            // O^T = (Q h)^T diag(e^gam) + U~^T P^T; the split U~ serves as the A operand of U~^T
-            // and the P fragments as the B operand of P^T
-            const ST us0 = O::split(ut[0], ut[1]);
-            const ST us1 = O::split(ut[2], ut[3]);
-            SplitPlane<In> pp;
-            pp.hi = reinterpret_cast<typename SplitPlaneT<In>::type *>(pplane);
-            pp.lo = reinterpret_cast<typename SplitPlaneT<In>::type *>(pplane + CH * C::PROW);
-            const int EB = C::BF ? 2 : 4;
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                f32x4 acc = eg[16 * rt + n16] * qh[rt];
-#pragma unroll
-                for (int ip = 0; ip <= rt / 2; ++ip) {
-                    const int row = 16 * rt + n16, byte = (32 * ip + 8 * g) * EB;
-                    acc = mma(acc, ip == 0 ? us0 : us1, pp.get8(SP::off(row, byte), SP::off(row, byte + 16)));
-                }
-                pend_o[rt] = p.scale * acc;
-            }
-            pend_ts = ts;
-            pend_n = n;
-        }
         // h' = e^{gam_last} h + K^T (exp(gam_last - gam) U~)
         {
             f32x4 y[4];
@@ -326,6 +303,35 @@ template <typename In, typename Out, int KD, bool STATES> struct Scan {
                 h[dt] = mma(h[dt], kt8<In, SK>(Ks, 0, c0, 8), rus0);
                 h[dt] = mma(h[dt], kt8<In, SK>(Ks, 32, c0, 8), rus1);
             }
+        }
+        ST us0, us1;
+        f32x4 oq[4];
+        if constexpr (EMIT) {
+            us0 = O::split(ut[0], ut[1]);
+            us1 = O::split(ut[2], ut[3]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) oq[rt] = eg[16 * rt + n16] * qh[rt];
+        }
+        __syncthreads();  // score planes complete
+        if constexpr (EMIT) {
+            // O^T = (Q h)^T diag(e^gam) + U~^T P^T; the split U~ serves as the A operand of U~^T
+            // and the P fragments as the B operand of P^T
+            SplitPlane<In> pp;
+            pp.hi = reinterpret_cast<typename SplitPlaneT<In>::type *>(pplane);
+            pp.lo = reinterpret_cast<typename SplitPlaneT<In>::type *>(pplane + CH * C::PROW);
+            const int EB = C::BF ? 2 : 4;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 acc = oq[rt];
+#pragma unroll
+                for (int ip = 0; ip <= rt / 2; ++ip) {
+                    const int row = 16 * rt + n16, byte = (32 * ip + 8 * g) * EB;
+                    acc = mma(acc, ip == 0 ? us0 : us1, pp.get8(SP::off(row, byte), SP::off(row, byte + 16)));
+                }
+                pend_o[rt] = p.scale * acc;
+            }
+            pend_ts = ts;
+            pend_n = n;
         }
     }
 
