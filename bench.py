@@ -227,6 +227,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cold", type=int, default=10,
                     help="extra steps timed after a 1 GiB cache scrub (median reported)")
+    ap.add_argument("--cp", choices=("auto", "off", "warmup"), default="auto",
+                    help="sequence split of the forward (training: always off)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -266,7 +268,8 @@ def main():
     a.dtype = _lib.BF16 if dt == torch.bfloat16 else _lib.F32
     a.out_dtype = _lib.F32
     a.scale = float(x["scale"])
-    a.cp_mode = _lib.CP_OFF if train else _lib.CP_AUTO
+    a.cp_mode = _lib.CP_OFF if train else {"auto": _lib.CP_AUTO, "off": _lib.CP_OFF,
+                                            "warmup": _lib.CP_WARMUP}[args.cp]
     a.q, a.k, a.v, a.g, a.beta = q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr()
     a.initial_state = None if h0 is None else h0.data_ptr()
     a.cu_seqlens = None if cu is None else cu.data_ptr()
@@ -393,6 +396,10 @@ def main():
     tflops = F_TRI * tokens * Hv / (ms * 1e-3) / 1e12
     wl = "%s: B=%d T=%d H_q=%d H_v=%d K=%d V=%d, %s q/k/v, fp32 g/beta/state/o" % (
         args.workload, B, T, Hq, Hv, K, V, x["dtype"])
+    if cu is not None:
+        wl += ", %d packed sequences (%d tokens)" % (n_seq, int(x["cu_seqlens"][-1]))
+    if not train and args.cp != "auto":
+        wl += ", sequence split %s" % args.cp
     rec = {
         "metric": METRIC if not train else
         "GDN chunked fwd+bwd (training step) tokens/s, H_v=%d K=V=%d T=%d" % (Hv, K, T),

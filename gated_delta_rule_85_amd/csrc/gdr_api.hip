@@ -15,6 +15,15 @@ constexpr size_t ALIGN = 256;
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// Packed sequences up to this count are scanned longest first (their order is
+// computed on the device with one thread per sequence, O(n_seq^2) work).
+constexpr int64_t LPT_MAX_SEQ = 8192;
+bool use_lpt(bool varlen, int64_t n_seq) { return varlen && n_seq <= LPT_MAX_SEQ; }
+// varlen bookkeeping: chunk offsets [n_seq + 1], then the length order [n_seq]
+size_t seq_table_bytes(bool varlen, int64_t n_seq) {
+    if (!varlen) return 0;
+    return up(sizeof(int32_t) * (size_t)(n_seq + 1 + (use_lpt(varlen, n_seq) ? n_seq : 0)));
+}
 
 struct FwdPlan {
     int64_t n_seq, tokens, nct, nt_ub;  // nct: chunks per sequence bound
@@ -49,7 +58,7 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl) {
     pl.nt_ub = varlen ? pl.nct + pl.n_seq : a->B * pl.nct;
     size_t off = 0;
     pl.off_chunk = off;
-    if (varlen) off += up(sizeof(int32_t) * (size_t)(pl.n_seq + 1));
+    off += seq_table_bytes(varlen, pl.n_seq);
     pl.off_tblk = off;
     off += up(tblock_bytes(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32) * (size_t)(pl.nt_ub * a->H_v));
     pl.total = off;
@@ -90,7 +99,7 @@ int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl) {
     const size_t nb = (size_t)(pl.nt_ub * a->H_v);
     size_t off = 0;
     pl.off_chunk = off;
-    if (varlen) off += up(sizeof(int32_t) * (size_t)(pl.n_seq + 1));
+    off += seq_table_bytes(varlen, pl.n_seq);
     pl.off_tblk = off;
     off += up(tblock_bytes(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32) * nb);
     pl.off_hs = off;
@@ -105,6 +114,7 @@ SeqMap make_map(const gdr_fwd_args *a, const FwdPlan &pl, const int32_t *chunk_o
     SeqMap m;
     m.cu = a->cu_seqlens;
     m.chunk_off = chunk_off;
+    m.order = use_lpt(a->cu_seqlens != nullptr, pl.n_seq) ? chunk_off + pl.n_seq + 1 : nullptr;
     m.T = a->T;
     m.n_seq = (int32_t)pl.n_seq;
     m.nct = (int32_t)pl.nct;
@@ -165,7 +175,8 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
     auto mark = [&](int i) {
         return !a->events || !a->events[i] || hipEventRecord(a->events[i], stream) == hipSuccess;
     };
-    if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, chunk_off, (int)pl.n_seq, stream) != hipSuccess)
+    if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, chunk_off, const_cast<int32_t *>(sm.order),
+                                              (int)pl.n_seq, stream) != hipSuccess)
         return GDR_ELAUNCH;
     if (!mark(0)) return GDR_ELAUNCH;
     if (pl.tokens > 0) {
@@ -258,6 +269,7 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
     SeqMap sm;
     sm.cu = a->cu_seqlens;
     sm.chunk_off = chunk_off;
+    sm.order = use_lpt(a->cu_seqlens != nullptr, pl.n_seq) ? chunk_off + pl.n_seq + 1 : nullptr;
     sm.T = a->T;
     sm.n_seq = (int32_t)pl.n_seq;
     sm.nct = (int32_t)pl.nct;
@@ -290,7 +302,8 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
     auto mark = [&](int i) {
         return !a->events || !a->events[i] || hipEventRecord(a->events[i], stream) == hipSuccess;
     };
-    if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, chunk_off, (int)pl.n_seq, stream) != hipSuccess)
+    if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, chunk_off, const_cast<int32_t *>(sm.order),
+                                              (int)pl.n_seq, stream) != hipSuccess)
         return GDR_ELAUNCH;
     if (!mark(0)) return GDR_ELAUNCH;
     if (pl.tokens > 0 && launch_tblocks(dt, bp, (int)pl.nt_ub, stream) != hipSuccess) return GDR_ELAUNCH;

@@ -162,9 +162,15 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_kernel(const BwdParams p, int n
     __shared__ float gam[CH], eg[CH], rr[CH], bet[CH];
 
     const int nvt = p.V / 64;
-    const int wid = xcd_remap(blockIdx.x, gridDim.x);
-    const int vt = wid % nvt, unit = wid / nvt;
-    if (unit >= n_units) return;
+    int vt, unit;
+    if (p.sm.order) {  // packed sequences: longest first
+        if (!lpt_item(p.sm, p.Hq, p.Hv, nvt, vt, unit)) return;
+    } else {
+        const int wid = xcd_remap(blockIdx.x, gridDim.x);
+        vt = wid % nvt;
+        unit = wid / nvt;
+        if (unit >= n_units) return;
+    }
     const int j = unit / p.Hv, hv = unit % p.Hv, hq = hv / (p.Hv / p.Hq);
     const int w = wave_id(), nn = ln16(), g = lg4();
     const int col = vt * 64 + 16 * w + nn;  // this lane's value column
@@ -539,7 +545,9 @@ hipError_t launch_bwd_t(const BwdParams &p, int n_chunks_ub, int n_units, const 
     if constexpr (sizeof(In) == 2) {
         e = launch_bwd_scan_bf16(KD, p, n_units, s);
     } else {
-        hipLaunchKernelGGL((bwd_scan_kernel<In, KD>), dim3(n_units * (p.V / 64)), dim3(NTHR), 0, s, p, n_units);
+        hipLaunchKernelGGL((bwd_scan_kernel<In, KD>),
+                           dim3(p.sm.order ? lpt_blocks(p.sm.n_seq, p.Hq, p.Hv, p.V / 64) : n_units * (p.V / 64)),
+                           dim3(NTHR), 0, s, p, n_units);
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;

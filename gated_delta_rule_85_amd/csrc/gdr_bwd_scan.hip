@@ -46,9 +46,15 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
     __shared__ __attribute__((aligned(16))) char Pt[2 * PPLANE];
 
     const int nvt = p.V / 64;
-    const int wid = xcd_remap(blockIdx.x, gridDim.x);
-    const int vt = wid % nvt, unit = wid / nvt;
-    if (unit >= n_units) return;
+    int vt, unit;
+    if (p.sm.order) {  // packed sequences: longest first
+        if (!lpt_item(p.sm, p.Hq, p.Hv, nvt, vt, unit)) return;
+    } else {
+        const int wid = xcd_remap(blockIdx.x, gridDim.x);
+        vt = wid % nvt;
+        unit = wid / nvt;
+        if (unit >= n_units) return;
+    }
     const int j = unit / p.Hv, hv = unit % p.Hv, hq = hv / (p.Hv / p.Hq);
     const int w = __builtin_amdgcn_readfirstlane(wave_id()), n16 = ln16(), g = lg4();
     const int col = vt * 64 + 16 * w + n16;
@@ -170,7 +176,7 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
 }  // namespace
 
 hipError_t launch_bwd_scan_bf16(int K, const BwdParams &p, int n_units, hipStream_t s) {
-    const dim3 grid(n_units * (p.V / 64));
+    const dim3 grid(p.sm.order ? lpt_blocks(p.sm.n_seq, p.Hq, p.Hv, p.V / 64) : n_units * (p.V / 64));
     if (K == 128)
         hipLaunchKernelGGL((bwd_scan_bf16<128>), grid, dim3(NTHR), 0, s, p, n_units);
     else

@@ -204,6 +204,7 @@ template <> struct Vec16<float> { typedef f32x4 type; static constexpr int n = 4
 struct SeqMap {
     const int32_t *cu;        // [n_seq+1] or null
     const int32_t *chunk_off; // [n_seq+1] or null (with cu)
+    const int32_t *order;     // [n_seq] sequences by decreasing length, or null (with cu)
     int64_t T;                // tokens per sequence without cu
     int32_t n_seq;
     int32_t nct;              // chunks per sequence without cu
@@ -243,6 +244,28 @@ struct SeqMap {
 __device__ __forceinline__ int xcd_remap(int id, int nb) {
     const int xcd = id & 7, pos = id >> 3, per = nb >> 3, rem = nb & 7;
     return xcd < rem ? xcd * (per + 1) + pos : rem * (per + 1) + (xcd - rem) * per + pos;
+}
+
+// Longest-first dealing of the (sequence, v head, value block) items of a scan
+// launch over packed sequences of different lengths.  Items are grouped by
+// (sequence, q/k head): the n_vt * (Hv / Hq) items of a group share K and Q.
+// Group rank r (0 = a group of the longest sequence) goes to XCD r % 8 at the
+// r / 8-th place of its queue, so that the first workgroups dispatched on every
+// XCD hold the longest sequences and a group's items share one L2.  The grid
+// has lpt_blocks() workgroups; false: this workgroup has no item.
+__host__ __device__ inline int lpt_blocks(int n_seq, int Hq, int Hv, int n_vt) {
+    return 8 * ((n_seq * Hq + 7) / 8) * n_vt * (Hv / Hq);
+}
+__device__ __forceinline__ bool lpt_item(const SeqMap &sm, int Hq, int Hv, int n_vt, int &vt, int &unit) {
+    const int G = Hv / Hq, members = n_vt * G;
+    const int b = blockIdx.x, x = b & 7, pp = b >> 3;
+    const int q = pp / members, m = pp - q * members;
+    const int r = q * 8 + x;
+    if (r >= sm.n_seq * Hq) return false;
+    const int j = sm.order[r / Hq], hq = r % Hq;
+    vt = m % n_vt;
+    unit = j * Hv + hq * G + m / n_vt;
+    return true;
 }
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }

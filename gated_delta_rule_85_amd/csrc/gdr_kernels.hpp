@@ -69,7 +69,8 @@ struct BwdParams {
     float scale;
 };
 
-hipError_t launch_chunk_offsets(const int32_t *cu, int32_t *chunk_off, int n_seq, hipStream_t s);
+// chunk offsets of packed sequences and (order non-null) their longest-first order
+hipError_t launch_chunk_offsets(const int32_t *cu, int32_t *chunk_off, int32_t *order, int n_seq, hipStream_t s);
 hipError_t launch_prep(Dt dt, int K, const PrepParams &p, int n_chunks_ub, hipStream_t s);
 hipError_t launch_scan_output(Dt dt, Dt out, int K, int V, const ScanParams &p, hipStream_t s);
 hipError_t launch_wu(Dt dt, const WUParams &p, int n_chunks_ub, hipStream_t s);

@@ -283,10 +283,25 @@ __global__ void chunk_offsets_kernel(const int32_t *cu, int32_t *off, int n_seq)
     }
 }
 
+// order[rank] = j: sequences by decreasing length, ties by index (one thread per
+// sequence counts the sequences ahead of it)
+__global__ void seq_order_kernel(const int32_t *cu, int32_t *order, int n_seq) {
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= n_seq) return;
+    const int lj = cu[j + 1] - cu[j];
+    int rank = 0;
+    for (int i = 0; i < n_seq; ++i) {
+        const int li = cu[i + 1] - cu[i];
+        rank += (li > lj) || (li == lj && i < j);
+    }
+    order[rank] = j;
+}
+
 }  // namespace
 
-hipError_t launch_chunk_offsets(const int32_t *cu, int32_t *chunk_off, int n_seq, hipStream_t s) {
+hipError_t launch_chunk_offsets(const int32_t *cu, int32_t *chunk_off, int32_t *order, int n_seq, hipStream_t s) {
     hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, s, cu, chunk_off, n_seq);
+    if (order) hipLaunchKernelGGL(seq_order_kernel, dim3((n_seq + 255) / 256), dim3(256), 0, s, cu, order, n_seq);
     return hipGetLastError();
 }
 

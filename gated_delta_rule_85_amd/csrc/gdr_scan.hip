@@ -373,12 +373,18 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
     S.buf[1] = buf1;
     S.pplane = pplane;
 
-    // work item: (v tile, v head, sequence, segment), XCD-grouped
-    const int wid = xcd_remap(blockIdx.x, gridDim.x);
-    S.vt = wid % p.n_vt;
-    const int rest = wid / p.n_vt;
-    S.unit = rest % p.n_units;
-    const int seg = rest / p.n_units;
+    // work item: (v tile, v head, sequence, segment), XCD-grouped; packed sequences
+    // of different lengths longest first
+    int seg = 0;
+    if (p.sm.order && p.n_seg == 1) {
+        if (!lpt_item(p.sm, p.Hq, p.Hv, p.n_vt, S.vt, S.unit)) return;
+    } else {
+        const int wid = xcd_remap(blockIdx.x, gridDim.x);
+        S.vt = wid % p.n_vt;
+        const int rest = wid / p.n_vt;
+        S.unit = rest % p.n_units;
+        seg = rest / p.n_units;
+    }
     S.j = S.unit / p.Hv;
     S.hv = S.unit % p.Hv;
     S.hq = S.hv / (p.Hv / p.Hq);
@@ -449,7 +455,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
 
 template <typename In, typename Out, int KD, bool STATES>
 hipError_t launch_scan_t(const ScanParams &p, hipStream_t s) {
-    const int nb = p.n_vt * p.n_units * p.n_seg;
+    const int nb = p.sm.order && p.n_seg == 1 ? lpt_blocks(p.sm.n_seq, p.Hq, p.Hv, p.n_vt)
+                                              : p.n_vt * p.n_units * p.n_seg;
     hipLaunchKernelGGL((scan_output_kernel<In, Out, KD, STATES>), dim3(nb), dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }

@@ -94,6 +94,12 @@ def test_workspace_sizes(L):
     assert rc == 0 and n == 256 + (4 + 3) * 4 * TBLOCK
     rc, n = rc_ws(L, fwd_args(L, dtype=L.F32, K=64, V=64))
     assert rc == 0 and n == 4 * 4 * TBLOCK
+    # up to 8192 packed sequences also get their longest-first order: (2 n_seq + 1)
+    # int32 entries; beyond that only the offsets
+    rc, n = rc_ws(L, fwd_args(L, cu_seqlens=16, n_seq=100))
+    assert rc == 0 and n == 1024 + (4 + 100) * 4 * TBLOCK
+    rc, n = rc_ws(L, fwd_args(L, cu_seqlens=16, n_seq=9000))
+    assert rc == 0 and n == 36096 + (4 + 9000) * 4 * TBLOCK
 
 
 @pytest.mark.parametrize("kw,code", [

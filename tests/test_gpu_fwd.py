@@ -82,6 +82,22 @@ def test_varlen_small_with_empty_sequence():
     assert np.array_equal(host(out[4])[3], x["initial_state"][3].astype(np.float64))
 
 
+def test_varlen_lengths_increasing_longest_first():
+    """Packed sequences are scanned longest first: lengths in increasing order (the
+    dispatch reverses them), fp32 with G = 3 and two value blocks."""
+    x = make_inputs(dict(lens=[1, 63, 64, 65, 128, 190, 257, 300], Hq=1, Hv=3, K=64, V=128,
+                         dtype="fp32", h0=True), seed=5)
+    check_all(x, run_fwd(x), ora(x, want_h=True))
+
+
+def test_varlen_many_short_sequences_natural_order():
+    """More than 8192 packed sequences keep their natural order (no length sort)."""
+    rng = np.random.default_rng(7)
+    lens = [int(v) for v in rng.integers(0, 5, size=8300)]
+    x = make_inputs(dict(lens=lens, Hq=1, Hv=2, K=64, V=64, dtype="fp32", h0=True), seed=6)
+    check_all(x, run_fwd(x), ora(x, want_h=True))
+
+
 def test_prefill_shard_full_size_sampled_units():
     """B=4, T=4096, H_q=16, H_v=32, K=V=128, bf16 (the timed workload), launched
     whole; the oracle runs whole (sequence, q/k head) groups."""
