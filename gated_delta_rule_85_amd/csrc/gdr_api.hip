@@ -44,7 +44,29 @@ int check_dims(int64_t B, int64_t T, int64_t Hq, int64_t Hv, int64_t K, int64_t 
     return GDR_OK;
 }
 
-int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl) {
+// Segment length of the sequence split when the caller leaves it open.  The
+// scan runs one workgroup per compute unit, so a launch of W workgroups per
+// segment index takes ceil(W S / slots) rounds, each as long as the longest
+// segment plus its warm-up window: choose the segment count S that minimises
+// rounds x (L + warm-up), L = ceil(N / S) (ties: fewer segments).  Returns
+// N + 1 (no split) when one segment is best.
+int64_t split_chunks(int64_t N, int64_t W, int64_t slots, int64_t wm) {
+    int64_t best_t = -1, best_L = N + 1;
+    for (int64_t S = 1; S <= N; ++S) {
+        const int64_t L = cdiv(N, S), Sx = cdiv(N, L);
+        if (Sx != S) continue;  // same L as a smaller S
+        const int64_t t = cdiv(W * S, slots) * (L + (S > 1 ? wm : 0));
+        if (best_t < 0 || t < best_t) {
+            best_t = t;
+            best_L = S > 1 ? L : N + 1;
+        }
+    }
+    return best_L;
+}
+
+// slots: workgroups the device runs at once (its compute units); 0 = unknown,
+// when the segment length is not needed (workspace sizing)
+int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     if (!a) return GDR_EINVAL;
     const bool varlen = a->cu_seqlens != nullptr;
     int rc = check_dims(a->B, a->T, a->H_q, a->H_v, a->K, a->V, a->n_seq, varlen, a->dtype);
@@ -66,16 +88,18 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl) {
     const int64_t bh = pl.n_seq * a->H_v;
     bool split = a->cp_mode == GDR_CP_WARMUP ||
                  (a->cp_mode == GDR_CP_AUTO && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
-    int L = a->cp_segment_chunks > 0 ? a->cp_segment_chunks
-                                      : (int)ceil(sqrt((double)(pl.nct > 0 ? pl.nct : 1)));
+    pl.warm_chunks = a->cp_warmup_chunks > 0 ? a->cp_warmup_chunks : 8;
+    const int64_t n_vt = a->V / scan_vtile(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32, (int)a->K, (int)a->V);
+    int64_t L = a->cp_segment_chunks > 0 ? a->cp_segment_chunks
+                : slots > 0 ? split_chunks(pl.nct, bh * n_vt, slots, pl.warm_chunks)
+                            : (int64_t)ceil(sqrt((double)(pl.nct > 0 ? pl.nct : 1)));
     if (L < 1) L = 1;
     if (!split || L >= pl.nct) {
         split = false;
-        L = (int)pl.nct + 1;
+        L = pl.nct + 1;
     }
     pl.split = split;
-    pl.seg_chunks = L;
-    pl.warm_chunks = a->cp_warmup_chunks > 0 ? a->cp_warmup_chunks : 8;
+    pl.seg_chunks = (int)L;
     pl.n_seg = split ? (int)cdiv(pl.nct, L) : 1;
     return GDR_OK;
 }
@@ -148,8 +172,13 @@ int gdr_fwd_workspace(const gdr_fwd_args *a, size_t *bytes) {
 }
 
 int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
+    // compute units of the stream's device: the scan's concurrent workgroups
+    int dev = 0, cus = 0;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return GDR_ELAUNCH;
     FwdPlan pl;
-    int rc = plan_fwd(a, pl);
+    int rc = plan_fwd(a, pl, cus);
     if (rc) return rc;
     if (pl.tokens > 0) {
         if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o) return GDR_EINVAL;

@@ -75,7 +75,8 @@ typedef struct {
     int32_t out_dtype; /* element type of o: GDR_F32 or GDR_BF16 */
     float scale;       /* output scale, usually K^-1/2 */
     int32_t cp_mode;           /* GDR_CP_* */
-    int32_t cp_segment_chunks; /* split mode: chunks per segment, 0 = ceil(sqrt(chunks)) */
+    int32_t cp_segment_chunks; /* split mode: chunks per segment; 0 = chosen for the device
+                                  (see gdr_fwd) */
     int32_t cp_warmup_chunks;  /* split mode: warm-up window in chunks, 0 = 8 */
     /* inputs */
     const void *q;              /* [B,T,H_q,K] dtype */
@@ -149,7 +150,13 @@ int gdr_fwd_workspace(const gdr_fwd_args *args, size_t *bytes);
    sequence may be partial; an empty sequence copies initial_state to
    final_state.  In split mode the chunk-start states and the output of
    segments after the first are the warm-up approximation (exact when the
-   window reaches the start of the sequence). */
+   window reaches the start of the sequence).  With cp_segment_chunks = 0 the
+   segment length L is chosen from the compute-unit count of the stream's
+   device (one scan workgroup per unit): the segment count S that minimises
+   ceil(S x workgroups per segment index / units) x (L + warm-up window),
+   L = ceil(chunks / S); the pages' sliding-window method leaves L to a
+   runtime model (they suggest sqrt(chunks) for theirs).  Returns GDR_ELAUNCH
+   if the device cannot be queried. */
 int gdr_fwd(const gdr_fwd_args *args, hipStream_t stream);
 
 /* Workspace bytes gdr_bwd needs for these sizes (pointers are not read):

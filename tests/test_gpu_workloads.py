@@ -77,13 +77,43 @@ def test_long_sequence_warmup_split(long_seq, wm):
     assert e_vs_exact <= 2e-2  # decaying gates: the split meets the same bar
 
 
+def split_chunks(N, W, slots, wm):
+    """Segment length of the device model: the segment count S minimising
+    ceil(W S / slots) * (L + wm), L = ceil(N / S), fewer segments on ties."""
+    best = None
+    for S in range(1, N + 1):
+        L = -(-N // S)
+        if -(-N // L) != S:
+            continue
+        t = -(-W * S // slots) * (L + (wm if S > 1 else 0))
+        if best is None or t < best[0]:
+            best = (t, L if S > 1 else N + 1)
+    return best[1]
+
+
+def test_segment_model_values():
+    # 8 v heads x 2 value blocks over 512 chunks on 256 CUs: 16 segments of 32 fill
+    # the device once; the full-width shard (256 workgroups) is not split
+    assert split_chunks(512, 16, 256, 8) == 32
+    assert split_chunks(64, 256, 256, 8) == 65
+
+
 def test_auto_mode_splits_the_long_sequence(long_seq):
-    """AutoCP: B*H_v = 8 <= 40 selects the split with L = ceil(sqrt(N)), Wm = 8."""
+    """AutoCP: B*H_v = 8 <= 40 selects the split, with the device model's segment
+    length and Wm = 8."""
+    import torch
     x = long_seq
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    L = split_chunks(512, 8 * 2, cus, 8)
+    print("compute units %d: segments of %d chunks" % (cus, L), flush=True)
     auto = host(run_fwd(x, return_h=False, cp_mode="auto")[2])
-    forced = host(run_fwd(x, return_h=False, cp_mode="warmup", cp_segment_chunks=23,
+    forced = host(run_fwd(x, return_h=False, cp_mode="warmup", cp_segment_chunks=L,
                           cp_warmup_chunks=8)[2])
     assert np.array_equal(auto, forced)
+    re = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"])
+    e = rel(auto, re["o"])
+    print("auto split vs exact %.3g" % e, flush=True)
+    assert e <= 2e-2
 
 
 @pytest.mark.parametrize("scale_g", [0.03, 0.01])
