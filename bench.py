@@ -227,7 +227,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cold", type=int, default=10,
                     help="extra steps timed after a 1 GiB cache scrub (median reported)")
-    ap.add_argument("--cp", choices=("auto", "off", "warmup"), default="auto",
+    ap.add_argument("--cp", choices=("auto", "off", "warmup", "exact"), default="auto",
                     help="sequence split of the forward (training: always off)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -269,7 +269,7 @@ def main():
     a.out_dtype = _lib.F32
     a.scale = float(x["scale"])
     a.cp_mode = _lib.CP_OFF if train else {"auto": _lib.CP_AUTO, "off": _lib.CP_OFF,
-                                            "warmup": _lib.CP_WARMUP}[args.cp]
+                                            "warmup": _lib.CP_WARMUP, "exact": _lib.CP_EXACT}[args.cp]
     a.q, a.k, a.v, a.g, a.beta = q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr()
     a.initial_state = None if h0 is None else h0.data_ptr()
     a.cu_seqlens = None if cu is None else cu.data_ptr()

@@ -16,7 +16,7 @@ import torch
 from . import _lib
 
 _DT = {torch.bfloat16: _lib.BF16, torch.float32: _lib.F32}
-_CP = {"auto": _lib.CP_AUTO, "off": _lib.CP_OFF, "exact": _lib.CP_OFF, "warmup": _lib.CP_WARMUP}
+_CP = {"auto": _lib.CP_AUTO, "off": _lib.CP_OFF, "warmup": _lib.CP_WARMUP, "exact": _lib.CP_EXACT}
 
 
 def _ptr(t):
@@ -63,7 +63,9 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     fp32 holds, per token, its row of T = (I + A_strict)^{-1} for its chunk;
     h [1,NT,H_v,K,V] fp32 the chunk-start states (None unless return_h);
     final_state [N,H_v,K,V] fp32 (None unless output_final_state).  With
-    ``return_wu`` also returns W, U [B,T,H_v,K|V] fp32.
+    ``return_wu`` also returns W, U [B,T,H_v,K|V] fp32.  ``cp_mode``: "auto"
+    (split long sequences of few heads), "off" (no split), "warmup" (split with
+    the sliding-window warm-up) or "exact" (split with the exact carry).
     """
     _check(q, k, v, g, beta, cu_seqlens)
     q, k, v = _c(q), _c(k), _c(v)

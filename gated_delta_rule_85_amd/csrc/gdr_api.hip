@@ -28,8 +28,10 @@ size_t seq_table_bytes(bool varlen, int64_t n_seq) {
 struct FwdPlan {
     int64_t n_seq, tokens, nct, nt_ub;  // nct: chunks per sequence bound
     size_t off_chunk, off_tblk, total;
+    // exact split: segment transitions, zero-start end states, true start states, a zero row
+    size_t off_M, off_b, off_hseg, off_zero;
     int seg_chunks, warm_chunks, n_seg;
-    bool split;
+    bool split, exact;
 };
 
 int check_dims(int64_t B, int64_t T, int64_t Hq, int64_t Hv, int64_t K, int64_t V, int64_t n_seq,
@@ -72,7 +74,7 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     int rc = check_dims(a->B, a->T, a->H_q, a->H_v, a->K, a->V, a->n_seq, varlen, a->dtype);
     if (rc) return rc;
     if (a->out_dtype != GDR_BF16 && a->out_dtype != GDR_F32) return GDR_ENOTSUP;
-    if (a->cp_mode < GDR_CP_AUTO || a->cp_mode > GDR_CP_WARMUP) return GDR_EINVAL;
+    if (a->cp_mode < GDR_CP_AUTO || a->cp_mode > GDR_CP_EXACT) return GDR_EINVAL;
     if (a->cp_segment_chunks < 0 || a->cp_warmup_chunks < 0) return GDR_EINVAL;
     pl.n_seq = varlen ? a->n_seq : a->B;
     pl.tokens = a->B * a->T;
@@ -86,7 +88,7 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     pl.total = off;
     // sequence split ("AutoCP"): the pages' trigger on batch x heads and length
     const int64_t bh = pl.n_seq * a->H_v;
-    bool split = a->cp_mode == GDR_CP_WARMUP ||
+    bool split = a->cp_mode == GDR_CP_WARMUP || a->cp_mode == GDR_CP_EXACT ||
                  (a->cp_mode == GDR_CP_AUTO && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
     pl.warm_chunks = a->cp_warmup_chunks > 0 ? a->cp_warmup_chunks : 8;
     const int64_t n_vt = a->V / scan_vtile(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32, (int)a->K, (int)a->V);
@@ -99,9 +101,27 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
         L = pl.nct + 1;
     }
     pl.split = split;
+    pl.exact = split && a->cp_mode == GDR_CP_EXACT;
+    if (pl.exact) pl.warm_chunks = 0;
     pl.seg_chunks = (int)L;
     pl.n_seg = split ? (int)cdiv(pl.nct, L) : 1;
+    pl.off_M = pl.off_b = pl.off_hseg = pl.off_zero = 0;
+    if (pl.exact) {
+        const size_t per = (size_t)bh * pl.n_seg * (size_t)a->K * sizeof(float);
+        pl.off_M = pl.total;
+        pl.off_b = pl.off_M + up(per * (size_t)a->K);
+        pl.off_hseg = pl.off_b + up(per * (size_t)a->V);
+        pl.off_zero = pl.off_hseg + up(per * (size_t)a->V);
+        pl.total = pl.off_zero + up(512);
+    }
     return GDR_OK;
+}
+
+// compute units of a device: the scan's concurrent workgroups (one per unit); 0 on failure
+int64_t device_slots(int dev) {
+    int cus = 0;
+    return hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0 ? cus
+                                                                                                          : 0;
 }
 
 struct BwdPlan {
@@ -164,21 +184,23 @@ const char *gdr_strerror(int code) {
 
 int gdr_fwd_workspace(const gdr_fwd_args *a, size_t *bytes) {
     if (!bytes) return GDR_EINVAL;
+    // the split's segment length, and with it the exact split's workspace, follows
+    // the compute units of the current device (without one: ceil(sqrt(chunks)))
+    int dev = 0;
+    const int64_t slots = hipGetDevice(&dev) == hipSuccess ? device_slots(dev) : 0;
     FwdPlan pl;
-    int rc = plan_fwd(a, pl);
+    int rc = plan_fwd(a, pl, slots);
     if (rc) return rc;
     *bytes = pl.total;
     return GDR_OK;
 }
 
 int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
-    // compute units of the stream's device: the scan's concurrent workgroups
-    int dev = 0, cus = 0;
-    if (hipStreamGetDevice(stream, &dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-        return GDR_ELAUNCH;
+    // host-side checks come first; the device query is needed only to launch
+    int dev = 0;
+    const int64_t slots = hipStreamGetDevice(stream, &dev) == hipSuccess ? device_slots(dev) : 0;
     FwdPlan pl;
-    int rc = plan_fwd(a, pl, cus);
+    int rc = plan_fwd(a, pl, slots);
     if (rc) return rc;
     if (pl.tokens > 0) {
         if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o) return GDR_EINVAL;
@@ -193,6 +215,7 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
         return GDR_EINVAL;
     if (a->workspace_bytes < pl.total || (pl.total > 0 && !a->workspace)) return GDR_EWORKSPACE;
     if (pl.total > 0 && !aligned(a->workspace, 16)) return GDR_EINVAL;
+    if (slots == 0) return GDR_ELAUNCH;
 
     char *ws = static_cast<char *>(a->workspace);
     int32_t *chunk_off = a->cu_seqlens ? reinterpret_cast<int32_t *>(ws + pl.off_chunk) : nullptr;
@@ -226,6 +249,11 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
     sp.q = a->q;
     sp.k = a->k;
     sp.v = a->v;
+    sp.v_tok = a->H_v * a->V;
+    sp.v_head = a->V;
+    sp.h0_seg = nullptr;
+    sp.hT_seg = nullptr;
+    sp.eye_h0 = 0;
     sp.tblk = tblk;
     sp.h0 = a->initial_state;
     sp.o = a->o;
@@ -242,6 +270,44 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
     sp.n_vt = (int)(a->V / scan_vtile(dt, (int)a->K, (int)a->V));
     sp.n_units = (int)(pl.n_seq * a->H_v);
     sp.n_seg = pl.n_seg;
+    if (pl.exact && pl.tokens > 0) {
+        // segment transitions: the scan from the identity over zero values (V = K) ...
+        float *Mb = reinterpret_cast<float *>(ws + pl.off_M), *bb = reinterpret_cast<float *>(ws + pl.off_b);
+        float *hseg = reinterpret_cast<float *>(ws + pl.off_hseg);
+        if (launch_fill_zero(ws + pl.off_zero, 512, stream) != hipSuccess) return GDR_ELAUNCH;
+        ScanParams tp = sp;
+        tp.v = ws + pl.off_zero;
+        tp.v_tok = tp.v_head = 0;
+        tp.V = (int)a->K;
+        tp.n_vt = (int)(a->K / scan_vtile(dt, (int)a->K, (int)a->K));
+        tp.eye_h0 = 1;
+        tp.h0 = nullptr;
+        tp.o = nullptr;
+        tp.hT = nullptr;
+        tp.hsnap = nullptr;
+        tp.hT_seg = Mb;
+        if (launch_scan_output(dt, ot, (int)a->K, (int)a->K, tp, stream) != hipSuccess) return GDR_ELAUNCH;
+        // ... the end states from a zero start (the first segment from the initial state) ...
+        ScanParams bp = sp;
+        bp.o = nullptr;
+        bp.hT = nullptr;
+        bp.hsnap = nullptr;
+        bp.hT_seg = bb;
+        if (launch_scan_output(dt, ot, (int)a->K, (int)a->V, bp, stream) != hipSuccess) return GDR_ELAUNCH;
+        // ... the serial carry over the segments, then the segments again from their true starts
+        CarryParams cp;
+        cp.M = Mb;
+        cp.b = bb;
+        cp.h0_seg = hseg;
+        cp.sm = sm;
+        cp.Hv = (int)a->H_v;
+        cp.K = (int)a->K;
+        cp.V = (int)a->V;
+        cp.seg_chunks = pl.seg_chunks;
+        cp.n_seg = pl.n_seg;
+        if (launch_carry(cp, (int)(pl.n_seq * a->H_v), stream) != hipSuccess) return GDR_ELAUNCH;
+        sp.h0_seg = hseg;
+    }
     if (launch_scan_output(dt, ot, (int)a->K, (int)a->V, sp, stream) != hipSuccess) return GDR_ELAUNCH;
     if (!mark(3) || !mark(4)) return GDR_ELAUNCH;
     if ((a->w_out || a->u_out) && pl.tokens > 0) {
@@ -343,6 +409,11 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
         sp.q = a->q;
         sp.k = a->k;
         sp.v = a->v;
+        sp.v_tok = a->H_v * a->V;
+        sp.v_head = a->V;
+        sp.h0_seg = nullptr;
+        sp.hT_seg = nullptr;
+        sp.eye_h0 = 0;
         sp.tblk = bp.tblk;
         sp.h0 = a->initial_state;
         sp.o = nullptr;

@@ -27,6 +27,8 @@ struct PrepParams {
 // chunks with the output of each chunk.
 struct ScanParams {
     const void *q, *k, *v;
+    int64_t v_tok, v_head;  // element strides of v between tokens and between v heads
+                            // (both 0: every row is the same, a zero row for transitions)
     const char *tblk;  // [chunks, H_v] T blocks from gdr_chunk_prep
     const float *h0;  // [N, H_v, K, V] or null
     void *o;          // [tokens, H_v, V]
@@ -40,6 +42,22 @@ struct ScanParams {
     int seg_chunks;   // chunks per segment
     int warm_chunks;  // warm-up window of segments after the first
     int n_vt, n_units, n_seg;
+    // exact sequence split: segments after the first start from h0_seg (or, eye_h0,
+    // from the identity, V = K, which makes the segment's end state its transition
+    // matrix); hT_seg receives every segment's end state.  [n_units][n_seg][K][V]
+    const float *h0_seg;
+    float *hT_seg;
+    int eye_h0;
+};
+
+// carry of the exact sequence split: for segments s = 1 .. of each unit,
+// start(s) = M(s-1) start(s-1) + b(s-1), start(1) = b(0), written to h0_seg
+struct CarryParams {
+    const float *M;    // [n_units][n_seg][K][K] segment transitions
+    const float *b;    // [n_units][n_seg][K][V] segment end states from a zero start (s = 0: from h0)
+    float *h0_seg;     // [n_units][n_seg][K][V]
+    SeqMap sm;
+    int Hv, K, V, seg_chunks, n_seg;
 };
 
 // optional materialisation of W = T diag(beta e^gam) K and U = T diag(beta) V
@@ -75,6 +93,8 @@ hipError_t launch_prep(Dt dt, int K, const PrepParams &p, int n_chunks_ub, hipSt
 hipError_t launch_scan_output(Dt dt, Dt out, int K, int V, const ScanParams &p, hipStream_t s);
 hipError_t launch_wu(Dt dt, const WUParams &p, int n_chunks_ub, hipStream_t s);
 hipError_t launch_scan_states(Dt dt, int K, const ScanParams &p, hipStream_t s);
+hipError_t launch_carry(const CarryParams &p, int n_units, hipStream_t s);
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_tblocks(Dt dt, const BwdParams &p, int n_chunks_ub, hipStream_t s);
 // ev: null or 3 events: after the reverse scan, before and after the local stage
 hipError_t launch_bwd(Dt dt, Dt gt, int K, const BwdParams &p, int n_chunks_ub, int n_units,

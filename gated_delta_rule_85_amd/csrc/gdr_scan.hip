@@ -133,10 +133,10 @@ template <typename In, typename Out, int KD, bool STATES> struct Scan {
         const int64_t ts = bos + (int64_t)c * CH;
         const int nm1 = (int)min<int64_t>(CH, eos - ts) - 1;
         const int l = lane_id();
-        const int krs = p.Hq * KD * C::ES, vrs = p.Hv * p.V * C::ES;  // row strides (bytes)
+        const int krs = p.Hq * KD * C::ES, vrs = (int)(p.v_tok * C::ES);  // row strides (bytes)
         const char *kb = reinterpret_cast<const char *>(kp + (ts * p.Hq + hq) * KD);
         const char *qb = reinterpret_cast<const char *>(qp + (ts * p.Hq + hq) * KD);
-        const char *vb = reinterpret_cast<const char *>(vp + (ts * p.Hv + hv) * p.V + vt * BV);
+        const char *vb = reinterpret_cast<const char *>(vp + ts * p.v_tok + hv * p.v_head + vt * BV);
 #pragma unroll
         for (int s = 0; s < C::NKI / NCW; ++s) {
             const uint32_t off = (uint32_t)(min(krow[s], nm1) * krs + kchk[s]);
@@ -351,7 +351,7 @@ template <typename In, typename Out, int KD, bool STATES> struct Scan {
         }
         if constexpr (STATES)
             step<false, true>(c, cur);
-        else if (c >= c_begin)
+        else if (c >= c_begin && p.o)
             step<true, true>(c, cur);
         else
             step<false, false>(c, cur);
@@ -410,13 +410,18 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
     S.setup_copies();
     const int64_t KV = (int64_t)KD * p.V;
     {
-        const bool from_h0 = (w_begin == 0) && p.h0 != nullptr;
-        const float *h0 = from_h0 ? p.h0 + (int64_t)S.unit * KV : nullptr;
+        const bool from_seg = seg > 0 && p.h0_seg != nullptr;
+        const bool from_h0 = !from_seg && (w_begin == 0) && p.h0 != nullptr;
+        const float *h0 = from_seg ? p.h0_seg + ((int64_t)S.unit * p.n_seg + seg) * KV
+                          : from_h0 ? p.h0 + (int64_t)S.unit * KV : nullptr;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S.h[dt][i] = from_h0 ? h0[(slot_base(dt, S.g) + i) * p.V + S.colw + S.n16] : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int key = slot_base(dt, S.g) + i;
+                S.h[dt][i] = p.eye_h0 ? (key == S.colw + S.n16 ? 1.f : 0.f)
+                             : h0 ? h0[key * p.V + S.colw + S.n16] : 0.f;
+            }
     }
     // score-plane tiles above the diagonal pairs, (0,1) and (2,3), are read as zero and never written
     {
@@ -444,6 +449,13 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
         if (c + 1 < c_end) S.template run<1>(c + 1, c_begin, c_end);
     }
     S.store_pending();
+    if (p.hT_seg) {
+        float *hs = p.hT_seg + ((int64_t)S.unit * p.n_seg + seg) * KV;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hs[(slot_base(dt, S.g) + i) * p.V + S.colw + S.n16] = S.h[dt][i];
+    }
     if (c_end == N && p.hT) {
         float *hT = p.hT + (int64_t)S.unit * KV;
 #pragma unroll
@@ -467,7 +479,78 @@ hipError_t launch_scan_k(int K, const ScanParams &p, hipStream_t s) {
     return launch_scan_t<In, Out, 64, STATES>(p, s);
 }
 
+// Carry of the exact sequence split, one workgroup per (unit, 16 value
+// columns): start(1) = b(0), start(s + 1) = M(s) start(s) + b(s).  The 16
+// columns of start(s) stay in LDS; wave w forms the row tiles 2w, 2w + 1 of the
+// next start on fp32 MFMA, with the rows of M(s) read from memory as A operands
+// (k = 16 dt + 4 g + j in instruction j, the B operand's rows in the same order).
+__global__ __launch_bounds__(NTHR) void carry_kernel(const CarryParams p) {
+    __shared__ float hs[128 * 16];
+    const int unit = blockIdx.x, c0 = blockIdx.y * 16;
+    int64_t bos, eos;
+    p.sm.bounds(unit / p.Hv, bos, eos);
+    const int N = (int)((eos - bos + CH - 1) / CH);
+    const int nseg = (N + p.seg_chunks - 1) / p.seg_chunks;
+    if (nseg < 2) return;
+    const int K = p.K, V = p.V, MT = K / 16;
+    const int w = wave_id(), n16 = ln16(), g = lg4();
+    const int64_t KV = (int64_t)K * V, KK = (int64_t)K * K, base = (int64_t)unit * p.n_seg;
+    for (int idx = threadIdx.x; idx < K * 16; idx += NTHR) {
+        const int r = idx >> 4, c = idx & 15;
+        const float v = p.b[base * KV + r * V + c0 + c];
+        hs[r * 16 + c] = v;
+        p.h0_seg[(base + 1) * KV + r * V + c0 + c] = v;
+    }
+    __syncthreads();
+    for (int s = 1; s + 1 < nseg; ++s) {
+        const float *Ms = p.M + (base + s) * KK;
+        const float *bs = p.b + (base + s) * KV;
+        f32x4 acc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int mt = 2 * w + t;
+            if (mt >= MT) break;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) acc[t][jj] = bs[(16 * mt + 4 * g + jj) * V + c0 + n16];
+            for (int dt = 0; dt < MT; ++dt) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4 *>(Ms + (16 * mt + n16) * K + 16 * dt + 4 * g);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[jj], hs[(16 * dt + 4 * g + jj) * 16 + n16],
+                                                                 acc[t], 0, 0, 0);
+            }
+        }
+        __syncthreads();  // start(s) read by every wave
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int mt = 2 * w + t;
+            if (mt >= MT) break;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = 16 * mt + 4 * g + jj;
+                hs[r * 16 + n16] = acc[t][jj];
+                p.h0_seg[(base + s + 1) * KV + r * V + c0 + n16] = acc[t][jj];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void fill_zero_kernel(uint32_t *p, size_t n) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_carry(const CarryParams &p, int n_units, hipStream_t s) {
+    hipLaunchKernelGGL(carry_kernel, dim3(n_units, p.V / 16), dim3(NTHR), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(256), 0, s, static_cast<uint32_t *>(p), bytes / 4);
+    return hipGetLastError();
+}
 
 int scan_vtile(Dt, int, int) { return BV; }
 

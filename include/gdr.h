@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 #define GDR_CHUNK 64
 #define GDR_FWD_STAGES 3
 #define GDR_BWD_STAGES 4
@@ -66,6 +66,10 @@ extern "C" {
 #define GDR_CP_AUTO 0   /* split when B*H_v <= 40, or B*H_v <= 56 and T >= 8192 */
 #define GDR_CP_OFF 1    /* exact scan, one segment per sequence */
 #define GDR_CP_WARMUP 2 /* always split; each segment warms up from a zero state */
+#define GDR_CP_EXACT 3  /* always split, exactly: each segment's transition matrix and
+                           zero-start end state are scanned in parallel, a serial carry
+                           over the segments gives their true start states, then the
+                           segments run again with output */
 
 typedef struct {
     /* sizes.  With cu_seqlens, B must be 1, T is the packed token count and
@@ -142,7 +146,10 @@ int gdr_abi_version(void);
 const char *gdr_strerror(int code);
 
 /* Workspace bytes gdr_fwd needs for these sizes and options (pointers are
-   not read).  Returns GDR_OK or a validation error. */
+   not read).  With a sequence split and cp_segment_chunks = 0 the segment
+   length, and with it the workspace of GDR_CP_EXACT, follows the compute
+   units of the current device: query with the device current that will run
+   the call.  Returns GDR_OK or a validation error. */
 int gdr_fwd_workspace(const gdr_fwd_args *args, size_t *bytes);
 
 /* Forward chunked prefill on `stream`.  Computes o (and the optional

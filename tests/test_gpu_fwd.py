@@ -98,6 +98,35 @@ def test_varlen_many_short_sequences_natural_order():
     check_all(x, run_fwd(x), ora(x, want_h=True))
 
 
+@pytest.mark.parametrize("shape,L", [
+    (dict(B=1, T=64 * 20 + 5, Hq=1, Hv=2, K=64, V=64, dtype="fp32", h0=True), 3),
+    (dict(B=2, T=64 * 9, Hq=1, Hv=2, K=128, V=64, dtype="bf16", h0=True), 2),
+    (dict(lens=[300, 1, 0, 700, 64, 129], Hq=2, Hv=4, K=64, V=128, dtype="fp32", h0=True), 3),
+    (dict(lens=[1000, 130, 5], Hq=1, Hv=1, K=128, V=128, dtype="bf16", h0=False), 4),
+])
+def test_exact_sequence_split(shape, L):
+    """Exact split: every segment's transition matrix and zero-start end state in
+    parallel, the serial carry, then the segments again from their true start
+    states: the result of the unsplit recurrence, chunk-start states included."""
+    x = make_inputs(shape, seed=8)
+    out = run_fwd(x, cp_mode="exact", cp_segment_chunks=L)
+    check_all(x, out, ora(x, want_h=True))
+
+
+def test_exact_split_where_the_warmup_fails():
+    """Gates that do not decay (g = 0 on one v head): the warm-up split is off by
+    far more than the bar, the exact split is not."""
+    x = make_inputs(dict(B=1, T=64 * 24, Hq=1, Hv=2, K=128, V=128, dtype="bf16", h0=True), seed=9)
+    x["g"][:, :, 1] = 0.0
+    ref = ora(x)
+    ex = host(run_fwd(x, cp_mode="exact", cp_segment_chunks=5)[2])
+    wu = host(run_fwd(x, cp_mode="warmup", cp_segment_chunks=5, cp_warmup_chunks=2)[2])
+    e_ex, e_wu = rel(ex, ref["o"]), rel(wu, ref["o"])
+    print("g = 0 head: exact split %.3g, warm-up split %.3g" % (e_ex, e_wu), flush=True)
+    assert e_ex <= 2e-2
+    assert e_wu > 2e-2
+
+
 def test_prefill_shard_full_size_sampled_units():
     """B=4, T=4096, H_q=16, H_v=32, K=V=128, bf16 (the timed workload), launched
     whole; the oracle runs whole (sequence, q/k head) groups."""

@@ -116,6 +116,18 @@ def test_auto_mode_splits_the_long_sequence(long_seq):
     assert e <= 2e-2
 
 
+def test_long_sequence_exact_split(long_seq):
+    """The exact split (segment transitions, serial carry, second pass) on the
+    32K-token sequence with the device's segment length: the exact result."""
+    x = long_seq
+    _, _, o, _, ht = run_fwd(x, return_h=False, cp_mode="exact")
+    o, ht = host(o), host(ht)
+    re = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"])
+    eo, eh = rel(o, re["o"]), rel(ht, re["final_state"])
+    print("exact split: o %.3g final %.3g" % (eo, eh), flush=True)
+    assert eo <= 2e-2 and eh <= 2e-2
+
+
 @pytest.mark.parametrize("scale_g", [0.03, 0.01])
 def test_weak_decay_split_diagnostic(scale_g):
     """Weak gates (g scaled down): the warm-up error becomes visible.  Reported,
