@@ -386,3 +386,25 @@ def test_p6_config_gates_make_warmup_exact_in_fp64():
     ex = run(x)
     s = split(x, 7, 8)
     assert rel(s["o"], ex["o"]) < 1e-12
+
+
+def test_p6_exact_split_carry_reproduces_the_unsplit_state():
+    """The exact sequence split rests on the recurrence being affine in its start
+    state: over a segment, start h -> M h + b with M the end state from h = I over
+    zero values (as many value columns as keys) and b the end state from zero over
+    the real values.  Chaining start(s+1) = M_s start(s) + b_s over three segments
+    from a random start must give the unsplit final state (fp64)."""
+    x = make_inputs(dict(B=1, T=64 * 3 + 21, Hq=1, Hv=2, K=8, V=5, dtype="fp32", h0=True), seed=11)
+    q, k, v, g, beta, sc = x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"]
+    K = q.shape[3]
+    bounds = [0, 64, 128 + 17, q.shape[1]]
+    h = x["initial_state"].astype(np.float64)
+    eye = np.broadcast_to(np.eye(K), (1, 2, K, K)).copy()
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        sl = lambda t: np.ascontiguousarray(t[:, a:b])
+        zero_v = np.zeros((1, b - a, 2, K))
+        M = oracle.fwd(sl(q), sl(k), zero_v, sl(g), sl(beta), sc, initial_state=eye)["final_state"]
+        off = oracle.fwd(sl(q), sl(k), sl(v), sl(g), sl(beta), sc)["final_state"]
+        h = np.einsum("nhij,nhjv->nhiv", M, h) + off
+    want = oracle.fwd(q, k, v, g, beta, sc, initial_state=x["initial_state"])["final_state"]
+    assert np.max(np.abs(h - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
