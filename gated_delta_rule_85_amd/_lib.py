@@ -10,7 +10,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 CHUNK = 64
 FWD_STAGES = 3
 BWD_STAGES = 4
@@ -44,7 +44,8 @@ class BwdArgs(ctypes.Structure):
     _fields_ = [
         ("B", _i64), ("T", _i64), ("H_q", _i64), ("H_v", _i64), ("K", _i64), ("V", _i64),
         ("n_seq", _i64),
-        ("dtype", _i32), ("grad_dtype", _i32), ("scale", ctypes.c_float),
+        ("dtype", _i32), ("grad_dtype", _i32), ("cp_mode", _i32), ("cp_segment_chunks", _i32),
+        ("scale", ctypes.c_float),
         ("q", _p), ("k", _p), ("v", _p), ("g_cum", _p), ("beta", _p), ("A", _p),
         ("dout", _p), ("dht", _p), ("initial_state", _p), ("cu_seqlens", _p),
         ("dq", _p), ("dk", _p), ("dv", _p), ("dbeta", _p), ("dg", _p), ("dh0", _p),

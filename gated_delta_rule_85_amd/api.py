@@ -114,12 +114,16 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
 
 
 def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, initial_state=None,
-                               cu_seqlens=None, *, grad_dtype=None):
+                               cu_seqlens=None, *, grad_dtype=None, cp_mode="auto", cp_segment_chunks=0):
     """Low-level backward.  ``g`` is the forward's g_cum, ``A`` its A.
     Returns ``(dq, dk, dv, db, dg, dh0)``; dh0 is None without initial_state.
     dq, dk, dv come in ``grad_dtype`` (default: the dtype of q), db, dg, dh0 in
     float32.  The gradients are accumulated in fp32; a bf16 dq/dk/dv adds one
-    rounding of up to 2^-9 |x| per element."""
+    rounding of up to 2^-9 |x| per element.  ``cp_mode``: "auto" (split the
+    recurrences of long sequences of few heads), "off" or "exact"; the split is
+    always exact here."""
+    if cp_mode not in ("auto", "off", "exact"):
+        raise ValueError("cp_mode of the backward: 'auto', 'off' or 'exact'")
     _check(q, k, v, g, beta, cu_seqlens)
     q, k, v, do = _c(q), _c(k), _c(v), _c(do, q.dtype)
     g, beta, A = _c(g, torch.float32), _c(beta, torch.float32), _c(A, torch.float32)
@@ -143,6 +147,8 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
     a.B, a.T, a.H_q, a.H_v, a.K, a.V, a.n_seq = B, T, Hq, Hv, K, V, n_seq
     a.dtype = _DT[q.dtype]
     a.grad_dtype = _DT[gdt]
+    a.cp_mode = _CP[cp_mode]
+    a.cp_segment_chunks = int(cp_segment_chunks)
     a.scale = float(scale)
     a.q, a.k, a.v, a.g_cum, a.beta, a.A = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A)
     a.dout, a.dht, a.initial_state, a.cu_seqlens = _ptr(do), _ptr(dht), _ptr(h0), _ptr(cu)

@@ -50,11 +50,11 @@ int check_dims(int64_t B, int64_t T, int64_t Hq, int64_t Hv, int64_t K, int64_t 
 // scan runs one workgroup per compute unit, so a launch of W workgroups per
 // segment index takes ceil(W S / slots) rounds, each as long as the longest
 // segment plus its warm-up window: choose the segment count S that minimises
-// rounds x (L + warm-up), L = ceil(N / S) (ties: fewer segments).  Returns
-// N + 1 (no split) when one segment is best.
-int64_t split_chunks(int64_t N, int64_t W, int64_t slots, int64_t wm) {
+// rounds x (L + warm-up), L = ceil(N / S) (ties: fewer segments), S >= min_seg.
+// Returns N + 1 (no split) when one segment is best.
+int64_t split_chunks(int64_t N, int64_t W, int64_t slots, int64_t wm, int64_t min_seg) {
     int64_t best_t = -1, best_L = N + 1;
-    for (int64_t S = 1; S <= N; ++S) {
+    for (int64_t S = min_seg; S <= N; ++S) {
         const int64_t L = cdiv(N, S), Sx = cdiv(N, L);
         if (Sx != S) continue;  // same L as a smaller S
         const int64_t t = cdiv(W * S, slots) * (L + (S > 1 ? wm : 0));
@@ -66,8 +66,10 @@ int64_t split_chunks(int64_t N, int64_t W, int64_t slots, int64_t wm) {
     return best_L;
 }
 
-// slots: workgroups the device runs at once (its compute units); 0 = unknown,
-// when the segment length is not needed (workspace sizing)
+// Compute units assumed when no device can be queried (an MI355X has 256).
+constexpr int64_t DEFAULT_SLOTS = 256;
+
+// slots: workgroups the device runs at once (its compute units); 0 = unknown
 int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     if (!a) return GDR_EINVAL;
     const bool varlen = a->cu_seqlens != nullptr;
@@ -92,9 +94,10 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
                  (a->cp_mode == GDR_CP_AUTO && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
     pl.warm_chunks = a->cp_warmup_chunks > 0 ? a->cp_warmup_chunks : 8;
     const int64_t n_vt = a->V / scan_vtile(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32, (int)a->K, (int)a->V);
-    int64_t L = a->cp_segment_chunks > 0 ? a->cp_segment_chunks
-                : slots > 0 ? split_chunks(pl.nct, bh * n_vt, slots, pl.warm_chunks)
-                            : (int64_t)ceil(sqrt((double)(pl.nct > 0 ? pl.nct : 1)));
+    int64_t L = a->cp_segment_chunks > 0
+                    ? a->cp_segment_chunks
+                    : split_chunks(pl.nct, bh * n_vt, slots > 0 ? slots : DEFAULT_SLOTS, pl.warm_chunks,
+                                   a->cp_mode == GDR_CP_AUTO ? 1 : 2);
     if (L < 1) L = 1;
     if (!split || L >= pl.nct) {
         split = false;
@@ -127,15 +130,22 @@ int64_t device_slots(int dev) {
 struct BwdPlan {
     int64_t n_seq, tokens, nct, nt_ub;
     size_t off_chunk, off_tblk, off_hs, off_dhs, total;
+    // exact split: transitions, zero-start end states, true start states, zero-end
+    // start gradients, true end gradients, a zero row
+    size_t off_M, off_b, off_hseg, off_d, off_gseg, off_zero;
+    int seg_chunks, n_seg;
+    bool split;
 };
 
 // workspace: [chunk offsets] | T blocks | chunk-start states | chunk-end state gradients
-int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl) {
+int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl, int64_t slots = 0) {
     if (!a) return GDR_EINVAL;
     const bool varlen = a->cu_seqlens != nullptr;
     int rc = check_dims(a->B, a->T, a->H_q, a->H_v, a->K, a->V, a->n_seq, varlen, a->dtype);
     if (rc) return rc;
     if (a->grad_dtype != GDR_BF16 && a->grad_dtype != GDR_F32) return GDR_ENOTSUP;
+    if (a->cp_mode != GDR_CP_AUTO && a->cp_mode != GDR_CP_OFF && a->cp_mode != GDR_CP_EXACT) return GDR_EINVAL;
+    if (a->cp_segment_chunks < 0) return GDR_EINVAL;
     pl.n_seq = varlen ? a->n_seq : a->B;
     pl.tokens = a->B * a->T;
     pl.nct = cdiv(a->T, GDR_CHUNK);
@@ -151,6 +161,34 @@ int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl) {
     pl.off_dhs = off;
     off += up(sizeof(float) * nb * (size_t)(a->K * a->V));
     pl.total = pl.tokens > 0 ? off : pl.off_tblk;
+    // exact sequence split of the state scan and the reverse scan: the forward's trigger
+    // and segment length
+    const int64_t bh = pl.n_seq * a->H_v;
+    bool split = a->cp_mode == GDR_CP_EXACT ||
+                 (a->cp_mode == GDR_CP_AUTO && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
+    const int64_t n_vt = a->V / 64;
+    int64_t L = a->cp_segment_chunks > 0 ? a->cp_segment_chunks
+                                          : split_chunks(pl.nct, bh * n_vt, slots > 0 ? slots : DEFAULT_SLOTS, 8,
+                                                         a->cp_mode == GDR_CP_AUTO ? 1 : 2);
+    if (L < 1) L = 1;
+    if (!split || L >= pl.nct || pl.tokens == 0) {
+        split = false;
+        L = pl.nct + 1;
+    }
+    pl.split = split;
+    pl.seg_chunks = (int)L;
+    pl.n_seg = split ? (int)cdiv(pl.nct, L) : 1;
+    pl.off_M = pl.off_b = pl.off_hseg = pl.off_d = pl.off_gseg = pl.off_zero = 0;
+    if (split) {
+        const size_t per = (size_t)bh * pl.n_seg * (size_t)a->K * sizeof(float);
+        pl.off_M = pl.total;
+        pl.off_b = pl.off_M + up(per * (size_t)a->K);
+        pl.off_hseg = pl.off_b + up(per * (size_t)a->V);
+        pl.off_d = pl.off_hseg + up(per * (size_t)a->V);
+        pl.off_gseg = pl.off_d + up(per * (size_t)a->V);
+        pl.off_zero = pl.off_gseg + up(per * (size_t)a->V);
+        pl.total = pl.off_zero + up(512);
+    }
     return GDR_OK;
 }
 
@@ -185,7 +223,7 @@ const char *gdr_strerror(int code) {
 int gdr_fwd_workspace(const gdr_fwd_args *a, size_t *bytes) {
     if (!bytes) return GDR_EINVAL;
     // the split's segment length, and with it the exact split's workspace, follows
-    // the compute units of the current device (without one: ceil(sqrt(chunks)))
+    // the compute units of the current device (without one: 256)
     int dev = 0;
     const int64_t slots = hipGetDevice(&dev) == hipSuccess ? device_slots(dev) : 0;
     FwdPlan pl;
@@ -305,6 +343,7 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
         cp.V = (int)a->V;
         cp.seg_chunks = pl.seg_chunks;
         cp.n_seg = pl.n_seg;
+        cp.rev = 0;
         if (launch_carry(cp, (int)(pl.n_seq * a->H_v), stream) != hipSuccess) return GDR_ELAUNCH;
         sp.h0_seg = hseg;
     }
@@ -332,16 +371,20 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
 
 int gdr_bwd_workspace(const gdr_bwd_args *a, size_t *bytes) {
     if (!bytes) return GDR_EINVAL;
+    int dev = 0;
+    const int64_t slots = hipGetDevice(&dev) == hipSuccess ? device_slots(dev) : 0;
     BwdPlan pl;
-    int rc = plan_bwd(a, pl);
+    int rc = plan_bwd(a, pl, slots);
     if (rc) return rc;
     *bytes = pl.total;
     return GDR_OK;
 }
 
 int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
+    int dev = 0;
+    const int64_t slots = hipStreamGetDevice(stream, &dev) == hipSuccess ? device_slots(dev) : 0;
     BwdPlan pl;
-    int rc = plan_bwd(a, pl);
+    int rc = plan_bwd(a, pl, slots);
     if (rc) return rc;
     if (pl.tokens > 0) {
         if (!a->q || !a->k || !a->v || !a->g_cum || !a->beta || !a->A || !a->dout || !a->dq || !a->dk ||
@@ -357,6 +400,7 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
         return GDR_EINVAL;
     if (a->workspace_bytes < pl.total || (pl.total > 0 && !a->workspace)) return GDR_EWORKSPACE;
     if (pl.total > 0 && !aligned(a->workspace, 16)) return GDR_EINVAL;
+    if (slots == 0) return GDR_ELAUNCH;
 
     char *ws = static_cast<char *>(a->workspace);
     int32_t *chunk_off = a->cu_seqlens ? reinterpret_cast<int32_t *>(ws + pl.off_chunk) : nullptr;
@@ -393,6 +437,10 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
     bp.Hv = (int)a->H_v;
     bp.V = (int)a->V;
     bp.scale = a->scale;
+    bp.seg_chunks = pl.seg_chunks;
+    bp.n_seg = pl.n_seg;
+    bp.dh_seg = nullptr;
+    bp.d_seg = nullptr;
 
     auto mark = [&](int i) {
         return !a->events || !a->events[i] || hipEventRecord(a->events[i], stream) == hipSuccess;
@@ -425,14 +473,68 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
         sp.Hv = (int)a->H_v;
         sp.V = (int)a->V;
         sp.scale = a->scale;
-        sp.seg_chunks = (int)pl.nct + 1;
+        sp.seg_chunks = pl.seg_chunks;
         sp.warm_chunks = 0;
         sp.n_vt = (int)(a->V / scan_vtile(dt, (int)a->K, (int)a->V));
         sp.n_units = n_units;
-        sp.n_seg = 1;
+        sp.n_seg = pl.n_seg;
+        if (pl.split) {
+            // the forward's exact split on the rebuilt T blocks: segment transitions from
+            // the identity over a zero row, zero-start end states, the carry; the states
+            // pass below then starts every segment from its true state
+            if (launch_fill_zero(ws + pl.off_zero, 512, stream) != hipSuccess) return GDR_ELAUNCH;
+            ScanParams tp = sp;
+            tp.v = ws + pl.off_zero;
+            tp.v_tok = tp.v_head = 0;
+            tp.V = (int)a->K;
+            tp.n_vt = (int)(a->K / scan_vtile(dt, (int)a->K, (int)a->K));
+            tp.eye_h0 = 1;
+            tp.h0 = nullptr;
+            tp.hsnap = nullptr;
+            tp.hT_seg = reinterpret_cast<float *>(ws + pl.off_M);
+            if (launch_scan_states(dt, (int)a->K, tp, stream) != hipSuccess) return GDR_ELAUNCH;
+            ScanParams zp = sp;
+            zp.hsnap = nullptr;
+            zp.hT_seg = reinterpret_cast<float *>(ws + pl.off_b);
+            if (launch_scan_states(dt, (int)a->K, zp, stream) != hipSuccess) return GDR_ELAUNCH;
+            CarryParams cp;
+            cp.M = reinterpret_cast<float *>(ws + pl.off_M);
+            cp.b = reinterpret_cast<float *>(ws + pl.off_b);
+            cp.h0_seg = reinterpret_cast<float *>(ws + pl.off_hseg);
+            cp.sm = sm;
+            cp.Hv = (int)a->H_v;
+            cp.K = (int)a->K;
+            cp.V = (int)a->V;
+            cp.seg_chunks = pl.seg_chunks;
+            cp.n_seg = pl.n_seg;
+            cp.rev = 0;
+            if (launch_carry(cp, n_units, stream) != hipSuccess) return GDR_ELAUNCH;
+            sp.h0_seg = cp.h0_seg;
+        }
         if (launch_scan_states(dt, (int)a->K, sp, stream) != hipSuccess) return GDR_ELAUNCH;
     }
     if (!mark(3) || !mark(4)) return GDR_ELAUNCH;
+    if (pl.split) {
+        // reverse scan: every segment's start gradient from a zero end gradient (the last
+        // segment from dht), the reverse carry with the transposed transitions, then the
+        // scan below from every segment's true end gradient
+        BwdParams dp = bp;
+        dp.d_seg = reinterpret_cast<float *>(ws + pl.off_d);
+        if (launch_bwd_reverse(dt, (int)a->K, dp, n_units, stream) != hipSuccess) return GDR_ELAUNCH;
+        CarryParams cp;
+        cp.M = reinterpret_cast<float *>(ws + pl.off_M);
+        cp.b = dp.d_seg;
+        cp.h0_seg = reinterpret_cast<float *>(ws + pl.off_gseg);
+        cp.sm = sm;
+        cp.Hv = (int)a->H_v;
+        cp.K = (int)a->K;
+        cp.V = (int)a->V;
+        cp.seg_chunks = pl.seg_chunks;
+        cp.n_seg = pl.n_seg;
+        cp.rev = 1;
+        if (launch_carry(cp, n_units, stream) != hipSuccess) return GDR_ELAUNCH;
+        bp.dh_seg = cp.h0_seg;
+    }
     const Dt gt = a->grad_dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
     const hipEvent_t *ev = a->events ? a->events + 5 : nullptr;  // reverse scan end, local start/end
     if (launch_bwd(dt, gt, (int)a->K, bp, pl.tokens > 0 ? (int)pl.nt_ub : 0, n_units, ev, stream) != hipSuccess)

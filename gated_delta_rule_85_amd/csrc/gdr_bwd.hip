@@ -162,14 +162,15 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_kernel(const BwdParams p, int n
     __shared__ float gam[CH], eg[CH], rr[CH], bet[CH];
 
     const int nvt = p.V / 64;
-    int vt, unit;
-    if (p.sm.order) {  // packed sequences: longest first
+    int vt, unit, seg = 0;
+    if (p.sm.order && p.n_seg == 1) {  // packed sequences: longest first
         if (!lpt_item(p.sm, p.Hq, p.Hv, nvt, vt, unit)) return;
     } else {
         const int wid = xcd_remap(blockIdx.x, gridDim.x);
         vt = wid % nvt;
-        unit = wid / nvt;
-        if (unit >= n_units) return;
+        unit = (wid / nvt) % n_units;
+        seg = wid / nvt / n_units;
+        if (seg >= p.n_seg) return;
     }
     const int j = unit / p.Hv, hv = unit % p.Hv, hq = hv / (p.Hv / p.Hq);
     const int w = wave_id(), nn = ln16(), g = lg4();
@@ -177,8 +178,15 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_kernel(const BwdParams p, int n
     int64_t bos, eos;
     p.sm.bounds(j, bos, eos);
     const int N = (int)((eos - bos + CH - 1) / CH);
+    // this workgroup's segment of chunks (the whole sequence without a split)
+    const int c_begin = seg * p.seg_chunks;
+    if (c_begin >= N && !(N == 0 && seg == 0)) return;
+    const int c_end = min(N, c_begin + p.seg_chunks);
     const int cb = p.sm.chunk_base(j);
     const int64_t KV = (int64_t)KD * p.V;
+    const float *dh_start = c_end == N ? (p.dht ? p.dht + unit * KV : nullptr)
+                            : p.d_seg ? nullptr
+                                      : p.dh_seg + ((int64_t)unit * p.n_seg + seg) * KV;
     const In *qp = reinterpret_cast<const In *>(p.q), *kp = reinterpret_cast<const In *>(p.k);
     const In *dop = reinterpret_cast<const In *>(p.dout);
 
@@ -187,9 +195,9 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_kernel(const BwdParams p, int n
     for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            dh[kb][i] = p.dht ? p.dht[unit * KV + (16 * kb + 4 * g + i) * p.V + col] : 0.f;
+            dh[kb][i] = dh_start ? dh_start[(16 * kb + 4 * g + i) * p.V + col] : 0.f;
 
-    for (int c = N - 1; c >= 0; --c) {
+    for (int c = c_end - 1; c >= c_begin; --c) {
         const int64_t ts = bos + (int64_t)c * CH;
         const int n = (int)min<int64_t>(CH, eos - ts);
         __syncthreads();  // previous chunk done with the LDS tiles
@@ -205,7 +213,7 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_kernel(const BwdParams p, int n
         }
         load_T(p, ts, n, hv, Tf);
         load_gates(p, ts, n, hv, gam, eg, rr, bet);
-        {  // gradient of this chunk's end state, for the chunk-local stage
+        if (!p.d_seg) {  // gradient of this chunk's end state, for the chunk-local stage
             float *o = p.dhs + ((int64_t)(cb + c) * p.Hv + hv) * KV;
 #pragma unroll
             for (int kb = 0; kb < NK; ++kb)
@@ -256,11 +264,13 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_kernel(const BwdParams p, int n
             dh[kb] = tile_rb(nd, ColI<In>{Ks, LK}, 16 * kb, bedx);
         }
     }
-    if (p.dh0) {
+    float *dh_out = p.d_seg ? p.d_seg + ((int64_t)unit * p.n_seg + seg) * KV
+                    : c_begin == 0 && p.dh0 ? p.dh0 + unit * KV : nullptr;
+    if (dh_out) {
 #pragma unroll
         for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p.dh0[unit * KV + (16 * kb + 4 * g + i) * p.V + col] = dh[kb][i];
+            for (int i = 0; i < 4; ++i) dh_out[(16 * kb + 4 * g + i) * p.V + col] = dh[kb][i];
     }
 }
 
@@ -546,7 +556,8 @@ hipError_t launch_bwd_t(const BwdParams &p, int n_chunks_ub, int n_units, const 
         e = launch_bwd_scan_bf16(KD, p, n_units, s);
     } else {
         hipLaunchKernelGGL((bwd_scan_kernel<In, KD>),
-                           dim3(p.sm.order ? lpt_blocks(p.sm.n_seq, p.Hq, p.Hv, p.V / 64) : n_units * (p.V / 64)),
+                           dim3(p.sm.order && p.n_seg == 1 ? lpt_blocks(p.sm.n_seq, p.Hq, p.Hv, p.V / 64)
+                                                           : n_units * (p.V / 64) * p.n_seg),
                            dim3(NTHR), 0, s, p, n_units);
         e = hipGetLastError();
     }
@@ -581,6 +592,17 @@ hipError_t launch_tblocks(Dt dt, const BwdParams &p, int n_chunks_ub, hipStream_
         hipLaunchKernelGGL(tblock_kernel<bf16>, grid, dim3(NTHR), 0, s, p);
     else
         hipLaunchKernelGGL(tblock_kernel<float>, grid, dim3(NTHR), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_reverse(Dt dt, int K, const BwdParams &p, int n_units, hipStream_t s) {
+    if (dt == Dt::BF16) return launch_bwd_scan_bf16(K, p, n_units, s);
+    const dim3 grid(p.sm.order && p.n_seg == 1 ? lpt_blocks(p.sm.n_seq, p.Hq, p.Hv, p.V / 64)
+                                               : n_units * (p.V / 64) * p.n_seg);
+    if (K == 128)
+        hipLaunchKernelGGL((bwd_scan_kernel<float, 128>), grid, dim3(NTHR), 0, s, p, n_units);
+    else
+        hipLaunchKernelGGL((bwd_scan_kernel<float, 64>), grid, dim3(NTHR), 0, s, p, n_units);
     return hipGetLastError();
 }
 

@@ -46,14 +46,15 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
     __shared__ __attribute__((aligned(16))) char Pt[2 * PPLANE];
 
     const int nvt = p.V / 64;
-    int vt, unit;
-    if (p.sm.order) {  // packed sequences: longest first
+    int vt, unit, seg = 0;
+    if (p.sm.order && p.n_seg == 1) {  // packed sequences: longest first
         if (!lpt_item(p.sm, p.Hq, p.Hv, nvt, vt, unit)) return;
     } else {
         const int wid = xcd_remap(blockIdx.x, gridDim.x);
         vt = wid % nvt;
-        unit = wid / nvt;
-        if (unit >= n_units) return;
+        unit = (wid / nvt) % n_units;
+        seg = wid / nvt / n_units;
+        if (seg >= p.n_seg) return;
     }
     const int j = unit / p.Hv, hv = unit % p.Hv, hq = hv / (p.Hv / p.Hq);
     const int w = __builtin_amdgcn_readfirstlane(wave_id()), n16 = ln16(), g = lg4();
@@ -61,6 +62,13 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
     int64_t bos, eos;
     p.sm.bounds(j, bos, eos);
     const int N = (int)((eos - bos + CH - 1) / CH);
+    // this workgroup's segment of chunks (the whole sequence without a split)
+    const int c_begin = seg * p.seg_chunks;
+    if (c_begin >= N && !(N == 0 && seg == 0)) return;
+    const int c_end = min(N, c_begin + p.seg_chunks);
+    const float *dh_start = c_end == N ? (p.dht ? p.dht + unit * ((int64_t)KD * p.V) : nullptr)
+                            : p.d_seg ? nullptr
+                                      : p.dh_seg + ((int64_t)unit * p.n_seg + seg) * ((int64_t)KD * p.V);
     const int cb = p.sm.chunk_base(j);
     const int64_t KV = (int64_t)KD * p.V;
     const char *kp = reinterpret_cast<const char *>(p.k), *qp = reinterpret_cast<const char *>(p.q);
@@ -74,10 +82,10 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            dh[dt][i] = p.dht ? p.dht[unit * KV + (slot_base(dt, g) + i) * p.V + col] : 0.f;
+            dh[dt][i] = dh_start ? dh_start[(slot_base(dt, g) + i) * p.V + col] : 0.f;
     zero_lower_pt(Pt);
 
-    for (int c = N - 1; c >= 0; --c) {
+    for (int c = c_end - 1; c >= c_begin; --c) {
         const int64_t ts = bos + (int64_t)c * CH;
         const int n = (int)min<int64_t>(CH, eos - ts);
         __syncthreads();  // the previous chunk is done with every tile
@@ -85,7 +93,7 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
         copy_tile<KROW>(Qs, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
         copy_tile<DROW>(Ds, dop + ((ts * p.Hv + hv) * p.V + vt * 64) * 2, p.Hv * p.V * 2, n - 1, w);
         copy_flat(Tb, p.tblk + ((int64_t)(cb + c) * p.Hv + hv) * TB::BYTES, TB::BYTES, w);
-        {  // gradient of this chunk's end state, for the chunk-local stage: hi, lo planes of dh'^T
+        if (!p.d_seg) {  // gradient of this chunk's end state, for the chunk-local stage: hi, lo planes of dh'^T
             char *o = reinterpret_cast<char *>(p.dhs + ((int64_t)(cb + c) * p.Hv + hv) * KV);
             const int plane = KD * p.V * 2;
 #pragma unroll
@@ -164,11 +172,13 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
             }
         }
     }
-    if (p.dh0) {
+    float *dh_out = p.d_seg ? p.d_seg + ((int64_t)unit * p.n_seg + seg) * KV
+                    : c_begin == 0 && p.dh0 ? p.dh0 + unit * KV : nullptr;
+    if (dh_out) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p.dh0[unit * KV + (slot_base(dt, g) + i) * p.V + col] = dh[dt][i];
+            for (int i = 0; i < 4; ++i) dh_out[(slot_base(dt, g) + i) * p.V + col] = dh[dt][i];
     }
 }
 
@@ -176,7 +186,8 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
 }  // namespace
 
 hipError_t launch_bwd_scan_bf16(int K, const BwdParams &p, int n_units, hipStream_t s) {
-    const dim3 grid(p.sm.order ? lpt_blocks(p.sm.n_seq, p.Hq, p.Hv, p.V / 64) : n_units * (p.V / 64));
+    const dim3 grid(p.sm.order && p.n_seg == 1 ? lpt_blocks(p.sm.n_seq, p.Hq, p.Hv, p.V / 64)
+                                               : n_units * (p.V / 64) * p.n_seg);
     if (K == 128)
         hipLaunchKernelGGL((bwd_scan_bf16<128>), grid, dim3(NTHR), 0, s, p, n_units);
     else

@@ -52,12 +52,16 @@ struct ScanParams {
 
 // carry of the exact sequence split: for segments s = 1 .. of each unit,
 // start(s) = M(s-1) start(s-1) + b(s-1), start(1) = b(0), written to h0_seg
+// With rev (the backward's reverse scan): for s = n-2 down to 0,
+// end(s) = M(s+1)^T end(s+1) + b(s+1), end(n-2) = b(n-1), written to h0_seg[s]
+// (b: each segment's start gradient from a zero end gradient, the last from dht).
 struct CarryParams {
     const float *M;    // [n_units][n_seg][K][K] segment transitions
     const float *b;    // [n_units][n_seg][K][V] segment end states from a zero start (s = 0: from h0)
     float *h0_seg;     // [n_units][n_seg][K][V]
     SeqMap sm;
     int Hv, K, V, seg_chunks, n_seg;
+    int rev;
 };
 
 // optional materialisation of W = T diag(beta e^gam) K and U = T diag(beta) V
@@ -85,6 +89,13 @@ struct BwdParams {
     SeqMap sm;
     int Hq, Hv, V;
     float scale;
+    // exact sequence split of the reverse scan: segments of seg_chunks chunks (n_seg = 1:
+    // none).  A segment other than the last starts from dh_seg (its end gradient) or,
+    // with d_seg set, from zero, and then writes its start gradient to d_seg and no
+    // chunk-end gradients.  [n_units][n_seg][K][V]
+    int seg_chunks, n_seg;
+    const float *dh_seg;
+    float *d_seg;
 };
 
 // chunk offsets of packed sequences and (order non-null) their longest-first order
@@ -96,6 +107,8 @@ hipError_t launch_scan_states(Dt dt, int K, const ScanParams &p, hipStream_t s);
 hipError_t launch_carry(const CarryParams &p, int n_units, hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_tblocks(Dt dt, const BwdParams &p, int n_chunks_ub, hipStream_t s);
+// the reverse scan alone (the exact split's pass from zero end gradients)
+hipError_t launch_bwd_reverse(Dt dt, int K, const BwdParams &p, int n_units, hipStream_t s);
 // ev: null or 3 events: after the reverse scan, before and after the local stage
 hipError_t launch_bwd(Dt dt, Dt gt, int K, const BwdParams &p, int n_chunks_ub, int n_units,
                       const hipEvent_t *ev, hipStream_t s);

@@ -484,6 +484,7 @@ hipError_t launch_scan_k(int K, const ScanParams &p, hipStream_t s) {
 // columns of start(s) stay in LDS; wave w forms the row tiles 2w, 2w + 1 of the
 // next start on fp32 MFMA, with the rows of M(s) read from memory as A operands
 // (k = 16 dt + 4 g + j in instruction j, the B operand's rows in the same order).
+// The reverse carry (rev) runs the segments backwards with M(s)^T.
 __global__ __launch_bounds__(NTHR) void carry_kernel(const CarryParams p) {
     __shared__ float hs[128 * 16];
     const int unit = blockIdx.x, c0 = blockIdx.y * 16;
@@ -495,14 +496,17 @@ __global__ __launch_bounds__(NTHR) void carry_kernel(const CarryParams p) {
     const int K = p.K, V = p.V, MT = K / 16;
     const int w = wave_id(), n16 = ln16(), g = lg4();
     const int64_t KV = (int64_t)K * V, KK = (int64_t)K * K, base = (int64_t)unit * p.n_seg;
+    // first carried segment: forward start(1) = b(0); reverse end(n-2) = b(n-1)
+    const int first_src = p.rev ? nseg - 1 : 0, first_dst = p.rev ? nseg - 2 : 1;
     for (int idx = threadIdx.x; idx < K * 16; idx += NTHR) {
         const int r = idx >> 4, c = idx & 15;
-        const float v = p.b[base * KV + r * V + c0 + c];
+        const float v = p.b[(base + first_src) * KV + r * V + c0 + c];
         hs[r * 16 + c] = v;
-        p.h0_seg[(base + 1) * KV + r * V + c0 + c] = v;
+        p.h0_seg[(base + first_dst) * KV + r * V + c0 + c] = v;
     }
     __syncthreads();
-    for (int s = 1; s + 1 < nseg; ++s) {
+    for (int step = 1; step + 1 < nseg; ++step) {
+        const int s = p.rev ? nseg - 1 - step : step, dst = p.rev ? s - 1 : s + 1;
         const float *Ms = p.M + (base + s) * KK;
         const float *bs = p.b + (base + s) * KV;
         f32x4 acc[2];
@@ -513,7 +517,13 @@ __global__ __launch_bounds__(NTHR) void carry_kernel(const CarryParams p) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) acc[t][jj] = bs[(16 * mt + 4 * g + jj) * V + c0 + n16];
             for (int dt = 0; dt < MT; ++dt) {
-                const f32x4 a4 = *reinterpret_cast<const f32x4 *>(Ms + (16 * mt + n16) * K + 16 * dt + 4 * g);
+                f32x4 a4;
+                if (p.rev) {  // rows of M^T: columns of M
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) a4[jj] = Ms[(16 * dt + 4 * g + jj) * K + 16 * mt + n16];
+                } else {
+                    a4 = *reinterpret_cast<const f32x4 *>(Ms + (16 * mt + n16) * K + 16 * dt + 4 * g);
+                }
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[jj], hs[(16 * dt + 4 * g + jj) * 16 + n16],
@@ -529,7 +539,7 @@ __global__ __launch_bounds__(NTHR) void carry_kernel(const CarryParams p) {
             for (int jj = 0; jj < 4; ++jj) {
                 const int r = 16 * mt + 4 * g + jj;
                 hs[r * 16 + n16] = acc[t][jj];
-                p.h0_seg[(base + s + 1) * KV + r * V + c0 + n16] = acc[t][jj];
+                p.h0_seg[(base + dst) * KV + r * V + c0 + n16] = acc[t][jj];
             }
         }
         __syncthreads();

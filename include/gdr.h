@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 2
+#define GDR_ABI_VERSION 3
 #define GDR_CHUNK 64
 #define GDR_FWD_STAGES 3
 #define GDR_BWD_STAGES 4
@@ -115,6 +115,10 @@ typedef struct {
     int64_t B, T, H_q, H_v, K, V, n_seq;
     int32_t dtype;      /* element type of q, k, v, do */
     int32_t grad_dtype; /* element type of dq, dk, dv: GDR_BF16 or GDR_F32 */
+    int32_t cp_mode;    /* sequence split of the recurrences: GDR_CP_AUTO (the forward's
+                           trigger), GDR_CP_OFF or GDR_CP_EXACT; the backward has no
+                           warm-up form (GDR_CP_WARMUP is an invalid argument) */
+    int32_t cp_segment_chunks; /* chunks per segment; 0 = chosen for the device as in gdr_fwd */
     float scale;
     const void *q, *k, *v;      /* as in gdr_fwd_args */
     const float *g_cum;         /* [B,T,H_v] the forward's g_cum */
@@ -148,8 +152,9 @@ const char *gdr_strerror(int code);
 /* Workspace bytes gdr_fwd needs for these sizes and options (pointers are
    not read).  With a sequence split and cp_segment_chunks = 0 the segment
    length, and with it the workspace of GDR_CP_EXACT, follows the compute
-   units of the current device: query with the device current that will run
-   the call.  Returns GDR_OK or a validation error. */
+   units of the current device (256 if none can be queried): query with the
+   device current that will run the call.  Returns GDR_OK or a validation
+   error. */
 int gdr_fwd_workspace(const gdr_fwd_args *args, size_t *bytes);
 
 /* Forward chunked prefill on `stream`.  Computes o (and the optional

@@ -147,12 +147,21 @@ def test_bwd_workspace_sizes(L):
     assert L.bwd_workspace(bwd_args(L)) == 4 * 4 * per
     assert L.bwd_workspace(bwd_args(L, cu_seqlens=16, n_seq=3)) == 256 + (4 + 3) * 4 * per
     assert L.bwd_workspace(bwd_args(L, T=0)) == 0
+    # exact sequence split forced: the device model (256 compute units without a device,
+    # 8 workgroups per segment index, 8-chunk overhead) puts the 4 chunks in 4 segments;
+    # per (sequence, v head, segment) a K x K transition and four K x V states, and a
+    # zero row
+    seg = 4 * 4 * 128 * 4
+    split = 4 * 4 * per + seg * 128 + 4 * seg * 128 + 512
+    assert L.bwd_workspace(bwd_args(L, cp_mode=L.CP_EXACT)) == split
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(H_v=3), -1), (dict(K=96), -2), (dict(dtype=7), -2), (dict(grad_dtype=9), -2),
     (dict(B=0), -1),
     (dict(cu_seqlens=16, n_seq=2, B=2), -1),
+    (dict(cp_mode=2), -1),                  # no warm-up split in the backward
+    (dict(cp_segment_chunks=-3), -1),
 ])
 def test_bwd_validation_errors(L, kw, code):
     n = ctypes.c_size_t(0)

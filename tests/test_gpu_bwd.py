@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 NAMES = ("dq", "dk", "dv", "dbeta", "dg", "dh0")
 
 
-def run_bwd(x, with_dht=True, grad_dtype=torch.float32):
+def run_bwd(x, with_dht=True, grad_dtype=torch.float32, **kw):
     from gated_delta_rule_85_amd import chunk_gated_delta_rule_bwd, chunk_gated_delta_rule_fwd
     d = gpu_inputs(x)
     dt = d["q"].dtype
@@ -36,7 +36,7 @@ def run_bwd(x, with_dht=True, grad_dtype=torch.float32):
     dht = dev(x["dht"]) if with_dht else None
     out = chunk_gated_delta_rule_bwd(d["q"], d["k"], d["v"], g_cum, d["beta"], A, do, dht,
                                      x["scale"], d["initial_state"], d["cu_seqlens"],
-                                     grad_dtype=grad_dtype)
+                                     grad_dtype=grad_dtype, **kw)
     torch.cuda.synchronize()
     return dict(zip(NAMES, out))
 
@@ -73,6 +73,41 @@ def test_small_ragged(shape):
     x = make_inputs(shape, seed=2, grads=True)
     print(shape, flush=True)
     compare(x, run_bwd(x), ora_bwd(x))
+
+
+@pytest.mark.parametrize("shape,L", [
+    (dict(B=1, T=64 * 9 + 30, Hq=1, Hv=2, K=64, V=64, dtype="fp32", h0=True), 2),
+    (dict(B=2, T=64 * 7, Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True), 3),
+    (dict(B=1, T=64 * 5 + 1, Hq=1, Hv=1, K=128, V=64, dtype="fp32", h0=False), 1),
+    (dict(lens=[400, 0, 65, 300, 1], Hq=1, Hv=2, K=64, V=128, dtype="fp32", h0=True), 2),
+])
+def test_exact_split_backward(shape, L):
+    """The backward's exact sequence split: the forward's split for the chunk-start
+    states, and for the reverse scan each segment's start gradient from a zero end
+    gradient, the carry with the transposed transitions, the scan from the true end
+    gradients.  Every element of every gradient against the unsplit oracle."""
+    x = make_inputs(shape, seed=12, grads=True)
+    print(shape, "segments of", L, flush=True)
+    compare(x, run_bwd(x, cp_mode="exact", cp_segment_chunks=L), ora_bwd(x))
+
+
+def test_exact_split_backward_non_decaying_head():
+    x = make_inputs(dict(B=1, T=64 * 12, Hq=1, Hv=2, K=128, V=128, dtype="fp32", h0=True), seed=13,
+                    grads=True)
+    x["g"][:, :, 0] = 0.0
+    compare(x, run_bwd(x, cp_mode="exact", cp_segment_chunks=3), ora_bwd(x))
+
+
+def test_small_head_long_sequence_backward_auto_split():
+    """B=1, T=8192, H_q=2, H_v=4, bf16: B*H_v = 4 triggers the split; the auto
+    backward (split) and the unsplit one both match the oracle."""
+    x = make_inputs(dict(B=1, T=8192, Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True), seed=14,
+                    grads=True)
+    ref = ora_bwd(x)
+    for mode in ("auto", "off"):
+        print(mode, flush=True)
+        got = run_bwd(x, cp_mode=mode)
+        compare(x, got, ref)
 
 
 def check_rounded(got, ref, names=("dq", "dk", "dv")):
