@@ -17,7 +17,7 @@ BWD_STAGES = 4
 
 OK, EINVAL, ENOTSUP, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
-CP_AUTO, CP_OFF, CP_WARMUP, CP_EXACT = 0, 1, 2, 3
+CP_AUTO, CP_OFF, CP_WARMUP, CP_EXACT, CP_AUTO_EXACT = 0, 1, 2, 3, 4
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64

@@ -16,7 +16,8 @@ import torch
 from . import _lib
 
 _DT = {torch.bfloat16: _lib.BF16, torch.float32: _lib.F32}
-_CP = {"auto": _lib.CP_AUTO, "off": _lib.CP_OFF, "warmup": _lib.CP_WARMUP, "exact": _lib.CP_EXACT}
+_CP = {"auto": _lib.CP_AUTO, "off": _lib.CP_OFF, "warmup": _lib.CP_WARMUP, "exact": _lib.CP_EXACT,
+       "auto_exact": _lib.CP_AUTO_EXACT}
 
 
 def _ptr(t):
@@ -64,8 +65,9 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     h [1,NT,H_v,K,V] fp32 the chunk-start states (None unless return_h);
     final_state [N,H_v,K,V] fp32 (None unless output_final_state).  With
     ``return_wu`` also returns W, U [B,T,H_v,K|V] fp32.  ``cp_mode``: "auto"
-    (split long sequences of few heads), "off" (no split), "warmup" (split with
-    the sliding-window warm-up) or "exact" (split with the exact carry).
+    (split long sequences of few heads, with the warm-up), "auto_exact" (the same
+    trigger, exact split), "off" (no split), "warmup" (split with the
+    sliding-window warm-up) or "exact" (split with the exact carry).
     """
     _check(q, k, v, g, beta, cu_seqlens)
     q, k, v = _c(q), _c(k), _c(v)
@@ -122,8 +124,8 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
     rounding of up to 2^-9 |x| per element.  ``cp_mode``: "auto" (split the
     recurrences of long sequences of few heads), "off" or "exact"; the split is
     always exact here."""
-    if cp_mode not in ("auto", "off", "exact"):
-        raise ValueError("cp_mode of the backward: 'auto', 'off' or 'exact'")
+    if cp_mode not in ("auto", "auto_exact", "off", "exact"):
+        raise ValueError("cp_mode of the backward: 'auto', 'auto_exact', 'off' or 'exact'")
     _check(q, k, v, g, beta, cu_seqlens)
     q, k, v, do = _c(q), _c(k), _c(v), _c(do, q.dtype)
     g, beta, A = _c(g, torch.float32), _c(beta, torch.float32), _c(A, torch.float32)
@@ -164,9 +166,10 @@ class _ChunkGDR(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
                 output_dtype, cp_mode):
-        # the backward differentiates the exact scan: no sequence split when training
+        # the backward differentiates the exact recurrence: when training, a split
+        # (the forward's trigger) is the exact one
         if any(ctx.needs_input_grad):
-            cp_mode = "off"
+            cp_mode = "off" if cp_mode == "off" else "auto_exact"
         g_cum, A, o, _, ht = chunk_gated_delta_rule_fwd(
             q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_state=True,
             output_dtype=output_dtype, return_h=False, cp_mode=cp_mode)
@@ -190,8 +193,8 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
     """High-level differentiable API.  Returns ``(o, final_state)``.
 
     Without gradients the forward may split long sequences (``cp_mode``);
-    when any input requires a gradient it runs the exact scan, which is what
-    the backward differentiates."""
+    when any input requires a gradient a split is the exact one, as in the
+    backward."""
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     o, ht = _ChunkGDR.apply(q, k, v, g, beta, scale, initial_state, output_final_state,

@@ -76,7 +76,7 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     int rc = check_dims(a->B, a->T, a->H_q, a->H_v, a->K, a->V, a->n_seq, varlen, a->dtype);
     if (rc) return rc;
     if (a->out_dtype != GDR_BF16 && a->out_dtype != GDR_F32) return GDR_ENOTSUP;
-    if (a->cp_mode < GDR_CP_AUTO || a->cp_mode > GDR_CP_EXACT) return GDR_EINVAL;
+    if (a->cp_mode < GDR_CP_AUTO || a->cp_mode > GDR_CP_AUTO_EXACT) return GDR_EINVAL;
     if (a->cp_segment_chunks < 0 || a->cp_warmup_chunks < 0) return GDR_EINVAL;
     pl.n_seq = varlen ? a->n_seq : a->B;
     pl.tokens = a->B * a->T;
@@ -90,21 +90,22 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     pl.total = off;
     // sequence split ("AutoCP"): the pages' trigger on batch x heads and length
     const int64_t bh = pl.n_seq * a->H_v;
+    const bool autom = a->cp_mode == GDR_CP_AUTO || a->cp_mode == GDR_CP_AUTO_EXACT;
     bool split = a->cp_mode == GDR_CP_WARMUP || a->cp_mode == GDR_CP_EXACT ||
-                 (a->cp_mode == GDR_CP_AUTO && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
+                 (autom && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
     pl.warm_chunks = a->cp_warmup_chunks > 0 ? a->cp_warmup_chunks : 8;
     const int64_t n_vt = a->V / scan_vtile(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32, (int)a->K, (int)a->V);
     int64_t L = a->cp_segment_chunks > 0
                     ? a->cp_segment_chunks
                     : split_chunks(pl.nct, bh * n_vt, slots > 0 ? slots : DEFAULT_SLOTS, pl.warm_chunks,
-                                   a->cp_mode == GDR_CP_AUTO ? 1 : 2);
+                                   autom ? 1 : 2);
     if (L < 1) L = 1;
     if (!split || L >= pl.nct) {
         split = false;
         L = pl.nct + 1;
     }
     pl.split = split;
-    pl.exact = split && a->cp_mode == GDR_CP_EXACT;
+    pl.exact = split && (a->cp_mode == GDR_CP_EXACT || a->cp_mode == GDR_CP_AUTO_EXACT);
     if (pl.exact) pl.warm_chunks = 0;
     pl.seg_chunks = (int)L;
     pl.n_seg = split ? (int)cdiv(pl.nct, L) : 1;
@@ -144,7 +145,9 @@ int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl, int64_t slots = 0) {
     int rc = check_dims(a->B, a->T, a->H_q, a->H_v, a->K, a->V, a->n_seq, varlen, a->dtype);
     if (rc) return rc;
     if (a->grad_dtype != GDR_BF16 && a->grad_dtype != GDR_F32) return GDR_ENOTSUP;
-    if (a->cp_mode != GDR_CP_AUTO && a->cp_mode != GDR_CP_OFF && a->cp_mode != GDR_CP_EXACT) return GDR_EINVAL;
+    if (a->cp_mode != GDR_CP_AUTO && a->cp_mode != GDR_CP_OFF && a->cp_mode != GDR_CP_EXACT &&
+        a->cp_mode != GDR_CP_AUTO_EXACT)
+        return GDR_EINVAL;
     if (a->cp_segment_chunks < 0) return GDR_EINVAL;
     pl.n_seq = varlen ? a->n_seq : a->B;
     pl.tokens = a->B * a->T;
@@ -164,12 +167,12 @@ int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl, int64_t slots = 0) {
     // exact sequence split of the state scan and the reverse scan: the forward's trigger
     // and segment length
     const int64_t bh = pl.n_seq * a->H_v;
-    bool split = a->cp_mode == GDR_CP_EXACT ||
-                 (a->cp_mode == GDR_CP_AUTO && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
+    const bool autom = a->cp_mode == GDR_CP_AUTO || a->cp_mode == GDR_CP_AUTO_EXACT;
+    bool split = a->cp_mode == GDR_CP_EXACT || (autom && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
     const int64_t n_vt = a->V / 64;
     int64_t L = a->cp_segment_chunks > 0 ? a->cp_segment_chunks
                                           : split_chunks(pl.nct, bh * n_vt, slots > 0 ? slots : DEFAULT_SLOTS, 8,
-                                                         a->cp_mode == GDR_CP_AUTO ? 1 : 2);
+                                                         autom ? 1 : 2);
     if (L < 1) L = 1;
     if (!split || L >= pl.nct || pl.tokens == 0) {
         split = false;

@@ -70,6 +70,7 @@ extern "C" {
                            zero-start end state are scanned in parallel, a serial carry
                            over the segments gives their true start states, then the
                            segments run again with output */
+#define GDR_CP_AUTO_EXACT 4 /* the GDR_CP_AUTO trigger with the exact split */
 
 typedef struct {
     /* sizes.  With cu_seqlens, B must be 1, T is the packed token count and
@@ -115,9 +116,10 @@ typedef struct {
     int64_t B, T, H_q, H_v, K, V, n_seq;
     int32_t dtype;      /* element type of q, k, v, do */
     int32_t grad_dtype; /* element type of dq, dk, dv: GDR_BF16 or GDR_F32 */
-    int32_t cp_mode;    /* sequence split of the recurrences: GDR_CP_AUTO (the forward's
-                           trigger), GDR_CP_OFF or GDR_CP_EXACT; the backward has no
-                           warm-up form (GDR_CP_WARMUP is an invalid argument) */
+    int32_t cp_mode;    /* sequence split of the recurrences: GDR_CP_AUTO or
+                           GDR_CP_AUTO_EXACT (the forward's trigger), GDR_CP_OFF or
+                           GDR_CP_EXACT; the split is always exact here (GDR_CP_WARMUP
+                           is an invalid argument) */
     int32_t cp_segment_chunks; /* chunks per segment; 0 = chosen for the device as in gdr_fwd */
     float scale;
     const void *q, *k, *v;      /* as in gdr_fwd_args */

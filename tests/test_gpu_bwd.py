@@ -178,6 +178,31 @@ def test_autograd_function_matches_low_level():
     compare(x, got, ref, names=("dbeta", "dg", "dh0"))
 
 
+def test_autograd_small_heads_long_sequence_splits_exactly():
+    """B*H_v = 2 and 40 chunks: the trigger fires, so the differentiable API runs
+    the forward's exact split and the backward's; o and every gradient against the
+    oracle (fp32 inputs, bar 1e-4)."""
+    from gated_delta_rule_85_amd import chunk_gated_delta_rule
+    x = make_inputs(dict(B=1, T=64 * 40 - 7, Hq=1, Hv=2, K=64, V=64, dtype="fp32", h0=True), seed=15,
+                    grads=True)
+    d = gpu_inputs(x)
+    leaves = {n: d[n].clone().requires_grad_(True) for n in ("q", "k", "v", "g", "beta",
+                                                             "initial_state")}
+    o, ht = chunk_gated_delta_rule(leaves["q"], leaves["k"], leaves["v"], leaves["g"],
+                                   leaves["beta"], x["scale"], leaves["initial_state"],
+                                   output_final_state=True)
+    loss = (o * dev(x["do"])).sum() + (ht * dev(x["dht"])).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    fwd = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], x["initial_state"])
+    e_o = rel(host(o.detach()), fwd["o"])
+    print("o %.3g" % e_o, flush=True)
+    assert e_o <= 1e-4
+    got = dict(dq=leaves["q"].grad, dk=leaves["k"].grad, dv=leaves["v"].grad,
+               dbeta=leaves["beta"].grad, dg=leaves["g"].grad, dh0=leaves["initial_state"].grad)
+    compare(x, got, ora_bwd(x))
+
+
 def test_training_shape_full_size_sampled_units():
     """B=8, T=4096, H_q=32, H_v=64, K=V=128, bf16: the whole backward on the GPU,
     four (sequence, q/k head) units against the oracle."""
