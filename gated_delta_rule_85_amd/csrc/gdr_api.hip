@@ -49,15 +49,19 @@ int check_dims(int64_t B, int64_t T, int64_t Hq, int64_t Hv, int64_t K, int64_t 
 // Segment length of the sequence split when the caller leaves it open.  The
 // scan runs one workgroup per compute unit, so a launch of W workgroups per
 // segment index takes ceil(W S / slots) rounds, each as long as the longest
-// segment plus its warm-up window: choose the segment count S that minimises
-// rounds x (L + warm-up), L = ceil(N / S) (ties: fewer segments), S >= min_seg.
+// segment: choose the segment count S >= min_seg that minimises, in chunk steps,
+//   warm-up split:  rounds x (L + wm)
+//   exact split:    rounds x 3 L + (S - 1)   (transitions, zero-start states and
+//                   output passes, one carry step per segment)
+// with L = ceil(N / S) (ties: fewer segments); one segment costs rounds x N.
 // Returns N + 1 (no split) when one segment is best.
-int64_t split_chunks(int64_t N, int64_t W, int64_t slots, int64_t wm, int64_t min_seg) {
+int64_t split_chunks(int64_t N, int64_t W, int64_t slots, int64_t wm, int64_t min_seg, bool exact = false) {
     int64_t best_t = -1, best_L = N + 1;
     for (int64_t S = min_seg; S <= N; ++S) {
         const int64_t L = cdiv(N, S), Sx = cdiv(N, L);
         if (Sx != S) continue;  // same L as a smaller S
-        const int64_t t = cdiv(W * S, slots) * (L + (S > 1 ? wm : 0));
+        const int64_t rounds = cdiv(W * S, slots);
+        const int64_t t = S == 1 ? rounds * N : exact ? rounds * 3 * L + (S - 1) : rounds * (L + wm);
         if (best_t < 0 || t < best_t) {
             best_t = t;
             best_L = S > 1 ? L : N + 1;
@@ -90,22 +94,25 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     pl.total = off;
     // sequence split ("AutoCP"): the pages' trigger on batch x heads and length
     const int64_t bh = pl.n_seq * a->H_v;
+    // GDR_CP_AUTO: the pages' trigger (warm-up split); GDR_CP_AUTO_EXACT: the device
+    // model alone decides (the exact split costs no accuracy)
     const bool autom = a->cp_mode == GDR_CP_AUTO || a->cp_mode == GDR_CP_AUTO_EXACT;
-    bool split = a->cp_mode == GDR_CP_WARMUP || a->cp_mode == GDR_CP_EXACT ||
-                 (autom && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
+    const bool exact_mode = a->cp_mode == GDR_CP_EXACT || a->cp_mode == GDR_CP_AUTO_EXACT;
+    bool split = a->cp_mode == GDR_CP_WARMUP || exact_mode ||
+                 (a->cp_mode == GDR_CP_AUTO && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
     pl.warm_chunks = a->cp_warmup_chunks > 0 ? a->cp_warmup_chunks : 8;
     const int64_t n_vt = a->V / scan_vtile(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32, (int)a->K, (int)a->V);
     int64_t L = a->cp_segment_chunks > 0
                     ? a->cp_segment_chunks
                     : split_chunks(pl.nct, bh * n_vt, slots > 0 ? slots : DEFAULT_SLOTS, pl.warm_chunks,
-                                   autom ? 1 : 2);
+                                   autom ? 1 : 2, exact_mode);
     if (L < 1) L = 1;
     if (!split || L >= pl.nct) {
         split = false;
         L = pl.nct + 1;
     }
     pl.split = split;
-    pl.exact = split && (a->cp_mode == GDR_CP_EXACT || a->cp_mode == GDR_CP_AUTO_EXACT);
+    pl.exact = split && exact_mode;
     if (pl.exact) pl.warm_chunks = 0;
     pl.seg_chunks = (int)L;
     pl.n_seg = split ? (int)cdiv(pl.nct, L) : 1;
@@ -167,12 +174,13 @@ int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl, int64_t slots = 0) {
     // exact sequence split of the state scan and the reverse scan: the forward's trigger
     // and segment length
     const int64_t bh = pl.n_seq * a->H_v;
+    // the device model decides for AUTO and AUTO_EXACT (the split is exact here)
     const bool autom = a->cp_mode == GDR_CP_AUTO || a->cp_mode == GDR_CP_AUTO_EXACT;
-    bool split = a->cp_mode == GDR_CP_EXACT || (autom && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
+    bool split = a->cp_mode == GDR_CP_EXACT || autom;
     const int64_t n_vt = a->V / 64;
     int64_t L = a->cp_segment_chunks > 0 ? a->cp_segment_chunks
                                           : split_chunks(pl.nct, bh * n_vt, slots > 0 ? slots : DEFAULT_SLOTS, 8,
-                                                         autom ? 1 : 2);
+                                                         autom ? 1 : 2, true);
     if (L < 1) L = 1;
     if (!split || L >= pl.nct || pl.tokens == 0) {
         split = false;
