@@ -70,7 +70,7 @@ extern "C" {
                            zero-start end state are scanned in parallel, a serial carry
                            over the segments gives their true start states, then the
                            segments run again with output */
-#define GDR_CP_AUTO_EXACT 4 /* the GDR_CP_AUTO trigger with the exact split */
+#define GDR_CP_AUTO_EXACT 4 /* the exact split where the device model predicts a gain */
 
 typedef struct {
     /* sizes.  With cu_seqlens, B must be 1, T is the packed token count and
@@ -117,9 +117,9 @@ typedef struct {
     int32_t dtype;      /* element type of q, k, v, do */
     int32_t grad_dtype; /* element type of dq, dk, dv: GDR_BF16 or GDR_F32 */
     int32_t cp_mode;    /* sequence split of the recurrences: GDR_CP_AUTO or
-                           GDR_CP_AUTO_EXACT (the forward's trigger), GDR_CP_OFF or
-                           GDR_CP_EXACT; the split is always exact here (GDR_CP_WARMUP
-                           is an invalid argument) */
+                           GDR_CP_AUTO_EXACT (split where the device model of gdr_fwd
+                           predicts a gain), GDR_CP_OFF or GDR_CP_EXACT; the split is
+                           always exact here (GDR_CP_WARMUP is an invalid argument) */
     int32_t cp_segment_chunks; /* chunks per segment; 0 = chosen for the device as in gdr_fwd */
     float scale;
     const void *q, *k, *v;      /* as in gdr_fwd_args */
@@ -167,10 +167,12 @@ int gdr_fwd_workspace(const gdr_fwd_args *args, size_t *bytes);
    window reaches the start of the sequence).  With cp_segment_chunks = 0 the
    segment length L is chosen from the compute-unit count of the stream's
    device (one scan workgroup per unit): the segment count S that minimises
-   ceil(S x workgroups per segment index / units) x (L + warm-up window),
-   L = ceil(chunks / S); the pages' sliding-window method leaves L to a
-   runtime model (they suggest sqrt(chunks) for theirs).  Returns GDR_ELAUNCH
-   if the device cannot be queried. */
+   rounds x (L + warm-up window) for the warm-up split and
+   rounds x 3 L + (S - 1) for the exact one, rounds = ceil(S x workgroups per
+   segment index / units), L = ceil(chunks / S); the pages' sliding-window
+   method leaves L to a runtime model (they suggest sqrt(chunks) for theirs).
+   GDR_CP_AUTO_EXACT splits only where that model predicts a gain over one
+   segment.  Returns GDR_ELAUNCH if the device cannot be queried. */
 int gdr_fwd(const gdr_fwd_args *args, hipStream_t stream);
 
 /* Workspace bytes gdr_bwd needs for these sizes (pointers are not read):
