@@ -167,7 +167,7 @@ class _ChunkGDR(torch.autograd.Function):
     def forward(ctx, q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
                 output_dtype, cp_mode):
         # the backward differentiates the exact recurrence: when training, a split
-        # (the forward's trigger) is the exact one
+        # (where the device model predicts a gain) is the exact one
         if any(ctx.needs_input_grad):
             cp_mode = "off" if cp_mode == "off" else "auto_exact"
         g_cum, A, o, _, ht = chunk_gated_delta_rule_fwd(

@@ -171,8 +171,8 @@ int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl, int64_t slots = 0) {
     pl.off_dhs = off;
     off += up(sizeof(float) * nb * (size_t)(a->K * a->V));
     pl.total = pl.tokens > 0 ? off : pl.off_tblk;
-    // exact sequence split of the state scan and the reverse scan: the forward's trigger
-    // and segment length
+    // exact sequence split of the state scan and the reverse scan: the device model
+    // chooses whether and how long (AUTO), or how long (EXACT)
     const int64_t bh = pl.n_seq * a->H_v;
     // the device model decides for AUTO and AUTO_EXACT (the split is exact here)
     const bool autom = a->cp_mode == GDR_CP_AUTO || a->cp_mode == GDR_CP_AUTO_EXACT;
