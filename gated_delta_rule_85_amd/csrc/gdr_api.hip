@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/gdr.h"
 #include "gdr_kernels.hpp"
 
@@ -54,10 +56,12 @@ int check_dims(int64_t B, int64_t T, int64_t Hq, int64_t Hv, int64_t K, int64_t 
 //   exact split:    rounds x 3 L + (S - 1)   (transitions, zero-start states and
 //                   output passes, one carry step per segment)
 // with L = ceil(N / S) (ties: fewer segments); one segment costs rounds x N.
+// Segment counts beyond eight rounds of the device are not considered.
 // Returns N + 1 (no split) when one segment is best.
 int64_t split_chunks(int64_t N, int64_t W, int64_t slots, int64_t wm, int64_t min_seg, bool exact = false) {
     int64_t best_t = -1, best_L = N + 1;
-    for (int64_t S = min_seg; S <= N; ++S) {
+    const int64_t s_max = std::min(N, 8 * cdiv(slots, std::max<int64_t>(W, 1)));
+    for (int64_t S = min_seg; S <= s_max; ++S) {
         const int64_t L = cdiv(N, S), Sx = cdiv(N, L);
         if (Sx != S) continue;  // same L as a smaller S
         const int64_t rounds = cdiv(W * S, slots);

@@ -78,10 +78,11 @@ def test_long_sequence_warmup_split(long_seq, wm):
 
 
 def split_chunks(N, W, slots, wm):
-    """Segment length of the device model: the segment count S minimising
-    ceil(W S / slots) * (L + wm), L = ceil(N / S), fewer segments on ties."""
+    """Segment length of the device model for the warm-up split: the segment count
+    S (up to eight rounds of the device) minimising ceil(W S / slots) * (L + wm),
+    L = ceil(N / S), fewer segments on ties."""
     best = None
-    for S in range(1, N + 1):
+    for S in range(1, min(N, 8 * -(-slots // W)) + 1):
         L = -(-N // S)
         if -(-N // L) != S:
             continue
