@@ -67,6 +67,7 @@ def compare(x, got, ref, t=None, names=NAMES):
     dict(B=2, T=300, Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True),
     dict(B=1, T=200, Hq=1, Hv=1, K=64, V=128, dtype="bf16", h0=True),
     dict(B=1, T=130, Hq=2, Hv=2, K=128, V=64, dtype="bf16", h0=False),
+    dict(B=2, T=250, Hq=2, Hv=6, K=64, V=64, dtype="bf16", h0=True),
 ])
 def test_small_ragged(shape):
     """Every element of every gradient; several chunks and a ragged tail."""

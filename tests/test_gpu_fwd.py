@@ -52,6 +52,7 @@ def test_tiny_fp32_workload():
     dict(B=2, T=300, Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True),
     dict(B=1, T=200, Hq=1, Hv=1, K=64, V=128, dtype="bf16", h0=True),
     dict(B=1, T=130, Hq=2, Hv=2, K=128, V=64, dtype="bf16", h0=False),
+    dict(B=2, T=250, Hq=2, Hv=6, K=64, V=64, dtype="bf16", h0=True),
     dict(B=3, T=77, Hq=1, Hv=2, K=64, V=64, dtype="fp32", h0=True),
     dict(B=1, T=190, Hq=1, Hv=3, K=128, V=128, dtype="fp32", h0=True),
 ])

@@ -41,6 +41,21 @@ def test_training_shape_forward_full_size():
         assert eo <= 2e-2 and eh <= 2e-2
 
 
+@pytest.mark.parametrize("Hv", [64, 48, 24, 16])
+def test_family_head_counts(Hv):
+    """The head counts the pages benchmark (64 to 8, TP1 to TP8) with H_q = H_v / 2,
+    B=2, T=2048, bf16, launched whole; two (sequence, q/k head) units sampled."""
+    x = make_inputs(dict(B=2, T=2048, Hq=Hv // 2, Hv=Hv, K=128, V=128, dtype="bf16", h0=True), seed=16)
+    g_cum, A, o, h, ht = run_fwd(x, return_h=False)
+    o, ht = host(o), host(ht)
+    for b, hq in ((0, 0), (1, Hv // 2 - 1)):
+        y, hs = slice_units(x, b, hq)
+        r = oracle.fwd(y["q"], y["k"], y["v"], y["g"], y["beta"], y["scale"], y["initial_state"])
+        eo, eh = rel(o[b:b + 1, :, hs], r["o"]), rel(ht[b:b + 1, hs], r["final_state"])
+        print("H_v=%d b=%d hq=%d o %.3g final %.3g" % (Hv, b, hq, eo, eh), flush=True)
+        assert eo <= 2e-2 and eh <= 2e-2
+
+
 @pytest.fixture(scope="module")
 def long_seq():
     """B=1, T=32768, H_q=4, H_v=8, K=V=128, bf16: 512 chunks per head."""
