@@ -17,22 +17,27 @@
 // T (split into bf16 hi/lo planes) and the gate scalars come from
 // gdr_chunk_prep as one LDS image per (chunk, v head).  Columns of h evolve
 // independently, so waves never exchange state; the four waves share the
-// decayed scores P through LDS (each forms some of its ten 16x16 tiles as
-// K Q^T, whose accumulator layout is P's A operand).  Products with fp32
-// operands use split-bf16 MFMA (gdr_device.hpp); accumulation is fp32.
+// decayed scores P through LDS (waves 2 and 3 form the ten 16x16 tiles as
+// K Q^T, whose accumulator layout is P's A operand, while waves 0 and 1 issue
+// the next chunk's copies).  Products with fp32 operands use split-bf16 MFMA
+// (gdr_device.hpp); accumulation is fp32.
 //
 // Data movement: K, Q, the V columns and the T block of the next chunk are
 // copied global -> LDS by the waves' direct-to-LDS loads while the current
 // chunk computes (two LDS buffers, bf16 inputs), into XOR-swizzled rows
 // (gdr_layout.hpp).  The K^T operand of the state update and the V columns
-// are read with the gfx950 transposing LDS read.  The output chunk is staged
-// in LDS and written with 16-byte stores during the next chunk.
+// are read with the gfx950 transposing LDS read.  Each wave keeps its output
+// tiles in registers and stores them (16 bytes per lane and row) at the start
+// of the next chunk.
 //
 // Sequence split (the pages' AutoCP with its sliding-window warm-up): with
 // seg_chunks smaller than the sequence, segment s > 0 starts from a zero
 // state warm_chunks chunks before its first chunk (from the true initial
 // state when that window reaches chunk 0) and runs the scan without output
-// over the window before its own chunks.
+// over the window before its own chunks.  For the exact split a segment can
+// instead start from a given state (h0_seg) or from the identity over a
+// shared zero row of values (its end state is then the segment's transition
+// matrix), and hand its end state to hT_seg; carry_kernel below chains them.
 #include <type_traits>
 
 #include "gdr_kernels.hpp"
