@@ -4,6 +4,8 @@
 // arithmetic); it sits in a file of its own because it is compiled with the
 // ILP-seeking scheduler (one wave per SIMD: operand reads must be issued well
 // ahead of their MFMAs).
+#include <type_traits>
+
 #include "gdr_bwd_ops.hpp"
 
 namespace gdr {
@@ -39,10 +41,13 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
     constexpr int KROW = KD * 2, DROW = 64 * 2, PROW = 64 * 2, PPLANE = CH * PROW;
     constexpr int DT = KD / 16, DP = KD / 32;
     using TB = TBlock<bf16>;
-    __shared__ __attribute__((aligned(16))) char Ks[CH * KROW];
-    __shared__ __attribute__((aligned(16))) char Qs[CH * KROW];
-    __shared__ __attribute__((aligned(16))) char Ds[CH * DROW];
-    __shared__ __attribute__((aligned(16))) char Tb[TB::BYTES];
+    // two sets of chunk tiles: the next chunk (in reverse order) is copied into one
+    // while the current one is read (separate arrays, so the compiler can tell the
+    // copies into one set from the reads of the other)
+    __shared__ __attribute__((aligned(16))) char Ks0[CH * KROW], Ks1[CH * KROW];
+    __shared__ __attribute__((aligned(16))) char Qs0[CH * KROW], Qs1[CH * KROW];
+    __shared__ __attribute__((aligned(16))) char Ds0[CH * DROW], Ds1[CH * DROW];
+    __shared__ __attribute__((aligned(16))) char Tb0[TB::BYTES], Tb1[TB::BYTES];
     __shared__ __attribute__((aligned(16))) char Pt[2 * PPLANE];
 
     const int nvt = p.V / 64;
@@ -73,8 +78,6 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
     const int64_t KV = (int64_t)KD * p.V;
     const char *kp = reinterpret_cast<const char *>(p.k), *qp = reinterpret_cast<const char *>(p.q);
     const char *dop = reinterpret_cast<const char *>(p.dout);
-    const float *sc = reinterpret_cast<const float *>(Tb + TB::SC);
-    const float *eg = sc + CH, *rr = sc + 2 * CH, *bet = sc + 3 * CH;
 
     // dh[dt][i] = key slot_base(dt, g) + i (the contiguous-slot order of gdr_lds.hpp), column col
     f32x4 dh[DT];
@@ -85,14 +88,30 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
             dh[dt][i] = dh_start ? dh_start[(slot_base(dt, g) + i) * p.V + col] : 0.f;
     zero_lower_pt(Pt);
 
-    for (int c = c_end - 1; c >= c_begin; --c) {
+    // copy chunk c into one set of tiles
+    auto issue = [&](int c, char *K_, char *Q_, char *D_, char *T_) {
         const int64_t ts = bos + (int64_t)c * CH;
         const int n = (int)min<int64_t>(CH, eos - ts);
-        __syncthreads();  // the previous chunk is done with every tile
-        copy_tile<KROW>(Ks, kp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
-        copy_tile<KROW>(Qs, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
-        copy_tile<DROW>(Ds, dop + ((ts * p.Hv + hv) * p.V + vt * 64) * 2, p.Hv * p.V * 2, n - 1, w);
-        copy_flat(Tb, p.tblk + ((int64_t)(cb + c) * p.Hv + hv) * TB::BYTES, TB::BYTES, w);
+        copy_tile<KROW>(K_, kp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
+        copy_tile<KROW>(Q_, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
+        copy_tile<DROW>(D_, dop + ((ts * p.Hv + hv) * p.V + vt * 64) * 2, p.Hv * p.V * 2, n - 1, w);
+        copy_flat(T_, p.tblk + ((int64_t)(cb + c) * p.Hv + hv) * TB::BYTES, TB::BYTES, w);
+    };
+    // chunk c from tile set CUR (landed, every wave past the barrier after it); chunk
+    // c - 1 is copied into the other set meanwhile
+    auto body = [&](auto cur, int c) {
+        constexpr bool ONE = decltype(cur)::value == 1;
+        const char *Ks = ONE ? Ks1 : Ks0, *Qs = ONE ? Qs1 : Qs0, *Ds = ONE ? Ds1 : Ds0, *Tb = ONE ? Tb1 : Tb0;
+        const float *sc = reinterpret_cast<const float *>(Tb + TB::SC);
+        const float *eg = sc + CH, *rr = sc + 2 * CH, *bet = sc + 3 * CH;
+        const int64_t ts = bos + (int64_t)c * CH;
+        const int n = (int)min<int64_t>(CH, eos - ts);
+        if (c - 1 >= c_begin) {
+            if constexpr (ONE)
+                issue(c - 1, Ks0, Qs0, Ds0, Tb0);
+            else
+                issue(c - 1, Ks1, Qs1, Ds1, Tb1);
+        }
         if (!p.d_seg) {  // gradient of this chunk's end state, for the chunk-local stage: hi, lo planes of dh'^T
             char *o = reinterpret_cast<char *>(p.dhs + ((int64_t)(cb + c) * p.Hv + hv) * KV);
             const int plane = KD * p.V * 2;
@@ -106,8 +125,6 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
                 *reinterpret_cast<bf16x8 *>(o + plane + off) = cat(lo0, lo1);
             }
         }
-        wait_dma();
-        __syncthreads();
         scores_t<KD>(Pt, Qs, Ks, sc, n, w);
         __syncthreads();
         // dU~ = diag(r) K dh' + s P^T dO  (rows = tokens, this wave's columns)
@@ -171,6 +188,15 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
                 dh[dt] = mma(dh[dt], kt_keys<KROW>(Ks, c0, ip), bdx[ip]);
             }
         }
+        wait_dma();
+        __syncthreads();  // chunk c done with its tiles and the score planes; c - 1 landed
+    };
+    if (c_end > c_begin) issue(c_end - 1, Ks0, Qs0, Ds0, Tb0);
+    wait_dma();
+    __syncthreads();
+    for (int c = c_end - 1; c >= c_begin; c -= 2) {
+        body(std::integral_constant<int, 0>{}, c);
+        if (c - 1 >= c_begin) body(std::integral_constant<int, 1>{}, c - 1);
     }
     float *dh_out = p.d_seg ? p.d_seg + ((int64_t)unit * p.n_seg + seg) * KV
                     : c_begin == 0 && p.dh0 ? p.dh0 + unit * KV : nullptr;
