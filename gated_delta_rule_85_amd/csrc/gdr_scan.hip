@@ -489,65 +489,91 @@ hipError_t launch_scan_k(int K, const ScanParams &p, hipStream_t s) {
 // columns of start(s) stay in LDS; wave w forms the row tiles 2w, 2w + 1 of the
 // next start on fp32 MFMA, with the rows of M(s) read from memory as A operands
 // (k = 16 dt + 4 g + j in instruction j, the B operand's rows in the same order).
-// The reverse carry (rev) runs the segments backwards with M(s)^T.
+// The reverse carry (rev) runs the segments backwards with M(s)^T.  Each step's
+// operands from memory (its rows of M and b) are loaded during the step before.
+template <int KD>
 __global__ __launch_bounds__(NTHR) void carry_kernel(const CarryParams p) {
-    __shared__ float hs[128 * 16];
+    constexpr int MT = KD / 16;
+    __shared__ float hs[KD * 16];
     const int unit = blockIdx.x, c0 = blockIdx.y * 16;
     int64_t bos, eos;
     p.sm.bounds(unit / p.Hv, bos, eos);
     const int N = (int)((eos - bos + CH - 1) / CH);
     const int nseg = (N + p.seg_chunks - 1) / p.seg_chunks;
     if (nseg < 2) return;
-    const int K = p.K, V = p.V, MT = K / 16;
+    const int V = p.V;
     const int w = wave_id(), n16 = ln16(), g = lg4();
-    const int64_t KV = (int64_t)K * V, KK = (int64_t)K * K, base = (int64_t)unit * p.n_seg;
+    const int64_t KV = (int64_t)KD * V, KK = (int64_t)KD * KD, base = (int64_t)unit * p.n_seg;
     // first carried segment: forward start(1) = b(0); reverse end(n-2) = b(n-1)
     const int first_src = p.rev ? nseg - 1 : 0, first_dst = p.rev ? nseg - 2 : 1;
-    for (int idx = threadIdx.x; idx < K * 16; idx += NTHR) {
+    for (int idx = threadIdx.x; idx < KD * 16; idx += NTHR) {
         const int r = idx >> 4, c = idx & 15;
         const float v = p.b[(base + first_src) * KV + r * V + c0 + c];
         hs[r * 16 + c] = v;
         p.h0_seg[(base + first_dst) * KV + r * V + c0 + c] = v;
     }
-    __syncthreads();
-    for (int step = 1; step + 1 < nseg; ++step) {
-        const int s = p.rev ? nseg - 1 - step : step, dst = p.rev ? s - 1 : s + 1;
+    // this wave's row tiles: 2w, 2w + 1 (K = 128) or w (K = 64)
+    constexpr int NT = MT >= 8 ? 2 : 1;
+    const bool active = (MT >= 8 ? 2 * w : w) < MT;
+    f32x4 a[NT][MT], bt[NT];
+    auto load = [&](int s) {
         const float *Ms = p.M + (base + s) * KK;
         const float *bs = p.b + (base + s) * KV;
-        f32x4 acc[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int mt = 2 * w + t;
-            if (mt >= MT) break;
+        for (int t = 0; t < NT; ++t) {
+            const int mt = (MT >= 8 ? 2 * w : w) + t;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) acc[t][jj] = bs[(16 * mt + 4 * g + jj) * V + c0 + n16];
+            for (int jj = 0; jj < 4; ++jj) bt[t][jj] = bs[(16 * mt + 4 * g + jj) * V + c0 + n16];
+#pragma unroll
             for (int dt = 0; dt < MT; ++dt) {
-                f32x4 a4;
                 if (p.rev) {  // rows of M^T: columns of M
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) a4[jj] = Ms[(16 * dt + 4 * g + jj) * K + 16 * mt + n16];
+                    for (int jj = 0; jj < 4; ++jj) a[t][dt][jj] = Ms[(16 * dt + 4 * g + jj) * KD + 16 * mt + n16];
                 } else {
-                    a4 = *reinterpret_cast<const f32x4 *>(Ms + (16 * mt + n16) * K + 16 * dt + 4 * g);
+                    a[t][dt] = *reinterpret_cast<const f32x4 *>(Ms + (16 * mt + n16) * KD + 16 * dt + 4 * g);
                 }
+            }
+        }
+    };
+    auto seg_of = [&](int step) { return p.rev ? nseg - 1 - step : step; };
+    if (active && nseg > 2) load(seg_of(1));
+    __syncthreads();
+    for (int step = 1; step + 1 < nseg; ++step) {
+        const int s = seg_of(step), dst = p.rev ? s - 1 : s + 1;
+        f32x4 acc[NT];
+        if (active) {
+            f32x4 y[MT];  // B operands: rows 16 dt + 4 g + j of start(s), read up front
+#pragma unroll
+            for (int dt = 0; dt < MT; ++dt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) y[dt][jj] = hs[(16 * dt + 4 * g + jj) * 16 + n16];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] = bt[t];
+#pragma unroll
+            for (int dt = 0; dt < MT; ++dt)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[jj], hs[(16 * dt + 4 * g + jj) * 16 + n16],
-                                                                 acc[t], 0, 0, 0);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t][dt][jj], y[dt][jj], acc[t], 0, 0, 0);
+            if (step + 2 < nseg) load(seg_of(step + 1));  // the next step's operands
+        }
+        // barriers that wait for LDS only: the stores of the carried states and the
+        // loads of the next step's operands stay in flight
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // start(s) read by every wave
+        if (active) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int mt = (MT >= 8 ? 2 * w : w) + t;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int r = 16 * mt + 4 * g + jj;
+                    hs[r * 16 + n16] = acc[t][jj];
+                    p.h0_seg[(base + dst) * KV + r * V + c0 + n16] = acc[t][jj];
+                }
             }
         }
-        __syncthreads();  // start(s) read by every wave
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int mt = 2 * w + t;
-            if (mt >= MT) break;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int r = 16 * mt + 4 * g + jj;
-                hs[r * 16 + n16] = acc[t][jj];
-                p.h0_seg[(base + dst) * KV + r * V + c0 + n16] = acc[t][jj];
-            }
-        }
-        __syncthreads();
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
 }
 
@@ -558,7 +584,10 @@ __global__ void fill_zero_kernel(uint32_t *p, size_t n) {
 }  // namespace
 
 hipError_t launch_carry(const CarryParams &p, int n_units, hipStream_t s) {
-    hipLaunchKernelGGL(carry_kernel, dim3(n_units, p.V / 16), dim3(NTHR), 0, s, p);
+    if (p.K == 128)
+        hipLaunchKernelGGL(carry_kernel<128>, dim3(n_units, p.V / 16), dim3(NTHR), 0, s, p);
+    else
+        hipLaunchKernelGGL(carry_kernel<64>, dim3(n_units, p.V / 16), dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
 
