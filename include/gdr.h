@@ -177,8 +177,11 @@ int gdr_fwd(const gdr_fwd_args *args, hipStream_t stream);
 
 /* Workspace bytes gdr_bwd needs for these sizes (pointers are not read):
    T blocks, the chunk-start states and the chunk-end state gradients,
-   4 K V bytes each per (chunk, v head).  Returns GDR_OK or a validation
-   error. */
+   4 K V bytes each per (chunk, v head); with a sequence split also, per
+   (sequence, v head, segment), the K x K transition and four K x V states
+   (fp32) and a 512-byte zero row.  The split follows the compute units of
+   the current device, as for gdr_fwd_workspace.  Returns GDR_OK or a
+   validation error. */
 int gdr_bwd_workspace(const gdr_bwd_args *args, size_t *bytes);
 
 /* Backward of the exact forward (GDR_CP_OFF) on `stream`: gradients of
@@ -186,7 +189,12 @@ int gdr_bwd_workspace(const gdr_bwd_args *args, size_t *bytes);
    beta, the raw per-token g and initial_state.  g_cum and A must be what
    gdr_fwd returned for the same inputs.  The chunk-start states are
    recomputed, not read.  dq and dk are written in full (rows of every
-   token); every output is overwritten, none accumulated into. */
+   token); every output is overwritten, none accumulated into.  With a
+   sequence split (cp_mode) the chunk-start states and the reverse scan are
+   split exactly (gdr_fwd's GDR_CP_EXACT applied to both recurrences; the
+   reverse one carries the end-state gradients with the transposed segment
+   transitions).  Returns GDR_ELAUNCH if the stream's device cannot be
+   queried. */
 int gdr_bwd(const gdr_bwd_args *args, hipStream_t stream);
 
 #ifdef __cplusplus
