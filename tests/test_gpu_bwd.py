@@ -81,6 +81,8 @@ def test_small_ragged(shape):
     (dict(B=2, T=64 * 7, Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True), 3),
     (dict(B=1, T=64 * 5 + 1, Hq=1, Hv=1, K=128, V=64, dtype="fp32", h0=False), 1),
     (dict(lens=[400, 0, 65, 300, 1], Hq=1, Hv=2, K=64, V=128, dtype="fp32", h0=True), 2),
+    (dict(B=1, T=64 * 6, Hq=2, Hv=4, K=64, V=64, dtype="bf16", h0=True), 1),
+    (dict(lens=[64] * 5 + [900, 0, 3], Hq=1, Hv=2, K=64, V=64, dtype="fp32", h0=False), 5),
 ])
 def test_exact_split_backward(shape, L):
     """The backward's exact sequence split: the forward's split for the chunk-start

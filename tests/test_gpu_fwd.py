@@ -104,6 +104,9 @@ def test_varlen_many_short_sequences_natural_order():
     (dict(B=2, T=64 * 9, Hq=1, Hv=2, K=128, V=64, dtype="bf16", h0=True), 2),
     (dict(lens=[300, 1, 0, 700, 64, 129], Hq=2, Hv=4, K=64, V=128, dtype="fp32", h0=True), 3),
     (dict(lens=[1000, 130, 5], Hq=1, Hv=1, K=128, V=128, dtype="bf16", h0=False), 4),
+    (dict(B=1, T=64 * 6, Hq=2, Hv=4, K=64, V=64, dtype="bf16", h0=True), 1),
+    (dict(lens=[64] * 5 + [900, 0, 3], Hq=1, Hv=2, K=64, V=64, dtype="fp32", h0=True), 5),
+    (dict(B=1, T=1, Hq=1, Hv=1, K=64, V=64, dtype="fp32", h0=True), 1),
 ])
 def test_exact_sequence_split(shape, L):
     """Exact split: every segment's transition matrix and zero-start end state in
