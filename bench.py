@@ -15,9 +15,11 @@ roofline entry.  The fp64 CPU oracle is timed on a bounded
 sample of the same workload for the cpu_baseline entry.
 
 ``--workload training`` instead times one training step of the operator:
-gdr_fwd (exact scan, writing the g_cum and A the backward needs) followed by
-gdr_bwd (dq, dk, dv in bf16; dbeta, dg, dh0 in fp32) at B=8, T=4096,
-H_q=32, H_v=64, K=V=128, with upstream gradients do and dht.
+gdr_fwd (exact scan, writing the g_cum and A the backward needs, and its
+chunk-start states in the backward's layout) followed by gdr_bwd (dq, dk, dv in
+bf16; dbeta, dg, dh0 in fp32) at B=8, T=4096, H_q=32, H_v=64, K=V=128, with
+upstream gradients do and dht (``--recompute-states``: the backward recomputes
+the states instead).
 
 Prints one JSON line.
 """
@@ -231,6 +233,8 @@ def main():
                     help="sequence split of the forward (training: always off)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--recompute-states", action="store_true",
+                    help="training: the backward recomputes the chunk-start states")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this operator has no multi-GPU path here "
@@ -279,6 +283,12 @@ def main():
         A = torch.empty((B, T, Hv, 64), dtype=torch.float32, device=dev)
         keep += [g_cum, A]
         a.g_cum, a.A = g_cum.data_ptr(), A.data_ptr()
+        if not args.recompute_states:
+            n_chunks = B * ((T + 63) // 64) if cu is None else \
+                int(((cu[1:] - cu[:-1]).cpu().long().add(63) // 64).sum())
+            hb = torch.empty((n_chunks, Hv, 4 * K * V), dtype=torch.uint8, device=dev)
+            keep.append(hb)
+            a.h_bwd = hb.data_ptr()
     nbytes = _lib.fwd_workspace(a)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
@@ -302,6 +312,7 @@ def main():
         bw.dq, bw.dk, bw.dv, bw.dbeta, bw.dg = dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), \
             db.data_ptr(), dg.data_ptr()
         bw.dh0 = dh0.data_ptr()
+        bw.h_bwd = a.h_bwd
         nb = _lib.bwd_workspace(bw)
         wsb = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
         keep.append(wsb)
@@ -407,7 +418,9 @@ def main():
         "steps": steps, "warmup": warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if dt == torch.bfloat16 else "f32", "data": "synthetic",
-        "config": {"workload": wl + (", fwd (exact) + bwd, bf16 dq/dk/dv" if train else ""),
+        "config": {"workload": wl + ((", fwd (exact) + bwd, bf16 dq/dk/dv, states "
+                                      + ("recomputed" if args.recompute_states else "from the forward"))
+                                     if train else ""),
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "kernel_ms": stage_ms,
         "breakdown_step_ms": median_ms,  # median step of the breakdown pass (every event recorded)

@@ -57,7 +57,8 @@ def num_chunks(T, B=1, cu_seqlens=None):
 def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
                                cu_seqlens=None, output_final_state=True, *,
                                output_dtype=torch.float32, return_h=True, cp_mode="auto",
-                               cp_segment_chunks=0, cp_warmup_chunks=0, return_wu=False):
+                               cp_segment_chunks=0, cp_warmup_chunks=0, return_wu=False,
+                               return_h_bwd=False):
     """Low-level forward.  Returns ``(g_cum, A, o, h, final_state)``.
 
     g_cum [B,T,H_v] fp32 is the in-chunk cumulative log-gate; A [B,T,H_v,64]
@@ -68,7 +69,15 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     (split long sequences of few heads, with the warm-up), "auto_exact" (the same
     trigger, exact split), "off" (no split), "warmup" (split with the
     sliding-window warm-up) or "exact" (split with the exact carry).
+
+    ``return_h_bwd`` replaces h by the chunk-start states in the backward's
+    layout (uint8 [NT,H_v,4KV]: fp32 [K][V] for fp32 inputs, bf16 hi then lo
+    planes of h^T for bf16 inputs); passed to :func:`chunk_gated_delta_rule_bwd`
+    as ``h_bwd`` it saves the backward's recompute of the states.  The states
+    are then exact: "auto" splits as "auto_exact" and "warmup" is refused.
     """
+    if return_h_bwd and cp_mode == "warmup":
+        raise ValueError("return_h_bwd needs exact states: not with cp_mode='warmup'")
     _check(q, k, v, g, beta, cu_seqlens)
     q, k, v = _c(q), _c(k), _c(v)
     g, beta = _c(g, torch.float32), _c(beta, torch.float32)
@@ -87,9 +96,12 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     A = torch.empty((B, T, Hv, _lib.CHUNK), dtype=torch.float32, device=dev)
     ht = torch.empty((n_seq, Hv, K, V), dtype=torch.float32, device=dev) if output_final_state else None
     h = None
-    if return_h:
+    if return_h and not return_h_bwd:
         h = torch.empty((1 if cu is not None else B, num_chunks(T, 1, cu) if cu is not None
                          else num_chunks(T), Hv, K, V), dtype=torch.float32, device=dev)
+    if return_h_bwd:
+        h = torch.empty((num_chunks(T, 1, cu) if cu is not None else num_chunks(T, B), Hv, 4 * K * V),
+                        dtype=torch.uint8, device=dev)
     w = u = None
     if return_wu:
         w = torch.empty((B, T, Hv, K), dtype=torch.float32, device=dev)
@@ -104,7 +116,11 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     a.cp_warmup_chunks = int(cp_warmup_chunks)
     a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
     a.initial_state, a.cu_seqlens = _ptr(h0), _ptr(cu)
-    a.o, a.final_state, a.g_cum, a.A, a.h = _ptr(o), _ptr(ht), _ptr(g_cum), _ptr(A), _ptr(h)
+    a.o, a.final_state, a.g_cum, a.A = _ptr(o), _ptr(ht), _ptr(g_cum), _ptr(A)
+    if return_h_bwd:
+        a.h_bwd = _ptr(h)
+    else:
+        a.h = _ptr(h)
     a.w_out, a.u_out = _ptr(w), _ptr(u)
     nbytes = _lib.fwd_workspace(a)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -116,14 +132,16 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
 
 
 def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, initial_state=None,
-                               cu_seqlens=None, *, grad_dtype=None, cp_mode="auto", cp_segment_chunks=0):
+                               cu_seqlens=None, *, grad_dtype=None, cp_mode="auto", cp_segment_chunks=0,
+                               h_bwd=None):
     """Low-level backward.  ``g`` is the forward's g_cum, ``A`` its A.
     Returns ``(dq, dk, dv, db, dg, dh0)``; dh0 is None without initial_state.
     dq, dk, dv come in ``grad_dtype`` (default: the dtype of q), db, dg, dh0 in
     float32.  The gradients are accumulated in fp32; a bf16 dq/dk/dv adds one
     rounding of up to 2^-9 |x| per element.  ``cp_mode``: "auto" (split the
     recurrences of long sequences of few heads), "off" or "exact"; the split is
-    always exact here."""
+    always exact here.  ``h_bwd``: the forward's chunk-start states
+    (``return_h_bwd``) for the same inputs; without it they are recomputed."""
     if cp_mode not in ("auto", "auto_exact", "off", "exact"):
         raise ValueError("cp_mode of the backward: 'auto', 'auto_exact', 'off' or 'exact'")
     _check(q, k, v, g, beta, cu_seqlens)
@@ -138,6 +156,10 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
     h0 = _c(initial_state, torch.float32)
     dht = _c(dht, torch.float32)
     cu = _c(cu_seqlens)
+    if h_bwd is not None:
+        nt = num_chunks(T, 1, cu) if cu is not None else num_chunks(T, B)
+        if h_bwd.dtype != torch.uint8 or h_bwd.shape != (nt, Hv, 4 * K * V) or not h_bwd.is_contiguous():
+            raise ValueError("h_bwd must be the forward's uint8 [NT,H_v,4KV] states")
     gdt = q.dtype if grad_dtype is None else grad_dtype
     dq = torch.empty(q.shape, dtype=gdt, device=dev)
     dk = torch.empty(k.shape, dtype=gdt, device=dev)
@@ -154,6 +176,7 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
     a.scale = float(scale)
     a.q, a.k, a.v, a.g_cum, a.beta, a.A = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A)
     a.dout, a.dht, a.initial_state, a.cu_seqlens = _ptr(do), _ptr(dht), _ptr(h0), _ptr(cu)
+    a.h_bwd = _ptr(h_bwd)
     a.dq, a.dk, a.dv, a.dbeta, a.dg, a.dh0 = _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(dg), _ptr(dh0)
     nbytes = _lib.bwd_workspace(a)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -165,38 +188,42 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
 class _ChunkGDR(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
-                output_dtype, cp_mode):
+                output_dtype, cp_mode, save_states):
         # the backward differentiates the exact recurrence: when training, a split
         # (where the device model predicts a gain) is the exact one
-        if any(ctx.needs_input_grad):
+        train = any(ctx.needs_input_grad)
+        if train:
             cp_mode = "off" if cp_mode == "off" else "auto_exact"
-        g_cum, A, o, _, ht = chunk_gated_delta_rule_fwd(
+        g_cum, A, o, hb, ht = chunk_gated_delta_rule_fwd(
             q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_state=True,
-            output_dtype=output_dtype, return_h=False, cp_mode=cp_mode)
-        ctx.save_for_backward(q, k, v, g_cum, beta, A, initial_state, cu_seqlens)
+            output_dtype=output_dtype, return_h=False, cp_mode=cp_mode,
+            return_h_bwd=train and save_states)
+        ctx.save_for_backward(q, k, v, g_cum, beta, A, initial_state, cu_seqlens, hb)
         ctx.scale = scale
         ctx.g_dtype = g.dtype
         return o, (ht if output_final_state else None)
 
     @staticmethod
     def backward(ctx, do, dht):
-        q, k, v, g_cum, beta, A, h0, cu = ctx.saved_tensors
+        q, k, v, g_cum, beta, A, h0, cu, hb = ctx.saved_tensors
         dq, dk, dv, db, dg, dh0 = chunk_gated_delta_rule_bwd(
-            q, k, v, g_cum, beta, A, do, dht, ctx.scale, h0, cu)
+            q, k, v, g_cum, beta, A, do, dht, ctx.scale, h0, cu, h_bwd=hb)
         return (dq, dk, dv, dg.to(ctx.g_dtype), db.to(beta.dtype), None, dh0, None, None, None,
-                None)
+                None, None)
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
                            output_final_state=False, cu_seqlens=None, *,
-                           output_dtype=torch.float32, cp_mode="auto"):
+                           output_dtype=torch.float32, cp_mode="auto", save_states=True):
     """High-level differentiable API.  Returns ``(o, final_state)``.
 
     Without gradients the forward may split long sequences (``cp_mode``);
     when any input requires a gradient a split is the exact one, as in the
-    backward."""
+    backward.  ``save_states``: when training, keep the forward's chunk-start
+    states (4 K V bytes per chunk and v head) for the backward instead of
+    recomputing them there."""
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     o, ht = _ChunkGDR.apply(q, k, v, g, beta, scale, initial_state, output_final_state,
-                            cu_seqlens, output_dtype, cp_mode)
+                            cu_seqlens, output_dtype, cp_mode, save_states)
     return o, ht

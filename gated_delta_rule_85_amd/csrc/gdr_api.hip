@@ -86,6 +86,9 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     if (a->out_dtype != GDR_BF16 && a->out_dtype != GDR_F32) return GDR_ENOTSUP;
     if (a->cp_mode < GDR_CP_AUTO || a->cp_mode > GDR_CP_AUTO_EXACT) return GDR_EINVAL;
     if (a->cp_segment_chunks < 0 || a->cp_warmup_chunks < 0) return GDR_EINVAL;
+    // the backward's states must be exact: no warm-up split, and AUTO splits as AUTO_EXACT
+    if (a->h_bwd && (a->h || a->cp_mode == GDR_CP_WARMUP)) return GDR_EINVAL;
+    const int32_t cp_mode = a->h_bwd && a->cp_mode == GDR_CP_AUTO ? GDR_CP_AUTO_EXACT : a->cp_mode;
     pl.n_seq = varlen ? a->n_seq : a->B;
     pl.tokens = a->B * a->T;
     pl.nct = cdiv(a->T, GDR_CHUNK);
@@ -100,10 +103,10 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     const int64_t bh = pl.n_seq * a->H_v;
     // GDR_CP_AUTO: the pages' trigger (warm-up split); GDR_CP_AUTO_EXACT: the device
     // model alone decides (the exact split costs no accuracy)
-    const bool autom = a->cp_mode == GDR_CP_AUTO || a->cp_mode == GDR_CP_AUTO_EXACT;
-    const bool exact_mode = a->cp_mode == GDR_CP_EXACT || a->cp_mode == GDR_CP_AUTO_EXACT;
-    bool split = a->cp_mode == GDR_CP_WARMUP || exact_mode ||
-                 (a->cp_mode == GDR_CP_AUTO && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
+    const bool autom = cp_mode == GDR_CP_AUTO || cp_mode == GDR_CP_AUTO_EXACT;
+    const bool exact_mode = cp_mode == GDR_CP_EXACT || cp_mode == GDR_CP_AUTO_EXACT;
+    bool split = cp_mode == GDR_CP_WARMUP || exact_mode ||
+                 (cp_mode == GDR_CP_AUTO && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
     pl.warm_chunks = a->cp_warmup_chunks > 0 ? a->cp_warmup_chunks : 8;
     const int64_t n_vt = a->V / scan_vtile(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32, (int)a->K, (int)a->V);
     int64_t L = a->cp_segment_chunks > 0
@@ -149,7 +152,8 @@ struct BwdPlan {
     bool split;
 };
 
-// workspace: [chunk offsets] | T blocks | chunk-start states | chunk-end state gradients
+// workspace: [chunk offsets] | T blocks | chunk-start states (unless the forward's
+// h_bwd is given) | chunk-end state gradients
 int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl, int64_t slots = 0) {
     if (!a) return GDR_EINVAL;
     const bool varlen = a->cu_seqlens != nullptr;
@@ -171,7 +175,7 @@ int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl, int64_t slots = 0) {
     pl.off_tblk = off;
     off += up(tblock_bytes(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32) * nb);
     pl.off_hs = off;
-    off += up(sizeof(float) * nb * (size_t)(a->K * a->V));
+    if (!a->h_bwd) off += up(sizeof(float) * nb * (size_t)(a->K * a->V));  // else the forward's
     pl.off_dhs = off;
     off += up(sizeof(float) * nb * (size_t)(a->K * a->V));
     pl.total = pl.tokens > 0 ? off : pl.off_tblk;
@@ -264,7 +268,7 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
     if ((a->A && !aligned(a->A, 16)) || (a->g_cum && !aligned(a->g_cum, 4)) ||
         (a->h && !aligned(a->h, 16)) || (a->final_state && !aligned(a->final_state, 16)) ||
         (a->initial_state && !aligned(a->initial_state, 16)) || (a->w_out && !aligned(a->w_out, 16)) ||
-        (a->u_out && !aligned(a->u_out, 16)))
+        (a->u_out && !aligned(a->u_out, 16)) || (a->h_bwd && !aligned(a->h_bwd, 16)))
         return GDR_EINVAL;
     if (a->workspace_bytes < pl.total || (pl.total > 0 && !a->workspace)) return GDR_EWORKSPACE;
     if (pl.total > 0 && !aligned(a->workspace, 16)) return GDR_EINVAL;
@@ -311,8 +315,9 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
     sp.h0 = a->initial_state;
     sp.o = a->o;
     sp.hT = a->final_state;
-    sp.hsnap = a->h;
-    sp.hsnap_split = 0;
+    // chunk-start states: h, or h_bwd in the backward's layout (bf16: split planes of h^T)
+    sp.hsnap = a->h_bwd ? static_cast<float *>(a->h_bwd) : a->h;
+    sp.hsnap_split = a->h_bwd && dt == Dt::BF16;
     sp.sm = sm;
     sp.Hq = (int)a->H_q;
     sp.Hv = (int)a->H_v;
@@ -411,7 +416,7 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
             return GDR_EINVAL;
     }
     if ((a->dht && !aligned(a->dht, 16)) || (a->initial_state && !aligned(a->initial_state, 16)) ||
-        (a->dh0 && !aligned(a->dh0, 16)))
+        (a->dh0 && !aligned(a->dh0, 16)) || (a->h_bwd && !aligned(a->h_bwd, 16)))
         return GDR_EINVAL;
     if (a->workspace_bytes < pl.total || (pl.total > 0 && !a->workspace)) return GDR_EWORKSPACE;
     if (pl.total > 0 && !aligned(a->workspace, 16)) return GDR_EINVAL;
@@ -439,7 +444,7 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
     bp.A = a->A;
     bp.dht = a->dht;
     bp.tblk = ws + pl.off_tblk;
-    bp.hs = reinterpret_cast<float *>(ws + pl.off_hs);
+    bp.hs = a->h_bwd ? static_cast<const float *>(a->h_bwd) : reinterpret_cast<float *>(ws + pl.off_hs);
     bp.dhs = reinterpret_cast<float *>(ws + pl.off_dhs);
     bp.dq = a->dq;
     bp.dk = a->dk;
@@ -466,7 +471,7 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
     if (!mark(0)) return GDR_ELAUNCH;
     if (pl.tokens > 0 && launch_tblocks(dt, bp, (int)pl.nt_ub, stream) != hipSuccess) return GDR_ELAUNCH;
     if (!mark(1) || !mark(2)) return GDR_ELAUNCH;
-    if (pl.tokens > 0) {
+    if (pl.tokens > 0 && !a->h_bwd) {
         // chunk-start states: the exact forward scan without its output
         ScanParams sp;
         sp.q = a->q;
@@ -527,6 +532,34 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
             sp.h0_seg = cp.h0_seg;
         }
         if (launch_scan_states(dt, (int)a->K, sp, stream) != hipSuccess) return GDR_ELAUNCH;
+    } else if (pl.tokens > 0 && pl.split) {
+        // states from the forward: the reverse carry still needs the segment transitions
+        ScanParams tp;
+        tp.q = a->q;
+        tp.k = a->k;
+        tp.v = ws + pl.off_zero;
+        tp.v_tok = tp.v_head = 0;
+        tp.h0_seg = nullptr;
+        tp.hT_seg = reinterpret_cast<float *>(ws + pl.off_M);
+        tp.eye_h0 = 1;
+        tp.tblk = bp.tblk;
+        tp.h0 = nullptr;
+        tp.o = nullptr;
+        tp.hT = nullptr;
+        tp.hsnap = nullptr;
+        tp.hsnap_split = 0;
+        tp.sm = sm;
+        tp.Hq = (int)a->H_q;
+        tp.Hv = (int)a->H_v;
+        tp.V = (int)a->K;
+        tp.scale = a->scale;
+        tp.seg_chunks = pl.seg_chunks;
+        tp.warm_chunks = 0;
+        tp.n_vt = (int)(a->K / scan_vtile(dt, (int)a->K, (int)a->K));
+        tp.n_units = n_units;
+        tp.n_seg = pl.n_seg;
+        if (launch_fill_zero(ws + pl.off_zero, 512, stream) != hipSuccess) return GDR_ELAUNCH;
+        if (launch_scan_states(dt, (int)a->K, tp, stream) != hipSuccess) return GDR_ELAUNCH;
     }
     if (!mark(3) || !mark(4)) return GDR_ELAUNCH;
     if (pl.split) {

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 3
+#define GDR_ABI_VERSION 4
 #define GDR_CHUNK 64
 #define GDR_FWD_STAGES 3
 #define GDR_BWD_STAGES 4
@@ -99,6 +99,13 @@ typedef struct {
                                    zero past the chunk end; NULL = kept in workspace */
     float *h;                   /* [NT,H_v,K,V] chunk-start states (NT = sum of ceil(len/64));
                                    NULL = not written */
+    void *h_bwd;                /* [NT,H_v] chunk-start states in the backward's layout, 4 K V
+                                   bytes each: fp32 [K][V] for fp32 inputs, for bf16 inputs
+                                   bf16 hi then lo planes of h^T [V][K]; passed on as
+                                   gdr_bwd_args.h_bwd, it saves the backward's recompute of
+                                   the states.  NULL = not written.  The states must be
+                                   exact: with h_bwd, GDR_CP_AUTO splits as
+                                   GDR_CP_AUTO_EXACT, and h or GDR_CP_WARMUP is GDR_EINVAL */
     float *w_out;               /* [B,T,H_v,K] W = T diag(beta e^g_cum) K, NULL = not computed */
     float *u_out;               /* [B,T,H_v,V] U = T diag(beta) V, NULL = not computed */
     /* timing hook: NULL, or a HOST array of 2*GDR_FWD_STAGES events that are
@@ -130,6 +137,8 @@ typedef struct {
     const float *dht;           /* [N,H_v,K,V] gradient of final_state; NULL = zeros */
     const float *initial_state; /* [N,H_v,K,V] or NULL */
     const int32_t *cu_seqlens;  /* [n_seq+1] or NULL */
+    const void *h_bwd;          /* the forward's h_bwd for the same inputs, or NULL (the states
+                                   are then recomputed) */
     void *dq, *dk;              /* [B,T,H_q,K] grad_dtype, summed over the v heads of each q/k head */
     void *dv;                   /* [B,T,H_v,V] grad_dtype */
     float *dbeta;               /* [B,T,H_v] gradient w.r.t. beta */

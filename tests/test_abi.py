@@ -132,6 +132,22 @@ def test_fwd_host_errors_before_any_launch(L):
         L.fwd_workspace(fwd_args(L, K=48))
 
 
+def test_forward_states_for_the_backward(L):
+    """h_bwd (the chunk-start states in the backward's layout) must be exact: with it
+    AUTO plans as AUTO_EXACT; with h or the warm-up split it is refused."""
+    long = dict(T=4096, H_q=1, H_v=1)
+    rc, n_auto = rc_ws(L, fwd_args(L, **long))
+    rc2, n_exact = rc_ws(L, fwd_args(L, cp_mode=L.CP_AUTO_EXACT, **long))
+    rc3, n_hb = rc_ws(L, fwd_args(L, h_bwd=16, **long))
+    assert rc == rc2 == rc3 == 0
+    assert n_hb == n_exact > n_auto  # the exact split's transitions and states
+    assert rc_ws(L, fwd_args(L, h_bwd=16, h=16))[0] == L.EINVAL
+    assert rc_ws(L, fwd_args(L, h_bwd=16, cp_mode=L.CP_WARMUP))[0] == L.EINVAL
+    a = fwd_args(L, q=16, k=16, v=16, g=16, beta=16, o=16, h_bwd=24, workspace=4096,
+                 workspace_bytes=1 << 30)
+    assert L.lib.gdr_fwd(ctypes.byref(a), None) == L.EINVAL  # misaligned h_bwd
+
+
 def bwd_args(L, **kw):
     a = L.BwdArgs()
     a.B, a.T, a.H_q, a.H_v, a.K, a.V, a.n_seq = 1, 256, 2, 4, 128, 128, 0
@@ -154,6 +170,10 @@ def test_bwd_workspace_sizes(L):
     seg = 4 * 4 * 128 * 4
     split = 4 * 4 * per + seg * 128 + 4 * seg * 128 + 512
     assert L.bwd_workspace(bwd_args(L, cp_mode=L.CP_EXACT)) == split
+    # the forward's states (h_bwd) replace the workspace's chunk-start states
+    states = 4 * 4 * 4 * 128 * 128
+    assert L.bwd_workspace(bwd_args(L, h_bwd=16)) == 4 * 4 * per - states
+    assert L.bwd_workspace(bwd_args(L, h_bwd=16, cp_mode=L.CP_EXACT)) == split - states
 
 
 @pytest.mark.parametrize("kw,code", [

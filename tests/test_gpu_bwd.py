@@ -25,13 +25,19 @@ pytestmark = pytest.mark.gpu
 NAMES = ("dq", "dk", "dv", "dbeta", "dg", "dh0")
 
 
-def run_bwd(x, with_dht=True, grad_dtype=torch.float32, **kw):
+def run_bwd(x, with_dht=True, grad_dtype=torch.float32, fwd_states=False, fwd_cp="off",
+            fwd_seg=0, **kw):
+    """The forward (g_cum, A; with fwd_states also its chunk-start states in the
+    backward's layout, split as fwd_cp / fwd_seg), then the backward."""
     from gated_delta_rule_85_amd import chunk_gated_delta_rule_bwd, chunk_gated_delta_rule_fwd
     d = gpu_inputs(x)
     dt = d["q"].dtype
-    g_cum, A, _, _, _ = chunk_gated_delta_rule_fwd(
+    g_cum, A, _, hb, _ = chunk_gated_delta_rule_fwd(
         d["q"], d["k"], d["v"], d["g"], d["beta"], x["scale"], d["initial_state"],
-        d["cu_seqlens"], output_final_state=False, return_h=False, cp_mode="off")
+        d["cu_seqlens"], output_final_state=False, return_h=False, cp_mode=fwd_cp,
+        cp_segment_chunks=fwd_seg, return_h_bwd=fwd_states)
+    if fwd_states:
+        kw["h_bwd"] = hb
     do = dev(x["do"], dt)
     dht = dev(x["dht"]) if with_dht else None
     out = chunk_gated_delta_rule_bwd(d["q"], d["k"], d["v"], g_cum, d["beta"], A, do, dht,
@@ -92,6 +98,44 @@ def test_exact_split_backward(shape, L):
     x = make_inputs(shape, seed=12, grads=True)
     print(shape, "segments of", L, flush=True)
     compare(x, run_bwd(x, cp_mode="exact", cp_segment_chunks=L), ora_bwd(x))
+
+
+@pytest.mark.parametrize("shape,fwd_cp,fwd_seg,bwd_cp,bwd_seg", [
+    (dict(B=2, T=300, Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True), "off", 0, "off", 0),
+    (dict(B=3, T=77, Hq=1, Hv=2, K=64, V=64, dtype="fp32", h0=True), "off", 0, "off", 0),
+    (dict(B=1, T=200, Hq=1, Hv=1, K=64, V=128, dtype="bf16", h0=False), "off", 0, "off", 0),
+    (dict(B=1, T=64 * 9 + 30, Hq=1, Hv=2, K=128, V=64, dtype="fp32", h0=True), "exact", 2, "exact", 3),
+    (dict(B=2, T=64 * 7, Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True), "exact", 3, "exact", 2),
+    (dict(lens=[400, 0, 65, 300, 1], Hq=1, Hv=2, K=64, V=128, dtype="bf16", h0=True), "off", 0, "exact", 2),
+    (dict(lens=[2300, 1, 0, 700, 129, 64], Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True),
+     "auto", 0, "auto", 0),
+])
+def test_backward_with_forward_states(shape, fwd_cp, fwd_seg, bwd_cp, bwd_seg):
+    """The forward hands its chunk-start states (h_bwd) to the backward, which then
+    skips its own states pass (with a split it still forms the transitions for the
+    reverse carry).  Every gradient element against the oracle, and against the
+    backward that recomputes the states (same bar)."""
+    x = make_inputs(shape, seed=16, grads=True)
+    print(shape, fwd_cp, fwd_seg, bwd_cp, bwd_seg, flush=True)
+    ref = ora_bwd(x)
+    got = run_bwd(x, fwd_states=True, fwd_cp=fwd_cp, fwd_seg=fwd_seg, cp_mode=bwd_cp,
+                  cp_segment_chunks=bwd_seg)
+    compare(x, got, ref)
+    own = run_bwd(x, cp_mode=bwd_cp, cp_segment_chunks=bwd_seg)
+    t = tol(x)
+    for n in NAMES:
+        if got[n] is not None:
+            e = rel(host(got[n]), host(own[n]).astype(np.float64))
+            assert e <= t, (n, e)
+
+
+def test_forward_states_refused_with_warmup_split():
+    from gated_delta_rule_85_amd import chunk_gated_delta_rule_fwd
+    x = make_inputs(dict(B=1, T=256, Hq=1, Hv=1, K=64, V=64, dtype="fp32", h0=False), seed=1)
+    d = gpu_inputs(x)
+    with pytest.raises(ValueError):
+        chunk_gated_delta_rule_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], x["scale"],
+                                   cp_mode="warmup", return_h_bwd=True)
 
 
 def test_exact_split_backward_non_decaying_head():
