@@ -15,11 +15,11 @@ roofline entry.  The fp64 CPU oracle is timed on a bounded
 sample of the same workload for the cpu_baseline entry.
 
 ``--workload training`` instead times one training step of the operator:
-gdr_fwd (exact scan, writing the g_cum and A the backward needs, and its
-chunk-start states in the backward's layout) followed by gdr_bwd (dq, dk, dv in
-bf16; dbeta, dg, dh0 in fp32) at B=8, T=4096, H_q=32, H_v=64, K=V=128, with
-upstream gradients do and dht (``--recompute-states``: the backward recomputes
-the states instead).
+gdr_fwd (exact scan, handing the backward its chunk-start states and T blocks)
+followed by gdr_bwd (dq, dk, dv in bf16; dbeta, dg, dh0 in fp32) at B=8,
+T=4096, H_q=32, H_v=64, K=V=128, with upstream gradients do and dht
+(``--recompute-states``: the forward writes g_cum and A instead, from which the
+backward rebuilds the T blocks and recomputes the states).
 
 Prints one JSON line.
 """
@@ -279,16 +279,18 @@ def main():
     a.cu_seqlens = None if cu is None else cu.data_ptr()
     a.o, a.final_state = o.data_ptr(), ht.data_ptr()
     if train:  # the forward keeps what the backward reads
-        g_cum = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
-        A = torch.empty((B, T, Hv, 64), dtype=torch.float32, device=dev)
-        keep += [g_cum, A]
-        a.g_cum, a.A = g_cum.data_ptr(), A.data_ptr()
-        if not args.recompute_states:
+        if args.recompute_states or dt != torch.bfloat16:  # T blocks rebuilt from g_cum and A
+            g_cum = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
+            A = torch.empty((B, T, Hv, 64), dtype=torch.float32, device=dev)
+            keep += [g_cum, A]
+            a.g_cum, a.A = g_cum.data_ptr(), A.data_ptr()
+        if not args.recompute_states:  # chunk-start states and T blocks handed over
             n_chunks = B * ((T + 63) // 64) if cu is None else \
                 int(((cu[1:] - cu[:-1]).cpu().long().add(63) // 64).sum())
             hb = torch.empty((n_chunks, Hv, 4 * K * V), dtype=torch.uint8, device=dev)
-            keep.append(hb)
-            a.h_bwd = hb.data_ptr()
+            tb = torch.empty(max(_lib.tblocks_bytes(a), 1), dtype=torch.uint8, device=dev)
+            keep += [hb, tb]
+            a.h_bwd, a.tblk_bwd = hb.data_ptr(), tb.data_ptr()
     nbytes = _lib.fwd_workspace(a)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
@@ -312,7 +314,7 @@ def main():
         bw.dq, bw.dk, bw.dv, bw.dbeta, bw.dg = dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), \
             db.data_ptr(), dg.data_ptr()
         bw.dh0 = dh0.data_ptr()
-        bw.h_bwd = a.h_bwd
+        bw.h_bwd, bw.tblk_bwd = a.h_bwd, a.tblk_bwd
         nb = _lib.bwd_workspace(bw)
         wsb = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
         keep.append(wsb)
@@ -419,7 +421,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if dt == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": wl + ((", fwd (exact) + bwd, bf16 dq/dk/dv, states "
-                                      + ("recomputed" if args.recompute_states else "from the forward"))
+                                      + ("recomputed" if args.recompute_states else "and T blocks from the forward"))
                                      if train else ""),
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "kernel_ms": stage_ms,

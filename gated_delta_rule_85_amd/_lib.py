@@ -10,7 +10,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 CHUNK = 64
 FWD_STAGES = 3
 BWD_STAGES = 4
@@ -33,7 +33,7 @@ class FwdArgs(ctypes.Structure):
         ("cp_mode", _i32), ("cp_segment_chunks", _i32), ("cp_warmup_chunks", _i32),
         ("q", _p), ("k", _p), ("v", _p), ("g", _p), ("beta", _p), ("initial_state", _p),
         ("cu_seqlens", _p),
-        ("o", _p), ("final_state", _p), ("g_cum", _p), ("A", _p), ("h", _p), ("h_bwd", _p),
+        ("o", _p), ("final_state", _p), ("g_cum", _p), ("A", _p), ("h", _p), ("h_bwd", _p), ("tblk_bwd", _p),
         ("w_out", _p), ("u_out", _p), ("events", _p),
         ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
     ]
@@ -47,7 +47,7 @@ class BwdArgs(ctypes.Structure):
         ("dtype", _i32), ("grad_dtype", _i32), ("cp_mode", _i32), ("cp_segment_chunks", _i32),
         ("scale", ctypes.c_float),
         ("q", _p), ("k", _p), ("v", _p), ("g_cum", _p), ("beta", _p), ("A", _p),
-        ("dout", _p), ("dht", _p), ("initial_state", _p), ("cu_seqlens", _p), ("h_bwd", _p),
+        ("dout", _p), ("dht", _p), ("initial_state", _p), ("cu_seqlens", _p), ("h_bwd", _p), ("tblk_bwd", _p),
         ("dq", _p), ("dk", _p), ("dv", _p), ("dbeta", _p), ("dg", _p), ("dh0", _p),
         ("events", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
     ]
@@ -70,6 +70,8 @@ def _load():
         fw = getattr(lib, name + "_workspace")
         fw.restype = ctypes.c_int
         fw.argtypes = [ctypes.POINTER(st), ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_tblocks_bytes.restype = ctypes.c_int
+    lib.gdr_tblocks_bytes.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(ctypes.c_size_t)]
     if lib.gdr_abi_version() != ABI_VERSION:
         raise ImportError("libgdr ABI version %d, binding expects %d"
                           % (lib.gdr_abi_version(), ABI_VERSION))
@@ -98,6 +100,14 @@ def fwd_workspace(args):
     rc = lib.gdr_fwd_workspace(ctypes.byref(args), ctypes.byref(n))
     if rc:
         raise GdrError("gdr_fwd_workspace", rc)
+    return n.value
+
+
+def tblocks_bytes(args):
+    n = ctypes.c_size_t(0)
+    rc = lib.gdr_tblocks_bytes(ctypes.byref(args), ctypes.byref(n))
+    if rc:
+        raise GdrError("gdr_tblocks_bytes", rc)
     return n.value
 
 

@@ -10,6 +10,7 @@ operator accumulates in fp32 and a bf16 ``o`` would add a rounding of up to
 2^-8 |o| per element (``output_dtype=torch.bfloat16`` selects it).
 """
 import math
+from typing import NamedTuple
 
 import torch
 
@@ -18,6 +19,15 @@ from . import _lib
 _DT = {torch.bfloat16: _lib.BF16, torch.float32: _lib.F32}
 _CP = {"auto": _lib.CP_AUTO, "off": _lib.CP_OFF, "warmup": _lib.CP_WARMUP, "exact": _lib.CP_EXACT,
        "auto_exact": _lib.CP_AUTO_EXACT}
+
+
+class SavedForBackward(NamedTuple):
+    """What the forward hands the backward (``return_h_bwd``): the chunk-start
+    states in the backward's layout (uint8 [NT,H_v,4KV]: fp32 [K][V] for fp32
+    inputs, bf16 hi then lo planes of h^T for bf16 inputs) and the T blocks
+    (uint8, one 17,408-byte block per chunk and v head for bf16 inputs)."""
+    states: torch.Tensor
+    tblocks: torch.Tensor
 
 
 def _ptr(t):
@@ -30,7 +40,7 @@ def _check(q, k, v, g, beta, cu_seqlens):
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share one dtype, bfloat16 or float32")
     B, T, Hv = v.shape[0], v.shape[1], v.shape[2]
-    if g.shape != (B, T, Hv) or beta.shape != (B, T, Hv):
+    if (g is not None and g.shape != (B, T, Hv)) or beta.shape != (B, T, Hv):
         raise ValueError("g and beta must be [B,T,H_v]")
     if not q.is_cuda:
         raise ValueError("inputs must be on the GPU")
@@ -58,7 +68,7 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
                                cu_seqlens=None, output_final_state=True, *,
                                output_dtype=torch.float32, return_h=True, cp_mode="auto",
                                cp_segment_chunks=0, cp_warmup_chunks=0, return_wu=False,
-                               return_h_bwd=False):
+                               return_h_bwd=False, return_ga=True):
     """Low-level forward.  Returns ``(g_cum, A, o, h, final_state)``.
 
     g_cum [B,T,H_v] fp32 is the in-chunk cumulative log-gate; A [B,T,H_v,64]
@@ -70,11 +80,14 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     trigger, exact split), "off" (no split), "warmup" (split with the
     sliding-window warm-up) or "exact" (split with the exact carry).
 
-    ``return_h_bwd`` replaces h by the chunk-start states in the backward's
-    layout (uint8 [NT,H_v,4KV]: fp32 [K][V] for fp32 inputs, bf16 hi then lo
-    planes of h^T for bf16 inputs); passed to :func:`chunk_gated_delta_rule_bwd`
-    as ``h_bwd`` it saves the backward's recompute of the states.  The states
-    are then exact: "auto" splits as "auto_exact" and "warmup" is refused.
+    ``return_h_bwd`` replaces h by a :class:`SavedForBackward` (the chunk-start
+    states in the backward's layout and the T blocks); passed to
+    :func:`chunk_gated_delta_rule_bwd` as ``h_bwd`` it saves the backward's
+    recompute of the states and rebuild of the T blocks (a ``tblocks`` of None
+    there has them rebuilt from g_cum and A).  The states are then
+    exact: "auto" splits as "auto_exact" and "warmup" is refused.  With
+    ``return_ga=False`` g_cum and A are not written (None): a bf16 backward
+    given ``h_bwd`` does not read them.
     """
     if return_h_bwd and cp_mode == "warmup":
         raise ValueError("return_h_bwd needs exact states: not with cp_mode='warmup'")
@@ -92,8 +105,10 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
         raise ValueError("initial_state must be [N,H_v,K,V]")
     cu = _c(cu_seqlens)
     o = torch.empty((B, T, Hv, V), dtype=output_dtype, device=dev)
-    g_cum = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
-    A = torch.empty((B, T, Hv, _lib.CHUNK), dtype=torch.float32, device=dev)
+    g_cum = A = None
+    if return_ga:
+        g_cum = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
+        A = torch.empty((B, T, Hv, _lib.CHUNK), dtype=torch.float32, device=dev)
     ht = torch.empty((n_seq, Hv, K, V), dtype=torch.float32, device=dev) if output_final_state else None
     h = None
     if return_h and not return_h_bwd:
@@ -118,7 +133,9 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     a.initial_state, a.cu_seqlens = _ptr(h0), _ptr(cu)
     a.o, a.final_state, a.g_cum, a.A = _ptr(o), _ptr(ht), _ptr(g_cum), _ptr(A)
     if return_h_bwd:
-        a.h_bwd = _ptr(h)
+        tb = torch.empty(max(_lib.tblocks_bytes(a), 1), dtype=torch.uint8, device=dev)
+        h = SavedForBackward(h, tb)
+        a.h_bwd, a.tblk_bwd = _ptr(h.states), _ptr(tb)
     else:
         a.h = _ptr(h)
     a.w_out, a.u_out = _ptr(w), _ptr(u)
@@ -140,11 +157,15 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
     float32.  The gradients are accumulated in fp32; a bf16 dq/dk/dv adds one
     rounding of up to 2^-9 |x| per element.  ``cp_mode``: "auto" (split the
     recurrences of long sequences of few heads), "off" or "exact"; the split is
-    always exact here.  ``h_bwd``: the forward's chunk-start states
-    (``return_h_bwd``) for the same inputs; without it they are recomputed."""
+    always exact here.  ``h_bwd``: the forward's :class:`SavedForBackward`
+    (``return_h_bwd``) for the same inputs; without it the chunk-start states
+    are recomputed and the T blocks rebuilt from ``g`` and ``A``, which with it
+    and bf16 inputs may be None."""
     if cp_mode not in ("auto", "auto_exact", "off", "exact"):
         raise ValueError("cp_mode of the backward: 'auto', 'auto_exact', 'off' or 'exact'")
     _check(q, k, v, g, beta, cu_seqlens)
+    if (g is None or A is None) and (h_bwd is None or h_bwd.tblocks is None or q.dtype != torch.bfloat16):
+        raise ValueError("g_cum and A are needed unless h_bwd (with T blocks) is given with bf16 inputs")
     q, k, v, do = _c(q), _c(k), _c(v), _c(do, q.dtype)
     g, beta, A = _c(g, torch.float32), _c(beta, torch.float32), _c(A, torch.float32)
     B, T, Hq, K = q.shape
@@ -158,8 +179,9 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
     cu = _c(cu_seqlens)
     if h_bwd is not None:
         nt = num_chunks(T, 1, cu) if cu is not None else num_chunks(T, B)
-        if h_bwd.dtype != torch.uint8 or h_bwd.shape != (nt, Hv, 4 * K * V) or not h_bwd.is_contiguous():
-            raise ValueError("h_bwd must be the forward's uint8 [NT,H_v,4KV] states")
+        st, tb = h_bwd
+        if st.dtype != torch.uint8 or st.shape != (nt, Hv, 4 * K * V) or not st.is_contiguous():
+            raise ValueError("h_bwd.states must be the forward's uint8 [NT,H_v,4KV] states")
     gdt = q.dtype if grad_dtype is None else grad_dtype
     dq = torch.empty(q.shape, dtype=gdt, device=dev)
     dk = torch.empty(k.shape, dtype=gdt, device=dev)
@@ -176,7 +198,15 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
     a.scale = float(scale)
     a.q, a.k, a.v, a.g_cum, a.beta, a.A = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A)
     a.dout, a.dht, a.initial_state, a.cu_seqlens = _ptr(do), _ptr(dht), _ptr(h0), _ptr(cu)
-    a.h_bwd = _ptr(h_bwd)
+    if h_bwd is not None:
+        a.h_bwd, a.tblk_bwd = _ptr(h_bwd.states), _ptr(h_bwd.tblocks)
+        if h_bwd.tblocks is not None:  # None: rebuilt from g and A
+            fa = _lib.FwdArgs()
+            fa.B, fa.T, fa.H_q, fa.H_v, fa.K, fa.V, fa.n_seq = B, T, Hq, Hv, K, V, n_seq
+            fa.dtype, fa.out_dtype = a.dtype, _lib.F32
+            fa.cu_seqlens = a.cu_seqlens
+            if h_bwd.tblocks.dtype != torch.uint8 or h_bwd.tblocks.numel() < _lib.tblocks_bytes(fa):
+                raise ValueError("h_bwd.tblocks must be the forward's T blocks")
     a.dq, a.dk, a.dv, a.dbeta, a.dg, a.dh0 = _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(dg), _ptr(dh0)
     nbytes = _lib.bwd_workspace(a)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -194,20 +224,24 @@ class _ChunkGDR(torch.autograd.Function):
         train = any(ctx.needs_input_grad)
         if train:
             cp_mode = "off" if cp_mode == "off" else "auto_exact"
+        saved = train and save_states
+        # a bf16 backward given the forward's T blocks reads neither g_cum nor A
         g_cum, A, o, hb, ht = chunk_gated_delta_rule_fwd(
             q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_state=True,
             output_dtype=output_dtype, return_h=False, cp_mode=cp_mode,
-            return_h_bwd=train and save_states)
-        ctx.save_for_backward(q, k, v, g_cum, beta, A, initial_state, cu_seqlens, hb)
+            return_h_bwd=saved, return_ga=not (saved and q.dtype == torch.bfloat16))
+        hs, tb = hb if saved else (None, None)
+        ctx.save_for_backward(q, k, v, g_cum, beta, A, initial_state, cu_seqlens, hs, tb)
         ctx.scale = scale
         ctx.g_dtype = g.dtype
         return o, (ht if output_final_state else None)
 
     @staticmethod
     def backward(ctx, do, dht):
-        q, k, v, g_cum, beta, A, h0, cu, hb = ctx.saved_tensors
+        q, k, v, g_cum, beta, A, h0, cu, hs, tb = ctx.saved_tensors
         dq, dk, dv, db, dg, dh0 = chunk_gated_delta_rule_bwd(
-            q, k, v, g_cum, beta, A, do, dht, ctx.scale, h0, cu, h_bwd=hb)
+            q, k, v, g_cum, beta, A, do, dht, ctx.scale, h0, cu,
+            h_bwd=None if hs is None else SavedForBackward(hs, tb))
         return (dq, dk, dv, dg.to(ctx.g_dtype), db.to(beta.dtype), None, dh0, None, None, None,
                 None, None)
 
@@ -220,8 +254,9 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
     Without gradients the forward may split long sequences (``cp_mode``);
     when any input requires a gradient a split is the exact one, as in the
     backward.  ``save_states``: when training, keep the forward's chunk-start
-    states (4 K V bytes per chunk and v head) for the backward instead of
-    recomputing them there."""
+    states (4 K V bytes per chunk and v head) and T blocks for the backward
+    instead of recomputing them there (for bf16 inputs g_cum and A are then
+    not kept)."""
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     o, ht = _ChunkGDR.apply(q, k, v, g, beta, scale, initial_state, output_final_state,

@@ -30,6 +30,7 @@ size_t seq_table_bytes(bool varlen, int64_t n_seq) {
 struct FwdPlan {
     int64_t n_seq, tokens, nct, nt_ub;  // nct: chunks per sequence bound
     size_t off_chunk, off_tblk, total;
+    size_t tblk_bytes;  // the T blocks (and, for tblk_bwd, their copy in the backward's order)
     // exact split: segment transitions, zero-start end states, true start states, a zero row
     size_t off_M, off_b, off_hseg, off_zero;
     int seg_chunks, warm_chunks, n_seg;
@@ -97,7 +98,8 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     pl.off_chunk = off;
     off += seq_table_bytes(varlen, pl.n_seq);
     pl.off_tblk = off;
-    off += up(tblock_bytes(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32) * (size_t)(pl.nt_ub * a->H_v));
+    pl.tblk_bytes = up(tblock_bytes(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32) * (size_t)(pl.nt_ub * a->H_v));
+    off += pl.tblk_bytes;
     pl.total = off;
     // sequence split ("AutoCP"): the pages' trigger on batch x heads and length
     const int64_t bh = pl.n_seq * a->H_v;
@@ -152,8 +154,8 @@ struct BwdPlan {
     bool split;
 };
 
-// workspace: [chunk offsets] | T blocks | chunk-start states (unless the forward's
-// h_bwd is given) | chunk-end state gradients
+// workspace: [chunk offsets] | T blocks | chunk-start states | chunk-end state
+// gradients (T blocks and states only where the forward's are not given)
 int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl, int64_t slots = 0) {
     if (!a) return GDR_EINVAL;
     const bool varlen = a->cu_seqlens != nullptr;
@@ -173,7 +175,7 @@ int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl, int64_t slots = 0) {
     pl.off_chunk = off;
     off += seq_table_bytes(varlen, pl.n_seq);
     pl.off_tblk = off;
-    off += up(tblock_bytes(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32) * nb);
+    if (!a->tblk_bwd) off += up(tblock_bytes(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32) * nb);  // else the forward's
     pl.off_hs = off;
     if (!a->h_bwd) off += up(sizeof(float) * nb * (size_t)(a->K * a->V));  // else the forward's
     pl.off_dhs = off;
@@ -252,6 +254,15 @@ int gdr_fwd_workspace(const gdr_fwd_args *a, size_t *bytes) {
     return GDR_OK;
 }
 
+int gdr_tblocks_bytes(const gdr_fwd_args *a, size_t *bytes) {
+    if (!bytes) return GDR_EINVAL;
+    FwdPlan pl;
+    int rc = plan_fwd(a, pl, DEFAULT_SLOTS);
+    if (rc) return rc;
+    *bytes = pl.tokens > 0 ? pl.tblk_bytes : 0;
+    return GDR_OK;
+}
+
 int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
     // host-side checks come first; the device query is needed only to launch
     int dev = 0;
@@ -268,7 +279,8 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
     if ((a->A && !aligned(a->A, 16)) || (a->g_cum && !aligned(a->g_cum, 4)) ||
         (a->h && !aligned(a->h, 16)) || (a->final_state && !aligned(a->final_state, 16)) ||
         (a->initial_state && !aligned(a->initial_state, 16)) || (a->w_out && !aligned(a->w_out, 16)) ||
-        (a->u_out && !aligned(a->u_out, 16)) || (a->h_bwd && !aligned(a->h_bwd, 16)))
+        (a->u_out && !aligned(a->u_out, 16)) || (a->h_bwd && !aligned(a->h_bwd, 16)) ||
+        (a->tblk_bwd && !aligned(a->tblk_bwd, 16)))
         return GDR_EINVAL;
     if (a->workspace_bytes < pl.total || (pl.total > 0 && !a->workspace)) return GDR_EWORKSPACE;
     if (pl.total > 0 && !aligned(a->workspace, 16)) return GDR_EINVAL;
@@ -296,6 +308,7 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
         pp.g_cum = a->g_cum;
         pp.Tm = a->A;
         pp.tblk = tblk;
+        pp.tblk_bwd = static_cast<char *>(a->tblk_bwd);
         pp.sm = sm;
         pp.Hq = (int)a->H_q;
         pp.Hv = (int)a->H_v;
@@ -407,12 +420,15 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
     int rc = plan_bwd(a, pl, slots);
     if (rc) return rc;
     if (pl.tokens > 0) {
-        if (!a->q || !a->k || !a->v || !a->g_cum || !a->beta || !a->A || !a->dout || !a->dq || !a->dk ||
-            !a->dv || !a->dbeta || !a->dg)
+        // the bf16 kernels read A and g_cum only to rebuild the T blocks
+        const bool need_ga = !a->tblk_bwd || a->dtype != GDR_BF16;
+        if (!a->q || !a->k || !a->v || (need_ga && (!a->g_cum || !a->A)) || !a->beta || !a->dout || !a->dq ||
+            !a->dk || !a->dv || !a->dbeta || !a->dg)
             return GDR_EINVAL;
         if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->dout, 16) ||
             !aligned(a->A, 16) || !aligned(a->dq, 16) || !aligned(a->dk, 16) || !aligned(a->dv, 16) ||
-            !aligned(a->g_cum, 4) || !aligned(a->beta, 4) || !aligned(a->dbeta, 4) || !aligned(a->dg, 4))
+            !aligned(a->g_cum, 4) || !aligned(a->beta, 4) || !aligned(a->dbeta, 4) || !aligned(a->dg, 4) ||
+            !aligned(a->tblk_bwd, 16))
             return GDR_EINVAL;
     }
     if ((a->dht && !aligned(a->dht, 16)) || (a->initial_state && !aligned(a->initial_state, 16)) ||
@@ -443,7 +459,7 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
     bp.beta = a->beta;
     bp.A = a->A;
     bp.dht = a->dht;
-    bp.tblk = ws + pl.off_tblk;
+    bp.tblk = a->tblk_bwd ? static_cast<char *>(const_cast<void *>(a->tblk_bwd)) : ws + pl.off_tblk;
     bp.hs = a->h_bwd ? static_cast<const float *>(a->h_bwd) : reinterpret_cast<float *>(ws + pl.off_hs);
     bp.dhs = reinterpret_cast<float *>(ws + pl.off_dhs);
     bp.dq = a->dq;
@@ -469,7 +485,8 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
                                               (int)pl.n_seq, stream) != hipSuccess)
         return GDR_ELAUNCH;
     if (!mark(0)) return GDR_ELAUNCH;
-    if (pl.tokens > 0 && launch_tblocks(dt, bp, (int)pl.nt_ub, stream) != hipSuccess) return GDR_ELAUNCH;
+    if (pl.tokens > 0 && !a->tblk_bwd && launch_tblocks(dt, bp, (int)pl.nt_ub, stream) != hipSuccess)
+        return GDR_ELAUNCH;
     if (!mark(1) || !mark(2)) return GDR_ELAUNCH;
     if (pl.tokens > 0 && !a->h_bwd) {
         // chunk-start states: the exact forward scan without its output

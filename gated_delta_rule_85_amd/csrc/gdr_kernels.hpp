@@ -18,7 +18,8 @@ struct PrepParams {
     const float *g, *beta;
     float *g_cum;  // [tokens, H_v] or null
     float *Tm;     // [tokens, H_v, 64] or null
-    char *tblk;    // [chunks, H_v] T blocks (gdr_layout.hpp)
+    char *tblk;    // [chunks, H_v] T blocks (gdr_layout.hpp), in the scan's swizzled order
+    char *tblk_bwd;  // null, or the same blocks in the backward's (unswizzled) order
     SeqMap sm;
     int Hq, Hv;
 };

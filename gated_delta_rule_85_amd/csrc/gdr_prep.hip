@@ -201,6 +201,10 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
         // T block for the scan: swizzled planes (rows past the chunk end zero) + scalars
         write_tblock<In, SwzTF<In>>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, Tm, LDF, gam, bet, n,
                          tid, NTHR);
+        // and, for a backward, in the layout its kernels copy (plain 16-byte-chunk order)
+        if (p.tblk_bwd)
+            write_tblock<In>(p.tblk_bwd + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, Tm, LDF, gam, bet, n, tid,
+                             NTHR);
         lds_barrier();  // Tm, A, gam, bet free again; the block's stores drain meanwhile
     }
 }

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 4
+#define GDR_ABI_VERSION 5
 #define GDR_CHUNK 64
 #define GDR_FWD_STAGES 3
 #define GDR_BWD_STAGES 4
@@ -106,6 +106,11 @@ typedef struct {
                                    the states.  NULL = not written.  The states must be
                                    exact: with h_bwd, GDR_CP_AUTO splits as
                                    GDR_CP_AUTO_EXACT, and h or GDR_CP_WARMUP is GDR_EINVAL */
+    void *tblk_bwd;             /* gdr_tblocks_bytes() bytes, or NULL: the per-(chunk, v head)
+                                   T blocks (T = (I+A)^{-1} and the chunk's gate scalars) are
+                                   also written here, in the backward's layout; passed on as
+                                   gdr_bwd_args.tblk_bwd, they save the backward's rebuild of
+                                   them from A and g_cum */
     float *w_out;               /* [B,T,H_v,K] W = T diag(beta e^g_cum) K, NULL = not computed */
     float *u_out;               /* [B,T,H_v,V] U = T diag(beta) V, NULL = not computed */
     /* timing hook: NULL, or a HOST array of 2*GDR_FWD_STAGES events that are
@@ -139,6 +144,9 @@ typedef struct {
     const int32_t *cu_seqlens;  /* [n_seq+1] or NULL */
     const void *h_bwd;          /* the forward's h_bwd for the same inputs, or NULL (the states
                                    are then recomputed) */
+    const void *tblk_bwd;       /* the forward's tblk_bwd for the same inputs, or NULL (the T
+                                   blocks are then rebuilt from A and g_cum).  With it and bf16
+                                   inputs, g_cum and A are not read and may be NULL */
     void *dq, *dk;              /* [B,T,H_q,K] grad_dtype, summed over the v heads of each q/k head */
     void *dv;                   /* [B,T,H_v,V] grad_dtype */
     float *dbeta;               /* [B,T,H_v] gradient w.r.t. beta */
@@ -184,9 +192,16 @@ int gdr_fwd_workspace(const gdr_fwd_args *args, size_t *bytes);
    segment.  Returns GDR_ELAUNCH if the device cannot be queried. */
 int gdr_fwd(const gdr_fwd_args *args, hipStream_t stream);
 
+/* Bytes of the T blocks of gdr_fwd_args.tblk_bwd for these sizes: one block
+   per (chunk, v head) for an upper bound on the chunk count (B ceil(T/64), or
+   ceil(T/64) + n_seq with cu_seqlens), 17,408 bytes each for bf16 inputs.
+   Returns GDR_OK or a validation error. */
+int gdr_tblocks_bytes(const gdr_fwd_args *args, size_t *bytes);
+
 /* Workspace bytes gdr_bwd needs for these sizes (pointers are not read):
-   T blocks, the chunk-start states and the chunk-end state gradients,
-   4 K V bytes each per (chunk, v head); with a sequence split also, per
+   T blocks (unless tblk_bwd is given), the chunk-start states (unless h_bwd
+   is given) and the chunk-end state gradients, 4 K V bytes each per
+   (chunk, v head); with a sequence split also, per
    (sequence, v head, segment), the K x K transition and four K x V states
    (fp32) and a 512-byte zero row.  The split follows the compute units of
    the current device, as for gdr_fwd_workspace.  Returns GDR_OK or a
@@ -197,7 +212,8 @@ int gdr_bwd_workspace(const gdr_bwd_args *args, size_t *bytes);
    <dout, o> + <dht, final_state> for an fp32 o, with respect to q, k, v,
    beta, the raw per-token g and initial_state.  g_cum and A must be what
    gdr_fwd returned for the same inputs.  The chunk-start states are
-   recomputed, not read.  dq and dk are written in full (rows of every
+   recomputed unless the forward's h_bwd is given, the T blocks rebuilt
+   unless its tblk_bwd is given.  dq and dk are written in full (rows of every
    token); every output is overwritten, none accumulated into.  With a
    sequence split (cp_mode) the chunk-start states and the reverse scan are
    split exactly (gdr_fwd's GDR_CP_EXACT applied to both recurrences; the

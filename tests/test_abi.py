@@ -148,6 +148,28 @@ def test_forward_states_for_the_backward(L):
     assert L.lib.gdr_fwd(ctypes.byref(a), None) == L.EINVAL  # misaligned h_bwd
 
 
+def test_forward_tblocks_for_the_backward(L):
+    """tblk_bwd: the forward also writes the T blocks, in the backward's layout, to a
+    caller buffer of gdr_tblocks_bytes(), and the backward takes them instead of its
+    own."""
+    assert L.tblocks_bytes(fwd_args(L)) == 4 * 4 * TBLOCK
+    assert L.tblocks_bytes(fwd_args(L, cu_seqlens=16, n_seq=3)) == (4 + 3) * 4 * TBLOCK
+    assert L.tblocks_bytes(fwd_args(L, T=0)) == 0
+    assert rc_ws(L, fwd_args(L, tblk_bwd=16)) == rc_ws(L, fwd_args(L))
+    a = fwd_args(L, q=16, k=16, v=16, g=16, beta=16, o=16, tblk_bwd=40, workspace=4096,
+                 workspace_bytes=1 << 30)
+    assert L.lib.gdr_fwd(ctypes.byref(a), None) == L.EINVAL  # misaligned tblk_bwd
+    per = 2 * 4 * 128 * 128
+    assert L.bwd_workspace(bwd_args(L, tblk_bwd=16)) == 4 * 4 * per
+    assert L.bwd_workspace(bwd_args(L, tblk_bwd=16, h_bwd=16)) == 4 * 4 * per // 2
+    # with the forward's T blocks a bf16 backward needs neither g_cum nor A (it gets as
+    # far as the workspace check); fp32 kernels still read them
+    noga = dict(q=16, k=16, v=16, beta=16, dout=16, dq=16, dk=16, dv=16, dbeta=16, dg=16)
+    assert L.lib.gdr_bwd(ctypes.byref(bwd_args(L, **noga)), None) == L.EINVAL
+    assert L.lib.gdr_bwd(ctypes.byref(bwd_args(L, tblk_bwd=16, **noga)), None) == L.EWORKSPACE
+    assert L.lib.gdr_bwd(ctypes.byref(bwd_args(L, tblk_bwd=16, dtype=L.F32, **noga)), None) == L.EINVAL
+
+
 def bwd_args(L, **kw):
     a = L.BwdArgs()
     a.B, a.T, a.H_q, a.H_v, a.K, a.V, a.n_seq = 1, 256, 2, 4, 128, 128, 0

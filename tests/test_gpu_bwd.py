@@ -26,18 +26,20 @@ NAMES = ("dq", "dk", "dv", "dbeta", "dg", "dh0")
 
 
 def run_bwd(x, with_dht=True, grad_dtype=torch.float32, fwd_states=False, fwd_cp="off",
-            fwd_seg=0, **kw):
-    """The forward (g_cum, A; with fwd_states also its chunk-start states in the
-    backward's layout, split as fwd_cp / fwd_seg), then the backward."""
-    from gated_delta_rule_85_amd import chunk_gated_delta_rule_bwd, chunk_gated_delta_rule_fwd
+            fwd_seg=0, fwd_ga=True, rebuild_tblocks=False, **kw):
+    """The forward (g_cum and A unless not fwd_ga; with fwd_states also its
+    chunk-start states and T blocks, split as fwd_cp / fwd_seg), then the backward
+    (rebuild_tblocks: with the forward's states but T blocks rebuilt from A)."""
+    from gated_delta_rule_85_amd import (SavedForBackward, chunk_gated_delta_rule_bwd,
+                                         chunk_gated_delta_rule_fwd)
     d = gpu_inputs(x)
     dt = d["q"].dtype
     g_cum, A, _, hb, _ = chunk_gated_delta_rule_fwd(
         d["q"], d["k"], d["v"], d["g"], d["beta"], x["scale"], d["initial_state"],
         d["cu_seqlens"], output_final_state=False, return_h=False, cp_mode=fwd_cp,
-        cp_segment_chunks=fwd_seg, return_h_bwd=fwd_states)
+        cp_segment_chunks=fwd_seg, return_h_bwd=fwd_states, return_ga=fwd_ga)
     if fwd_states:
-        kw["h_bwd"] = hb
+        kw["h_bwd"] = SavedForBackward(hb.states, None) if rebuild_tblocks else hb
     do = dev(x["do"], dt)
     dht = dev(x["dht"]) if with_dht else None
     out = chunk_gated_delta_rule_bwd(d["q"], d["k"], d["v"], g_cum, d["beta"], A, do, dht,
@@ -118,9 +120,16 @@ def test_backward_with_forward_states(shape, fwd_cp, fwd_seg, bwd_cp, bwd_seg):
     x = make_inputs(shape, seed=16, grads=True)
     print(shape, fwd_cp, fwd_seg, bwd_cp, bwd_seg, flush=True)
     ref = ora_bwd(x)
+    # bf16: the forward writes neither g_cum nor A, which the backward then does not read
     got = run_bwd(x, fwd_states=True, fwd_cp=fwd_cp, fwd_seg=fwd_seg, cp_mode=bwd_cp,
-                  cp_segment_chunks=bwd_seg)
+                  cp_segment_chunks=bwd_seg, fwd_ga=x["dtype"] != "bf16")
     compare(x, got, ref)
+    # the forward's T blocks are those the backward rebuilds from A and g_cum, bit for bit
+    reb = run_bwd(x, fwd_states=True, fwd_cp=fwd_cp, fwd_seg=fwd_seg, cp_mode=bwd_cp,
+                  cp_segment_chunks=bwd_seg, rebuild_tblocks=True)
+    for n in NAMES:
+        if got[n] is not None:
+            assert torch.equal(got[n], reb[n]), n
     own = run_bwd(x, cp_mode=bwd_cp, cp_segment_chunks=bwd_seg)
     t = tol(x)
     for n in NAMES:
