@@ -260,20 +260,25 @@ def test_autograd_small_heads_long_sequence_splits_exactly():
 
 
 def test_training_shape_full_size_sampled_units():
-    """B=8, T=4096, H_q=32, H_v=64, K=V=128, bf16: the whole backward on the GPU,
-    four (sequence, q/k head) units against the oracle."""
+    """B=8, T=4096, H_q=32, H_v=64, K=V=128, bf16: the whole backward on the GPU, as
+    the training step runs it (chunk-start states and T blocks from the forward, no
+    A or g_cum) and recomputing them from A and g_cum; four (sequence, q/k head)
+    units of each against the oracle."""
     x = make_inputs("training", seed=0)
-    got = run_bwd(x)
+    runs = {"handed over": run_bwd(x, fwd_states=True, fwd_ga=False)}
+    torch.cuda.empty_cache()
+    runs["recomputed"] = run_bwd(x)
     for b, hq in [(0, 0), (3, 17), (5, 9), (7, 31)]:
         y, hs = slice_units(x, b, hq)
         y["do"] = x["do"][b:b + 1, :, hs]
         y["dht"] = x["dht"][b:b + 1, hs]
         ref = ora_bwd(y)
-        sub = dict(dq=got["dq"][b:b + 1, :, hq:hq + 1], dk=got["dk"][b:b + 1, :, hq:hq + 1],
-                   dv=got["dv"][b:b + 1, :, hs], dbeta=got["dbeta"][b:b + 1, :, hs],
-                   dg=got["dg"][b:b + 1, :, hs], dh0=got["dh0"][b:b + 1, hs])
-        print((b, hq), end=" ")
-        compare(y, sub, ref)
+        for mode, got in runs.items():
+            sub = dict(dq=got["dq"][b:b + 1, :, hq:hq + 1], dk=got["dk"][b:b + 1, :, hq:hq + 1],
+                       dv=got["dv"][b:b + 1, :, hs], dbeta=got["dbeta"][b:b + 1, :, hs],
+                       dg=got["dg"][b:b + 1, :, hs], dh0=got["dh0"][b:b + 1, hs])
+            print((b, hq), mode, end=" ")
+            compare(y, sub, ref)
 
 
 def test_varlen_mixed_lengths_bf16():
