@@ -20,20 +20,20 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(ROOT, "include")]
 # MFMA operands and results in VGPRs rather than AGPRs (fewer copies in the
-# scan's register-resident loops); the backward's LDS-fed kernels are left to
-# the default allocation, which the option crashes on.
+# register-resident loops of every kernel that keeps its work in registers).
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 # The scans run one wave per SIMD, so nothing hides an LDS read's latency but
 # the wave's own later instructions: the ILP-seeking scheduler issues the
 # operand reads well ahead of their MFMAs (the default one waits on each).
 ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
-# The backward's chunk-local kernel (also one wave per SIMD, at the register limit)
-# spills under the ILP scheduler; the max-ILP one spills 9 registers where the
-# default spills 17 and runs it 4% faster (the minimum-register one spills 1 but
-# is slower).  On the scans the max-ILP scheduler costs 30%.
+# The backward's chunk-local kernel (also one wave per SIMD, at the register
+# limit) spills under the iterative ILP scheduler; with the max-ILP one and
+# VGPR-form MFMAs it spills nothing (default scheduler: 17 registers) and runs 8%
+# faster.  On the scans the max-ILP scheduler costs 30%.
 MAX_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 SOURCES = {"gdr_api.hip": VGPR_FORM, "gdr_prep.hip": VGPR_FORM, "gdr_scan.hip": VGPR_FORM + ILP,
-           "gdr_bwd.hip": VGPR_FORM, "gdr_bwd_scan.hip": ILP, "gdr_bwd_mfma.hip": MAX_ILP}
+           "gdr_bwd.hip": VGPR_FORM, "gdr_bwd_scan.hip": VGPR_FORM + ILP,
+           "gdr_bwd_mfma.hip": VGPR_FORM + MAX_ILP}
 
 
 def _compile(src):
