@@ -36,6 +36,12 @@ int main(void) {
     CHECK(gdr_fwd_workspace(&a, &bytes) == GDR_ENOTSUP, "fwd K");
     a.K = 128;
     CHECK(gdr_fwd(&a, NULL) == GDR_EINVAL, "fwd null pointers rejected before any launch");
+    CHECK(gdr_tblocks_bytes(&a, &bytes) == GDR_OK && bytes == 4 * 4 * 17408, "T blocks for the backward");
+    a.h_bwd = (void *)16;
+    a.cp_mode = GDR_CP_WARMUP;
+    CHECK(gdr_fwd_workspace(&a, &bytes) == GDR_EINVAL, "fwd states for the backward need an exact scan");
+    a.cp_mode = GDR_CP_OFF;
+    a.h_bwd = NULL;
 
     gdr_bwd_args b;
     memset(&b, 0, sizeof b);
@@ -43,6 +49,11 @@ int main(void) {
     b.dtype = GDR_BF16; b.grad_dtype = GDR_BF16; b.scale = 0.088f; b.cp_mode = GDR_CP_OFF;
     CHECK(gdr_bwd_workspace(&b, &bytes) == GDR_OK && bytes == 4 * 4 * (17408 + 2 * 4 * 128 * 128),
           "bwd workspace");
+    b.h_bwd = (const void *)16;
+    b.tblk_bwd = (const void *)16;
+    CHECK(gdr_bwd_workspace(&b, &bytes) == GDR_OK && bytes == 4 * 4 * 4 * 128 * 128,
+          "bwd workspace with the forward's states and T blocks");
+    b.h_bwd = b.tblk_bwd = NULL;
     b.cp_mode = GDR_CP_WARMUP;
     CHECK(gdr_bwd_workspace(&b, &bytes) == GDR_EINVAL, "bwd has no warm-up split");
     return fails != 0;
