@@ -85,14 +85,17 @@ def bwd_algorithmic_flops(cfg):
     return {"gdr_bwd_scan": scan, "gdr_bwd_local": local, "gdr_bwd_states": states}
 
 
-# sources of the forward kernels: a traffic summary counts only if taken on these
+# sources of the forward kernels and of the backward's chunk-local kernel: a
+# traffic summary counts only if taken on these
 FWD_SOURCES = ("gdr_scan.hip", "gdr_prep.hip", "gdr_device.hpp", "gdr_layout.hpp", "gdr_lds.hpp",
                "gdr_kernels.hpp")
+BWD_LOCAL_SOURCES = ("gdr_bwd_mfma.hip", "gdr_bwd_ops.hpp", "gdr_device.hpp", "gdr_layout.hpp",
+                     "gdr_lds.hpp", "gdr_kernels.hpp")
 
 
-def source_hash():
+def source_hash(files=FWD_SOURCES):
     h = hashlib.sha256()
-    for f in FWD_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "gated_delta_rule_85_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -107,7 +110,8 @@ def measured_traffic(kernel, workload):
         return None
     with open(path) as f:
         t = json.loads(f.read().strip().splitlines()[-1])
-    if t.get("source_hash") != source_hash():
+    files = BWD_LOCAL_SOURCES if kernel == "gdr_bwd_local" else FWD_SOURCES
+    if t.get("source_hash") != source_hash(files):
         return None
     return t.get("bytes_per_launch")
 
@@ -447,7 +451,7 @@ def main():
         peak = MFMA_BF16_PEAK_TFLOPS if dt == torch.bfloat16 else FP32_MFMA_PEAK_TFLOPS
         rec["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": achieved,
                            "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                           "traffic": None, "algorithmic_flops": af[dom]}
+                           "traffic": measured_traffic(dom, args.workload), "algorithmic_flops": af[dom]}
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds, train)
         rec["cpu_single_core"] = cpu_single_core(x, train)
