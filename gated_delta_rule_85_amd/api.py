@@ -83,8 +83,9 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     ``return_h_bwd`` replaces h by a :class:`SavedForBackward` (the chunk-start
     states in the backward's layout and the T blocks); passed to
     :func:`chunk_gated_delta_rule_bwd` as ``h_bwd`` it saves the backward's
-    recompute of the states and rebuild of the T blocks (a ``tblocks`` of None
-    there has them rebuilt from g_cum and A).  The states are then
+    recompute of the states and rebuild of the T blocks (a ``states`` or
+    ``tblocks`` of None there has that part recomputed: the T blocks from g_cum
+    and A).  The states are then
     exact: "auto" splits as "auto_exact" and "warmup" is refused.  With
     ``return_ga=False`` g_cum and A are not written (None): a bf16 backward
     given ``h_bwd`` does not read them.
@@ -179,8 +180,9 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
     cu = _c(cu_seqlens)
     if h_bwd is not None:
         nt = num_chunks(T, 1, cu) if cu is not None else num_chunks(T, B)
-        st, tb = h_bwd
-        if st.dtype != torch.uint8 or st.shape != (nt, Hv, 4 * K * V) or not st.is_contiguous():
+        st = h_bwd.states
+        if st is not None and (st.dtype != torch.uint8 or st.shape != (nt, Hv, 4 * K * V)
+                               or not st.is_contiguous()):
             raise ValueError("h_bwd.states must be the forward's uint8 [NT,H_v,4KV] states")
     gdt = q.dtype if grad_dtype is None else grad_dtype
     dq = torch.empty(q.shape, dtype=gdt, device=dev)
@@ -205,7 +207,8 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
             fa.B, fa.T, fa.H_q, fa.H_v, fa.K, fa.V, fa.n_seq = B, T, Hq, Hv, K, V, n_seq
             fa.dtype, fa.out_dtype = a.dtype, _lib.F32
             fa.cu_seqlens = a.cu_seqlens
-            if h_bwd.tblocks.dtype != torch.uint8 or h_bwd.tblocks.numel() < _lib.tblocks_bytes(fa):
+            if h_bwd.tblocks.dtype != torch.uint8 or h_bwd.tblocks.numel() < _lib.tblocks_bytes(fa) \
+                    or not h_bwd.tblocks.is_contiguous():
                 raise ValueError("h_bwd.tblocks must be the forward's T blocks")
     a.dq, a.dk, a.dv, a.dbeta, a.dg, a.dh0 = _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(dg), _ptr(dh0)
     nbytes = _lib.bwd_workspace(a)

@@ -26,10 +26,11 @@ NAMES = ("dq", "dk", "dv", "dbeta", "dg", "dh0")
 
 
 def run_bwd(x, with_dht=True, grad_dtype=torch.float32, fwd_states=False, fwd_cp="off",
-            fwd_seg=0, fwd_ga=True, rebuild_tblocks=False, **kw):
+            fwd_seg=0, fwd_ga=True, rebuild_tblocks=False, recompute_states=False, **kw):
     """The forward (g_cum and A unless not fwd_ga; with fwd_states also its
     chunk-start states and T blocks, split as fwd_cp / fwd_seg), then the backward
-    (rebuild_tblocks: with the forward's states but T blocks rebuilt from A)."""
+    (rebuild_tblocks: with the forward's states but T blocks rebuilt from A;
+    recompute_states: with the forward's T blocks but the states recomputed)."""
     from gated_delta_rule_85_amd import (SavedForBackward, chunk_gated_delta_rule_bwd,
                                          chunk_gated_delta_rule_fwd)
     d = gpu_inputs(x)
@@ -39,7 +40,8 @@ def run_bwd(x, with_dht=True, grad_dtype=torch.float32, fwd_states=False, fwd_cp
         d["cu_seqlens"], output_final_state=False, return_h=False, cp_mode=fwd_cp,
         cp_segment_chunks=fwd_seg, return_h_bwd=fwd_states, return_ga=fwd_ga)
     if fwd_states:
-        kw["h_bwd"] = SavedForBackward(hb.states, None) if rebuild_tblocks else hb
+        kw["h_bwd"] = SavedForBackward(hb.states, None) if rebuild_tblocks else \
+            SavedForBackward(None, hb.tblocks) if recompute_states else hb
     do = dev(x["do"], dt)
     dht = dev(x["dht"]) if with_dht else None
     out = chunk_gated_delta_rule_bwd(d["q"], d["k"], d["v"], g_cum, d["beta"], A, do, dht,
@@ -136,6 +138,22 @@ def test_backward_with_forward_states(shape, fwd_cp, fwd_seg, bwd_cp, bwd_seg):
         if got[n] is not None:
             e = rel(host(got[n]), host(own[n]).astype(np.float64))
             assert e <= t, (n, e)
+
+
+@pytest.mark.parametrize("shape,cp,seg", [
+    (dict(B=2, T=300, Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True), "off", 0),
+    (dict(B=1, T=64 * 9 + 30, Hq=1, Hv=2, K=64, V=128, dtype="fp32", h0=True), "exact", 3),
+    (dict(lens=[400, 0, 65, 300, 1], Hq=1, Hv=2, K=64, V=64, dtype="bf16", h0=True), "exact", 2),
+])
+def test_backward_with_forward_tblocks_only(shape, cp, seg):
+    """The forward's T blocks without its states: the backward's states pass (and,
+    split, its transitions) runs on the handed-over blocks; bf16 inputs without
+    g_cum and A.  Every gradient element against the oracle."""
+    x = make_inputs(shape, seed=17, grads=True)
+    print(shape, cp, seg, flush=True)
+    got = run_bwd(x, fwd_states=True, recompute_states=True, fwd_ga=x["dtype"] != "bf16",
+                  cp_mode=cp, cp_segment_chunks=seg)
+    compare(x, got, ora_bwd(x))
 
 
 def test_forward_states_refused_with_warmup_split():
