@@ -143,7 +143,8 @@ def cpu_single_core(x, train=False):
 
 def cpu_baseline(x, seconds, train=False):
     """Time the fp64 oracle (forward, plus backward when `train`) on whole
-    sequences of the workload until about `seconds` of CPU time have been spent."""
+    sequences of the workload, taken in turn and again from the first once all
+    are done, until about `seconds` of CPU time have been spent."""
     import numpy as np
 
     import oracle
@@ -152,7 +153,8 @@ def cpu_baseline(x, seconds, train=False):
     done = 0
     elapsed = 0.0
     threads = 0
-    for b in range(B):
+    for i in range(64 * B):
+        b = i % B
         sl = {n: np.ascontiguousarray(x[n][b:b + 1], dtype=np.float64)
               for n in ("q", "k", "v", "g", "beta")}
         h0 = None if x["initial_state"] is None else \
@@ -168,7 +170,8 @@ def cpu_baseline(x, seconds, train=False):
         if elapsed >= seconds:
             break
     return {"value": done * T / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d sequences (all %d v heads, T=%d)%s in %.1f s" %
+            "sample": "%d sequence runs over the workload's %d sequences (all %d v heads, "
+                      "T=%d)%s in %.1f s" %
                       (done, B, x["v"].shape[2], T, ", forward + backward" if train else "",
                        elapsed)}
 
