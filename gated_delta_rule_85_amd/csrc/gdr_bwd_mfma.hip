@@ -103,13 +103,16 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
         float dec = 0.f;
 
         // stage keys [64 hf, 64 hf + 64) of the value block vb of h^T and dh'^T (split planes,
-        // rows = value columns) by direct copies; with `dot`, add this thread's share of <dh', h>
-        auto stage = [&](int hf, int vb, bool dot) {
+        // rows = value columns) into B (Hs, or Wm while it is free) by direct copies ...
+        auto stage = [&](char (*B)[2 * PPL], int hf, int vb) {
             const int src = (vb * KD + 64 * hf) * 2;
-            copy_rows<128>(Hs[0], hsb + src, KD * 2, 63, w, 4);
-            copy_rows<128>(Hs[0] + PPL, hsb + splane + src, KD * 2, 63, w, 4);
-            copy_rows<128>(Hs[1], dhsb + src, KD * 2, 63, w, 4);
-            copy_rows<128>(Hs[1] + PPL, dhsb + splane + src, KD * 2, 63, w, 4);
+            copy_rows<128>(B[0], hsb + src, KD * 2, 63, w, 4);
+            copy_rows<128>(B[0] + PPL, hsb + splane + src, KD * 2, 63, w, 4);
+            copy_rows<128>(B[1], dhsb + src, KD * 2, 63, w, 4);
+            copy_rows<128>(B[1] + PPL, dhsb + splane + src, KD * 2, 63, w, 4);
+        };
+        // ... wait for them; with `dot`, add this thread's share of <dh', h>
+        auto land = [&](char (*B)[2 * PPL], bool dot) {
             wait_dma();
             __syncthreads();
             if (dot) {
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
                     auto ld = [&](const char *pl) {
                         return __builtin_convertvector(*reinterpret_cast<const bf16x4 *>(pl + off), f32x4);
                     };
-                    const f32x4 hx = ld(Hs[0]) + ld(Hs[0] + PPL), dx = ld(Hs[1]) + ld(Hs[1] + PPL);
+                    const f32x4 hx = ld(B[0]) + ld(B[0] + PPL), dx = ld(B[1]) + ld(B[1] + PPL);
                     dec += hx[0] * dx[0] + hx[1] * dx[1] + hx[2] * dx[2] + hx[3] * dx[3];
                 }
             }
@@ -134,15 +137,20 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
             f32x4 kh[4], kd[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) kh[rt] = kd[rt] = zero4();
+            // the first of two halves goes to Wm (free until U~ and dX are formed), the
+            // second to Hs, copied while the first half's products run; Hs then holds the
+            // last half, which the dq, dk pass below starts from
 #pragma unroll 1
             for (int hf = 0; hf < NH; ++hf) {
-                if (hf > 0) __syncthreads();  // every wave is done with the previous half
-                stage(hf, vb, true);
+                char (*B)[2 * PPL] = NH == 2 && hf == 0 ? Wm : Hs;
+                if (hf == 0) stage(B, 0, vb);
+                land(B, true);
+                if (hf + 1 < NH) stage(Hs, hf + 1, vb);
 #pragma unroll
                 for (int ip = 0; ip < 2; ++ip) {
                     // B operands of h, dh' (k = keys 64 hf + 32 ip .., column 16 w + lane16)
-                    const OpS hb = frag_s<128>(Hs[0], PPL, 16 * w + n16, (32 * ip + 4 * g) * 2);
-                    const OpS db = frag_s<128>(Hs[1], PPL, 16 * w + n16, (32 * ip + 4 * g) * 2);
+                    const OpS hb = frag_s<128>(B[0], PPL, 16 * w + n16, (32 * ip + 4 * g) * 2);
+                    const OpS db = frag_s<128>(B[1], PPL, 16 * w + n16, (32 * ip + 4 * g) * 2);
 #pragma unroll
                     for (int rt = 0; rt < 4; ++rt) {
                         const OpX kf = frag<bf16, KROW>(Ks, 16 * rt + n16, (64 * hf + 32 * ip + 4 * g) * 2);
@@ -222,7 +230,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
             for (int s = TD - 1; s >= 0; --s) {
                 if (s != NH - 1) {
                     __syncthreads();  // every wave is done with the staged half
-                    stage(s, vb, false);
+                    stage(Hs, s, vb);
+                    land(Hs, false);
                 }
                 // transposed tiles: lane (token 16 tr + lane16, g) holds keys 16 td + 4 g .. + 3
                 f32x4 aQ[4], aKa[4], aKe[4];
