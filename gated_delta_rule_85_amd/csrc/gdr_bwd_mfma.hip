@@ -87,21 +87,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
         const char *dhsb = reinterpret_cast<const char *>(p.dhs + hoff);
         const int splane = KD * V * 2;
         Gt *dvb = dvp + (ts * p.Hv + hv) * V;                      // row tok at tok * Hv * V
-        __syncthreads();  // the previous v head is done with every LDS array
-        copy_flat(Tb, p.tblk + ((int64_t)gid * p.Hv + hv) * TB::BYTES, TB::BYTES, w);
-        wait_dma();
-        __syncthreads();
-        scores_t<KD>(Pt, Qs, Ks, gam, n, w);
-
-        f32x4 dPa[4], dAa[4];
-#pragma unroll
-        for (int tr = 0; tr < 4; ++tr) dPa[tr] = dAa[tr] = zero4();
-        float rsum[3][4];  // partial row sums over this lane's 4 keys (token 16 rt + lane16)
-        float rs3[4];      // dX.V partial over this lane's 4 columns (token 16 rt + lane16)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) rsum[0][rt] = rsum[1][rt] = rsum[2][rt] = rs3[rt] = 0.f;
         float dec = 0.f;
-
         // stage keys [64 hf, 64 hf + 64) of the value block vb of h^T and dh'^T (split planes,
         // rows = value columns) into B (Hs, or Wm while it is free) by direct copies ...
         auto stage = [&](char (*B)[2 * PPL], int hf, int vb) {
@@ -129,10 +115,30 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
             }
         };
 
+        __syncthreads();  // the previous v head is done with every LDS array
+        copy_flat(Tb, p.tblk + ((int64_t)gid * p.Hv + hv) * TB::BYTES, TB::BYTES, w);
+        wait_dma();
+        __syncthreads();
+        // the first value block's dO, V and first key half are copied while the scores form
+        copy_tile<VROW>(Ds, dop + (ts * p.Hv + hv) * V * 2, p.Hv * V * 2, n - 1, w);
+        copy_tile<VROW>(Vs, vpc + (ts * p.Hv + hv) * V * 2, p.Hv * V * 2, n - 1, w);
+        stage(NH == 2 ? Wm : Hs, 0, 0);
+        scores_t<KD>(Pt, Qs, Ks, gam, n, w);
+
+        f32x4 dPa[4], dAa[4];
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr) dPa[tr] = dAa[tr] = zero4();
+        float rsum[3][4];  // partial row sums over this lane's 4 keys (token 16 rt + lane16)
+        float rs3[4];      // dX.V partial over this lane's 4 columns (token 16 rt + lane16)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) rsum[0][rt] = rsum[1][rt] = rsum[2][rt] = rs3[rt] = 0.f;
+
         for (int vb = 0; vb < V; vb += 64) {
             __syncthreads();  // the previous block is done with Ds, Vs, Wm, Hs; scores complete
-            copy_tile<VROW>(Ds, dop + ((ts * p.Hv + hv) * V + vb) * 2, p.Hv * V * 2, n - 1, w);
-            copy_tile<VROW>(Vs, vpc + ((ts * p.Hv + hv) * V + vb) * 2, p.Hv * V * 2, n - 1, w);
+            if (vb > 0) {  // (the first block's were issued before the scores)
+                copy_tile<VROW>(Ds, dop + ((ts * p.Hv + hv) * V + vb) * 2, p.Hv * V * 2, n - 1, w);
+                copy_tile<VROW>(Vs, vpc + ((ts * p.Hv + hv) * V + vb) * 2, p.Hv * V * 2, n - 1, w);
+            }
             // K h, K dh' for this wave's columns, over the halves of the key dimension
             f32x4 kh[4], kd[4];
 #pragma unroll
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
 #pragma unroll 1
             for (int hf = 0; hf < NH; ++hf) {
                 char (*B)[2 * PPL] = NH == 2 && hf == 0 ? Wm : Hs;
-                if (hf == 0) stage(B, 0, vb);
+                if (hf == 0 && vb > 0) stage(B, 0, vb);
                 land(B, true);
                 if (hf + 1 < NH) stage(Hs, hf + 1, vb);
 #pragma unroll
