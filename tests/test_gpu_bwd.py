@@ -299,6 +299,24 @@ def test_training_shape_full_size_sampled_units():
             compare(y, sub, ref)
 
 
+def test_varlen_packed_batch_full_size():
+    """16 packed sequences (61,412 tokens, lengths 129 to 11,956), H_q=16, H_v=32,
+    K=V=128, bf16, as a training step runs it (states and T blocks from the
+    forward, sequences scanned longest first): two q/k heads over every sequence
+    against the oracle."""
+    x = make_inputs("varlen", seed=0, grads=True)
+    got = run_bwd(x, fwd_states=True, fwd_ga=False)
+    for hq in (0, 11):
+        y, hs = slice_units(x, 0, hq)
+        y["do"] = x["do"][:, :, hs]
+        y["dht"] = x["dht"][:, hs]
+        ref = ora_bwd(y)
+        sub = dict(dq=got["dq"][:, :, hq:hq + 1], dk=got["dk"][:, :, hq:hq + 1], dv=got["dv"][:, :, hs],
+                   dbeta=got["dbeta"][:, :, hs], dg=got["dg"][:, :, hs])
+        print("hq=%d" % hq, end=" ")
+        compare(y, sub, ref, names=("dq", "dk", "dv", "dbeta", "dg"))
+
+
 def test_varlen_mixed_lengths_bf16():
     """Packed batch with lengths from 1 to ~2.3k tokens (ragged tails, single-token
     and empty sequences), the GQA shape of the workloads; every gradient element."""
