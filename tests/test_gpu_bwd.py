@@ -317,6 +317,16 @@ def test_varlen_packed_batch_full_size():
         compare(y, sub, ref, names=("dq", "dk", "dv", "dbeta", "dg"))
 
 
+def test_long_sequence_full_size_split_with_forward_states():
+    """B=1, T=32768, H_q=4, H_v=8, K=V=128, bf16 (512 chunks per head), as a training
+    step runs it: the forward's exact split writes the states and T blocks, and the
+    backward's own exact split (the device model's segment length) forms only the
+    transitions for its reverse carry.  Every gradient element against the oracle."""
+    x = make_inputs("small_head_long", seed=0, grads=True)
+    got = run_bwd(x, fwd_states=True, fwd_ga=False, fwd_cp="auto_exact", cp_mode="auto")
+    compare(x, got, ora_bwd(x))
+
+
 def test_varlen_mixed_lengths_bf16():
     """Packed batch with lengths from 1 to ~2.3k tokens (ragged tails, single-token
     and empty sequences), the GQA shape of the workloads; every gradient element."""
