@@ -253,6 +253,87 @@ def test_p4_chunked_form_equals_token_recurrence(case):
     assert rel(c["gam"], r["g_cum"]) < 1e-14
 
 
+# ------------------------------------------ P4 chunked intermediates (T, W, U) pinned
+def delta_errors(kc, vc, gc, bc, S0):
+    """Per-token delta-rule errors u_t = beta_t (v_t - exp(g_t) S_{t-1} k_t) of the
+    recurrence S_t = exp(g_t) S_{t-1} + k-write, run in the V x K form over one
+    chunk from the start state S0 (V x K).  Written from the recurrence alone."""
+    S = np.array(S0, np.float64)
+    out = []
+    for t in range(len(gc)):
+        a = math.exp(gc[t])
+        u = bc[t] * (vc[t] - a * (S @ kc[t]))
+        S = a * S + np.outer(u, kc[t])
+        out.append(u)
+    return np.array(out)
+
+
+def chunk_spans(x, chunk=64):
+    """(sequence, first token, token count) of every chunk of a packed problem."""
+    B, T = x["q"].shape[0], x["q"].shape[1]
+    cu = x["cu_seqlens"]
+    off = list(range(0, B * T + 1, T)) if cu is None else [int(c) for c in cu]
+    for j in range(len(off) - 1):
+        for s in range(off[j], off[j + 1], chunk):
+            yield j, s, min(chunk, off[j + 1] - s)
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=1, T=150, Hq=1, Hv=2, K=16, V=8, h0=True),
+    dict(lens=[70, 1, 130, 0, 64], Hq=1, Hv=2, K=8, V=4, h0=False),
+    dict(B=1, T=64, Hq=2, Hv=4, K=64, V=16, h0=True),
+])
+def test_p4_chunk_intermediates_match_the_recurrence(case):
+    """chunk_form's per-chunk T, W and U, pinned by the token recurrence itself.
+    Row r of U - W h is the delta-rule error u_r of token r when the chunk starts
+    from state h, so with the recurrence run over the chunk alone:
+      U        = errors from a zero start with the chunk's values,
+      W[:, d]  = -errors from the start state with h[d, 0] = 1 and zero values,
+      T[:, i]  = errors from a zero start with a unit value at token i only, / beta_i;
+    and T is zero past the chunk end.  Also the residuals of the definitions
+    (efeozkan, "2. Hardware-Friendly Algebraic Reformulation": A, then W and U):
+    |T (I + A) - I|, |(I + A) U - diag(beta) V|, |(I + A) W - diag(beta e^gam) K|."""
+    x = problem(seed=23, **case)
+    c = oracle.chunk_form(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"],
+                          initial_state=x["initial_state"], cu_seqlens=x["cu_seqlens"])
+    Hq, K = x["q"].shape[2], x["q"].shape[3]
+    Hv, V = x["v"].shape[2], x["v"].shape[3]
+    G = Hv // Hq
+    kf, vf = x["k"].reshape(-1, Hq, K).astype(np.float64), x["v"].reshape(-1, Hv, V).astype(np.float64)
+    gf, bf = x["g"].reshape(-1, Hv).astype(np.float64), x["beta"].reshape(-1, Hv).astype(np.float64)
+    Tr, Wf, Uf = c["T_rows"].reshape(-1, Hv, 64), c["W"].reshape(-1, Hv, K), c["U"].reshape(-1, Hv, V)
+    worst = 0.0
+    for _, s, n in chunk_spans(x):
+        for hv in range(Hv):
+            kc, vc = kf[s:s + n, hv // G], vf[s:s + n, hv]
+            gc, bc = gf[s:s + n, hv], bf[s:s + n, hv]
+            U_pin = delta_errors(kc, vc, gc, bc, np.zeros((V, K)))
+            W_pin = np.zeros((n, K))
+            for d in range(K):
+                S0 = np.zeros((1, K))
+                S0[0, d] = 1.0
+                W_pin[:, d] = -delta_errors(kc, np.zeros((n, 1)), gc, bc, S0)[:, 0]
+            T_pin = np.zeros((n, n))
+            for i in range(n):
+                e = np.zeros((n, 1))
+                e[i, 0] = 1.0
+                T_pin[:, i] = delta_errors(kc, e, gc, bc, np.zeros((1, K)))[:, 0] / bc[i]
+            Tc = Tr[s:s + n, hv, :n]
+            assert np.all(Tr[s:s + n, hv, n:] == 0.0)
+            for got, want in ((Uf[s:s + n, hv], U_pin), (Wf[s:s + n, hv], W_pin), (Tc, T_pin)):
+                e_ = np.max(np.abs(got - want)) / max(np.max(np.abs(want)), 1e-300)
+                worst = max(worst, e_)
+                assert e_ < 1e-12
+            # residuals of the definitions
+            gam = np.cumsum(gc)
+            A = np.tril(bc[:, None] * (kc @ kc.T) * np.exp(gam[:, None] - gam[None, :]), -1)
+            IA = np.eye(n) + A
+            assert np.max(np.abs(Tc @ IA - np.eye(n))) < 1e-12
+            assert np.max(np.abs(IA @ Uf[s:s + n, hv] - bc[:, None] * vc)) < 1e-12
+            assert np.max(np.abs(IA @ Wf[s:s + n, hv] - (bc * np.exp(gam))[:, None] * kc)) < 1e-12
+    print("worst relative deviation of T, W, U from the recurrence: %.3g" % worst)
+
+
 def test_p4_numpy_twin_matches_c():
     x = problem(B=2, T=70, Hq=2, Hv=4, K=8, V=8, seed=19)
     o, hT = oracle.token_recurrence_np(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"],
