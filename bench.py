@@ -45,6 +45,22 @@ STAGES = ("gdr_chunk_prep", "gdr_scan_output", "gdr_wu")
 TBLOCK = 17408  # bytes of one (chunk, v head) T block: T hi/lo planes + gate scalars
 
 
+def minimal_bytes_per_token_head(cfg, out_bytes=None):
+    """Least HBM bytes the forward must move per token and v head: q and k read
+    once (each shared by the H_v/H_q v heads of its group), v, g and beta read, o
+    written in the input dtype (out_bytes: another output width), and the initial
+    and final states amortised over the sequence.  808 B at K=V=128, G=2, T=4096,
+    bf16 with an initial state."""
+    Hq, Hv, K, V = cfg["Hq"], cfg["Hv"], cfg["K"], cfg["V"]
+    tokens = cfg["B"] * cfg["T"]
+    n_seq = cfg.get("n_seq", cfg["B"])
+    e = 2 if cfg["dtype"] == "bf16" else 4
+    eo = e if out_bytes is None else out_bytes
+    G = Hv // Hq
+    states = (2 if cfg.get("h0") else 1) * K * V * 4 * n_seq / tokens
+    return 2 * K * e / G + V * e + 8 + V * eo + states
+
+
 def algorithmic_bytes(cfg, out_bytes=4):
     """Bytes each kernel must move once per launch in this design (every
     tensor it reads or writes counted once; q/k shared by the v heads of a
@@ -236,7 +252,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cold", type=int, default=10,
                     help="extra steps timed after a 1 GiB cache scrub (median reported)")
-    ap.add_argument("--cp", choices=("auto", "off", "warmup", "exact"), default="auto",
+    ap.add_argument("--cp", choices=("auto", "off", "warmup", "exact", "auto_exact", "auto_pages"), default="auto",
                     help="sequence split of the forward (training: always off)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -280,7 +296,9 @@ def main():
     a.out_dtype = _lib.F32
     a.scale = float(x["scale"])
     a.cp_mode = _lib.CP_OFF if train else {"auto": _lib.CP_AUTO, "off": _lib.CP_OFF,
-                                            "warmup": _lib.CP_WARMUP, "exact": _lib.CP_EXACT}[args.cp]
+                                            "warmup": _lib.CP_WARMUP, "exact": _lib.CP_EXACT,
+                                            "auto_exact": _lib.CP_AUTO_EXACT,
+                                            "auto_pages": _lib.CP_AUTO_PAGES}[args.cp]
     a.q, a.k, a.v, a.g, a.beta = q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr()
     a.initial_state = None if h0 is None else h0.data_ptr()
     a.cu_seqlens = None if cu is None else cu.data_ptr()
@@ -292,8 +310,7 @@ def main():
             keep += [g_cum, A]
             a.g_cum, a.A = g_cum.data_ptr(), A.data_ptr()
         if not args.recompute_states:  # chunk-start states and T blocks handed over
-            n_chunks = B * ((T + 63) // 64) if cu is None else \
-                int(((cu[1:] - cu[:-1]).cpu().long().add(63) // 64).sum())
+            n_chunks = B * ((T + 63) // 64) if cu is None else (T + 63) // 64 + n_seq  # bound
             hb = torch.empty((n_chunks, Hv, 4 * K * V), dtype=torch.uint8, device=dev)
             tb = torch.empty(max(_lib.tblocks_bytes(a), 1), dtype=torch.uint8, device=dev)
             keep += [hb, tb]
@@ -438,14 +455,24 @@ def main():
     if cold:
         rec["cold_step_ms"] = sorted(cold)[len(cold) // 2]
     if not train:
-        ab = model
-        achieved = ab[dom] / (dom_ms * 1e-3) / 1e9
+        # the path's minimal bytes (per token and v head, times the launch's tokens and
+        # v heads) over the dominant kernel's measured duration, against HBM peak; the
+        # same bytes over the whole step; this design's own bytes per kernel beside them
+        bpt = minimal_bytes_per_token_head(dict(cfg, B=B, T=T, n_seq=n_seq))
+        bmin = bpt * tokens * Hv
+        achieved = bmin / (dom_ms * 1e-3) / 1e9
+        design = model[dom] / (dom_ms * 1e-3) / 1e9
         rec["tflops_algorithmic"] = tflops
         rec["mfma_bf16_peak_frac"] = tflops / MFMA_BF16_PEAK_TFLOPS
         rec["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": achieved,
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                            "traffic": measured_traffic(dom, args.workload),
-                           "algorithmic_bytes": ab[dom]}
+                           "algorithmic_bytes": bmin, "bytes_per_token_head": bpt,
+                           "step_frac": bmin / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "frac_fp32_o": minimal_bytes_per_token_head(dict(cfg, B=B, T=T, n_seq=n_seq), 4)
+                           * tokens * Hv
+                           / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "design_bytes": model[dom], "design_frac": design / HBM_PEAK_GBS}
     else:
         af = model
         achieved = af[dom] / (dom_ms * 1e-3) / 1e12

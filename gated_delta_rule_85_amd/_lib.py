@@ -10,14 +10,14 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 CHUNK = 64
 FWD_STAGES = 3
 BWD_STAGES = 4
 
 OK, EINVAL, ENOTSUP, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
-CP_AUTO, CP_OFF, CP_WARMUP, CP_EXACT, CP_AUTO_EXACT = 0, 1, 2, 3, 4
+CP_AUTO, CP_OFF, CP_WARMUP, CP_EXACT, CP_AUTO_EXACT, CP_AUTO_PAGES = 0, 1, 2, 3, 4, 5
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64

@@ -18,7 +18,7 @@ from . import _lib
 
 _DT = {torch.bfloat16: _lib.BF16, torch.float32: _lib.F32}
 _CP = {"auto": _lib.CP_AUTO, "off": _lib.CP_OFF, "warmup": _lib.CP_WARMUP, "exact": _lib.CP_EXACT,
-       "auto_exact": _lib.CP_AUTO_EXACT}
+       "auto_exact": _lib.CP_AUTO_EXACT, "auto_pages": _lib.CP_AUTO_PAGES}
 
 
 class SavedForBackward(NamedTuple):
@@ -46,6 +46,18 @@ def _check(q, k, v, g, beta, cu_seqlens):
         raise ValueError("inputs must be on the GPU")
     if cu_seqlens is not None and (B != 1 or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1):
         raise ValueError("cu_seqlens must be int32 [N+1] with B == 1")
+    if cu_seqlens is not None and not cu_seqlens.is_cuda:
+        # offsets on the host are checked here; on the device the library clamps them
+        # (reading them here would synchronise the stream)
+        check_offsets(cu_seqlens, T)
+
+
+def check_offsets(cu_seqlens, T):
+    """Raise ValueError unless the host offsets start at 0, never decrease and end
+    at T (the packed token count)."""
+    c = torch.as_tensor(cu_seqlens).to(torch.int64)
+    if c.dim() != 1 or c.numel() < 2 or int(c[0]) != 0 or int(c[-1]) != T or bool((c[1:] < c[:-1]).any()):
+        raise ValueError("cu_seqlens must start at 0, never decrease and end at T")
 
 
 def _c(t, dtype=None):
@@ -57,11 +69,19 @@ def _c(t, dtype=None):
 
 
 def num_chunks(T, B=1, cu_seqlens=None):
-    """Chunk-start state count of the forward's h (host sync with cu_seqlens)."""
+    """Chunk-start state count of the forward's h (with device cu_seqlens this reads
+    them back, a host synchronisation)."""
     if cu_seqlens is None:
         return B * ((T + _lib.CHUNK - 1) // _lib.CHUNK)
     lens = (cu_seqlens[1:] - cu_seqlens[:-1]).to("cpu", torch.int64)
     return int(((lens + _lib.CHUNK - 1) // _lib.CHUNK).sum())
+
+
+def chunk_bound(T, B=1, n_seq=None):
+    """Upper bound on the chunk count without reading cu_seqlens: B ceil(T/64), or
+    ceil(T/64) + n_seq for n_seq packed sequences (the bound the library uses)."""
+    nct = (T + _lib.CHUNK - 1) // _lib.CHUNK
+    return B * nct if n_seq is None else nct + n_seq
 
 
 def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
@@ -76,9 +96,12 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     h [1,NT,H_v,K,V] fp32 the chunk-start states (None unless return_h);
     final_state [N,H_v,K,V] fp32 (None unless output_final_state).  With
     ``return_wu`` also returns W, U [B,T,H_v,K|V] fp32.  ``cp_mode``: "auto"
-    (split long sequences of few heads, with the warm-up), "auto_exact" (the same
-    trigger, exact split), "off" (no split), "warmup" (split with the
-    sliding-window warm-up) or "exact" (split with the exact carry).
+    (split where the device model predicts a gain; each segment warms up over a
+    window chosen from its gates, or from the sequence start where they do not
+    decay: exact to fp32 rounding for any gates), "auto_exact" (the device model,
+    exact carry), "auto_pages" (the pages' trigger with a fixed warm-up window),
+    "off" (no split), "warmup" (split with a fixed warm-up window of
+    ``cp_warmup_chunks``) or "exact" (split with the exact carry).
 
     ``return_h_bwd`` replaces h by a :class:`SavedForBackward` (the chunk-start
     states in the backward's layout and the T blocks); passed to
@@ -90,8 +113,8 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     ``return_ga=False`` g_cum and A are not written (None): a bf16 backward
     given ``h_bwd`` does not read them.
     """
-    if return_h_bwd and cp_mode == "warmup":
-        raise ValueError("return_h_bwd needs exact states: not with cp_mode='warmup'")
+    if return_h_bwd and cp_mode in ("warmup", "auto_pages"):
+        raise ValueError("return_h_bwd needs exact states: not with a fixed warm-up window")
     _check(q, k, v, g, beta, cu_seqlens)
     q, k, v = _c(q), _c(k), _c(v)
     g, beta = _c(g, torch.float32), _c(beta, torch.float32)
@@ -104,7 +127,7 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     h0 = _c(initial_state, torch.float32)
     if h0 is not None and h0.shape != (n_seq, Hv, K, V):
         raise ValueError("initial_state must be [N,H_v,K,V]")
-    cu = _c(cu_seqlens)
+    cu = None if cu_seqlens is None else _c(cu_seqlens).to(dev)
     o = torch.empty((B, T, Hv, V), dtype=output_dtype, device=dev)
     g_cum = A = None
     if return_ga:
@@ -113,10 +136,12 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     ht = torch.empty((n_seq, Hv, K, V), dtype=torch.float32, device=dev) if output_final_state else None
     h = None
     if return_h and not return_h_bwd:
-        h = torch.empty((1 if cu is not None else B, num_chunks(T, 1, cu) if cu is not None
+        # the exact chunk count: from host offsets as given, else read back (a sync)
+        h = torch.empty((1 if cu is not None else B, num_chunks(T, 1, cu_seqlens) if cu is not None
                          else num_chunks(T), Hv, K, V), dtype=torch.float32, device=dev)
     if return_h_bwd:
-        h = torch.empty((num_chunks(T, 1, cu) if cu is not None else num_chunks(T, B), Hv, 4 * K * V),
+        # sized by the bound, so the training path never reads the offsets back
+        h = torch.empty((chunk_bound(T, B, n_seq if cu is not None else None), Hv, 4 * K * V),
                         dtype=torch.uint8, device=dev)
     w = u = None
     if return_wu:
@@ -177,9 +202,9 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
         scale = 1.0 / math.sqrt(K)
     h0 = _c(initial_state, torch.float32)
     dht = _c(dht, torch.float32)
-    cu = _c(cu_seqlens)
+    cu = None if cu_seqlens is None else _c(cu_seqlens).to(dev)
     if h_bwd is not None:
-        nt = num_chunks(T, 1, cu) if cu is not None else num_chunks(T, B)
+        nt = chunk_bound(T, B, n_seq if cu is not None else None)
         st = h_bwd.states
         if st is not None and (st.dtype != torch.uint8 or st.shape != (nt, Hv, 4 * K * V)
                                or not st.is_contiguous()):

@@ -21,11 +21,15 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // computed on the device with one thread per sequence, O(n_seq^2) work).
 constexpr int64_t LPT_MAX_SEQ = 8192;
 bool use_lpt(bool varlen, int64_t n_seq) { return varlen && n_seq <= LPT_MAX_SEQ; }
-// varlen bookkeeping: chunk offsets [n_seq + 1], then the length order [n_seq]
+// varlen bookkeeping: chunk offsets [n_seq + 1], the clamped sequence bounds
+// [n_seq + 1] that every kernel reads, then the length order [n_seq]
 size_t seq_table_bytes(bool varlen, int64_t n_seq) {
     if (!varlen) return 0;
-    return up(sizeof(int32_t) * (size_t)(n_seq + 1 + (use_lpt(varlen, n_seq) ? n_seq : 0)));
+    return up(sizeof(int32_t) * (size_t)(2 * (n_seq + 1) + (use_lpt(varlen, n_seq) ? n_seq : 0)));
 }
+// the table's parts, from its base (the chunk offsets)
+int32_t *seq_bounds(int32_t *chunk_off, int64_t n_seq) { return chunk_off + n_seq + 1; }
+int32_t *seq_order(int32_t *chunk_off, int64_t n_seq) { return chunk_off + 2 * (n_seq + 1); }
 
 struct FwdPlan {
     int64_t n_seq, tokens, nct, nt_ub;  // nct: chunks per sequence bound
@@ -34,7 +38,7 @@ struct FwdPlan {
     // exact split: segment transitions, zero-start end states, true start states, a zero row
     size_t off_M, off_b, off_hseg, off_zero;
     int seg_chunks, warm_chunks, n_seg;
-    bool split, exact;
+    bool split, exact, gated;  // gated: gate-driven warm-up windows (GDR_CP_AUTO)
 };
 
 int check_dims(int64_t B, int64_t T, int64_t Hq, int64_t Hv, int64_t K, int64_t V, int64_t n_seq,
@@ -45,7 +49,7 @@ int check_dims(int64_t B, int64_t T, int64_t Hq, int64_t Hv, int64_t K, int64_t 
     if (dtype != GDR_BF16 && dtype != GDR_F32) return GDR_ENOTSUP;
     if ((K != 64 && K != 128) || (V != 64 && V != 128)) return GDR_ENOTSUP;
     // 32-bit limits of the chunk bookkeeping
-    if (B * T > (int64_t)1 << 31 || (varlen ? n_seq : B) * Hv > (int64_t)1 << 30) return GDR_EINVAL;
+    if (B * T >= (int64_t)1 << 31 || (varlen ? n_seq : B) * Hv > (int64_t)1 << 30) return GDR_EINVAL;
     return GDR_OK;
 }
 
@@ -57,11 +61,15 @@ int check_dims(int64_t B, int64_t T, int64_t Hq, int64_t Hv, int64_t K, int64_t 
 //   exact split:    rounds x 3 L + (S - 1)   (transitions, zero-start states and
 //                   output passes, one carry step per segment)
 // with L = ceil(N / S) (ties: fewer segments); one segment costs rounds x N.
-// Segment counts beyond eight rounds of the device are not considered.
-// Returns N + 1 (no split) when one segment is best.
-int64_t split_chunks(int64_t N, int64_t W, int64_t slots, int64_t wm, int64_t min_seg, bool exact = false) {
+// Segment counts beyond eight rounds of the device are not considered, and with
+// one_round none beyond one round (the gate-driven split: a head whose gates do
+// not decay makes every segment scan from the sequence start, which then costs
+// no more than one unsplit pass).  Returns N + 1 (no split) when one segment is best.
+int64_t split_chunks(int64_t N, int64_t W, int64_t slots, int64_t wm, int64_t min_seg, bool exact = false,
+                     bool one_round = false) {
     int64_t best_t = -1, best_L = N + 1;
-    const int64_t s_max = std::min(N, 8 * cdiv(slots, std::max<int64_t>(W, 1)));
+    const int64_t per_round = std::max<int64_t>(1, slots / std::max<int64_t>(W, 1));
+    const int64_t s_max = std::min(N, one_round ? per_round : 8 * cdiv(slots, std::max<int64_t>(W, 1)));
     for (int64_t S = min_seg; S <= s_max; ++S) {
         const int64_t L = cdiv(N, S), Sx = cdiv(N, L);
         if (Sx != S) continue;  // same L as a smaller S
@@ -85,10 +93,10 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     int rc = check_dims(a->B, a->T, a->H_q, a->H_v, a->K, a->V, a->n_seq, varlen, a->dtype);
     if (rc) return rc;
     if (a->out_dtype != GDR_BF16 && a->out_dtype != GDR_F32) return GDR_ENOTSUP;
-    if (a->cp_mode < GDR_CP_AUTO || a->cp_mode > GDR_CP_AUTO_EXACT) return GDR_EINVAL;
+    if (a->cp_mode < GDR_CP_AUTO || a->cp_mode > GDR_CP_AUTO_PAGES) return GDR_EINVAL;
     if (a->cp_segment_chunks < 0 || a->cp_warmup_chunks < 0) return GDR_EINVAL;
-    // the backward's states must be exact: no warm-up split, and AUTO splits as AUTO_EXACT
-    if (a->h_bwd && (a->h || a->cp_mode == GDR_CP_WARMUP)) return GDR_EINVAL;
+    // the backward's states must be exact: no fixed warm-up window, and AUTO splits as AUTO_EXACT
+    if (a->h_bwd && (a->h || a->cp_mode == GDR_CP_WARMUP || a->cp_mode == GDR_CP_AUTO_PAGES)) return GDR_EINVAL;
     const int32_t cp_mode = a->h_bwd && a->cp_mode == GDR_CP_AUTO ? GDR_CP_AUTO_EXACT : a->cp_mode;
     pl.n_seq = varlen ? a->n_seq : a->B;
     pl.tokens = a->B * a->T;
@@ -101,20 +109,24 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     pl.tblk_bytes = up(tblock_bytes(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32) * (size_t)(pl.nt_ub * a->H_v));
     off += pl.tblk_bytes;
     pl.total = off;
-    // sequence split ("AutoCP"): the pages' trigger on batch x heads and length
+    // sequence split ("AutoCP")
     const int64_t bh = pl.n_seq * a->H_v;
-    // GDR_CP_AUTO: the pages' trigger (warm-up split); GDR_CP_AUTO_EXACT: the device
-    // model alone decides (the exact split costs no accuracy)
-    const bool autom = cp_mode == GDR_CP_AUTO || cp_mode == GDR_CP_AUTO_EXACT;
+    // GDR_CP_AUTO: the device model decides, segments warm up over a gate-driven
+    // window; GDR_CP_AUTO_EXACT: the device model decides, exact carry;
+    // GDR_CP_AUTO_PAGES: the pages' trigger on batch x heads and length, fixed window
+    const bool autom = cp_mode == GDR_CP_AUTO || cp_mode == GDR_CP_AUTO_EXACT || cp_mode == GDR_CP_AUTO_PAGES;
     const bool exact_mode = cp_mode == GDR_CP_EXACT || cp_mode == GDR_CP_AUTO_EXACT;
-    bool split = cp_mode == GDR_CP_WARMUP || exact_mode ||
-                 (cp_mode == GDR_CP_AUTO && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
+    const bool gated = cp_mode == GDR_CP_AUTO;
+    bool split = cp_mode == GDR_CP_WARMUP || exact_mode || gated ||
+                 (cp_mode == GDR_CP_AUTO_PAGES && (bh <= 40 || (bh <= 56 && a->T >= 8192)));
     pl.warm_chunks = a->cp_warmup_chunks > 0 ? a->cp_warmup_chunks : 8;
     const int64_t n_vt = a->V / scan_vtile(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32, (int)a->K, (int)a->V);
+    // the gate-driven window is priced at one chunk (gates that decay as the
+    // workloads' do need one)
     int64_t L = a->cp_segment_chunks > 0
                     ? a->cp_segment_chunks
-                    : split_chunks(pl.nct, bh * n_vt, slots > 0 ? slots : DEFAULT_SLOTS, pl.warm_chunks,
-                                   autom ? 1 : 2, exact_mode);
+                    : split_chunks(pl.nct, bh * n_vt, slots > 0 ? slots : DEFAULT_SLOTS,
+                                   gated ? 1 : pl.warm_chunks, autom ? 1 : 2, exact_mode, gated);
     if (L < 1) L = 1;
     if (!split || L >= pl.nct) {
         split = false;
@@ -122,7 +134,8 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     }
     pl.split = split;
     pl.exact = split && exact_mode;
-    if (pl.exact) pl.warm_chunks = 0;
+    pl.gated = split && gated;
+    if (pl.exact || pl.gated) pl.warm_chunks = 0;
     pl.seg_chunks = (int)L;
     pl.n_seg = split ? (int)cdiv(pl.nct, L) : 1;
     pl.off_M = pl.off_b = pl.off_hseg = pl.off_zero = 0;
@@ -213,14 +226,16 @@ int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl, int64_t slots = 0) {
     return GDR_OK;
 }
 
-SeqMap make_map(const gdr_fwd_args *a, const FwdPlan &pl, const int32_t *chunk_off) {
+// sequence view of a launch; with packed sequences the kernels read the clamped
+// bounds written by launch_chunk_offsets, never the caller's cu_seqlens
+SeqMap make_map(bool varlen, int64_t T, int64_t n_seq, int64_t nct, int32_t *chunk_off) {
     SeqMap m;
-    m.cu = a->cu_seqlens;
+    m.cu = varlen ? seq_bounds(chunk_off, n_seq) : nullptr;
     m.chunk_off = chunk_off;
-    m.order = use_lpt(a->cu_seqlens != nullptr, pl.n_seq) ? chunk_off + pl.n_seq + 1 : nullptr;
-    m.T = a->T;
-    m.n_seq = (int32_t)pl.n_seq;
-    m.nct = (int32_t)pl.nct;
+    m.order = use_lpt(varlen, n_seq) ? seq_order(chunk_off, n_seq) : nullptr;
+    m.T = T;
+    m.n_seq = (int32_t)n_seq;
+    m.nct = (int32_t)nct;
     return m;
 }
 
@@ -291,13 +306,14 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
     char *tblk = ws + pl.off_tblk;
     const Dt dt = a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
     const Dt ot = a->out_dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
-    const SeqMap sm = make_map(a, pl, chunk_off);
+    const SeqMap sm = make_map(a->cu_seqlens != nullptr, a->T, pl.n_seq, pl.nct, chunk_off);
 
     auto mark = [&](int i) {
         return !a->events || !a->events[i] || hipEventRecord(a->events[i], stream) == hipSuccess;
     };
-    if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, chunk_off, const_cast<int32_t *>(sm.order),
-                                              (int)pl.n_seq, stream) != hipSuccess)
+    if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, const_cast<int32_t *>(sm.cu), chunk_off,
+                                              const_cast<int32_t *>(sm.order), (int)pl.n_seq, a->T,
+                                              stream) != hipSuccess)
         return GDR_ELAUNCH;
     if (!mark(0)) return GDR_ELAUNCH;
     if (pl.tokens > 0) {
@@ -338,6 +354,7 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
     sp.scale = a->scale;
     sp.seg_chunks = pl.seg_chunks;
     sp.warm_chunks = pl.warm_chunks;
+    sp.warm_gated = pl.gated;
     sp.n_vt = (int)(a->V / scan_vtile(dt, (int)a->K, (int)a->V));
     sp.n_units = (int)(pl.n_seq * a->H_v);
     sp.n_seg = pl.n_seg;
@@ -441,13 +458,7 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
     char *ws = static_cast<char *>(a->workspace);
     int32_t *chunk_off = a->cu_seqlens ? reinterpret_cast<int32_t *>(ws + pl.off_chunk) : nullptr;
     const Dt dt = a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
-    SeqMap sm;
-    sm.cu = a->cu_seqlens;
-    sm.chunk_off = chunk_off;
-    sm.order = use_lpt(a->cu_seqlens != nullptr, pl.n_seq) ? chunk_off + pl.n_seq + 1 : nullptr;
-    sm.T = a->T;
-    sm.n_seq = (int32_t)pl.n_seq;
-    sm.nct = (int32_t)pl.nct;
+    const SeqMap sm = make_map(a->cu_seqlens != nullptr, a->T, pl.n_seq, pl.nct, chunk_off);
     const int n_units = (int)(pl.n_seq * a->H_v);
 
     BwdParams bp;
@@ -481,8 +492,9 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
     auto mark = [&](int i) {
         return !a->events || !a->events[i] || hipEventRecord(a->events[i], stream) == hipSuccess;
     };
-    if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, chunk_off, const_cast<int32_t *>(sm.order),
-                                              (int)pl.n_seq, stream) != hipSuccess)
+    if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, const_cast<int32_t *>(sm.cu), chunk_off,
+                                              const_cast<int32_t *>(sm.order), (int)pl.n_seq, a->T,
+                                              stream) != hipSuccess)
         return GDR_ELAUNCH;
     if (!mark(0)) return GDR_ELAUNCH;
     if (pl.tokens > 0 && !a->tblk_bwd && launch_tblocks(dt, bp, (int)pl.nt_ub, stream) != hipSuccess)
@@ -512,6 +524,7 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
         sp.scale = a->scale;
         sp.seg_chunks = pl.seg_chunks;
         sp.warm_chunks = 0;
+        sp.warm_gated = 0;
         sp.n_vt = (int)(a->V / scan_vtile(dt, (int)a->K, (int)a->V));
         sp.n_units = n_units;
         sp.n_seg = pl.n_seg;
@@ -572,6 +585,7 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
         tp.scale = a->scale;
         tp.seg_chunks = pl.seg_chunks;
         tp.warm_chunks = 0;
+        tp.warm_gated = 0;
         tp.n_vt = (int)(a->K / scan_vtile(dt, (int)a->K, (int)a->K));
         tp.n_units = n_units;
         tp.n_seg = pl.n_seg;

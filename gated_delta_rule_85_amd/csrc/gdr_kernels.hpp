@@ -42,6 +42,10 @@ struct ScanParams {
     float scale;
     int seg_chunks;   // chunks per segment
     int warm_chunks;  // warm-up window of segments after the first
+    // gate-driven warm-up (instead of warm_chunks): a segment after the first starts
+    // from a zero state at the latest chunk from which the gates decay the state by
+    // at least 2^-24 up to the segment's start, or from the sequence start
+    int warm_gated;
     int n_vt, n_units, n_seg;
     // exact sequence split: segments after the first start from h0_seg (or, eye_h0,
     // from the identity, V = K, which makes the segment's end state its transition
@@ -99,8 +103,10 @@ struct BwdParams {
     float *d_seg;
 };
 
-// chunk offsets of packed sequences and (order non-null) their longest-first order
-hipError_t launch_chunk_offsets(const int32_t *cu, int32_t *chunk_off, int32_t *order, int n_seq, hipStream_t s);
+// clamped bounds (cuc) and chunk offsets of packed sequences and (order non-null)
+// their longest-first order; every kernel reads the bounds from cuc
+hipError_t launch_chunk_offsets(const int32_t *cu, int32_t *cuc, int32_t *chunk_off, int32_t *order, int n_seq,
+                               int64_t T, hipStream_t s);
 hipError_t launch_prep(Dt dt, int K, const PrepParams &p, int n_chunks_ub, hipStream_t s);
 hipError_t launch_scan_output(Dt dt, Dt out, int K, int V, const ScanParams &p, hipStream_t s);
 hipError_t launch_wu(Dt dt, const WUParams &p, int n_chunks_ub, hipStream_t s);

@@ -275,20 +275,29 @@ __global__ __launch_bounds__(NTHR) void wu_kernel(const WUParams p) {
     }
 }
 
-// chunk offsets of packed sequences: chunk_off[j] = sum_{i<j} ceil(len_i/64)
-__global__ void chunk_offsets_kernel(const int32_t *cu, int32_t *off, int n_seq) {
+// Sequence bounds of packed sequences, clamped so that no kernel can index
+// past the packed tokens whatever the caller's offsets hold: cuc[0] =
+// clamp(cu[0], 0, T), cuc[j] = clamp(cu[j], cuc[j-1], T) (non-decreasing, at
+// most T), and chunk_off[j] = sum_{i<j} ceil((cuc[i+1] - cuc[i]) / 64).  For
+// valid offsets (cu[0] = 0, non-decreasing, cu[n] = T) cuc equals cu.
+__global__ void chunk_offsets_kernel(const int32_t *cu, int32_t *cuc, int32_t *off, int n_seq, int32_t T) {
     if (threadIdx.x == 0 && blockIdx.x == 0) {
         int32_t acc = 0;
+        int32_t prev = min(max(cu[0], 0), T);
+        cuc[0] = prev;
         for (int j = 0; j < n_seq; ++j) {
+            const int32_t nx = min(max(cu[j + 1], prev), T);
+            cuc[j + 1] = nx;
             off[j] = acc;
-            acc += (cu[j + 1] - cu[j] + CH - 1) / CH;
+            acc += (nx - prev + CH - 1) / CH;
+            prev = nx;
         }
         off[n_seq] = acc;
     }
 }
 
 // order[rank] = j: sequences by decreasing length, ties by index (one thread per
-// sequence counts the sequences ahead of it)
+// sequence counts the sequences ahead of it); cu is the clamped table
 __global__ void seq_order_kernel(const int32_t *cu, int32_t *order, int n_seq) {
     const int j = blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= n_seq) return;
@@ -303,9 +312,10 @@ __global__ void seq_order_kernel(const int32_t *cu, int32_t *order, int n_seq) {
 
 }  // namespace
 
-hipError_t launch_chunk_offsets(const int32_t *cu, int32_t *chunk_off, int32_t *order, int n_seq, hipStream_t s) {
-    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, s, cu, chunk_off, n_seq);
-    if (order) hipLaunchKernelGGL(seq_order_kernel, dim3((n_seq + 255) / 256), dim3(256), 0, s, cu, order, n_seq);
+hipError_t launch_chunk_offsets(const int32_t *cu, int32_t *cuc, int32_t *chunk_off, int32_t *order, int n_seq,
+                               int64_t T, hipStream_t s) {
+    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, s, cu, cuc, chunk_off, n_seq, (int32_t)T);
+    if (order) hipLaunchKernelGGL(seq_order_kernel, dim3((n_seq + 255) / 256), dim3(256), 0, s, cuc, order, n_seq);
     return hipGetLastError();
 }
 

@@ -34,7 +34,10 @@
 // seg_chunks smaller than the sequence, segment s > 0 starts from a zero
 // state warm_chunks chunks before its first chunk (from the true initial
 // state when that window reaches chunk 0) and runs the scan without output
-// over the window before its own chunks.  For the exact split a segment can
+// over the window before its own chunks.  With warm_gated the window is
+// chosen from the gates instead (gated_window_start): the shortest one whose
+// decay makes the zero start as good as the true state in fp32, or the whole
+// prefix when the gates do not decay that much.  For the exact split a segment can
 // instead start from a given state (h0_seg) or from the identity over a
 // shared zero row of values (its end state is then the segment's transition
 // matrix), and hand its end state to hT_seg; carry_kernel below chains them.
@@ -365,6 +368,36 @@ template <typename In, typename Out, int KD, bool STATES> struct Scan {
     }
 };
 
+// First chunk of the gate-driven warm-up window of a segment that starts at
+// chunk c_begin of its sequence: the latest chunk w such that the log-gates of
+// chunks [w, c_begin) sum to -24 ln 2 or less, so that the zero-state start at
+// w differs from the true state at c_begin by at most 2^-24 of the state at w
+// (each token maps the state error e to e^g (I - beta k k^T) e, of norm at most
+// e^g |e| for a unit key and 0 <= beta <= 2); 0 (the sequence start, from the
+// true initial state, exact) when the gates of the whole prefix decay less.
+// Each chunk's total log-gate is the last entry of its T block's running sum.
+// Wave-uniform result; all lanes take part.
+template <int TBYTES>
+__device__ int gated_window_start(const char *tblk, int64_t cb, int Hv, int hv, int c_begin, int sc_off) {
+    constexpr float LOG_2M24 = -16.6355323f;  // -24 ln 2
+    const int l = lane_id();
+    float acc = 0.f;
+    int c = c_begin;
+    while (c > 0) {
+        const int cnt = min(c, 64);
+        float x = 0.f;
+        if (l < cnt)
+            x = *reinterpret_cast<const float *>(tblk + ((cb + c - 1 - l) * Hv + hv) * (int64_t)TBYTES + sc_off +
+                                                 4 * (CH - 1));
+        const float ps = acc + wave_prefix_sum(x);  // chunks c-1 .. c-1-l
+        const uint64_t hit = __ballot(l < cnt && ps <= LOG_2M24);
+        if (hit) return c - 1 - __builtin_ctzll(hit);
+        acc = __shfl(ps, cnt - 1);
+        c -= cnt;
+    }
+    return 0;
+}
+
 // STATES: chunk-start states only (no scores, no output), for the backward
 template <typename In, typename Out, int KD, bool STATES>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_output_kernel(const ScanParams p) {
@@ -398,7 +431,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
     const int c_begin = seg * p.seg_chunks;
     if (c_begin >= N && !(N == 0 && seg == 0)) return;
     const int c_end = min(N, c_begin + p.seg_chunks);
-    const int w_begin = seg == 0 ? 0 : max(0, c_begin - p.warm_chunks);
+    S.cb = p.sm.chunk_base(S.j);
+    int w_begin = seg == 0 ? 0 : max(0, c_begin - p.warm_chunks);
+    if (seg > 0 && p.warm_gated)
+        w_begin = __builtin_amdgcn_readfirstlane(gated_window_start<C::TB::BYTES>(
+            p.tblk, S.cb, p.Hv, S.hv, c_begin, C::TB::SC));
 
     S.tid = threadIdx.x;
     S.w = __builtin_amdgcn_readfirstlane(wave_id());
@@ -409,7 +446,6 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
     S.kp = reinterpret_cast<const In *>(p.k);
     S.vp = reinterpret_cast<const In *>(p.v);
     S.op = reinterpret_cast<Out *>(p.o);
-    S.cb = p.sm.chunk_base(S.j);
     S.pend_ts = -1;
     S.pend_n = 0;
     S.setup_copies();

@@ -14,13 +14,14 @@
  * strictly lower decayed beta*K K^T matrix A, T = (I + A)^{-1}, and a serial
  * scan over chunks that produces the chunk-start states and the output.
  *
- * Argument names and order follow the README's low-level API,
- *     g, A, o, h, final_state = chunk_gated_delta_rule_fwd(q, k, v, g, beta,
- *                                   scale, initial_state, cu_seqlens)
- *     dq, dk, dv, db, dg, dh0 = chunk_gated_delta_rule_bwd(q, k, v, g, beta,
- *                                   A, do, dht, scale, initial_state, cu_seqlens)
- * where the forward's returned g is the in-chunk cumulative log-gate and A is
- * T, one 64-wide row per token.
+ * The argument lists follow the low-level API of the README ("Usage", "Low-level
+ * API"): the forward takes the five input tensors, the output scale, an optional
+ * initial state and optional sequence offsets, and hands back five results in
+ * the order gate cumsum, A, o, chunk-start states, final state; the backward
+ * takes the same inputs plus the forward's gate cumsum and A, the gradients of
+ * o and of the final state, and hands back the gradients of q, k, v, beta, g
+ * and the initial state, in that order.  Here the forward's gate result is the
+ * in-chunk cumulative log-gate and its A is T, one 64-wide row per token.
  *
  * Conventions (all entry points):
  *  - Every pointer in an args struct is a DEVICE pointer unless stated; all
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 5
+#define GDR_ABI_VERSION 6
 #define GDR_CHUNK 64
 #define GDR_FWD_STAGES 3
 #define GDR_BWD_STAGES 4
@@ -62,15 +63,30 @@ extern "C" {
 #define GDR_BF16 0
 #define GDR_F32 1
 
-/* sequence-split ("AutoCP") modes of the forward */
-#define GDR_CP_AUTO 0   /* split when B*H_v <= 40, or B*H_v <= 56 and T >= 8192 */
+/* sequence-split ("AutoCP") modes of the forward.  The pages' AutoCP splits a
+   long sequence into segments that run in parallel, each warmed up from a zero
+   state over a few chunks before its own (aiboss88 "Core advantages"; efeozkan
+   blog "1. Gate-Driven Automatic Intra-Card Context Parallelism (AutoCP)"). */
+#define GDR_CP_AUTO 0   /* split where the device model of gdr_fwd predicts a gain, with
+                           one dispatch round at most; each segment warms up over a
+                           window chosen from its gates: the latest chunk from which the
+                           log-gates up to the segment's start sum to -24 ln 2 or less
+                           (the zero start is then within 2^-24 of the true state), or
+                           the sequence start (exact) when none does.  Safe for gates
+                           that do not decay; costs about one chunk of warm-up per
+                           segment on gates that decay as the configs' do */
 #define GDR_CP_OFF 1    /* exact scan, one segment per sequence */
-#define GDR_CP_WARMUP 2 /* always split; each segment warms up from a zero state */
+#define GDR_CP_WARMUP 2 /* always split; each segment warms up from a zero state over
+                           cp_warmup_chunks chunks (the pages use 6 to 8): approximate
+                           where the gates do not decay within that window */
 #define GDR_CP_EXACT 3  /* always split, exactly: each segment's transition matrix and
                            zero-start end state are scanned in parallel, a serial carry
                            over the segments gives their true start states, then the
                            segments run again with output */
 #define GDR_CP_AUTO_EXACT 4 /* the exact split where the device model predicts a gain */
+#define GDR_CP_AUTO_PAGES 5 /* the pages' trigger and window: split when B*H_v <= 40, or
+                               B*H_v <= 56 and T >= 8192 (constants tuned for a 132-SM
+                               GPU), warming up over cp_warmup_chunks as GDR_CP_WARMUP */
 
 typedef struct {
     /* sizes.  With cu_seqlens, B must be 1, T is the packed token count and
@@ -90,7 +106,14 @@ typedef struct {
     const float *g;             /* [B,T,H_v] per-token log-decay (<= 0 for decay) */
     const float *beta;          /* [B,T,H_v] */
     const float *initial_state; /* [N,H_v,K,V], N = B or n_seq; NULL = zeros */
-    const int32_t *cu_seqlens;  /* [n_seq+1] monotone token offsets, or NULL */
+    const int32_t *cu_seqlens;  /* [n_seq+1] token offsets: 0, non-decreasing, T last; or NULL.
+                                   The library reads them on the device only and clamps
+                                   each entry to [previous entry, T] (the first to [0, T])
+                                   before any kernel uses them, so offsets outside that
+                                   range cannot make a kernel touch memory past the
+                                   tensors; the results are then those of the clamped
+                                   offsets.  Callers validate them where they are on the
+                                   host (the Python binding does) */
     /* outputs */
     void *o;                    /* [B,T,H_v,V] out_dtype */
     float *final_state;         /* [N,H_v,K,V]; NULL = not wanted */
@@ -105,7 +128,8 @@ typedef struct {
                                    gdr_bwd_args.h_bwd, it saves the backward's recompute of
                                    the states.  NULL = not written.  The states must be
                                    exact: with h_bwd, GDR_CP_AUTO splits as
-                                   GDR_CP_AUTO_EXACT, and h or GDR_CP_WARMUP is GDR_EINVAL */
+                                   GDR_CP_AUTO_EXACT, and h, GDR_CP_WARMUP or
+                                   GDR_CP_AUTO_PAGES is GDR_EINVAL */
     void *tblk_bwd;             /* gdr_tblocks_bytes() bytes, or NULL: the per-(chunk, v head)
                                    T blocks (T = (I+A)^{-1} and the chunk's gate scalars) are
                                    also written here, in the backward's layout; passed on as

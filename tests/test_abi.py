@@ -88,18 +88,18 @@ def test_workspace_sizes(L):
     assert rc == 0 and n == 4 * 4 * TBLOCK
     rc, n = rc_ws(L, fwd_args(L, g_cum=16, A=16))
     assert rc == 0 and n == 4 * 4 * TBLOCK
-    # packed sequences: chunk-offset table (256-byte aligned) + blocks for up to
-    # ceil(T/64) + n_seq chunks
+    # packed sequences: chunk offsets and clamped bounds (2 (n_seq + 1) int32, the
+    # table 256-byte aligned) + blocks for up to ceil(T/64) + n_seq chunks
     rc, n = rc_ws(L, fwd_args(L, cu_seqlens=16, n_seq=3))
     assert rc == 0 and n == 256 + (4 + 3) * 4 * TBLOCK
     rc, n = rc_ws(L, fwd_args(L, dtype=L.F32, K=64, V=64))
     assert rc == 0 and n == 4 * 4 * TBLOCK
-    # up to 8192 packed sequences also get their longest-first order: (2 n_seq + 1)
-    # int32 entries; beyond that only the offsets
+    # up to 8192 packed sequences also get their longest-first order: (3 n_seq + 2)
+    # int32 entries; beyond that only the offsets and bounds
     rc, n = rc_ws(L, fwd_args(L, cu_seqlens=16, n_seq=100))
-    assert rc == 0 and n == 1024 + (4 + 100) * 4 * TBLOCK
+    assert rc == 0 and n == 1280 + (4 + 100) * 4 * TBLOCK
     rc, n = rc_ws(L, fwd_args(L, cu_seqlens=16, n_seq=9000))
-    assert rc == 0 and n == 36096 + (4 + 9000) * 4 * TBLOCK
+    assert rc == 0 and n == 72192 + (4 + 9000) * 4 * TBLOCK
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -112,7 +112,8 @@ def test_workspace_sizes(L):
     (dict(T=-1), -1),
     (dict(cu_seqlens=16, n_seq=0), -1),
     (dict(cu_seqlens=16, n_seq=2, B=2), -1),
-    (dict(cp_mode=5), -1),
+    (dict(cp_mode=6), -1),
+    (dict(cp_mode=-1), -1),
     (dict(cp_segment_chunks=-1), -1),
 ])
 def test_validation_errors(L, kw, code):
@@ -143,6 +144,7 @@ def test_forward_states_for_the_backward(L):
     assert n_hb == n_exact > n_auto  # the exact split's transitions and states
     assert rc_ws(L, fwd_args(L, h_bwd=16, h=16))[0] == L.EINVAL
     assert rc_ws(L, fwd_args(L, h_bwd=16, cp_mode=L.CP_WARMUP))[0] == L.EINVAL
+    assert rc_ws(L, fwd_args(L, h_bwd=16, cp_mode=L.CP_AUTO_PAGES))[0] == L.EINVAL
     a = fwd_args(L, q=16, k=16, v=16, g=16, beta=16, o=16, h_bwd=24, workspace=4096,
                  workspace_bytes=1 << 30)
     assert L.lib.gdr_fwd(ctypes.byref(a), None) == L.EINVAL  # misaligned h_bwd
@@ -218,3 +220,14 @@ def test_bwd_host_errors_before_any_launch(L):
     assert L.lib.gdr_bwd(ctypes.byref(bwd_args(L, **full)), None) == L.EWORKSPACE
     bad = dict(full, dq=24, workspace=4096, workspace_bytes=1 << 34)
     assert L.lib.gdr_bwd(ctypes.byref(bwd_args(L, **bad)), None) == L.EINVAL
+
+
+def test_host_offsets_are_validated(L):
+    """Packed-sequence offsets given on the host are checked by the binding before
+    anything reaches the device: 0 first, never decreasing, T last."""
+    import torch
+    from gated_delta_rule_85_amd.api import check_offsets
+    check_offsets(torch.tensor([0, 5, 5, 9], dtype=torch.int32), 9)
+    for bad in ([1, 5, 9], [0, 5, 4, 9], [0, 5, 10], [0, 5, 8], [0]):
+        with pytest.raises(ValueError):
+            check_offsets(torch.tensor(bad, dtype=torch.int32), 9)

@@ -38,3 +38,14 @@ def test_backward_flop_model_is_positive_and_scales_with_tokens():
     two = bench.bwd_algorithmic_flops(dict(cfg, B=2))
     for k in one:
         assert one[k] > 0 and two[k] == 2 * one[k]
+
+
+def test_minimal_bytes_of_the_prefill_shard():
+    """The path's least bytes per token and v head at K = V = 128, G = 2, bf16, T = 4096
+    with an initial state: q and k 128 each (shared by 2 v heads), v 256, g and beta 8,
+    o 256 in bf16 (512 in fp32), the two states amortised 32."""
+    cfg = dict(B=4, T=4096, Hq=16, Hv=32, K=128, V=128, dtype="bf16", h0=True)
+    assert bench.minimal_bytes_per_token_head(cfg) == 808
+    assert bench.minimal_bytes_per_token_head(cfg, out_bytes=4) == 1064
+    # packed sequences: the states of every sequence over the packed tokens
+    assert bench.minimal_bytes_per_token_head(dict(cfg, B=1, T=16384, n_seq=4)) == 808

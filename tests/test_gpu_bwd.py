@@ -340,3 +340,32 @@ def test_fp32_inputs_longer_sequence():
     x = make_inputs(dict(B=1, T=1000, Hq=1, Hv=2, K=128, V=128, dtype="fp32", h0=True), seed=8,
                     grads=True)
     compare(x, run_bwd(x), ora_bwd(x))
+
+
+def test_varlen_autograd_step_without_host_sync():
+    """A differentiable varlen step (forward handing its states and T blocks to the
+    backward, offsets on the device) makes no host synchronisation: torch's sync
+    debug mode raises on any .cpu(), .item() or blocking copy on the path."""
+    from gated_delta_rule_85_amd import chunk_gated_delta_rule
+    x = make_inputs(dict(lens=[300, 1, 0, 700, 129], Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True),
+                    seed=17, grads=True)
+    d = gpu_inputs(x)
+    leaves = {n: d[n].clone().requires_grad_(True) for n in ("q", "k", "v", "g", "beta",
+                                                             "initial_state")}
+    do, dht = dev(x["do"]), dev(x["dht"])
+    torch.cuda.synchronize()
+    torch.cuda.set_sync_debug_mode("error")
+    try:
+        o, ht = chunk_gated_delta_rule(leaves["q"], leaves["k"], leaves["v"], leaves["g"], leaves["beta"],
+                                       x["scale"], leaves["initial_state"], output_final_state=True,
+                                       cu_seqlens=d["cu_seqlens"])
+        loss = (o * do).sum() + (ht * dht).sum()
+        loss.backward()
+    finally:
+        torch.cuda.set_sync_debug_mode(0)
+    torch.cuda.synchronize()
+    ref = ora_bwd(x)
+    got = dict(dq=leaves["q"].grad, dk=leaves["k"].grad, dv=leaves["v"].grad,
+               dbeta=leaves["beta"].grad, dg=leaves["g"].grad, dh0=leaves["initial_state"].grad)
+    check_rounded(got, ref)
+    compare(x, got, ref, names=("dbeta", "dg", "dh0"))

@@ -203,3 +203,23 @@ def test_timing_events_with_null_entries():
         hip.hipEventDestroy(arr[i])
     assert torch.equal(o, ref[2]) and torch.equal(ht, ref[4])
     assert torch.equal(gc, ref[0]) and torch.equal(A, ref[1])
+
+
+def test_device_offsets_are_clamped():
+    """Offsets on the device are never read on the host; the library clamps each to
+    [previous, T] before any kernel uses them.  Offsets with a decreasing entry and a
+    last entry past T give the result of the clamped offsets [0, 70, 70, 200, 260]:
+    an empty second sequence (final state = initial state) and a last one that ends
+    at T."""
+    x = make_inputs(dict(lens=[70, 0, 130, 60], Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True), seed=13)
+    d = gpu_inputs(x)
+    bad = torch.tensor([0, 70, 60, 200, 400], dtype=torch.int32, device="cuda")
+    from gated_delta_rule_85_amd import chunk_gated_delta_rule_fwd
+    _, _, o, _, ht = chunk_gated_delta_rule_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], x["scale"],
+                                                d["initial_state"], bad, return_h=False)
+    torch.cuda.synchronize()
+    ref = ora(x)
+    eo, eh = rel(host(o), ref["o"]), rel(host(ht), ref["final_state"])
+    print("clamped offsets: o %.3g final %.3g" % (eo, eh), flush=True)
+    assert eo <= 2e-2 and eh <= 2e-2
+    assert np.array_equal(host(ht)[1], x["initial_state"][1].astype(np.float64))

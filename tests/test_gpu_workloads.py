@@ -114,22 +114,67 @@ def test_segment_model_values():
     assert split_chunks(64, 256, 256, 8) == 65
 
 
+def split_chunks_one_round(N, W, slots, wm=1):
+    """Segment length of the gate-driven split (GDR_CP_AUTO): one dispatch round at
+    most, the window priced at wm chunks."""
+    best = None
+    for S in range(1, min(N, max(1, slots // W)) + 1):
+        L = -(-N // S)
+        if -(-N // L) != S:
+            continue
+        t = -(-W * S // slots) * (L + (wm if S > 1 else 0))
+        if best is None or t < best[0]:
+            best = (t, L if S > 1 else N + 1)
+    return best[1]
+
+
 def test_auto_mode_splits_the_long_sequence(long_seq):
-    """AutoCP: B*H_v = 8 <= 40 selects the split, with the device model's segment
-    length and Wm = 8."""
+    """AutoCP on the 32K-token sequence: "auto" splits with the device model's
+    segment length and a gate-driven window.  The workload's gates decay by far
+    more than 2^-24 within every chunk, so each window is one chunk: the result
+    is bitwise that of the fixed one-chunk warm-up.  "auto_pages" (the pages'
+    trigger, B*H_v = 8 <= 40) is the fixed 8-chunk warm-up."""
     import torch
     x = long_seq
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    L = split_chunks(512, 8 * 2, cus, 8)
-    print("compute units %d: segments of %d chunks" % (cus, L), flush=True)
+    L = split_chunks_one_round(512, 8 * 2, cus)
+    Lp = split_chunks(512, 8 * 2, cus, 8)
+    print("compute units %d: segments of %d (auto) and %d (auto_pages) chunks" % (cus, L, Lp), flush=True)
     auto = host(run_fwd(x, return_h=False, cp_mode="auto")[2])
     forced = host(run_fwd(x, return_h=False, cp_mode="warmup", cp_segment_chunks=L,
-                          cp_warmup_chunks=8)[2])
+                          cp_warmup_chunks=1)[2])
     assert np.array_equal(auto, forced)
+    pages = host(run_fwd(x, return_h=False, cp_mode="auto_pages")[2])
+    forced8 = host(run_fwd(x, return_h=False, cp_mode="warmup", cp_segment_chunks=Lp,
+                           cp_warmup_chunks=8)[2])
+    assert np.array_equal(pages, forced8)
     re = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"])
-    e = rel(auto, re["o"])
-    print("auto split vs exact %.3g" % e, flush=True)
-    assert e <= 2e-2
+    e, ep = rel(auto, re["o"]), rel(pages, re["o"])
+    print("auto split vs exact %.3g, auto_pages %.3g" % (e, ep), flush=True)
+    assert e <= 2e-2 and ep <= 2e-2
+
+
+def test_auto_mode_with_gates_that_do_not_decay():
+    """"auto" on heads whose gates do not decay (g = 0), beside a decaying head and
+    one that decays slowly: the gate-driven window reaches back to the sequence
+    start where it must, so every head meets the bar against the exact oracle,
+    while the fixed 8-chunk warm-up of the pages' trigger does not."""
+    x = make_inputs(dict(B=1, T=64 * 40 - 9, Hq=1, Hv=4, K=128, V=128, dtype="bf16", h0=True), seed=21)
+    x["g"][:, :, 1] = 0.0
+    x["g"][:, :, 2] = (x["g"][:, :, 2] * 0.02).astype(np.float32)
+    ref = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], x["initial_state"])
+    _, _, o, _, ht = run_fwd(x, return_h=False, cp_mode="auto")
+    o, ht = host(o), host(ht)
+    off = host(run_fwd(x, return_h=False, cp_mode="off")[2])
+    pages = host(run_fwd(x, return_h=False, cp_mode="auto_pages")[2])
+    for hv in range(4):
+        eo = rel(o[:, :, hv], ref["o"][:, :, hv])
+        eh = rel(ht[:, hv], ref["final_state"][:, hv])
+        print("head %d: auto o %.3g final %.3g | off %.3g | auto_pages %.3g" % (
+            hv, eo, eh, rel(off[:, :, hv], ref["o"][:, :, hv]), rel(pages[:, :, hv], ref["o"][:, :, hv])),
+            flush=True)
+        assert eo <= 2e-2 and eh <= 2e-2
+    assert rel(pages[:, :, 1], ref["o"][:, :, 1]) > 2e-2
 
 
 def test_long_sequence_exact_split(long_seq):
