@@ -10,12 +10,13 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 CHUNK = 64
 FWD_STAGES = 3
 BWD_STAGES = 4
 
-OK, EINVAL, ENOTSUP, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
+OK, EINVAL, ENOTSUP, EWORKSPACE, ELAUNCH, ESCRATCH = 0, -1, -2, -3, -4, -5
+SCRATCH_BYTES = 256 << 20  # GDR_SCRATCH_BYTES: gdr_fwd_noalloc's per-device scratch
 BF16, F32 = 0, 1
 CP_AUTO, CP_OFF, CP_WARMUP, CP_EXACT, CP_AUTO_EXACT, CP_AUTO_PAGES = 0, 1, 2, 3, 4, 5
 
@@ -70,6 +71,8 @@ def _load():
         fw = getattr(lib, name + "_workspace")
         fw.restype = ctypes.c_int
         fw.argtypes = [ctypes.POINTER(st), ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_fwd_noalloc.restype = ctypes.c_int
+    lib.gdr_fwd_noalloc.argtypes = [ctypes.POINTER(FwdArgs), _p]
     lib.gdr_tblocks_bytes.restype = ctypes.c_int
     lib.gdr_tblocks_bytes.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(ctypes.c_size_t)]
     if lib.gdr_abi_version() != ABI_VERSION:
@@ -115,6 +118,13 @@ def fwd(args, stream):
     rc = lib.gdr_fwd(ctypes.byref(args), _p(stream))
     if rc:
         raise GdrError("gdr_fwd", rc)
+
+
+def fwd_noalloc(args, stream):
+    """gdr_fwd on the library's static per-device scratch (args.workspace ignored)."""
+    rc = lib.gdr_fwd_noalloc(ctypes.byref(args), _p(stream))
+    if rc:
+        raise GdrError("gdr_fwd_noalloc", rc)
 
 
 def bwd_workspace(args):

@@ -33,7 +33,7 @@ ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 MAX_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 SOURCES = {"gdr_api.hip": VGPR_FORM, "gdr_prep.hip": VGPR_FORM, "gdr_scan.hip": VGPR_FORM + ILP,
            "gdr_bwd.hip": VGPR_FORM, "gdr_bwd_scan.hip": VGPR_FORM + ILP,
-           "gdr_bwd_mfma.hip": VGPR_FORM + MAX_ILP}
+           "gdr_bwd_mfma.hip": VGPR_FORM + MAX_ILP, "gdr_noalloc.hip": []}
 
 
 def _compile(src):

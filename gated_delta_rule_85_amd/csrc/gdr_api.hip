@@ -252,6 +252,7 @@ const char *gdr_strerror(int code) {
         case GDR_ENOTSUP: return "unsupported size or dtype";
         case GDR_EWORKSPACE: return "workspace too small";
         case GDR_ELAUNCH: return "kernel launch failed";
+        case GDR_ESCRATCH: return "problem needs more than the library's static scratch buffer";
         default: return "unknown error";
     }
 }
@@ -278,7 +279,16 @@ int gdr_tblocks_bytes(const gdr_fwd_args *a, size_t *bytes) {
     return GDR_OK;
 }
 
-int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
+int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) { return gdr::fwd_impl(a, stream, nullptr, 0); }
+
+}  // extern "C"
+
+// The forward on the caller's workspace (scratch_for null) or, for the
+// allocation-free entry point, on the library's per-device scratch buffer of
+// scratch_bytes bytes, whose device address scratch_for(device) returns (null
+// when it cannot be had).  Every host-side check runs before the scratch is
+// looked up or anything is launched.
+int gdr::fwd_impl(const gdr_fwd_args *a, hipStream_t stream, void *(*scratch_for)(int), size_t scratch_bytes) {
     // host-side checks come first; the device query is needed only to launch
     int dev = 0;
     const int64_t slots = hipStreamGetDevice(stream, &dev) == hipSuccess ? device_slots(dev) : 0;
@@ -297,11 +307,18 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
         (a->u_out && !aligned(a->u_out, 16)) || (a->h_bwd && !aligned(a->h_bwd, 16)) ||
         (a->tblk_bwd && !aligned(a->tblk_bwd, 16)))
         return GDR_EINVAL;
-    if (a->workspace_bytes < pl.total || (pl.total > 0 && !a->workspace)) return GDR_EWORKSPACE;
-    if (pl.total > 0 && !aligned(a->workspace, 16)) return GDR_EINVAL;
-    if (slots == 0) return GDR_ELAUNCH;
-
-    char *ws = static_cast<char *>(a->workspace);
+    char *ws;
+    if (scratch_for) {
+        if (pl.total > scratch_bytes) return GDR_ESCRATCH;
+        if (slots == 0) return GDR_ELAUNCH;
+        ws = static_cast<char *>(scratch_for(dev));
+        if (!ws) return GDR_ELAUNCH;
+    } else {
+        if (a->workspace_bytes < pl.total || (pl.total > 0 && !a->workspace)) return GDR_EWORKSPACE;
+        if (pl.total > 0 && !aligned(a->workspace, 16)) return GDR_EINVAL;
+        if (slots == 0) return GDR_ELAUNCH;
+        ws = static_cast<char *>(a->workspace);
+    }
     int32_t *chunk_off = a->cu_seqlens ? reinterpret_cast<int32_t *>(ws + pl.off_chunk) : nullptr;
     char *tblk = ws + pl.off_tblk;
     const Dt dt = a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
@@ -418,6 +435,8 @@ int gdr_fwd(const gdr_fwd_args *a, hipStream_t stream) {
     if (!mark(5)) return GDR_ELAUNCH;
     return GDR_OK;
 }
+
+extern "C" {
 
 int gdr_bwd_workspace(const gdr_bwd_args *a, size_t *bytes) {
     if (!bytes) return GDR_EINVAL;

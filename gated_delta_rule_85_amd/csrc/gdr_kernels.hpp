@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdr.h"
 #include "gdr_device.hpp"
 #include "gdr_layout.hpp"
 
@@ -122,6 +123,10 @@ hipError_t launch_bwd(Dt dt, Dt gt, int K, const BwdParams &p, int n_chunks_ub, 
 hipError_t launch_bwd_scan_bf16(int K, const BwdParams &p, int n_units, hipStream_t s);
 hipError_t launch_bwd_local_bf16(Dt gt, int K, const BwdParams &p, int n_chunks_ub, hipStream_t s);
 size_t tblock_bytes(Dt dt);
+// Body of gdr_fwd (gdr_api.hip): on the caller's workspace (scratch_for null), or
+// on a library-owned buffer of scratch_bytes bytes whose device address
+// scratch_for(device) returns (null: not available), as gdr_fwd_noalloc does.
+int fwd_impl(const gdr_fwd_args *a, hipStream_t stream, void *(*scratch_for)(int), size_t scratch_bytes);
 int scan_vtile(Dt dt, int K, int V);  // V columns per scan workgroup
 
 }  // namespace gdr

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 6
+#define GDR_ABI_VERSION 7
 #define GDR_CHUNK 64
 #define GDR_FWD_STAGES 3
 #define GDR_BWD_STAGES 4
@@ -58,6 +58,10 @@ extern "C" {
 #define GDR_ENOTSUP -2    /* K or V not in {64, 128}; unsupported dtype */
 #define GDR_EWORKSPACE -3 /* workspace_bytes below what gdr_*_workspace reports */
 #define GDR_ELAUNCH -4    /* a HIP launch failed */
+#define GDR_ESCRATCH -5   /* gdr_fwd_noalloc: the problem needs more scratch than GDR_SCRATCH_BYTES */
+
+/* size of the static per-device scratch buffer of gdr_fwd_noalloc */
+#define GDR_SCRATCH_BYTES ((size_t)256 << 20)
 
 /* element types */
 #define GDR_BF16 0
@@ -215,6 +219,24 @@ int gdr_fwd_workspace(const gdr_fwd_args *args, size_t *bytes);
    GDR_CP_AUTO_EXACT splits only where that model predicts a gain over one
    segment.  Returns GDR_ELAUNCH if the device cannot be queried. */
 int gdr_fwd(const gdr_fwd_args *args, hipStream_t stream);
+
+/* The forward of gdr_fwd for callers that cannot allocate device memory (code
+   under HIP graph capture, serving loops that must not allocate, harnesses that
+   forbid it): the same arguments, outputs and kernels, but the scratch that
+   gdr_fwd takes in args->workspace (T blocks, packed-sequence tables, the exact
+   split's states) comes from a buffer the library owns: a static device array of
+   GDR_SCRATCH_BYTES (256 MiB) per GPU, which each GPU the library runs this
+   entry point on holds until the process ends.  args->workspace and
+   workspace_bytes are ignored.  No hipMalloc, hipFree or other allocating call is
+   made.  Returns GDR_ESCRATCH, launching nothing, when the problem needs more
+   scratch than that (gdr_fwd_workspace gives the need: the prefill shard of
+   B=4, T=4096, H_v=32, K=V=128 takes 139 MB; about 15,000 (chunk, v head) pairs
+   fit); GDR_ELAUNCH if the buffer's device address cannot be had.  Every call on
+   one GPU uses that GPU's one buffer: calls that overlap in time on one GPU
+   (other streams, other host threads) race and must be serialised by the
+   caller; consecutive calls on one stream are ordered.  Nothing in the buffer
+   needs to start at zero: each call writes what it reads. */
+int gdr_fwd_noalloc(const gdr_fwd_args *args, hipStream_t stream);
 
 /* Bytes of the T blocks of gdr_fwd_args.tblk_bwd for these sizes: one block
    per (chunk, v head) for an upper bound on the chunk count (B ceil(T/64), or

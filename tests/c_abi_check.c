@@ -36,6 +36,9 @@ int main(void) {
     CHECK(gdr_fwd_workspace(&a, &bytes) == GDR_ENOTSUP, "fwd K");
     a.K = 128;
     CHECK(gdr_fwd(&a, NULL) == GDR_EINVAL, "fwd null pointers rejected before any launch");
+    CHECK(gdr_fwd_noalloc(&a, NULL) == GDR_EINVAL, "fwd_noalloc null pointers rejected before any launch");
+    CHECK(strcmp(gdr_strerror(GDR_ESCRATCH), "problem needs more than the library's static scratch buffer") == 0,
+          "strerror scratch");
     CHECK(gdr_tblocks_bytes(&a, &bytes) == GDR_OK && bytes == 4 * 4 * 17408, "T blocks for the backward");
     a.h_bwd = (void *)16;
     a.cp_mode = GDR_CP_WARMUP;

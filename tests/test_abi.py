@@ -231,3 +231,15 @@ def test_host_offsets_are_validated(L):
     for bad in ([1, 5, 9], [0, 5, 4, 9], [0, 5, 10], [0, 5, 8], [0]):
         with pytest.raises(ValueError):
             check_offsets(torch.tensor(bad, dtype=torch.int32), 9)
+
+
+def test_noalloc_host_errors_before_any_launch(L):
+    """gdr_fwd_noalloc validates like gdr_fwd, ignores the workspace fields, and
+    refuses a problem whose scratch exceeds GDR_SCRATCH_BYTES with GDR_ESCRATCH,
+    all before looking up its buffer or launching anything."""
+    assert L.lib.gdr_fwd_noalloc(ctypes.byref(fwd_args(L)), None) == L.EINVAL
+    assert L.lib.gdr_fwd_noalloc(ctypes.byref(fwd_args(L, K=96)), None) == L.ENOTSUP
+    big = fwd_args(L, B=8, T=4096, H_q=32, H_v=64, q=16, k=16, v=16, g=16, beta=16, o=16)
+    assert rc_ws(L, big)[1] > L.SCRATCH_BYTES
+    assert L.lib.gdr_fwd_noalloc(ctypes.byref(big), None) == L.ESCRATCH
+    assert L.strerror(L.ESCRATCH).startswith("problem needs more")
