@@ -19,7 +19,12 @@ def dev(x, dtype=torch.float32):
 
 
 def host(t):
-    return None if t is None else t.detach().float().cpu().numpy().astype(np.float64)
+    """fp64 host copy of a device tensor (numpy arrays pass through as fp64)."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64, copy=False)
+    return t.detach().float().cpu().numpy().astype(np.float64)
 
 
 def gpu_inputs(x):

@@ -131,18 +131,48 @@ def test_exact_split_where_the_warmup_fails():
     assert e_wu > 2e-2
 
 
-def test_prefill_shard_full_size_sampled_units():
-    """B=4, T=4096, H_q=16, H_v=32, K=V=128, bf16 (the timed workload), launched
-    whole; the oracle runs whole (sequence, q/k head) groups."""
+def test_prefill_shard_full_size_every_unit():
+    """B=4, T=4096, H_q=16, H_v=32, K=V=128, bf16 (the timed workload), launched whole:
+    every element of o, the final state, the chunk-start states h, g_cum and A
+    (T, one row per token) against the oracle over all 128 (sequence, v head)
+    units; A against the chunked form, one (sequence, q/k head) group at a time."""
     x = make_inputs("prefill_shard", seed=0)
-    g_cum, A, o, h, ht = run_fwd(x, return_h=False)
-    o, ht = host(o), host(ht)
-    for b, hq in ((0, 0), (3, 15), (1, 7)):
-        y, hs = slice_units(x, b, hq)
-        r = ora(y)
-        eo, eh = rel(o[b:b + 1, :, hs], r["o"]), rel(ht[b:b + 1, hs], r["final_state"])
-        print("b=%d hq=%d o %.3g final %.3g" % (b, hq, eo, eh), flush=True)
-        assert eo <= 2e-2 and eh <= 2e-2
+    g_cum, A, o, h, ht = run_fwd(x, return_h=True)
+    ref = ora(x, want_h=True)
+    errs = {"o": rel(host(o), ref["o"]), "final_state": rel(host(ht), ref["final_state"]),
+            "g_cum": rel(host(g_cum), ref["g_cum"])}
+    del o, ht, g_cum
+    errs["h"] = rel(host(h), ref["h"])
+    del h, ref
+    A = host(A)
+    worst = 0.0
+    rms = 0.0
+    for b in range(4):
+        for hq in range(16):
+            y, hs = slice_units(x, b, hq)
+            c = oracle.chunk_form(y["q"], y["k"], y["v"], y["g"], y["beta"], y["scale"], y["initial_state"])
+            worst = max(worst, float(np.max(np.abs(A[b:b + 1, :, hs] - c["T_rows"]))))
+            rms += float(np.sum(c["T_rows"] ** 2))
+    errs["A"] = worst / np.sqrt(rms / A.size)
+    print({k: "%.3g" % v for k, v in errs.items()}, flush=True)
+    for k, e in errs.items():
+        assert e <= 2e-2, (k, e)
+
+
+def test_strong_decay_past_fp32_exp_range():
+    """Gates eight times the recipe's (mean log-decay about -3.2 per token): the
+    running log-gate of a chunk spans about -200, past the fp32 range of exp, so
+    e^gam of the chunk's later tokens underflows and only the difference form
+    exp(gam_r - gam_i) keeps the in-chunk decays.  Every element against the oracle,
+    bf16 and fp32, with ragged tails and an initial state."""
+    for shape in (dict(B=2, T=300, Hq=2, Hv=4, K=128, V=128, dtype="bf16", h0=True),
+                  dict(B=1, T=190, Hq=1, Hv=2, K=64, V=64, dtype="fp32", h0=True)):
+        x = make_inputs(shape, seed=14)
+        x["g"] = (x["g"] * 8.0).astype(np.float32)
+        span = float(np.min(oracle.chunk_cumsum(x["g"], np.arange(x["q"].shape[0] + 1) * x["q"].shape[1])))
+        print(shape["dtype"], "most negative in-chunk running log-gate %.1f" % span, flush=True)
+        assert span < -88.0
+        check_all(x, run_fwd(x), ora(x, want_h=True))
 
 
 def test_bf16_output_within_rounding_bound():

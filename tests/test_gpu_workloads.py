@@ -15,30 +15,25 @@ pytestmark = pytest.mark.gpu
 
 def test_varlen_packed_batch_full_size():
     """16 packed sequences (61,412 tokens, seed-0 lengths), H_q=16, H_v=32,
-    K=V=128, bf16, zero initial states, per-sequence final states."""
+    K=V=128, bf16, zero initial states, per-sequence final states: every element
+    of o and of every final state, all 16 q/k heads."""
     x = make_inputs("varlen", seed=0)
     g_cum, A, o, h, ht = run_fwd(x, return_h=False)
-    o, ht = host(o), host(ht)
-    for hq in (0, 9):
-        y, hs = slice_units(x, 0, hq)
-        r = oracle.fwd(y["q"], y["k"], y["v"], y["g"], y["beta"], y["scale"],
-                       cu_seqlens=y["cu_seqlens"])
-        eo, eh = rel(o[:, :, hs], r["o"]), rel(ht[:, hs], r["final_state"])
-        print("hq=%d o %.3g final %.3g" % (hq, eo, eh), flush=True)
-        assert eo <= 2e-2 and eh <= 2e-2
+    r = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], cu_seqlens=x["cu_seqlens"])
+    eo, eh = rel(host(o), r["o"]), rel(host(ht), r["final_state"])
+    print("o %.3g final %.3g" % (eo, eh), flush=True)
+    assert eo <= 2e-2 and eh <= 2e-2
 
 
 def test_training_shape_forward_full_size():
-    """B=8, T=4096, H_q=32, H_v=64, K=V=128, bf16 with initial state (forward part)."""
+    """B=8, T=4096, H_q=32, H_v=64, K=V=128, bf16 with initial state (forward part):
+    every element of o and of the final states, all 512 (sequence, v head) units."""
     x = make_inputs("training", seed=0, grads=False)
     g_cum, A, o, h, ht = run_fwd(x, return_h=False)
-    o, ht = host(o), host(ht)
-    for b, hq in ((0, 0), (7, 31)):
-        y, hs = slice_units(x, b, hq)
-        r = oracle.fwd(y["q"], y["k"], y["v"], y["g"], y["beta"], y["scale"], y["initial_state"])
-        eo, eh = rel(o[b:b + 1, :, hs], r["o"]), rel(ht[b:b + 1, hs], r["final_state"])
-        print("b=%d hq=%d o %.3g final %.3g" % (b, hq, eo, eh), flush=True)
-        assert eo <= 2e-2 and eh <= 2e-2
+    r = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], x["initial_state"])
+    eo, eh = rel(host(o), r["o"]), rel(host(ht), r["final_state"])
+    print("o %.3g final %.3g" % (eo, eh), flush=True)
+    assert eo <= 2e-2 and eh <= 2e-2
 
 
 @pytest.mark.parametrize("Hv", [64, 48, 24, 16])
