@@ -241,6 +241,76 @@ class Events:
                     self.hip.hipEventDestroy(arr[i])
 
 
+CP_MODES = ("off", "warmup", "exact", "auto", "auto_exact", "auto_pages")
+
+
+def cp_sweep(steps=40, warmup=5):
+    """Forward time of every sequence-split mode over the family's head counts
+    (H_v = 64 .. 8, H_q = H_v / 2, the README's TP1..TP8) at three batch x length
+    mixes of 16,384 tokens (bf16, K = V = 128, initial state, fp32 o).  Inputs are
+    drawn on the device with the recipe's distributions (unit-norm q, k; g =
+    -softplus(N(0,1))/2; beta = sigmoid(N(0,1))).  Each mode: median of `steps`
+    HIP-event-timed gdr_fwd calls after `warmup`, buffers allocated beforehand.
+    Prints one JSON line per (mix, H_v)."""
+    import torch
+
+    from gated_delta_rule_85_amd import _lib
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    gen = torch.Generator(device=dev).manual_seed(0)
+    modes = {"off": _lib.CP_OFF, "warmup": _lib.CP_WARMUP, "exact": _lib.CP_EXACT, "auto": _lib.CP_AUTO,
+             "auto_exact": _lib.CP_AUTO_EXACT, "auto_pages": _lib.CP_AUTO_PAGES}
+    for B, T in ((4, 4096), (1, 16384), (16, 1024)):
+        for Hv in (64, 48, 32, 24, 16, 8):
+            Hq, K, V = Hv // 2, 128, 128
+            rn = lambda *shape: torch.randn(*shape, device=dev, generator=gen)
+            q = torch.nn.functional.normalize(rn(B, T, Hq, K), dim=-1).to(torch.bfloat16)
+            k = torch.nn.functional.normalize(rn(B, T, Hq, K), dim=-1).to(torch.bfloat16)
+            v = rn(B, T, Hv, V).to(torch.bfloat16)
+            g = -0.5 * torch.nn.functional.softplus(rn(B, T, Hv))
+            beta = torch.sigmoid(rn(B, T, Hv))
+            h0 = 0.1 * rn(B, Hv, K, V)
+            o = torch.empty(B, T, Hv, V, device=dev)
+            ht = torch.empty(B, Hv, K, V, device=dev)
+            row = {"B": B, "T": T, "H_v": Hv}
+            args = {}
+            for name, mode in modes.items():
+                a = _lib.FwdArgs()
+                a.B, a.T, a.H_q, a.H_v, a.K, a.V, a.n_seq = B, T, Hq, Hv, K, V, B
+                a.dtype, a.out_dtype, a.scale, a.cp_mode = _lib.BF16, _lib.F32, K ** -0.5, mode
+                a.q, a.k, a.v, a.g, a.beta = q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr()
+                a.initial_state, a.o, a.final_state = h0.data_ptr(), o.data_ptr(), ht.data_ptr()
+                n = _lib.fwd_workspace(a)
+                ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+                a.workspace, a.workspace_bytes = ws.data_ptr(), n
+                args[name] = (a, ws)
+                for _ in range(warmup):
+                    _lib.fwd(a, stream.cuda_stream)
+            # the modes take turns, `rounds` times, so that clock changes hit them alike
+            ts = {name: [] for name in modes}
+            rounds = 4
+            for _ in range(rounds):
+                for name in modes:
+                    a = args[name][0]
+                    for _ in range(max(1, steps // rounds)):
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        _lib.fwd(a, stream.cuda_stream)
+                        e1.record(stream)
+                        e1.synchronize()
+                        ts[name].append(e0.elapsed_time(e1))
+            for name in modes:
+                row[name] = sorted(ts[name])[len(ts[name]) // 2]
+            del args
+            best = min(row[m] for m in ("off", "warmup", "exact"))
+            row["auto_vs_best"] = row["auto"] / best
+            print(json.dumps(row), flush=True)
+            del q, k, v, g, beta, h0, o, ht
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,11 +328,18 @@ def main():
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--recompute-states", action="store_true",
                     help="training: the backward recomputes the chunk-start states")
+    ap.add_argument("--cp-sweep", action="store_true",
+                    help="instead of the bench line: forward time of every split mode over the "
+                         "family's head counts (one JSON line per shape)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this operator has no multi-GPU path here "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.cp_sweep:
+        cp_sweep()
+        return
 
     import numpy as np
     import torch

@@ -61,15 +61,11 @@ int check_dims(int64_t B, int64_t T, int64_t Hq, int64_t Hv, int64_t K, int64_t 
 //   exact split:    rounds x 3 L + (S - 1)   (transitions, zero-start states and
 //                   output passes, one carry step per segment)
 // with L = ceil(N / S) (ties: fewer segments); one segment costs rounds x N.
-// Segment counts beyond eight rounds of the device are not considered, and with
-// one_round none beyond one round (the gate-driven split: a head whose gates do
-// not decay makes every segment scan from the sequence start, which then costs
-// no more than one unsplit pass).  Returns N + 1 (no split) when one segment is best.
-int64_t split_chunks(int64_t N, int64_t W, int64_t slots, int64_t wm, int64_t min_seg, bool exact = false,
-                     bool one_round = false) {
+// Segment counts beyond eight rounds of the device are not considered.
+// Returns N + 1 (no split) when one segment is best.
+int64_t split_chunks(int64_t N, int64_t W, int64_t slots, int64_t wm, int64_t min_seg, bool exact = false) {
     int64_t best_t = -1, best_L = N + 1;
-    const int64_t per_round = std::max<int64_t>(1, slots / std::max<int64_t>(W, 1));
-    const int64_t s_max = std::min(N, one_round ? per_round : 8 * cdiv(slots, std::max<int64_t>(W, 1)));
+    const int64_t s_max = std::min(N, 8 * cdiv(slots, std::max<int64_t>(W, 1)));
     for (int64_t S = min_seg; S <= s_max; ++S) {
         const int64_t L = cdiv(N, S), Sx = cdiv(N, L);
         if (Sx != S) continue;  // same L as a smaller S
@@ -122,11 +118,12 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     pl.warm_chunks = a->cp_warmup_chunks > 0 ? a->cp_warmup_chunks : 8;
     const int64_t n_vt = a->V / scan_vtile(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32, (int)a->K, (int)a->V);
     // the gate-driven window is priced at one chunk (gates that decay as the
-    // workloads' do need one)
+    // workloads' do need one; a head whose gates do not decay costs its segments
+    // up to the whole prefix, no more than rounds x N)
     int64_t L = a->cp_segment_chunks > 0
                     ? a->cp_segment_chunks
                     : split_chunks(pl.nct, bh * n_vt, slots > 0 ? slots : DEFAULT_SLOTS,
-                                   gated ? 1 : pl.warm_chunks, autom ? 1 : 2, exact_mode, gated);
+                                   gated ? 1 : pl.warm_chunks, autom ? 1 : 2, exact_mode);
     if (L < 1) L = 1;
     if (!split || L >= pl.nct) {
         split = false;

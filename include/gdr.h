@@ -71,8 +71,8 @@ extern "C" {
    long sequence into segments that run in parallel, each warmed up from a zero
    state over a few chunks before its own (aiboss88 "Core advantages"; efeozkan
    blog "1. Gate-Driven Automatic Intra-Card Context Parallelism (AutoCP)"). */
-#define GDR_CP_AUTO 0   /* split where the device model of gdr_fwd predicts a gain, with
-                           one dispatch round at most; each segment warms up over a
+#define GDR_CP_AUTO 0   /* split where the device model of gdr_fwd predicts a gain (the
+                           window priced at one chunk); each segment warms up over a
                            window chosen from its gates: the latest chunk from which the
                            log-gates up to the segment's start sum to -24 ln 2 or less
                            (the zero start is then within 2^-24 of the true state), or

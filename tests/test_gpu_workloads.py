@@ -109,30 +109,16 @@ def test_segment_model_values():
     assert split_chunks(64, 256, 256, 8) == 65
 
 
-def split_chunks_one_round(N, W, slots, wm=1):
-    """Segment length of the gate-driven split (GDR_CP_AUTO): one dispatch round at
-    most, the window priced at wm chunks."""
-    best = None
-    for S in range(1, min(N, max(1, slots // W)) + 1):
-        L = -(-N // S)
-        if -(-N // L) != S:
-            continue
-        t = -(-W * S // slots) * (L + (wm if S > 1 else 0))
-        if best is None or t < best[0]:
-            best = (t, L if S > 1 else N + 1)
-    return best[1]
-
-
 def test_auto_mode_splits_the_long_sequence(long_seq):
     """AutoCP on the 32K-token sequence: "auto" splits with the device model's
-    segment length and a gate-driven window.  The workload's gates decay by far
+    segment length (the window priced at one chunk) and a gate-driven window.  The workload's gates decay by far
     more than 2^-24 within every chunk, so each window is one chunk: the result
     is bitwise that of the fixed one-chunk warm-up.  "auto_pages" (the pages'
     trigger, B*H_v = 8 <= 40) is the fixed 8-chunk warm-up."""
     import torch
     x = long_seq
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    L = split_chunks_one_round(512, 8 * 2, cus)
+    L = split_chunks(512, 8 * 2, cus, 1)
     Lp = split_chunks(512, 8 * 2, cus, 8)
     print("compute units %d: segments of %d (auto) and %d (auto_pages) chunks" % (cus, L, Lp), flush=True)
     auto = host(run_fwd(x, return_h=False, cp_mode="auto")[2])
@@ -198,3 +184,29 @@ def test_weak_decay_split_diagnostic(scale_g):
     print("g x %.2f: split-vs-exact (fp64) %.3g, gpu-vs-split %.3g"
           % (scale_g, rel(rs["o"], re["o"]), rel(o, rs["o"])), flush=True)
     assert rel(o, rs["o"]) <= 2e-2
+
+
+@pytest.mark.parametrize("B,T,Hv", [(4, 1024, 64), (2, 2048, 16), (1, 64 * 40, 2)])
+def test_auto_rule(B, T, Hv):
+    """The device rule of "auto": the segment length minimising rounds x (L + 1) over
+    the compute units (the gate-driven window priced at one chunk).  Where it keeps
+    one segment (4 x 1024 at 64 heads: 512 workgroups already take two rounds) the
+    output is bitwise the unsplit scan's; where it splits, the workload's gates decay
+    below 2^-24 within one chunk, so the output is bitwise the one-chunk warm-up of
+    that length; both against the oracle at the bar."""
+    import torch
+    x = make_inputs(dict(B=B, T=T, Hq=max(1, Hv // 2), Hv=Hv, K=128, V=128, dtype="bf16", h0=True), seed=22)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N = -(-T // 64)
+    L = split_chunks(N, B * Hv * 2, cus, 1)
+    auto = host(run_fwd(x, return_h=False, cp_mode="auto")[2])
+    if L > N:
+        same = host(run_fwd(x, return_h=False, cp_mode="off")[2])
+    else:
+        same = host(run_fwd(x, return_h=False, cp_mode="warmup", cp_segment_chunks=L, cp_warmup_chunks=1)[2])
+    print("%d x %d, H_v=%d: %s" % (B, T, Hv, "no split" if L > N else "segments of %d chunks" % L), flush=True)
+    assert np.array_equal(auto, same)
+    r = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], x["initial_state"])
+    e = rel(auto, r["o"])
+    print("auto vs exact %.3g" % e, flush=True)
+    assert e <= 2e-2
