@@ -42,7 +42,7 @@ F_TRI = 139264                  # algorithmic flop per token per v head (C=64, K
 STAGES = ("gdr_chunk_prep", "gdr_scan_output", "gdr_wu")
 
 
-TBLOCK = 17408  # bytes of one (chunk, v head) T block: T hi/lo planes + gate scalars
+TBLOCK = 13312  # bytes of one (chunk, v head) forward T block: T hi/lo planes (rows 0-31 at half width) + scalars
 
 
 def minimal_bytes_per_token_head(cfg, out_bytes=None):

@@ -34,7 +34,8 @@ int32_t *seq_order(int32_t *chunk_off, int64_t n_seq) { return chunk_off + 2 * (
 struct FwdPlan {
     int64_t n_seq, tokens, nct, nt_ub;  // nct: chunks per sequence bound
     size_t off_chunk, off_tblk, total;
-    size_t tblk_bytes;  // the T blocks (and, for tblk_bwd, their copy in the backward's order)
+    size_t tblk_bytes;  // the scan's T blocks in the workspace
+    size_t tblk_bwd_bytes;  // their copy in the backward's layout (tblk_bwd)
     // exact split: segment transitions, zero-start end states, true start states, a zero row
     size_t off_M, off_b, off_hseg, off_zero;
     int seg_chunks, warm_chunks, n_seg;
@@ -102,7 +103,9 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     pl.off_chunk = off;
     off += seq_table_bytes(varlen, pl.n_seq);
     pl.off_tblk = off;
-    pl.tblk_bytes = up(tblock_bytes(a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32) * (size_t)(pl.nt_ub * a->H_v));
+    const Dt pdt = a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
+    pl.tblk_bytes = up(tblock_bytes_fwd(pdt) * (size_t)(pl.nt_ub * a->H_v));
+    pl.tblk_bwd_bytes = up(tblock_bytes(pdt) * (size_t)(pl.nt_ub * a->H_v));
     off += pl.tblk_bytes;
     pl.total = off;
     // sequence split ("AutoCP")
@@ -272,7 +275,7 @@ int gdr_tblocks_bytes(const gdr_fwd_args *a, size_t *bytes) {
     FwdPlan pl;
     int rc = plan_fwd(a, pl, DEFAULT_SLOTS);
     if (rc) return rc;
-    *bytes = pl.tokens > 0 ? pl.tblk_bytes : 0;
+    *bytes = pl.tokens > 0 ? pl.tblk_bwd_bytes : 0;
     return GDR_OK;
 }
 

@@ -122,7 +122,8 @@ hipError_t launch_bwd(Dt dt, Dt gt, int K, const BwdParams &p, int n_chunks_ub, 
                       const hipEvent_t *ev, hipStream_t s);
 hipError_t launch_bwd_scan_bf16(int K, const BwdParams &p, int n_units, hipStream_t s);
 hipError_t launch_bwd_local_bf16(Dt gt, int K, const BwdParams &p, int n_chunks_ub, hipStream_t s);
-size_t tblock_bytes(Dt dt);
+size_t tblock_bytes(Dt dt);      // the backward's T blocks (and the forward's tblk_bwd copy)
+size_t tblock_bytes_fwd(Dt dt);  // the forward's T blocks, read by the scan
 // Body of gdr_fwd (gdr_api.hip): on the caller's workspace (scratch_for null), or
 // on a library-owned buffer of scratch_bytes bytes whose device address
 // scratch_for(device) returns (null: not available), as gdr_fwd_noalloc does.

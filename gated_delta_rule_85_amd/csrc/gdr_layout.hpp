@@ -52,6 +52,7 @@ template <int ROWB, typename KEY = KeyRow> struct Swz {
     static __device__ __forceinline__ int chunk(int row, int p) { return p ^ (KEY::key(row) & (S - 1)); }
 };
 
+// The backward's T blocks: full planes, rows swizzled by KeyRow.
 template <typename In> struct TBlock {
     static constexpr bool BF = sizeof(In) == 2;
     static constexpr int ROWB = CH * (BF ? 2 : 4);  // bytes per plane row
@@ -60,11 +61,51 @@ template <typename In> struct TBlock {
     static constexpr int SC = NPL * PLANE;          // scalars
     static constexpr int BYTES = SC + 4 * CH * 4;
     static_assert(BYTES % 1024 == 0, "block copied in 1 KB wave transfers");
+    // byte offset of (row, byte-in-row) within a plane
+    static __device__ __forceinline__ int off(int row, int byte) { return Swz<ROWB>::off(row, byte); }
 };
-// swizzle of the T blocks gdr_chunk_prep writes for the scan (the backward's
-// blocks keep KeyRow)
+// swizzle of the full-width rows of the T blocks gdr_chunk_prep writes for the scan
 template <typename In> using SwzTF = Swz<TBlock<In>::ROWB, KeyT>;
 
+// The forward's T blocks, the LDS image gdr_scan_output copies in.  For bf16
+// inputs the scan reads rows 0-31 of T only in their first 32 columns (their
+// other columns are zero: T is lower triangular), so each plane holds rows
+// 0-31 at 64 bytes (logical 16-byte chunk q of row r at physical chunk
+// q ^ (r >> 3), which keeps the scan's 16-row operand reads on distinct banks)
+// and then rows 32-63 at 128 bytes (KeyT swizzle): 6 KB per plane, 13 KB per
+// block with the scalars instead of 17 KB.  fp32 inputs keep full rows.
+template <typename In> struct TBlockF;
+template <> struct TBlockF<bf16> {
+    static constexpr bool BF = true;
+    static constexpr int HALF = 32 * 64;           // rows 0-31 of a plane
+    static constexpr int PLANE = HALF + 32 * 128;  // then rows 32-63
+    static constexpr int NPL = 2;
+    static constexpr int SC = NPL * PLANE;         // scalars
+    static constexpr int BYTES = SC + 4 * CH * 4;
+    static_assert(BYTES % 1024 == 0, "block copied in 1 KB wave transfers");
+    static __device__ __forceinline__ int off(int row, int byte) {
+        return row < 32 ? row * 64 + ((((byte >> 4) ^ (row >> 3)) & 3) << 4) + (byte & 15)
+                        : HALF + (row - 32) * 128 + ((((byte >> 4) ^ KeyT::key(row)) & 7) << 4) + (byte & 15);
+    }
+};
+template <> struct TBlockF<float> : TBlock<float> {
+    static __device__ __forceinline__ int off(int row, int byte) { return SwzTF<float>::off(row, byte); }
+};
+
+
+// The scalars of a T block: gam (padded with its last value), e^gam,
+// e^(gam_last - gam), beta
+template <typename TB>
+__device__ __forceinline__ void write_tblock_scalars(char *blk, const float *gam, const float *bet, int n, int tid) {
+    if (tid < CH) {
+        float *sc = reinterpret_cast<float *>(blk + TB::SC);
+        const float gl = gam[n - 1];
+        sc[tid] = gam[tid];
+        sc[CH + tid] = fast_exp(gam[tid]);
+        sc[2 * CH + tid] = fast_exp(gl - gam[tid]);
+        sc[3 * CH + tid] = bet[tid];
+    }
+}
 
 // Write one T block from an fp32 row-major T (row r, column i at T[r * ld + i])
 // and the chunk's 64 gate values (gam padded with its last value, bet zero
@@ -96,13 +137,37 @@ __device__ __forceinline__ void write_tblock(char *blk, const float *T, int ld, 
             *reinterpret_cast<f32x4 *>(blk + r * TB::ROWB + 16 * pc) = x0;
         }
     }
-    if (tid < CH) {
-        float *sc = reinterpret_cast<float *>(blk + TB::SC);
-        const float gl = gam[n - 1];
-        sc[tid] = gam[tid];
-        sc[CH + tid] = fast_exp(gam[tid]);
-        sc[2 * CH + tid] = fast_exp(gl - gam[tid]);
-        sc[3 * CH + tid] = bet[tid];
+    write_tblock_scalars<TB>(blk, gam, bet, n, tid);
+}
+
+// The forward's T block (TBlockF) from the same fp32 T and gates.
+template <typename In>
+__device__ __forceinline__ void write_tblock_f(char *blk, const float *T, int ld, const float *gam,
+                                               const float *bet, int n, int tid, int nthr) {
+    if constexpr (sizeof(In) == 4) {
+        write_tblock<float, SwzTF<float>>(blk, T, ld, gam, bet, n, tid, nthr);
+    } else {
+        using TB = TBlockF<bf16>;
+        // 16-byte chunks of a plane: 4 in each of rows 0-31, 8 in each of rows 32-63
+        for (int idx = tid; idx < 32 * 4 + 32 * 8; idx += nthr) {
+            const int r = idx < 128 ? idx >> 2 : 32 + ((idx - 128) >> 3);
+            const int lc = idx < 128 ? idx & 3 : (idx - 128) & 7;
+            f32x4 x0 = zero4(), x1 = zero4();
+            if (r < n) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x0[e] = T[r * ld + 8 * lc + e];
+                    x1[e] = T[r * ld + 8 * lc + 4 + e];
+                }
+            }
+            bf16x4 h0, l0, h1, l1;
+            split4(x0, h0, l0);
+            split4(x1, h1, l1);
+            const int off = TB::off(r, 16 * lc);
+            *reinterpret_cast<bf16x8 *>(blk + off) = cat(h0, h1);
+            *reinterpret_cast<bf16x8 *>(blk + TB::PLANE + off) = cat(l0, l1);
+        }
+        write_tblock_scalars<TB>(blk, gam, bet, n, tid);
     }
 }
 

@@ -199,8 +199,8 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
             }
         }
         // T block for the scan: swizzled planes (rows past the chunk end zero) + scalars
-        write_tblock<In, SwzTF<In>>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, Tm, LDF, gam, bet, n,
-                         tid, NTHR);
+        write_tblock_f<In>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlockF<In>::BYTES, Tm, LDF, gam, bet, n, tid,
+                           NTHR);
         // and, for a backward, in the layout its kernels copy (plain 16-byte-chunk order)
         if (p.tblk_bwd)
             write_tblock<In>(p.tblk_bwd + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, Tm, LDF, gam, bet, n, tid,
@@ -230,16 +230,16 @@ hipError_t launch_prep_t(const PrepParams &p, int n_chunks_ub, hipStream_t s) {
 // ---------------------------------------------------------------- W, U
 // Materialises W = T diag(beta e^gam) K and U = T diag(beta) V in fp32 (a
 // check of the algebra; not used by the forward itself).
+// entry (r, i), i <= r, of the T of a forward T block
 template <typename In>
 __device__ __forceinline__ float tblock_T(const char *blk, int r, int i) {
-    using TB = TBlock<In>;
-    using SW = SwzTF<In>;
+    using TB = TBlockF<In>;
     const int byte = i * (TB::BF ? 2 : 4);
     if constexpr (TB::BF)
-        return to_f32(*reinterpret_cast<const bf16 *>(blk + SW::off(r, byte))) +
-               to_f32(*reinterpret_cast<const bf16 *>(blk + TB::PLANE + SW::off(r, byte)));
+        return to_f32(*reinterpret_cast<const bf16 *>(blk + TB::off(r, byte))) +
+               to_f32(*reinterpret_cast<const bf16 *>(blk + TB::PLANE + TB::off(r, byte)));
     else
-        return *reinterpret_cast<const float *>(blk + SW::off(r, byte));
+        return *reinterpret_cast<const float *>(blk + TB::off(r, byte));
 }
 
 template <typename In>
@@ -254,8 +254,8 @@ __global__ __launch_bounds__(NTHR) void wu_kernel(const WUParams p) {
     const int hq = hv / (p.Hv / p.Hq);
     const In *kp = reinterpret_cast<const In *>(p.k);
     const In *vp = reinterpret_cast<const In *>(p.v);
-    const char *blk = p.tblk + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES;
-    const float *sc = reinterpret_cast<const float *>(blk + TBlock<In>::SC);
+    const char *blk = p.tblk + ((int64_t)gid * p.Hv + hv) * TBlockF<In>::BYTES;
+    const float *sc = reinterpret_cast<const float *>(blk + TBlockF<In>::SC);
     for (int idx = threadIdx.x; idx < n * (p.K + p.V); idx += NTHR) {
         const int r = idx / (p.K + p.V), col = idx % (p.K + p.V);
         const bool isw = col < p.K;
@@ -326,6 +326,7 @@ hipError_t launch_prep(Dt dt, int K, const PrepParams &p, int n_chunks_ub, hipSt
 }
 
 size_t tblock_bytes(Dt dt) { return dt == Dt::BF16 ? TBlock<bf16>::BYTES : TBlock<float>::BYTES; }
+size_t tblock_bytes_fwd(Dt dt) { return dt == Dt::BF16 ? TBlockF<bf16>::BYTES : TBlockF<float>::BYTES; }
 
 hipError_t launch_wu(Dt dt, const WUParams &p, int n_chunks_ub, hipStream_t s) {
     dim3 grid(n_chunks_ub, p.Hv);

@@ -52,14 +52,15 @@ namespace {
 
 constexpr int BV = 64;  // value columns per workgroup (16 per wave)
 
-template <typename In, int KD> struct Cfg {
+// FULLT: the backward's T blocks (the states pass), else the forward's
+template <typename In, int KD, bool FULLT = false> struct Cfg {
     static constexpr bool BF = sizeof(In) == 2;
     static constexpr int NB = BF ? 2 : 1;          // LDS buffers
     static constexpr int ES = sizeof(In);
     static constexpr int EV = 16 / ES;             // elements per 16-byte chunk
     static constexpr int KROW = KD * ES, VROW = BV * ES;
     static constexpr int KT = CH * KROW, VT = CH * VROW;
-    using TB = TBlock<In>;
+    using TB = typename std::conditional<FULLT, TBlock<In>, TBlockF<In>>::type;
     static constexpr int OFF_K = 0, OFF_Q = KT, OFF_V = 2 * KT, OFF_T = 2 * KT + VT;
     static constexpr int BUF = OFF_T + TB::BYTES;
     static constexpr int PROW = CH * (BF ? 2 : 4);  // score plane row bytes
@@ -81,14 +82,13 @@ template <> struct OutVec<bf16> {
 
 // STATES: the backward's states pass, which reads the backward's T blocks
 template <typename In, typename Out, int KD, bool STATES> struct Scan {
-    using C = Cfg<In, KD>;
+    using C = Cfg<In, KD, STATES>;
     using O = Ops<In>;
     using XT = typename O::X;
     using ST = typename O::S;
     using TB = typename C::TB;
     using SK = Swz<C::KROW, KeyKQ>;
     using SV = Swz<C::VROW, KeyVP>;
-    using ST_ = typename std::conditional<STATES, Swz<TB::ROWB>, SwzTF<In>>::type;
     using SP = Swz<C::PROW, KeyVP>;
 
     const ScanParams &p;
@@ -291,7 +291,7 @@ template <typename In, typename Out, int KD, bool STATES> struct Scan {
 #pragma unroll
                 for (int ip = 0; ip <= rt / 2; ++ip) {
                     const int row = slot_row(rt, n16), byte = (32 * ip + 8 * g) * (C::BF ? 2 : 4);
-                    const int o0 = ST_::off(row, byte), o1 = ST_::off(row, byte + 16);
+                    const int o0 = TB::off(row, byte), o1 = TB::off(row, byte + 16);
                     ut[rt] = mma(ut[rt], tp.get8(o0, o1), ip == 0 ? xs0 : xs1);
                 }
             }
@@ -401,7 +401,7 @@ __device__ int gated_window_start(const char *tblk, int64_t cb, int Hv, int hv, 
 // STATES: chunk-start states only (no scores, no output), for the backward
 template <typename In, typename Out, int KD, bool STATES>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_output_kernel(const ScanParams p) {
-    using C = Cfg<In, KD>;
+    using C = Cfg<In, KD, STATES>;
     __shared__ __attribute__((aligned(16))) char buf0[C::BUF];
     __shared__ __attribute__((aligned(16))) char buf1[C::NB == 2 ? C::BUF : 16];
     __shared__ __attribute__((aligned(16))) char pplane[C::PBYTES];

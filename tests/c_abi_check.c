@@ -28,8 +28,8 @@ int main(void) {
     a.B = 1; a.T = 256; a.H_q = 2; a.H_v = 4; a.K = 128; a.V = 128;
     a.dtype = GDR_BF16; a.out_dtype = GDR_F32; a.scale = 0.088f; a.cp_mode = GDR_CP_OFF;
     size_t bytes = 0;
-    /* 4 chunks x 4 v heads of 17,408-byte T blocks */
-    CHECK(gdr_fwd_workspace(&a, &bytes) == GDR_OK && bytes == 4 * 4 * 17408, "fwd workspace");
+    /* 4 chunks x 4 v heads of the forward's 13,312-byte T blocks */
+    CHECK(gdr_fwd_workspace(&a, &bytes) == GDR_OK && bytes == 4 * 4 * 13312, "fwd workspace");
     a.H_v = 3;
     CHECK(gdr_fwd_workspace(&a, &bytes) == GDR_EINVAL, "fwd H_v % H_q");
     a.H_v = 4; a.K = 96;

@@ -79,27 +79,28 @@ def rc_ws(L, a):
     return L.lib.gdr_fwd_workspace(ctypes.byref(a), ctypes.byref(n)), n.value
 
 
-TBLOCK = 17408  # one (chunk, v head) T block: bf16 hi/lo planes of T + gate scalars
+TBLOCK = 17408      # one (chunk, v head) T block of the backward: bf16 hi/lo planes of T + gate scalars
+TBLOCK_FWD = 13312  # the forward's (bf16): rows 0-31 of each plane at half width
 
 
 def test_workspace_sizes(L):
     # T=256: 4 chunks x 4 v heads of T blocks
     rc, n = rc_ws(L, fwd_args(L))
-    assert rc == 0 and n == 4 * 4 * TBLOCK
+    assert rc == 0 and n == 4 * 4 * TBLOCK_FWD
     rc, n = rc_ws(L, fwd_args(L, g_cum=16, A=16))
-    assert rc == 0 and n == 4 * 4 * TBLOCK
+    assert rc == 0 and n == 4 * 4 * TBLOCK_FWD
     # packed sequences: chunk offsets and clamped bounds (2 (n_seq + 1) int32, the
     # table 256-byte aligned) + blocks for up to ceil(T/64) + n_seq chunks
     rc, n = rc_ws(L, fwd_args(L, cu_seqlens=16, n_seq=3))
-    assert rc == 0 and n == 256 + (4 + 3) * 4 * TBLOCK
+    assert rc == 0 and n == 256 + (4 + 3) * 4 * TBLOCK_FWD
     rc, n = rc_ws(L, fwd_args(L, dtype=L.F32, K=64, V=64))
-    assert rc == 0 and n == 4 * 4 * TBLOCK
+    assert rc == 0 and n == 4 * 4 * TBLOCK  # fp32: full rows
     # up to 8192 packed sequences also get their longest-first order: (3 n_seq + 2)
     # int32 entries; beyond that only the offsets and bounds
     rc, n = rc_ws(L, fwd_args(L, cu_seqlens=16, n_seq=100))
-    assert rc == 0 and n == 1280 + (4 + 100) * 4 * TBLOCK
+    assert rc == 0 and n == 1280 + (4 + 100) * 4 * TBLOCK_FWD
     rc, n = rc_ws(L, fwd_args(L, cu_seqlens=16, n_seq=9000))
-    assert rc == 0 and n == 72192 + (4 + 9000) * 4 * TBLOCK
+    assert rc == 0 and n == 72192 + (4 + 9000) * 4 * TBLOCK_FWD
 
 
 @pytest.mark.parametrize("kw,code", [

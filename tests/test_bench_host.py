@@ -21,7 +21,7 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 def test_algorithmic_bytes_of_the_prefill_shard():
     """Per chunk-head (K = V = 128, bf16, G = 2, fp32 o): the scan reads q and k (8 KB
-    each, shared by the 2 v heads), v 16 KB and the 17 KB T block and writes o 32 KB;
+    each, shared by the 2 v heads), v 16 KB and the 13 KB T block and writes o 32 KB;
     plus the initial and final states.  Prep reads k and the gates and writes the T block."""
     cfg = dict(B=4, T=4096, Hq=16, Hv=32, K=128, V=128, dtype="bf16", h0=True)
     ab = bench.algorithmic_bytes(cfg, out_bytes=4)
