@@ -89,7 +89,7 @@ template <typename In, typename Out, int KD, bool STATES> struct Scan {
     using TB = typename C::TB;
     using SK = Swz<C::KROW, KeyKQ>;
     using SV = Swz<C::VROW, KeyVP>;
-    using SP = Swz<C::PROW, KeyVP>;
+    using SP = Swz<C::PROW, typename std::conditional<C::BF, KeyP, KeyVP>::type>;
 
     const ScanParams &p;
     char *buf[2];
