@@ -230,8 +230,8 @@ int gdr_fwd(const gdr_fwd_args *args, hipStream_t stream);
    workspace_bytes are ignored.  No hipMalloc, hipFree or other allocating call is
    made.  Returns GDR_ESCRATCH, launching nothing, when the problem needs more
    scratch than that (gdr_fwd_workspace gives the need: the prefill shard of
-   B=4, T=4096, H_v=32, K=V=128 takes 139 MB; about 15,000 (chunk, v head) pairs
-   fit); GDR_ELAUNCH if the buffer's device address cannot be had.  Every call on
+   B=4, T=4096, H_v=32, K=V=128 takes 109 MB; about 20,000 (chunk, v head) pairs
+   of bf16 inputs fit); GDR_ELAUNCH if the buffer's device address cannot be had.  Every call on
    one GPU uses that GPU's one buffer: calls that overlap in time on one GPU
    (other streams, other host threads) race and must be serialised by the
    caller; consecutive calls on one stream are ordered.  Nothing in the buffer
