@@ -197,19 +197,27 @@ int gdr_abi_version(void);
 const char *gdr_strerror(int code);
 
 /* Workspace bytes gdr_fwd needs for these sizes and options (pointers are
-   not read).  With a sequence split and cp_segment_chunks = 0 the segment
+   not read).  The workspace is this library's own (the pages define no such
+   argument): the caller allocates it, so the library itself never does.  With a sequence split and cp_segment_chunks = 0 the segment
    length, and with it the workspace of GDR_CP_EXACT, follows the compute
    units of the current device (256 if none can be queried): query with the
    device current that will run the call.  Returns GDR_OK or a validation
    error. */
 int gdr_fwd_workspace(const gdr_fwd_args *args, size_t *bytes);
 
-/* Forward chunked prefill on `stream`.  Computes o (and the optional
-   outputs).  Chunks never cross a sequence boundary; the last chunk of a
-   sequence may be partial; an empty sequence copies initial_state to
-   final_state.  In split mode the chunk-start states and the output of
-   segments after the first are the warm-up approximation (exact when the
-   window reaches the start of the sequence).  With cp_segment_chunks = 0 the
+/* Forward chunked prefill on `stream`: the low-level forward of the README
+   ("Usage", "Low-level API"), which returns the in-chunk cumulative gate, A,
+   o, the chunk-start states and the final state, evaluated by the chunked
+   steps of the efeozkan blog ("2. Hardware-Friendly Algebraic
+   Reformulation").  Computes o (and the optional outputs).  Chunks never
+   cross a sequence boundary; the last chunk of a sequence may be partial; an
+   empty sequence copies initial_state to final_state.  With GDR_CP_WARMUP and
+   GDR_CP_AUTO_PAGES the chunk-start states and the output of segments after
+   the first are the warm-up approximation (exact when the window reaches the
+   start of the sequence); GDR_CP_AUTO chooses each segment's window on the
+   device from the gates, so that its result differs from the exact one by at
+   most 2^-24 of the state (the window reaches back to the sequence start
+   where the gates do not decay).  With cp_segment_chunks = 0 the
    segment length L is chosen from the compute-unit count of the stream's
    device (one scan workgroup per unit): the segment count S that minimises
    rounds x (L + warm-up window) for the warm-up split and
@@ -244,7 +252,8 @@ int gdr_fwd_noalloc(const gdr_fwd_args *args, hipStream_t stream);
    Returns GDR_OK or a validation error. */
 int gdr_tblocks_bytes(const gdr_fwd_args *args, size_t *bytes);
 
-/* Workspace bytes gdr_bwd needs for these sizes (pointers are not read):
+/* Workspace bytes gdr_bwd needs for these sizes (pointers are not read; the
+   workspace is this library's own, as for gdr_fwd_workspace):
    T blocks (unless tblk_bwd is given), the chunk-start states (unless h_bwd
    is given) and the chunk-end state gradients, 4 K V bytes each per
    (chunk, v head); with a sequence split also, per
@@ -254,9 +263,11 @@ int gdr_tblocks_bytes(const gdr_fwd_args *args, size_t *bytes);
    validation error. */
 int gdr_bwd_workspace(const gdr_bwd_args *args, size_t *bytes);
 
-/* Backward of the exact forward (GDR_CP_OFF) on `stream`: gradients of
-   <dout, o> + <dht, final_state> for an fp32 o, with respect to q, k, v,
-   beta, the raw per-token g and initial_state.  g_cum and A must be what
+/* Backward of the exact forward (GDR_CP_OFF) on `stream`: the low-level
+   backward of the README ("Usage", "Low-level API"), which takes the forward's
+   g and A with the output gradient and returns dq, dk, dv, dbeta, dg and dh0.
+   Gradients of <dout, o> + <dht, final_state> for an fp32 o, with respect to
+   q, k, v, beta, the raw per-token g and initial_state.  g_cum and A must be what
    gdr_fwd returned for the same inputs.  The chunk-start states are
    recomputed unless the forward's h_bwd is given, the T blocks rebuilt
    unless its tblk_bwd is given.  dq and dk are written in full (rows of every
