@@ -2,7 +2,7 @@
 //
 // Tiles in LDS are row-major with their 16-byte chunks XOR-swizzled by row:
 // physical chunk p of row r holds logical chunk p ^ (key(r) mod S), S =
-// min(16, chunks per row), key(r) = r unless stated.  Sixteen consecutive rows read at one column (the MFMA
+// min(16, chunks per row), key(r) = r unless stated (KeyB for 128-byte rows).  Sixteen consecutive rows read at one column (the MFMA
 // operand pattern) then fall into different banks, and a wave's direct
 // global->LDS copy (64 lanes x 16 bytes, lane l -> base + 16 l) can still
 // fill whole rows in order.
@@ -54,7 +54,20 @@ struct KeyP {
     static __device__ __forceinline__ int key(int r) { return (r >> 1) & 7; }
 };
 
-template <int ROWB, typename KEY = KeyRow> struct Swz {
+// Default key of 128-byte rows (the backward's value-column tiles and split
+// planes, its T blocks, the key tiles of K = 64): key bits 1, 2 are row bits
+// 1, 2, and row bit 3 flips key bits 0 and 2.  16 consecutive rows then fill
+// every 8-byte slot once per 32-lane pass of an 8-byte read at one column (two
+// rows share a 256-byte bank row), the transposing 8-byte reads of 8 rows x 2
+// chunks do too, and the 16-byte reads of 16 consecutive or slot-order rows
+// are conflict-free under the lane grouping described above.
+struct KeyB {
+    static __device__ __forceinline__ int key(int r) { return (r & 6) ^ (((r >> 3) & 1) * 5); }
+};
+template <int ROWB> struct DefaultKey { using type = KeyRow; };
+template <> struct DefaultKey<128> { using type = KeyB; };
+
+template <int ROWB, typename KEY = typename DefaultKey<ROWB>::type> struct Swz {
     static constexpr int CPR = ROWB / 16;
     static constexpr int S = CPR < 16 ? CPR : 16;
     // byte offset of (row, byte-in-row) in the swizzled tile
@@ -65,7 +78,8 @@ template <int ROWB, typename KEY = KeyRow> struct Swz {
     static __device__ __forceinline__ int chunk(int row, int p) { return p ^ (KEY::key(row) & (S - 1)); }
 };
 
-// The backward's T blocks: full planes, rows swizzled by KeyRow.
+// The backward's T blocks: full planes, rows swizzled by the default key
+// (KeyB for the 128-byte rows of bf16 inputs).
 template <typename In> struct TBlock {
     static constexpr bool BF = sizeof(In) == 2;
     static constexpr int ROWB = CH * (BF ? 2 : 4);  // bytes per plane row
