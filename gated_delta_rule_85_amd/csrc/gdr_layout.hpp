@@ -31,27 +31,27 @@ namespace gdr {
 // over plain 16-lane groups.  An 8-byte transposing read is served 32 lanes
 // per pass.
 struct KeyRow {
-    static __device__ __forceinline__ int key(int r) { return r; }
+    static __host__ __device__ __forceinline__ int key(int r) { return r; }
 };
 // K and Q tiles (256-byte rows): key bits 2, 0, 1, 3 are row bits 0, 1,
 // 2 ^ 4, 3.  Both the 16-consecutive-row reads and the slot-order reads then
 // see every bank column once per pass.
 struct KeyKQ {
-    static __device__ __forceinline__ int key(int r) {
+    static __host__ __device__ __forceinline__ int key(int r) {
         return ((r & 1) << 2) | ((r >> 1) & 1) | ((((r >> 2) ^ (r >> 4)) & 1) << 1) | (r & 8);
     }
 };
 // T blocks read by the scan (128-byte rows): key bits are row bits 1, 3, 4
 struct KeyT {
-    static __device__ __forceinline__ int key(int r) { return ((r >> 1) & 1) | ((r >> 2) & 6); }
+    static __host__ __device__ __forceinline__ int key(int r) { return ((r >> 1) & 1) | ((r >> 2) & 6); }
 };
 // V tiles (128-byte rows, read transposed): key bits are row bits 2, 1, 3
 struct KeyVP {
-    static __device__ __forceinline__ int key(int r) { return ((r >> 2) & 1) | (r & 2) | ((r >> 1) & 4); }
+    static __host__ __device__ __forceinline__ int key(int r) { return ((r >> 2) & 1) | (r & 2) | ((r >> 1) & 4); }
 };
 // bf16 score planes (128-byte rows, read as 16 consecutive rows): key bits are row bits 1, 2, 3
 struct KeyP {
-    static __device__ __forceinline__ int key(int r) { return (r >> 1) & 7; }
+    static __host__ __device__ __forceinline__ int key(int r) { return (r >> 1) & 7; }
 };
 
 // Default key of 128-byte rows (the backward's value-column tiles and split
@@ -62,7 +62,7 @@ struct KeyP {
 // chunks do too, and the 16-byte reads of 16 consecutive or slot-order rows
 // are conflict-free under the lane grouping described above.
 struct KeyB {
-    static __device__ __forceinline__ int key(int r) { return (r & 6) ^ (((r >> 3) & 1) * 5); }
+    static __host__ __device__ __forceinline__ int key(int r) { return (r & 6) ^ (((r >> 3) & 1) * 5); }
 };
 template <int ROWB> struct DefaultKey { using type = KeyRow; };
 template <> struct DefaultKey<128> { using type = KeyB; };
@@ -71,11 +71,11 @@ template <int ROWB, typename KEY = typename DefaultKey<ROWB>::type> struct Swz {
     static constexpr int CPR = ROWB / 16;
     static constexpr int S = CPR < 16 ? CPR : 16;
     // byte offset of (row, byte-in-row) in the swizzled tile
-    static __device__ __forceinline__ int off(int row, int byte) {
+    static __host__ __device__ __forceinline__ int off(int row, int byte) {
         return row * ROWB + ((((byte >> 4) ^ (KEY::key(row) & (S - 1)))) << 4) + (byte & 15);
     }
     // logical chunk held by physical chunk p of row r (an involution)
-    static __device__ __forceinline__ int chunk(int row, int p) { return p ^ (KEY::key(row) & (S - 1)); }
+    static __host__ __device__ __forceinline__ int chunk(int row, int p) { return p ^ (KEY::key(row) & (S - 1)); }
 };
 
 // The backward's T blocks: full planes, rows swizzled by the default key
@@ -89,7 +89,7 @@ template <typename In> struct TBlock {
     static constexpr int BYTES = SC + 4 * CH * 4;
     static_assert(BYTES % 1024 == 0, "block copied in 1 KB wave transfers");
     // byte offset of (row, byte-in-row) within a plane
-    static __device__ __forceinline__ int off(int row, int byte) { return Swz<ROWB>::off(row, byte); }
+    static __host__ __device__ __forceinline__ int off(int row, int byte) { return Swz<ROWB>::off(row, byte); }
 };
 // swizzle of the full-width rows of the T blocks gdr_chunk_prep writes for the scan
 template <typename In> using SwzTF = Swz<TBlock<In>::ROWB, KeyT>;
@@ -112,14 +112,14 @@ template <> struct TBlockF<bf16> {
     static constexpr int SC = NPL * PLANE;         // scalars
     static constexpr int BYTES = SC + 4 * CH * 4;
     static_assert(BYTES % 1024 == 0, "block copied in 1 KB wave transfers");
-    static __device__ __forceinline__ int key0(int r) { return (((r >> 3) & 1) << 1) ^ (((r >> 4) & 1) * 3); }
-    static __device__ __forceinline__ int off(int row, int byte) {
+    static __host__ __device__ __forceinline__ int key0(int r) { return (((r >> 3) & 1) << 1) ^ (((r >> 4) & 1) * 3); }
+    static __host__ __device__ __forceinline__ int off(int row, int byte) {
         return row < 32 ? row * 64 + ((((byte >> 4) ^ key0(row)) & 3) << 4) + (byte & 15)
                         : HALF + (row - 32) * 128 + ((((byte >> 4) ^ KeyT::key(row)) & 7) << 4) + (byte & 15);
     }
 };
 template <> struct TBlockF<float> : TBlock<float> {
-    static __device__ __forceinline__ int off(int row, int byte) { return SwzTF<float>::off(row, byte); }
+    static __host__ __device__ __forceinline__ int off(int row, int byte) { return SwzTF<float>::off(row, byte); }
 };
 
 

@@ -115,9 +115,9 @@ __device__ __forceinline__ typename Ops<In>::X kt_operand(const char *Ks, int d0
 // to hold k = 8g + i in tile t0 and 8g + 4 + i in tile t0+1 at row 4g + i, so
 // the rows of tile t of a 64-row block are taken in the order
 //   row 4g + i of tile t  <->  index slot_base(t, g) + i.
-__device__ __forceinline__ int slot_base(int t, int g) { return 32 * (t >> 1) + 4 * (t & 1) + 8 * g; }
+__host__ __device__ __forceinline__ int slot_base(int t, int g) { return 32 * (t >> 1) + 4 * (t & 1) + 8 * g; }
 // index held by A-operand row n (0..15) of tile t in that order
-__device__ __forceinline__ int slot_row(int t, int n) { return slot_base(t, n >> 2) + (n & 3); }
+__host__ __device__ __forceinline__ int slot_row(int t, int n) { return slot_base(t, n >> 2) + (n & 3); }
 
 // A operand (row `row`, k = 8 consecutive elements from byte `byte`, which is
 // a multiple of 16) of a row-major tile with swizzle S
