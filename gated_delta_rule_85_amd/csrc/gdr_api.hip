@@ -137,6 +137,9 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     pl.gated = split && gated;
     if (pl.exact || pl.gated) pl.warm_chunks = 0;
     pl.seg_chunks = (int)L;
+    // segments x units bounds the scan grids (x 2 column blocks) and the split's
+    // workspace sizes; a caller's short segment length can otherwise overflow them
+    if (split && cdiv(pl.nct, L) * bh > ((int64_t)1 << 30)) return GDR_EINVAL;
     pl.n_seg = split ? (int)cdiv(pl.nct, L) : 1;
     pl.off_M = pl.off_b = pl.off_hseg = pl.off_zero = 0;
     if (pl.exact) {
@@ -211,6 +214,7 @@ int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl, int64_t slots = 0) {
     }
     pl.split = split;
     pl.seg_chunks = (int)L;
+    if (split && cdiv(pl.nct, L) * bh > ((int64_t)1 << 30)) return GDR_EINVAL;  // as in plan_fwd
     pl.n_seg = split ? (int)cdiv(pl.nct, L) : 1;
     pl.off_M = pl.off_b = pl.off_hseg = pl.off_d = pl.off_gseg = pl.off_zero = 0;
     if (split) {

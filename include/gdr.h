@@ -202,7 +202,8 @@ const char *gdr_strerror(int code);
    length, and with it the workspace of GDR_CP_EXACT, follows the compute
    units of the current device (256 if none can be queried): query with the
    device current that will run the call.  Returns GDR_OK or a validation
-   error. */
+   error (GDR_EINVAL also when a split would give more than 2^30 (segment,
+   sequence, v head) triples, which would overflow the launch grid). */
 int gdr_fwd_workspace(const gdr_fwd_args *args, size_t *bytes);
 
 /* Forward chunked prefill on `stream`: the low-level forward of the README

@@ -123,6 +123,20 @@ def test_validation_errors(L, kw, code):
     assert L.lib.gdr_fwd(ctypes.byref(fwd_args(L, **kw)), None) == code
 
 
+def test_segment_count_is_bounded(L):
+    """A caller's segment length of one chunk over many units would overflow the
+    scan grid and the exact split's workspace size; the plan refuses it."""
+    many = dict(T=1 << 20, H_q=1, H_v=1 << 17, cp_segment_chunks=1)  # 16,384 segments x 2^17 units
+    for mode in (L.CP_EXACT, L.CP_WARMUP):
+        rc, _ = rc_ws(L, fwd_args(L, cp_mode=mode, **many))
+        assert rc == L.EINVAL
+    n = ctypes.c_size_t(0)
+    assert L.lib.gdr_bwd_workspace(ctypes.byref(bwd_args(L, cp_mode=L.CP_EXACT, **many)), ctypes.byref(n)) == L.EINVAL
+    # the same shape unsplit, or with segments of 64 chunks, plans normally
+    assert rc_ws(L, fwd_args(L, cp_mode=L.CP_OFF, **many))[0] == 0
+    assert rc_ws(L, fwd_args(L, cp_mode=L.CP_EXACT, **dict(many, cp_segment_chunks=64)))[0] == 0
+
+
 def test_fwd_host_errors_before_any_launch(L):
     a = fwd_args(L)  # all pointers null
     assert L.lib.gdr_fwd(ctypes.byref(a), None) == L.EINVAL
