@@ -51,6 +51,18 @@ def run_bwd(x, with_dht=True, grad_dtype=torch.float32, fwd_states=False, fwd_cp
     return dict(zip(NAMES, out))
 
 
+
+@pytest.mark.parametrize("with_dht", [True, False])
+def test_no_tokens_passes_the_state_gradient_through(with_dht):
+    """T = 0: the final state is the initial state, so dh0 = dht (zeros without
+    it) and every other gradient is empty."""
+    x = make_inputs(dict(B=2, T=0, Hq=1, Hv=2, K=64, V=64, dtype="bf16", h0=True), seed=5, grads=True)
+    got = run_bwd(x, with_dht=with_dht)
+    for name in ("dq", "dk", "dv", "dbeta", "dg"):
+        assert got[name].numel() == 0, name
+    want = x["dht"] if with_dht else np.zeros((2, 2, 64, 64))
+    assert np.array_equal(host(got["dh0"]), np.asarray(want, np.float64))
+
 def ora_bwd(x, with_dht=True):
     return oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], x["scale"],
                       initial_state=x["initial_state"], dht=x["dht"] if with_dht else None,

@@ -68,6 +68,18 @@ def test_small_ragged(shape):
     assert rel(host(out[6]), ch["U"]) <= t
 
 
+@pytest.mark.parametrize("h0", [True, False])
+def test_no_tokens_returns_the_initial_state(h0):
+    """T = 0: nothing to scan; o is empty and the final state is the initial state
+    (zeros without one), as the recurrence over an empty sequence gives."""
+    x = make_inputs(dict(B=2, T=0, Hq=1, Hv=2, K=64, V=64, dtype="bf16", h0=h0), seed=5)
+    out = run_fwd(x)
+    assert tuple(out[2].shape) == (2, 0, 2, 64)
+    ht = host(out[4])
+    want = x["initial_state"] if h0 else np.zeros((2, 2, 64, 64))
+    assert np.array_equal(ht, np.asarray(want, np.float64))
+
+
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 128])
 def test_short_sequences(T):
     x = make_inputs(dict(B=2, T=T, Hq=1, Hv=2, K=128, V=128, dtype="bf16", h0=True), seed=2)
