@@ -60,7 +60,7 @@ def run(x, noalloc, cp_mode, seg=0):
 
 def test_noalloc_matches_the_workspace_forward_on_calls_of_decreasing_size():
     from gated_delta_rule_85_amd import _lib
-    # 1: the prefill shard, unsplit (T blocks fill 139 MB of the scratch)
+    # 1: the prefill shard, unsplit (T blocks fill 109 MB of the scratch)
     x = make_inputs("prefill_shard", seed=0)
     o_n, h_n = run(x, True, _lib.CP_OFF)
     o_w, h_w = run(x, False, _lib.CP_OFF)
