@@ -104,8 +104,10 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     off += seq_table_bytes(varlen, pl.n_seq);
     pl.off_tblk = off;
     const Dt pdt = a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
-    pl.tblk_bytes = up(tblock_bytes_fwd(pdt) * (size_t)(pl.nt_ub * a->H_v));
     pl.tblk_bwd_bytes = up(tblock_bytes(pdt) * (size_t)(pl.nt_ub * a->H_v));
+    // bf16: the forward's T blocks are the backward's, so with tblk_bwd they are written
+    // there and take no workspace
+    pl.tblk_bytes = a->tblk_bwd && pdt == Dt::BF16 ? 0 : up(tblock_bytes_fwd(pdt) * (size_t)(pl.nt_ub * a->H_v));
     off += pl.tblk_bytes;
     pl.total = off;
     // sequence split ("AutoCP")
@@ -324,7 +326,9 @@ int gdr::fwd_impl(const gdr_fwd_args *a, hipStream_t stream, void *(*scratch_for
         ws = static_cast<char *>(a->workspace);
     }
     int32_t *chunk_off = a->cu_seqlens ? reinterpret_cast<int32_t *>(ws + pl.off_chunk) : nullptr;
-    char *tblk = ws + pl.off_tblk;
+    // T blocks: the caller's tblk_bwd for bf16 inputs when given (the backward reads the
+    // same blocks), else the workspace
+    char *tblk = a->tblk_bwd && a->dtype == GDR_BF16 ? static_cast<char *>(a->tblk_bwd) : ws + pl.off_tblk;
     const Dt dt = a->dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
     const Dt ot = a->out_dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
     const SeqMap sm = make_map(a->cu_seqlens != nullptr, a->T, pl.n_seq, pl.nct, chunk_off);
@@ -345,7 +349,7 @@ int gdr::fwd_impl(const gdr_fwd_args *a, hipStream_t stream, void *(*scratch_for
         pp.g_cum = a->g_cum;
         pp.Tm = a->A;
         pp.tblk = tblk;
-        pp.tblk_bwd = static_cast<char *>(a->tblk_bwd);
+        pp.tblk_bwd = dt == Dt::F32 ? static_cast<char *>(a->tblk_bwd) : nullptr;
         pp.sm = sm;
         pp.Hq = (int)a->H_q;
         pp.Hv = (int)a->H_v;

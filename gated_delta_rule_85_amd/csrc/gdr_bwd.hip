@@ -146,8 +146,12 @@ __global__ __launch_bounds__(NTHR) void tblock_kernel(const BwdParams p) {
     load_T(p, ts, n, hv, Tf);
     load_gates(p, ts, n, hv, gam, eg, rr, bet);
     __syncthreads();
-    write_tblock<In>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, Tf, LF, gam, bet, n,
-                     threadIdx.x, NTHR);
+    if constexpr (sizeof(In) == 2)  // the compact block the bf16 kernels read
+        write_tblock_f<In>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlockF<In>::BYTES, Tf, LF, gam, bet, n,
+                           threadIdx.x, NTHR);
+    else
+        write_tblock<In>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, Tf, LF, gam, bet, n,
+                         threadIdx.x, NTHR);
 }
 
 // ------------------------------------------------------------- reverse scan

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
     constexpr int DP = KD / 32, TD = KD / 64, NH = KD / 64;  // 64-row halves of h
     constexpr int NQ = 7;
     // row sums: 0 Q.(dO h^T), 1 K.(dX h^T), 2 K.(U~ dh'^T), 3 dX.V, 4 dP*P, 5 dA*A, 6 dbeta via A
-    using TB = TBlock<bf16>;
+    using TB = TBlockF<bf16>;  // compact T blocks: rows 0-31 stored in their first 32 columns
     using S128 = Swz<128>;
     __shared__ __attribute__((aligned(16))) char Ks[CH * KROW];
     __shared__ __attribute__((aligned(16))) char Qs[CH * KROW];
@@ -200,10 +200,10 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
                 f32x4 ut = zero4(), dxt = zero4();
 #pragma unroll
                 for (int ip = 0; ip <= rt / 2; ++ip)
-                    ut = mma(ut, ip == 0 ? xs0 : xs1, frag_s<TB::ROWB>(Tb, TB::PLANE, tok, (32 * ip + 4 * g) * 2));
+                    ut = mma(ut, ip == 0 ? xs0 : xs1, frag_s_in<TB>(Tb, TB::PLANE, tok, (32 * ip + 4 * g) * 2));
 #pragma unroll
                 for (int ip = rt / 2; ip < 2; ++ip)  // dX^T = dU~^T T (T^T upper triangular)
-                    dxt = mma(dxt, ip == 0 ? dus0 : dus1, kt_s<TB::ROWB>(Tb, TB::PLANE, 16 * rt, ip));
+                    dxt = mma(dxt, ip == 0 ? dus0 : dus1, kt_s_in<TB>(Tb, TB::PLANE, 16 * rt, ip));
                 put4_s(Wm[0], PPL, tok, c4, ut);
                 put4_s(Wm[1], PPL, tok, c4, dxt);
                 if (tok < n) {

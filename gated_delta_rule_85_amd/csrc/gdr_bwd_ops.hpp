@@ -10,11 +10,11 @@ namespace gdr {
 namespace bwd {
 
 
-// split operands from the hi plane at `hi` and the lo plane `plane` bytes after it
-template <int ROWB>
-__device__ __forceinline__ OpS frag_s(const char *hi, int plane, int row, int byte) {
-    using S = Swz<ROWB>;
-    const int o0 = S::off(row, byte), o1 = S::off(row, byte + 32);
+// split operands from the hi plane at `hi` and the lo plane `plane` bytes after it,
+// in layout L (L::off(row, byte): a swizzled tile, or the compact T block)
+template <typename L>
+__device__ __forceinline__ OpS frag_s_in(const char *hi, int plane, int row, int byte) {
+    const int o0 = L::off(row, byte), o1 = L::off(row, byte + 32);
     OpS r;
     r.h0 = *reinterpret_cast<const bf16x4 *>(hi + o0);
     r.h1 = *reinterpret_cast<const bf16x4 *>(hi + o1);
@@ -23,14 +23,32 @@ __device__ __forceinline__ OpS frag_s(const char *hi, int plane, int row, int by
     return r;
 }
 template <int ROWB>
-__device__ __forceinline__ OpS kt_s(const char *hi, int plane, int c0, int ip) {
-    const OpX a = kt_operand<bf16, ROWB>(hi, c0, ip), b = kt_operand<bf16, ROWB>(hi + plane, c0, ip);
+__device__ __forceinline__ OpS frag_s(const char *hi, int plane, int row, int byte) {
+    return frag_s_in<Swz<ROWB>>(hi, plane, row, byte);
+}
+// A operand of M^T (rows = columns c0 + lane16 of M, k = its rows 32 ip ..), layout L
+template <typename L>
+__device__ __forceinline__ OpX kt_in(const char *M, int c0, int ip) {
+    const int n = ln16(), g = lg4();
+    const int row = 32 * ip + 4 * g + (n >> 2), byte = 2 * (c0 + 4 * (n & 3));
+    OpX r;
+    r.b0 = lds_tr4(M + L::off(row, byte));
+    r.b1 = lds_tr4(M + L::off(row + 16, byte));
+    return r;
+}
+template <typename L>
+__device__ __forceinline__ OpS kt_s_in(const char *hi, int plane, int c0, int ip) {
+    const OpX a = kt_in<L>(hi, c0, ip), b = kt_in<L>(hi + plane, c0, ip);
     OpS r;
     r.h0 = a.b0;
     r.h1 = a.b1;
     r.l0 = b.b0;
     r.l1 = b.b1;
     return r;
+}
+template <int ROWB>
+__device__ __forceinline__ OpS kt_s(const char *hi, int plane, int c0, int ip) {
+    return kt_s_in<Swz<ROWB>>(hi, plane, c0, ip);
 }
 
 template <int ROWB>

@@ -40,7 +40,7 @@ template <int KD>
 __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_units) {
     constexpr int KROW = KD * 2, DROW = 64 * 2, PROW = 64 * 2, PPLANE = CH * PROW;
     constexpr int DT = KD / 16, DP = KD / 32;
-    using TB = TBlock<bf16>;
+    using TB = TBlockF<bf16>;  // compact T blocks: rows 0-31 stored in their first 32 columns
     // two sets of chunk tiles: the next chunk (in reverse order) is copied into one
     // while the current one is read (separate arrays, so the compiler can tell the
     // copies into one set from the reads of the other)
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_u
             dx[rt] = zero4();
 #pragma unroll
             for (int ip = rt / 2; ip < 2; ++ip)
-                dx[rt] = mma(dx[rt], kt_s<TB::ROWB>(Tb, TB::PLANE, 16 * rt, ip), ip == 0 ? dus0 : dus1);
+                dx[rt] = mma(dx[rt], kt_s_in<TB>(Tb, TB::PLANE, 16 * rt, ip), ip == 0 ? dus0 : dus1);
         }
         // dh = e_last dh' + Q^T diag(s e) dO - K^T diag(beta e) dX
         OpS edo[2], bdx[2];

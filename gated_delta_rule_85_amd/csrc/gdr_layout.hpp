@@ -41,7 +41,7 @@ struct KeyKQ {
         return ((r & 1) << 2) | ((r >> 1) & 1) | ((((r >> 2) ^ (r >> 4)) & 1) << 1) | (r & 8);
     }
 };
-// T blocks read by the scan (128-byte rows): key bits are row bits 1, 3, 4
+// fp32 T blocks read by the forward scan (256-byte rows): key bits are row bits 1, 3, 4
 struct KeyT {
     static __host__ __device__ __forceinline__ int key(int r) { return ((r >> 1) & 1) | ((r >> 2) & 6); }
 };
@@ -97,12 +97,14 @@ template <typename In> using SwzTF = Swz<TBlock<In>::ROWB, KeyT>;
 // The forward's T blocks, the LDS image gdr_scan_output copies in.  For bf16
 // inputs the scan reads rows 0-31 of T only in their first 32 columns (their
 // other columns are zero: T is lower triangular), so each plane holds rows
-// 0-31 at 64 bytes and then rows 32-63 at 128 bytes (KeyT swizzle): 6 KB per
-// plane, 13 KB per block with the scalars instead of 17 KB.  In rows 0-31
-// logical 16-byte chunk q of row r sits at physical chunk q ^ key0(r), key0
-// taking row bits 3 and 4 to 2 and 3 (the values 0, 2, 3, 1): the scan's
-// slot-order operand reads of those rows then use each bank column once per
-// pass of the lane grouping described above.  fp32 inputs keep full rows.
+// 0-31 at 64 bytes and then rows 32-63 at 128 bytes (KeyB swizzle): 6 KB per
+// plane, 13 KB per block with the scalars instead of 17 KB.  The backward of
+// bf16 inputs reads the same blocks (it never touches the zero quadrant
+// either).  In rows 0-31 logical 16-byte chunk q of row r sits at physical
+// chunk q ^ key0(r), key0 taking row bit 2 to 2 and row bit 3 to 3: the
+// scan's 16-byte slot-order reads of those rows, the backward's 8-byte reads of
+// 16 consecutive rows and its transposing reads of 8 rows then all use each
+// bank slot once per pass.  fp32 inputs keep full rows.
 template <typename In> struct TBlockF;
 template <> struct TBlockF<bf16> {
     static constexpr bool BF = true;
@@ -112,10 +114,10 @@ template <> struct TBlockF<bf16> {
     static constexpr int SC = NPL * PLANE;         // scalars
     static constexpr int BYTES = SC + 4 * CH * 4;
     static_assert(BYTES % 1024 == 0, "block copied in 1 KB wave transfers");
-    static __host__ __device__ __forceinline__ int key0(int r) { return (((r >> 3) & 1) << 1) ^ (((r >> 4) & 1) * 3); }
+    static __host__ __device__ __forceinline__ int key0(int r) { return (((r >> 2) & 1) << 1) ^ (((r >> 3) & 1) * 3); }
     static __host__ __device__ __forceinline__ int off(int row, int byte) {
         return row < 32 ? row * 64 + ((((byte >> 4) ^ key0(row)) & 3) << 4) + (byte & 15)
-                        : HALF + (row - 32) * 128 + ((((byte >> 4) ^ KeyT::key(row)) & 7) << 4) + (byte & 15);
+                        : HALF + (row - 32) * 128 + ((((byte >> 4) ^ KeyB::key(row)) & 7) << 4) + (byte & 15);
     }
 };
 template <> struct TBlockF<float> : TBlock<float> {

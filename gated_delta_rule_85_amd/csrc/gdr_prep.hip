@@ -201,10 +201,12 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
         // T block for the scan: swizzled planes (rows past the chunk end zero) + scalars
         write_tblock_f<In>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlockF<In>::BYTES, Tm, LDF, gam, bet, n, tid,
                            NTHR);
-        // and, for a backward, in the layout its kernels copy (plain 16-byte-chunk order)
-        if (p.tblk_bwd)
-            write_tblock<In>(p.tblk_bwd + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, Tm, LDF, gam, bet, n, tid,
-                             NTHR);
+        // and, for the backward of fp32 inputs, in the layout its kernels copy (plain
+        // 16-byte-chunk order); the bf16 backward reads the blocks above
+        if constexpr (sizeof(In) == 4)
+            if (p.tblk_bwd)
+                write_tblock<In>(p.tblk_bwd + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, Tm, LDF, gam, bet, n,
+                                 tid, NTHR);
         lds_barrier();  // Tm, A, gam, bet free again; the block's stores drain meanwhile
     }
 }
@@ -325,7 +327,7 @@ hipError_t launch_prep(Dt dt, int K, const PrepParams &p, int n_chunks_ub, hipSt
     return K == 128 ? launch_prep_t<float, 128>(p, n_chunks_ub, s) : launch_prep_t<float, 64>(p, n_chunks_ub, s);
 }
 
-size_t tblock_bytes(Dt dt) { return dt == Dt::BF16 ? TBlock<bf16>::BYTES : TBlock<float>::BYTES; }
+size_t tblock_bytes(Dt dt) { return dt == Dt::BF16 ? TBlockF<bf16>::BYTES : TBlock<float>::BYTES; }
 size_t tblock_bytes_fwd(Dt dt) { return dt == Dt::BF16 ? TBlockF<bf16>::BYTES : TBlockF<float>::BYTES; }
 
 hipError_t launch_wu(Dt dt, const WUParams &p, int n_chunks_ub, hipStream_t s) {

@@ -60,7 +60,7 @@ template <typename In, int KD, bool FULLT = false> struct Cfg {
     static constexpr int EV = 16 / ES;             // elements per 16-byte chunk
     static constexpr int KROW = KD * ES, VROW = BV * ES;
     static constexpr int KT = CH * KROW, VT = CH * VROW;
-    using TB = typename std::conditional<FULLT, TBlock<In>, TBlockF<In>>::type;
+    using TB = typename std::conditional<FULLT && !BF, TBlock<In>, TBlockF<In>>::type;
     static constexpr int OFF_K = 0, OFF_Q = KT, OFF_V = 2 * KT, OFF_T = 2 * KT + VT;
     static constexpr int BUF = OFF_T + TB::BYTES;
     static constexpr int PROW = CH * (BF ? 2 : 4);  // score plane row bytes

@@ -39,7 +39,7 @@ int main(void) {
     CHECK(gdr_fwd_noalloc(&a, NULL) == GDR_EINVAL, "fwd_noalloc null pointers rejected before any launch");
     CHECK(strcmp(gdr_strerror(GDR_ESCRATCH), "problem needs more than the library's static scratch buffer") == 0,
           "strerror scratch");
-    CHECK(gdr_tblocks_bytes(&a, &bytes) == GDR_OK && bytes == 4 * 4 * 17408, "T blocks for the backward");
+    CHECK(gdr_tblocks_bytes(&a, &bytes) == GDR_OK && bytes == 4 * 4 * 13312, "T blocks for the backward");
     a.h_bwd = (void *)16;
     a.cp_mode = GDR_CP_WARMUP;
     CHECK(gdr_fwd_workspace(&a, &bytes) == GDR_EINVAL, "fwd states for the backward need an exact scan");
@@ -50,7 +50,7 @@ int main(void) {
     memset(&b, 0, sizeof b);
     b.B = 1; b.T = 256; b.H_q = 2; b.H_v = 4; b.K = 128; b.V = 128;
     b.dtype = GDR_BF16; b.grad_dtype = GDR_BF16; b.scale = 0.088f; b.cp_mode = GDR_CP_OFF;
-    CHECK(gdr_bwd_workspace(&b, &bytes) == GDR_OK && bytes == 4 * 4 * (17408 + 2 * 4 * 128 * 128),
+    CHECK(gdr_bwd_workspace(&b, &bytes) == GDR_OK && bytes == 4 * 4 * (13312 + 2 * 4 * 128 * 128),
           "bwd workspace");
     b.h_bwd = (const void *)16;
     b.tblk_bwd = (const void *)16;

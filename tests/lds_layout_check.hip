@@ -99,10 +99,19 @@ int main() {
     // 8-byte writes of rows 16 rt + n at columns 16 w + 4 g
     printf("bwd_put4 %.2f\n", worst(16, false, [](int i, int n, int g) {
                return S128::off(16 * (i & 3) + n, 2 * (16 * (i >> 2) + 4 * g)); }));
-    // the states pass's 16-byte T reads (full T planes), slot rows
+    // the compact T block as the backward reads it: 8-byte reads of rows 16 rt + n
+    // (k block ip <= rt / 2, bytes 64 ip + 8 g and 32 more) and transposing reads of
+    // rows 32 ip + 4 g + n / 4 (+16) at columns 16 rt + 4 (n % 4), ip >= rt / 2
+    printf("bwd_T_rows %.2f\n", worst(16, false, [](int i, int n, int g) {
+               const int rt = i & 3, ip = ((i >> 2) & 1) <= rt / 2 ? ((i >> 2) & 1) : 0;
+               return TF::off(16 * rt + n, 64 * ip + 8 * g + ((i >> 3) & 1) * 32); }));
+    printf("bwd_T_tr %.2f\n", worst(16, false, [](int i, int n, int g) {
+               const int rt = i & 3, ip = ((i >> 2) & 1) >= rt / 2 ? ((i >> 2) & 1) : 1;
+               return TF::off(32 * ip + 4 * g + (n >> 2) + ((i >> 3) & 1) * 16, 2 * (16 * rt + 4 * (n & 3))); }));
+    // the states pass's 16-byte T reads of fp32-free blocks: the compact block, slot rows
     printf("bwd_states_T %.2f\n", worst(8, true, [](int i, int n, int g) {
                const int rt = i & 3, ip = (i >> 2) <= rt / 2 ? (i >> 2) : 0;
-               return TBlock<bf16>::off(slot_row(rt, n), (32 * ip + 8 * g) * 2); }));
+               return TF::off(slot_row(rt, n), (32 * ip + 8 * g) * 2); }));
 
     // ---- every row's chunk map is a permutation (no two logical chunks share a slot)
     bool ok = true;

@@ -79,8 +79,8 @@ def rc_ws(L, a):
     return L.lib.gdr_fwd_workspace(ctypes.byref(a), ctypes.byref(n)), n.value
 
 
-TBLOCK = 17408      # one (chunk, v head) T block of the backward: bf16 hi/lo planes of T + gate scalars
-TBLOCK_FWD = 13312  # the forward's (bf16): rows 0-31 of each plane at half width
+TBLOCK = 17408      # one (chunk, v head) T block with full rows (fp32 inputs): T + gate scalars
+TBLOCK_FWD = 13312  # bf16 inputs, forward and backward: hi/lo planes, rows 0-31 at half width
 
 
 def test_workspace_sizes(L):
@@ -166,13 +166,18 @@ def test_forward_states_for_the_backward(L):
 
 
 def test_forward_tblocks_for_the_backward(L):
-    """tblk_bwd: the forward also writes the T blocks, in the backward's layout, to a
-    caller buffer of gdr_tblocks_bytes(), and the backward takes them instead of its
-    own."""
-    assert L.tblocks_bytes(fwd_args(L)) == 4 * 4 * TBLOCK
-    assert L.tblocks_bytes(fwd_args(L, cu_seqlens=16, n_seq=3)) == (4 + 3) * 4 * TBLOCK
+    """tblk_bwd: a caller buffer of gdr_tblocks_bytes() that the backward takes instead
+    of rebuilding its T blocks.  For bf16 inputs the forward writes its own blocks there
+    (the backward reads the same layout), so they leave the workspace; for fp32 inputs
+    it writes a second copy in the backward's layout."""
+    assert L.tblocks_bytes(fwd_args(L)) == 4 * 4 * TBLOCK_FWD
+    assert L.tblocks_bytes(fwd_args(L, cu_seqlens=16, n_seq=3)) == (4 + 3) * 4 * TBLOCK_FWD
     assert L.tblocks_bytes(fwd_args(L, T=0)) == 0
-    assert rc_ws(L, fwd_args(L, tblk_bwd=16)) == rc_ws(L, fwd_args(L))
+    assert L.tblocks_bytes(fwd_args(L, dtype=L.F32, K=64, V=64)) == 4 * 4 * TBLOCK
+    assert rc_ws(L, fwd_args(L, tblk_bwd=16)) == (0, 0)
+    assert rc_ws(L, fwd_args(L, tblk_bwd=16, cu_seqlens=16, n_seq=3)) == (0, 256)
+    f32 = dict(dtype=L.F32, K=64, V=64)
+    assert rc_ws(L, fwd_args(L, tblk_bwd=16, **f32)) == rc_ws(L, fwd_args(L, **f32))
     a = fwd_args(L, q=16, k=16, v=16, g=16, beta=16, o=16, tblk_bwd=40, workspace=4096,
                  workspace_bytes=1 << 30)
     assert L.lib.gdr_fwd(ctypes.byref(a), None) == L.EINVAL  # misaligned tblk_bwd
@@ -198,7 +203,7 @@ def bwd_args(L, **kw):
 
 def test_bwd_workspace_sizes(L):
     # T blocks + chunk-start states + chunk-end state gradients, per (chunk, v head)
-    per = TBLOCK + 2 * 4 * 128 * 128
+    per = TBLOCK_FWD + 2 * 4 * 128 * 128
     assert L.bwd_workspace(bwd_args(L)) == 4 * 4 * per
     assert L.bwd_workspace(bwd_args(L, cu_seqlens=16, n_seq=3)) == 256 + (4 + 3) * 4 * per
     assert L.bwd_workspace(bwd_args(L, T=0)) == 0

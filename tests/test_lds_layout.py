@@ -37,7 +37,7 @@ def layout_costs(tmp_path_factory):
 
 
 CONFLICT_FREE = ["fwd_Kh", "fwd_KQ_rows", "fwd_T", "fwd_P_read", "fwd_P_write", "fwd_V_tr",
-                 "bwd_rows_b64", "bwd_tr", "bwd_put4", "bwd_states_T"]
+                 "bwd_rows_b64", "bwd_tr", "bwd_put4", "bwd_T_rows", "bwd_T_tr", "bwd_states_T"]
 
 
 @pytest.mark.parametrize("name", CONFLICT_FREE)
