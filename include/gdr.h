@@ -135,10 +135,12 @@ typedef struct {
                                    GDR_CP_AUTO_EXACT, and h, GDR_CP_WARMUP or
                                    GDR_CP_AUTO_PAGES is GDR_EINVAL */
     void *tblk_bwd;             /* gdr_tblocks_bytes() bytes, or NULL: the per-(chunk, v head)
-                                   T blocks (T = (I+A)^{-1} and the chunk's gate scalars) are
-                                   also written here, in the backward's layout; passed on as
-                                   gdr_bwd_args.tblk_bwd, they save the backward's rebuild of
-                                   them from A and g_cum */
+                                   T blocks (T = (I+A)^{-1} and the chunk's gate scalars) in
+                                   the backward's layout; for bf16 inputs the forward's own
+                                   blocks (the backward reads the same layout, and they then
+                                   take no workspace), for fp32 inputs a second copy; passed
+                                   on as gdr_bwd_args.tblk_bwd, they save the backward's
+                                   rebuild of them from A and g_cum */
     float *w_out;               /* [B,T,H_v,K] W = T diag(beta e^g_cum) K, NULL = not computed */
     float *u_out;               /* [B,T,H_v,V] U = T diag(beta) V, NULL = not computed */
     /* timing hook: NULL, or a HOST array of 2*GDR_FWD_STAGES events that are
@@ -249,7 +251,9 @@ int gdr_fwd_noalloc(const gdr_fwd_args *args, hipStream_t stream);
 
 /* Bytes of the T blocks of gdr_fwd_args.tblk_bwd for these sizes: one block
    per (chunk, v head) for an upper bound on the chunk count (B ceil(T/64), or
-   ceil(T/64) + n_seq with cu_seqlens), 17,408 bytes each for bf16 inputs.
+   ceil(T/64) + n_seq with cu_seqlens), 13,312 bytes each for bf16 inputs
+   (rows 0-31 of T stored at half width: the other half is zero) and 17,408
+   for fp32 inputs.
    Returns GDR_OK or a validation error. */
 int gdr_tblocks_bytes(const gdr_fwd_args *args, size_t *bytes);
 
