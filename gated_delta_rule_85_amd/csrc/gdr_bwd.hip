@@ -131,7 +131,8 @@ __device__ __forceinline__ void load_T(const BwdParams &p, int64_t ts, int n, in
 }
 
 // ------------------------------------------------------------------ T blocks
-// The scan's T blocks, rebuilt from the forward's A rows and g_cum.
+// The T blocks, rebuilt from the forward's A rows and g_cum: the compact form the
+// forward writes for bf16 inputs, full rows for the fp32 kernels.
 template <typename In>
 __global__ __launch_bounds__(NTHR) void tblock_kernel(const BwdParams p) {
     __shared__ float Tf[CH * LF];

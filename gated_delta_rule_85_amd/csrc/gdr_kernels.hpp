@@ -19,8 +19,8 @@ struct PrepParams {
     const float *g, *beta;
     float *g_cum;  // [tokens, H_v] or null
     float *Tm;     // [tokens, H_v, 64] or null
-    char *tblk;    // [chunks, H_v] T blocks (gdr_layout.hpp), in the scan's swizzled order
-    char *tblk_bwd;  // null, or the same blocks in the backward's (unswizzled) order
+    char *tblk;    // [chunks, H_v] T blocks (gdr_layout.hpp), the compact form the scan reads
+    char *tblk_bwd;  // fp32 inputs: null, or the same blocks with full rows for the backward
     SeqMap sm;
     int Hq, Hv;
 };
@@ -122,7 +122,7 @@ hipError_t launch_bwd(Dt dt, Dt gt, int K, const BwdParams &p, int n_chunks_ub, 
                       const hipEvent_t *ev, hipStream_t s);
 hipError_t launch_bwd_scan_bf16(int K, const BwdParams &p, int n_units, hipStream_t s);
 hipError_t launch_bwd_local_bf16(Dt gt, int K, const BwdParams &p, int n_chunks_ub, hipStream_t s);
-size_t tblock_bytes(Dt dt);      // the backward's T blocks (and the forward's tblk_bwd copy)
+size_t tblock_bytes(Dt dt);      // the backward's T blocks (bf16: the forward's compact ones)
 size_t tblock_bytes_fwd(Dt dt);  // the forward's T blocks, read by the scan
 // Body of gdr_fwd (gdr_api.hip): on the caller's workspace (scratch_for null), or
 // on a library-owned buffer of scratch_bytes bytes whose device address
