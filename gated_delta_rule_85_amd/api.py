@@ -25,7 +25,8 @@ class SavedForBackward(NamedTuple):
     """What the forward hands the backward (``return_h_bwd``): the chunk-start
     states in the backward's layout (uint8 [NT,H_v,4KV]: fp32 [K][V] for fp32
     inputs, bf16 hi then lo planes of h^T for bf16 inputs) and the T blocks
-    (uint8, one 17,408-byte block per chunk and v head for bf16 inputs)."""
+    (uint8, one 13,312-byte block per chunk and v head for bf16 inputs: the
+    forward's own, which it writes there; 17,408 bytes with full rows for fp32)."""
     states: torch.Tensor
     tblocks: torch.Tensor
 
