@@ -506,11 +506,369 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
     }
 }
 
+// ------------------------------------------------------------------ role split
+// The bf16 forward with eight waves, two per SIMD: waves 0-3 ("chain") own the
+// state columns [16w, 16w+16) of the block and form K h, Q h, X, U~, h' and the
+// output tiles, with no global memory traffic inside the chunk loop; waves 4-7
+// ("io") copy the next chunk into LDS, form the ten decayed score tiles, and
+// store each chunk's output, which the chain waves leave in an LDS plane, one
+// chunk later as whole 256-byte token rows.  Same work items, chunk order and
+// arithmetic as scan_output_kernel, so the results are bit-identical to it.
+template <typename In, typename Out, int KD> struct ScanRS {
+    using C = Cfg<In, KD, false>;
+    using O = Ops<In>;
+    using ST = typename O::S;
+    using TB = typename C::TB;
+    using SK = Swz<C::KROW, KeyKQ>;
+    using SV = Swz<C::VROW, KeyVP>;
+    using SP = Swz<C::PROW, KeyP>;
+    using SO = Swz<BV * 4>;  // fp32 output plane, 256-byte token rows
+    static constexpr int NIO = 4;  // io waves
+    static constexpr int NCP = 2;  // of which copy waves
+    static_assert(C::BF, "bf16 inputs only");
+};
+
+template <typename In, typename Out, int KD>
+__global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_output_roles_kernel(
+    const ScanParams p) {
+    using R = ScanRS<In, Out, KD>;
+    using C = typename R::C;
+    using O = typename R::O;
+    using ST = typename R::ST;
+    using TB = typename R::TB;
+    using SK = typename R::SK;
+    using SV = typename R::SV;
+    using SP = typename R::SP;
+    using SO = typename R::SO;
+    __shared__ __attribute__((aligned(16))) char buf0[C::BUF];
+    __shared__ __attribute__((aligned(16))) char buf1[C::BUF];
+    __shared__ __attribute__((aligned(16))) char pplane[C::PBYTES];
+    __shared__ __attribute__((aligned(16))) char oplane[CH * BV * 4];
+
+    int vt, unit, seg = 0;
+    if (p.sm.order && p.n_seg == 1) {
+        if (!lpt_item(p.sm, p.Hq, p.Hv, p.n_vt, vt, unit)) return;
+    } else {
+        const int wid = xcd_remap(blockIdx.x, gridDim.x);
+        vt = wid % p.n_vt;
+        const int rest = wid / p.n_vt;
+        unit = rest % p.n_units;
+        seg = rest / p.n_units;
+    }
+    const int j = unit / p.Hv, hv = unit % p.Hv, hq = hv / (p.Hv / p.Hq);
+    int64_t bos, eos;
+    p.sm.bounds(j, bos, eos);
+    const int N = (int)((eos - bos + CH - 1) / CH);
+    const int c_begin = seg * p.seg_chunks;
+    if (c_begin >= N && !(N == 0 && seg == 0)) return;
+    const int c_end = min(N, c_begin + p.seg_chunks);
+    const int cb = p.sm.chunk_base(j);
+    int w_begin = seg == 0 ? 0 : max(0, c_begin - p.warm_chunks);
+    if (seg > 0 && p.warm_gated)
+        w_begin = __builtin_amdgcn_readfirstlane(
+            gated_window_start<C::TB::BYTES>(p.tblk, cb, p.Hv, hv, c_begin, C::TB::SC));
+    const int wv = __builtin_amdgcn_readfirstlane(wave_id());
+    const int n16 = ln16(), g = lg4(), l = lane_id();
+    const int64_t KV = (int64_t)KD * p.V;
+    const bool emit_any = p.o != nullptr;
+
+    if (wv < 4) {
+        // ------------------------------------------------------------ chain waves
+        const int colw = vt * BV + wv * 16;
+        f32x4 h[C::DT];
+        {
+            const bool from_seg = seg > 0 && p.h0_seg != nullptr;
+            const bool from_h0 = !from_seg && (w_begin == 0) && p.h0 != nullptr;
+            const float *h0 = from_seg ? p.h0_seg + ((int64_t)unit * p.n_seg + seg) * KV
+                              : from_h0 ? p.h0 + (int64_t)unit * KV : nullptr;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = slot_base(dt, g) + i;
+                    h[dt][i] = p.eye_h0 ? (key == colw + n16 ? 1.f : 0.f) : h0 ? h0[key * p.V + colw + n16] : 0.f;
+                }
+        }
+        __syncthreads();  // first chunk landed
+        for (int c = w_begin; c < c_end; ++c) {
+            const char *b = ((c - w_begin) & 1) ? buf1 : buf0;
+            const bool emit = emit_any && c >= c_begin;
+            const char *Ks = b + C::OFF_K, *Qs = b + C::OFF_Q, *Vs = b + C::OFF_V, *Tb = b + C::OFF_T;
+            const float *sc = reinterpret_cast<const float *>(Tb + TB::SC);
+            const float *eg = sc + CH, *rr = sc + 2 * CH, *bet = sc + 3 * CH;
+            if (p.hsnap && c >= c_begin) {  // the segment's own chunks (not its warm-up window)
+                float *hs = p.hsnap + ((int64_t)(cb + c) * p.Hv + hv) * KV;
+                if (p.hsnap_split) {
+                    char *hb = reinterpret_cast<char *>(hs);
+                    const int plane = KD * p.V * 2;
+#pragma unroll
+                    for (int dp = 0; dp < C::DP; ++dp) {
+                        bf16x4 hi0, lo0, hi1, lo1;
+                        split4(h[2 * dp], hi0, lo0);
+                        split4(h[2 * dp + 1], hi1, lo1);
+                        const uint32_t off = (uint32_t)(((colw + n16) * KD + slot_base(2 * dp, g)) * 2);
+                        *reinterpret_cast<bf16x8 *>(hb + off) = cat(hi0, hi1);
+                        *reinterpret_cast<bf16x8 *>(hb + plane + off) = cat(lo0, lo1);
+                    }
+                } else {
+                    int rs = p.V;
+                    asm volatile("" : "+s"(rs));
+                    float *hl = hs + 8 * g * rs + colw + n16;
+#pragma unroll
+                    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            hl[(uint32_t)((32 * (dt >> 1) + 4 * (dt & 1) + i) * rs)] = h[dt][i];
+                }
+            }
+            f32x4 kh[4], qh[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) kh[rt] = qh[rt] = zero4();
+#pragma unroll
+            for (int dp = 0; dp < C::DP; ++dp) {
+                const ST hb = O::split(h[2 * dp], h[2 * dp + 1]);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    // (Q h also for warm-up chunks, whose output is dropped: one straight-line
+                    // block for the scheduler)
+                    kh[rt] = mma(kh[rt], frag8<In, SK>(Ks, slot_row(rt, n16), (32 * dp + 8 * g) * C::ES), hb);
+                    qh[rt] = mma(qh[rt], hb, frag8<In, SK>(Qs, 16 * rt + n16, (32 * dp + 8 * g) * C::ES));
+                }
+            }
+            ST xs0, xs1;
+            {
+                f32x4 x[4];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    const int tb = slot_base(rt, g);
+                    const f32x4 vv = rows4b<In, SV>(Vs, tb, wv * 16);
+                    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bet + tb);
+                    const f32x4 e4 = *reinterpret_cast<const f32x4 *>(eg + tb);
+                    x[rt] = b4 * (vv - e4 * kh[rt]);
+                }
+                xs0 = O::split(x[0], x[1]);
+                xs1 = O::split(x[2], x[3]);
+            }
+            f32x4 ut[4];
+            {
+                SplitPlane<In> tp;
+                tp.hi = reinterpret_cast<bf16 *>(const_cast<char *>(Tb));
+                tp.lo = reinterpret_cast<bf16 *>(const_cast<char *>(Tb) + TB::PLANE);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    ut[rt] = zero4();
+#pragma unroll
+                    for (int ip = 0; ip <= rt / 2; ++ip) {
+                        const int row = slot_row(rt, n16), byte = (32 * ip + 8 * g) * 2;
+                        ut[rt] = mma(ut[rt], tp.get8(TB::off(row, byte), 0), ip == 0 ? xs0 : xs1);
+                    }
+                }
+            }
+            {
+                f32x4 y[4];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) y[rt] = *reinterpret_cast<const f32x4 *>(rr + slot_base(rt, g)) * ut[rt];
+                const ST rus0 = O::split(y[0], y[1]);
+                const ST rus1 = O::split(y[2], y[3]);
+                const float ec = eg[CH - 1];
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) {
+                    h[dt] *= ec;
+                    const int c0 = 32 * (dt >> 1) + 4 * (dt & 1);
+                    h[dt] = mma(h[dt], kt8<In, SK>(Ks, 0, c0, 8), rus0);
+                    h[dt] = mma(h[dt], kt8<In, SK>(Ks, 32, c0, 8), rus1);
+                }
+            }
+            if (emit) {
+                const ST us0 = O::split(ut[0], ut[1]);
+                const ST us1 = O::split(ut[2], ut[3]);
+                f32x4 oq[4];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) oq[rt] = eg[16 * rt + n16] * qh[rt];
+                __syncthreads();  // score planes complete, output plane free
+                SplitPlane<In> pp;
+                pp.hi = reinterpret_cast<bf16 *>(pplane);
+                pp.lo = reinterpret_cast<bf16 *>(pplane + CH * C::PROW);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    f32x4 acc = oq[rt];
+#pragma unroll
+                    for (int ip = 0; ip <= rt / 2; ++ip) {
+                        const int row = 16 * rt + n16, byte = (32 * ip + 8 * g) * 2;
+                        acc = mma(acc, ip == 0 ? us0 : us1, pp.get8(SP::off(row, byte), 0));
+                    }
+                    *reinterpret_cast<f32x4 *>(oplane + SO::off(16 * rt + n16, (wv * 16 + 4 * g) * 4)) = p.scale * acc;
+                }
+            }
+            __syncthreads();  // chunk done with its buffer, the next one landed, output plane written
+        }
+        if (p.hT_seg) {
+            float *hs = p.hT_seg + ((int64_t)unit * p.n_seg + seg) * KV;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hs[(slot_base(dt, g) + i) * p.V + colw + n16] = h[dt][i];
+        }
+        if (c_end == N && p.hT) {
+            float *hT = p.hT + (int64_t)unit * KV;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hT[(slot_base(dt, g) + i) * p.V + colw + n16] = h[dt][i];
+        }
+    } else {
+        // --------------------------------------------------------------- io waves
+        // waves 4-5 copy the next chunk and store the output, waves 6-7 form the
+        // decayed score tiles (five each)
+        const int iw = wv - 4;
+        const In *qp = reinterpret_cast<const In *>(p.q), *kp = reinterpret_cast<const In *>(p.k);
+        const In *vp = reinterpret_cast<const In *>(p.v);
+        // score-plane tiles above the diagonal pairs, (0,1) and (2,3), are read as zero and never written
+        for (int idx = threadIdx.x - 4 * 64; idx < 2 * 16 * 16; idx += R::NIO * 64) {
+            const int t = idx >> 8, r = 32 * t + ((idx >> 4) & 15), i = 32 * t + 16 + (idx & 15);
+            const int off = SP::off(r, i * 2);
+            *reinterpret_cast<bf16 *>(pplane + off) = bf16(0.f);
+            *reinterpret_cast<bf16 *>(pplane + CH * C::PROW + off) = bf16(0.f);
+        }
+        if (iw < R::NCP) {
+            // copy pieces of this wave (fixed for the whole scan)
+            constexpr int NK = C::NKI / R::NCP, NV = C::NVI / R::NCP;
+            static_assert(C::NKI % R::NCP == 0 && C::NVI % R::NCP == 0, "copies spread over the copy waves");
+            int krow[NK], kchk[NK], vrow[NV], vchk[NV];
+#pragma unroll
+            for (int s = 0; s < NK; ++s) {
+                const int byte = (iw + R::NCP * s) * 1024 + 16 * l, r = byte / C::KROW;
+                krow[s] = r;
+                kchk[s] = 16 * SK::chunk(r, (byte % C::KROW) / 16);
+            }
+#pragma unroll
+            for (int s = 0; s < NV; ++s) {
+                const int byte = (iw + R::NCP * s) * 1024 + 16 * l, r = byte / C::VROW;
+                vrow[s] = r;
+                vchk[s] = 16 * SV::chunk(r, (byte % C::VROW) / 16);
+            }
+            auto issue = [&](int c, char *b) {
+                const int64_t ts = bos + (int64_t)c * CH;
+                const int nm1 = (int)min<int64_t>(CH, eos - ts) - 1;
+                const int krs = p.Hq * KD * C::ES, vrs = (int)(p.v_tok * C::ES);
+                const char *kb = reinterpret_cast<const char *>(kp + (ts * p.Hq + hq) * KD);
+                const char *qb = reinterpret_cast<const char *>(qp + (ts * p.Hq + hq) * KD);
+                const char *vb = reinterpret_cast<const char *>(vp + ts * p.v_tok + hv * p.v_head + vt * BV);
+#pragma unroll
+                for (int s = 0; s < NK; ++s) {
+                    const uint32_t off = (uint32_t)(min(krow[s], nm1) * krs + kchk[s]);
+                    const int i = iw + R::NCP * s;
+                    dma16(kb + off, b + C::OFF_K + i * 1024);
+                    dma16(qb + off, b + C::OFF_Q + i * 1024);
+                }
+#pragma unroll
+                for (int s = 0; s < NV; ++s) {
+                    const uint32_t off = (uint32_t)(min(vrow[s], nm1) * vrs + vchk[s]);
+                    dma16(vb + off, b + C::OFF_V + (iw + R::NCP * s) * 1024);
+                }
+                const char *blk = p.tblk + ((int64_t)(cb + c) * p.Hv + hv) * TB::BYTES;
+                for (int i = iw; i < C::NTI; i += R::NCP) dma16(blk + i * 1024 + 16 * l, b + C::OFF_T + i * 1024);
+            };
+            // output of chunk c from the output plane: this wave's 32 token rows, 4
+            // rows per instruction
+            auto store_out = [&](int c) {
+                const int64_t ts = bos + (int64_t)c * CH;
+                const int n = (int)min<int64_t>(CH, eos - ts);
+                Out *ob = reinterpret_cast<Out *>(p.o) + (ts * p.Hv + hv) * p.V + vt * BV + 4 * n16;
+                const int rstride = p.Hv * p.V;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int tok = 32 * iw + 4 * k + g;
+                    const f32x4 x = *reinterpret_cast<const f32x4 *>(oplane + SO::off(tok, 16 * n16));
+                    if (tok < n) OutVec<Out>::put(ob + (uint32_t)(tok * rstride), x);
+                }
+            };
+            if (w_begin < c_end) issue(w_begin, buf0);
+            wait_dma();
+            __syncthreads();  // first chunk landed
+            int pend = -1;
+            for (int c = w_begin; c < c_end; ++c) {
+                char *nb = ((c - w_begin) & 1) ? buf0 : buf1;
+                const bool emit = emit_any && c >= c_begin;
+                if (c + 1 < c_end) issue(c + 1, nb);
+                if (pend >= 0) store_out(pend);
+                pend = -1;
+                if (emit) {
+                    __syncthreads();  // score planes complete, output plane free
+                    pend = c;
+                }
+                wait_dma();
+                __syncthreads();  // chunk done with its buffer, the next one landed, output plane written
+            }
+            if (pend >= 0) store_out(pend);
+        } else {
+            // tiles t = PAR, PAR + 2, ... of the ten on or below the diagonal (t -> (tr, ti)
+            // row-major), every operand read issued before the first product
+            auto tiles = [&](auto par_tag, const char *b) {
+                constexpr int PAR = decltype(par_tag)::value;
+                const char *Ks = b + C::OFF_K, *Qs = b + C::OFF_Q;
+                const float *gam = reinterpret_cast<const float *>(b + C::OFF_T + TB::SC);
+                typename O::X kf[5][C::DP], qf[5][C::DP];
+#pragma unroll
+                for (int k = 0; k < 5; ++k) {
+                    const int t = PAR + 2 * k;
+                    const int tr = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+                    const int ti = t - tr * (tr + 1) / 2;
+#pragma unroll
+                    for (int dp = 0; dp < C::DP; ++dp) {
+                        kf[k][dp] = frag8<In, SK>(Ks, 16 * ti + n16, (32 * dp + 8 * g) * 2);
+                        qf[k][dp] = frag8<In, SK>(Qs, 16 * tr + n16, (32 * dp + 8 * g) * 2);
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < 5; ++k) {
+                    const int t = PAR + 2 * k;
+                    const int tr = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+                    const int ti = t - tr * (tr + 1) / 2;
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int dp = 0; dp < C::DP; ++dp) acc = mma(acc, kf[k][dp], qf[k][dp]);
+                    // acc[jj] = P[r][i], r = 16 tr + n16, i = 16 ti + 4g + jj
+                    const int r = 16 * tr + n16;
+                    const float gr = gam[r];
+                    const f32x4 gi = *reinterpret_cast<const f32x4 *>(gam + 16 * ti + 4 * g);
+                    f32x4 v;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const float e = acc[jj] * fast_exp(gr - gi[jj]);
+                        v[jj] = (ti < tr || 4 * g + jj <= n16) ? e : 0.f;
+                    }
+                    const int off = SP::off(r, (16 * ti + 4 * g) * 2);
+                    bf16x4 hi, lo;
+                    split4(v, hi, lo);
+                    *reinterpret_cast<bf16x4 *>(pplane + off) = hi;
+                    *reinterpret_cast<bf16x4 *>(pplane + CH * C::PROW + off) = lo;
+                }
+            };
+            __syncthreads();  // first chunk landed
+            for (int c = w_begin; c < c_end; ++c) {
+                const char *b = ((c - w_begin) & 1) ? buf1 : buf0;
+                if (emit_any && c >= c_begin) {
+                    if (iw == R::NCP)
+                        tiles(std::integral_constant<int, 0>{}, b);
+                    else
+                        tiles(std::integral_constant<int, 1>{}, b);
+                    __syncthreads();  // score planes complete, output plane free
+                }
+                __syncthreads();  // chunk done with its buffer, the next one landed, output plane written
+            }
+        }
+    }
+}
+
 template <typename In, typename Out, int KD, bool STATES>
 hipError_t launch_scan_t(const ScanParams &p, hipStream_t s) {
     const int nb = p.sm.order && p.n_seg == 1 ? lpt_blocks(p.sm.n_seq, p.Hq, p.Hv, p.n_vt)
                                               : p.n_vt * p.n_units * p.n_seg;
-    hipLaunchKernelGGL((scan_output_kernel<In, Out, KD, STATES>), dim3(nb), dim3(NTHR), 0, s, p);
+    if constexpr (sizeof(In) == 2 && !STATES)
+        hipLaunchKernelGGL((scan_output_roles_kernel<In, Out, KD>), dim3(nb), dim3(2 * NTHR), 0, s, p);
+    else
+        hipLaunchKernelGGL((scan_output_kernel<In, Out, KD, STATES>), dim3(nb), dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
 
