@@ -624,17 +624,22 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))
             f32x4 kh[4], qh[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) kh[rt] = qh[rt] = zero4();
+            // K h first, on the chain; Q h (also for warm-up chunks, whose output is
+            // dropped: one straight-line block for the scheduler) queues behind it on
+            // the matrix unit while X is formed
+            ST hb[C::DP];
 #pragma unroll
             for (int dp = 0; dp < C::DP; ++dp) {
-                const ST hb = O::split(h[2 * dp], h[2 * dp + 1]);
+                hb[dp] = O::split(h[2 * dp], h[2 * dp + 1]);
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    // (Q h also for warm-up chunks, whose output is dropped: one straight-line
-                    // block for the scheduler)
-                    kh[rt] = mma(kh[rt], frag8<In, SK>(Ks, slot_row(rt, n16), (32 * dp + 8 * g) * C::ES), hb);
-                    qh[rt] = mma(qh[rt], hb, frag8<In, SK>(Qs, 16 * rt + n16, (32 * dp + 8 * g) * C::ES));
-                }
+                for (int rt = 0; rt < 4; ++rt)
+                    kh[rt] = mma(kh[rt], frag8<In, SK>(Ks, slot_row(rt, n16), (32 * dp + 8 * g) * C::ES), hb[dp]);
             }
+#pragma unroll
+            for (int dp = 0; dp < C::DP; ++dp)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    qh[rt] = mma(qh[rt], hb[dp], frag8<In, SK>(Qs, 16 * rt + n16, (32 * dp + 8 * g) * C::ES));
             ST xs0, xs1;
             {
                 f32x4 x[4];
