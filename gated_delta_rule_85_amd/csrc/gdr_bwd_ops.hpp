@@ -112,6 +112,18 @@ __device__ __forceinline__ void zero_lower_pt(char *Pt) {
     }
 }
 
+// the same, by the threads of an eight-wave workgroup
+__device__ __forceinline__ void zero_lower_pt2(char *Pt) {
+    constexpr int PROW = 128, PPLANE = CH * PROW;
+    using SP = Swz<PROW>;
+    for (int idx = threadIdx.x; idx < 2 * 16 * 16; idx += 2 * NTHR) {
+        const int t = idx >> 8, r = 16 + 32 * t + ((idx >> 4) & 15), i = 32 * t + (idx & 15);
+        const int off = SP::off(r, 2 * i);
+        *reinterpret_cast<bf16 *>(Pt + off) = bf16(0.f);
+        *reinterpret_cast<bf16 *>(Pt + PPLANE + off) = bf16(0.f);
+    }
+}
+
 // sum over the 4 lane groups
 __device__ __forceinline__ float sum_groups(float v) {
     v += __shfl_xor(v, 16, 64);

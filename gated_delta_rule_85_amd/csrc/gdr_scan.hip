@@ -690,7 +690,7 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))
                 f32x4 oq[4];
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) oq[rt] = eg[16 * rt + n16] * qh[rt];
-                __syncthreads();  // score planes complete, output plane free
+                lds_barrier();  // score planes complete, output plane free
                 SplitPlane<In> pp;
                 pp.hi = reinterpret_cast<bf16 *>(pplane);
                 pp.lo = reinterpret_cast<bf16 *>(pplane + CH * C::PROW);
@@ -705,7 +705,7 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))
                     *reinterpret_cast<f32x4 *>(oplane + SO::off(16 * rt + n16, (wv * 16 + 4 * g) * 4)) = p.scale * acc;
                 }
             }
-            __syncthreads();  // chunk done with its buffer, the next one landed, output plane written
+            lds_barrier();  // chunk done with its buffer, the next one landed, output plane written
         }
         if (p.hT_seg) {
             float *hs = p.hT_seg + ((int64_t)unit * p.n_seg + seg) * KV;
@@ -799,11 +799,11 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))
                 if (pend >= 0) store_out(pend);
                 pend = -1;
                 if (emit) {
-                    __syncthreads();  // score planes complete, output plane free
+                    lds_barrier();  // score planes complete, output plane free
                     pend = c;
                 }
                 wait_dma();
-                __syncthreads();  // chunk done with its buffer, the next one landed, output plane written
+                lds_barrier();  // chunk done with its buffer, the next one landed, output plane written
             }
             if (pend >= 0) store_out(pend);
         } else {
@@ -858,9 +858,9 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))
                         tiles(std::integral_constant<int, 0>{}, b);
                     else
                         tiles(std::integral_constant<int, 1>{}, b);
-                    __syncthreads();  // score planes complete, output plane free
+                    lds_barrier();  // score planes complete, output plane free
                 }
-                __syncthreads();  // chunk done with its buffer, the next one landed, output plane written
+                lds_barrier();  // chunk done with its buffer, the next one landed, output plane written
             }
         }
     }
