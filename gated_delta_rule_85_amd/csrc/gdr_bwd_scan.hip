@@ -1,9 +1,9 @@
 // Reverse state scan of the backward for bf16 inputs on bf16 MFMA.
 //
 // Part of the backward described in gdr_bwd_mfma.hip (the same split-bf16
-// arithmetic); it sits in a file of its own because it is compiled with the
-// ILP-seeking scheduler (one wave per SIMD: operand reads must be issued well
-// ahead of their MFMAs).
+// arithmetic); it sits in a file of its own because it is compiled with a
+// scheduler of its own (the default one; the chain waves' operand reads are
+// pipelined by hand, a stage ahead of their products).
 #include <type_traits>
 
 #include "gdr_bwd_ops.hpp"
@@ -15,11 +15,11 @@ namespace {
 using namespace bwd;
 
 // ------------------------------------------------------------- reverse scan
-// One workgroup per (sequence, v head, 64 value columns); wave w owns
+// One workgroup per (sequence, v head, 64 value columns); chain wave w owns
 // columns 16 w .. 16 w + 15 and keeps its K x 16 slice of dh in registers
 // (dh[dt] = keys slot_base(dt, g) + i, column 16 w + lane16).
 // Per chunk, from the end: the transposed decayed scores P^T (upper
-// triangular, shared split planes), then per wave
+// triangular, shared split planes), then per chain wave
 //   dU~ = diag(r) K dh' + s P^T dO,  dX = T^T dU~,
 //   dh  = e_last dh' + Q^T diag(s e) dO - K^T diag(beta e) dX.
 // A operand of M^T for a K x V tile in the contiguous-slot key order: row n is
@@ -36,186 +36,12 @@ __device__ __forceinline__ OpX kt_keys(const char *M, int c0, int ip) {
     return r;
 }
 
-template <int KD>
-__global__ __launch_bounds__(NTHR) void bwd_scan_bf16(const BwdParams p, int n_units) {
-    constexpr int KROW = KD * 2, DROW = 64 * 2, PROW = 64 * 2, PPLANE = CH * PROW;
-    constexpr int DT = KD / 16, DP = KD / 32;
-    using TB = TBlockF<bf16>;  // compact T blocks: rows 0-31 stored in their first 32 columns
-    // two sets of chunk tiles: the next chunk (in reverse order) is copied into one
-    // while the current one is read (separate arrays, so the compiler can tell the
-    // copies into one set from the reads of the other)
-    __shared__ __attribute__((aligned(16))) char Ks0[CH * KROW], Ks1[CH * KROW];
-    __shared__ __attribute__((aligned(16))) char Qs0[CH * KROW], Qs1[CH * KROW];
-    __shared__ __attribute__((aligned(16))) char Ds0[CH * DROW], Ds1[CH * DROW];
-    __shared__ __attribute__((aligned(16))) char Tb0[TB::BYTES], Tb1[TB::BYTES];
-    __shared__ __attribute__((aligned(16))) char Pt[2 * PPLANE];
-
-    const int nvt = p.V / 64;
-    int vt, unit, seg = 0;
-    if (p.sm.order && p.n_seg == 1) {  // packed sequences: longest first
-        if (!lpt_item(p.sm, p.Hq, p.Hv, nvt, vt, unit)) return;
-    } else {
-        const int wid = xcd_remap(blockIdx.x, gridDim.x);
-        vt = wid % nvt;
-        unit = (wid / nvt) % n_units;
-        seg = wid / nvt / n_units;
-        if (seg >= p.n_seg) return;
-    }
-    const int j = unit / p.Hv, hv = unit % p.Hv, hq = hv / (p.Hv / p.Hq);
-    const int w = __builtin_amdgcn_readfirstlane(wave_id()), n16 = ln16(), g = lg4();
-    const int col = vt * 64 + 16 * w + n16;
-    int64_t bos, eos;
-    p.sm.bounds(j, bos, eos);
-    const int N = (int)((eos - bos + CH - 1) / CH);
-    // this workgroup's segment of chunks (the whole sequence without a split)
-    const int c_begin = seg * p.seg_chunks;
-    if (c_begin >= N && !(N == 0 && seg == 0)) return;
-    const int c_end = min(N, c_begin + p.seg_chunks);
-    const float *dh_start = c_end == N ? (p.dht ? p.dht + unit * ((int64_t)KD * p.V) : nullptr)
-                            : p.d_seg ? nullptr
-                                      : p.dh_seg + ((int64_t)unit * p.n_seg + seg) * ((int64_t)KD * p.V);
-    const int cb = p.sm.chunk_base(j);
-    const int64_t KV = (int64_t)KD * p.V;
-    const char *kp = reinterpret_cast<const char *>(p.k), *qp = reinterpret_cast<const char *>(p.q);
-    const char *dop = reinterpret_cast<const char *>(p.dout);
-
-    // dh[dt][i] = key slot_base(dt, g) + i (the contiguous-slot order of gdr_lds.hpp), column col
-    f32x4 dh[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            dh[dt][i] = dh_start ? dh_start[(slot_base(dt, g) + i) * p.V + col] : 0.f;
-    zero_lower_pt(Pt);
-
-    // copy chunk c into one set of tiles
-    auto issue = [&](int c, char *K_, char *Q_, char *D_, char *T_) {
-        const int64_t ts = bos + (int64_t)c * CH;
-        const int n = (int)min<int64_t>(CH, eos - ts);
-        copy_tile<KROW>(K_, kp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
-        copy_tile<KROW>(Q_, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
-        copy_tile<DROW>(D_, dop + ((ts * p.Hv + hv) * p.V + vt * 64) * 2, p.Hv * p.V * 2, n - 1, w);
-        copy_flat(T_, p.tblk + ((int64_t)(cb + c) * p.Hv + hv) * TB::BYTES, TB::BYTES, w);
-    };
-    // chunk c from tile set CUR (landed, every wave past the barrier after it); chunk
-    // c - 1 is copied into the other set meanwhile
-    auto body = [&](auto cur, int c) {
-        constexpr bool ONE = decltype(cur)::value == 1;
-        const char *Ks = ONE ? Ks1 : Ks0, *Qs = ONE ? Qs1 : Qs0, *Ds = ONE ? Ds1 : Ds0, *Tb = ONE ? Tb1 : Tb0;
-        const float *sc = reinterpret_cast<const float *>(Tb + TB::SC);
-        const float *eg = sc + CH, *rr = sc + 2 * CH, *bet = sc + 3 * CH;
-        const int64_t ts = bos + (int64_t)c * CH;
-        const int n = (int)min<int64_t>(CH, eos - ts);
-        if (c - 1 >= c_begin) {
-            if constexpr (ONE)
-                issue(c - 1, Ks0, Qs0, Ds0, Tb0);
-            else
-                issue(c - 1, Ks1, Qs1, Ds1, Tb1);
-        }
-        if (!p.d_seg) {  // gradient of this chunk's end state, for the chunk-local stage: hi, lo planes of dh'^T
-            char *o = reinterpret_cast<char *>(p.dhs + ((int64_t)(cb + c) * p.Hv + hv) * KV);
-            const int plane = KD * p.V * 2;
-#pragma unroll
-            for (int dp = 0; dp < DP; ++dp) {  // tiles 2dp, 2dp + 1: keys 32dp + 8g .. + 7
-                bf16x4 hi0, lo0, hi1, lo1;
-                split4(dh[2 * dp], hi0, lo0);
-                split4(dh[2 * dp + 1], hi1, lo1);
-                const uint32_t off = (uint32_t)((col * KD + slot_base(2 * dp, g)) * 2);
-                *reinterpret_cast<bf16x8 *>(o + off) = cat(hi0, hi1);
-                *reinterpret_cast<bf16x8 *>(o + plane + off) = cat(lo0, lo1);
-            }
-        }
-        scores_t<KD>(Pt, Qs, Ks, sc, n, w);
-        __syncthreads();
-        // dU~ = diag(r) K dh' + s P^T dO  (rows = tokens, this wave's columns)
-        f32x4 du[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) du[rt] = zero4();
-#pragma unroll
-        for (int dp = 0; dp < DP; ++dp) {
-            const OpS hb = Ops<bf16>::split(dh[2 * dp], dh[2 * dp + 1]);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-                du[rt] = mma(du[rt], frag8<bf16, Swz<KROW>>(Ks, 16 * rt + n16, (32 * dp + 8 * g) * 2), hb);
-        }
-        const OpX dob0 = kt_operand<bf16, DROW>(Ds, 16 * w, 0), dob1 = kt_operand<bf16, DROW>(Ds, 16 * w, 1);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            f32x4 pd = zero4();
-#pragma unroll
-            for (int ip = rt / 2; ip < 2; ++ip)
-                pd = mma(pd, frag_s<PROW>(Pt, PPLANE, 16 * rt + n16, (32 * ip + 4 * g) * 2), ip == 0 ? dob0 : dob1);
-            const f32x4 r4 = *reinterpret_cast<const f32x4 *>(rr + 16 * rt + 4 * g);
-            du[rt] = r4 * du[rt] + p.scale * pd;
-        }
-        // dX = T^T dU~ (T^T upper triangular)
-        const OpS dus0 = Ops<bf16>::split(du[0], du[1]), dus1 = Ops<bf16>::split(du[2], du[3]);
-        f32x4 dx[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            dx[rt] = zero4();
-#pragma unroll
-            for (int ip = rt / 2; ip < 2; ++ip)
-                dx[rt] = mma(dx[rt], kt_s_in<TB>(Tb, TB::PLANE, 16 * rt, ip), ip == 0 ? dus0 : dus1);
-        }
-        // dh = e_last dh' + Q^T diag(s e) dO - K^T diag(beta e) dX
-        OpS edo[2], bdx[2];
-        {
-            f32x4 y[4], z[4];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const int r0 = 16 * rt + 4 * g;
-                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(eg + r0);
-                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bet + r0);
-                const f32x4 d4 = rows4<bf16, DROW>(Ds, 16 * rt, 16 * w);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) y[rt][i] = r0 + i < n ? p.scale * e4[i] * d4[i] : 0.f;
-                z[rt] = -(b4 * e4) * dx[rt];
-            }
-            edo[0] = Ops<bf16>::split(y[0], y[1]);
-            edo[1] = Ops<bf16>::split(y[2], y[3]);
-            bdx[0] = Ops<bf16>::split(z[0], z[1]);
-            bdx[1] = Ops<bf16>::split(z[2], z[3]);
-        }
-        const float el = eg[CH - 1];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            dh[dt] *= el;
-            const int c0 = 32 * (dt >> 1) + 4 * (dt & 1);  // rows of tile dt: keys c0 + 8m + i
-#pragma unroll
-            for (int ip = 0; ip < 2; ++ip) {
-                dh[dt] = mma(dh[dt], kt_keys<KROW>(Qs, c0, ip), edo[ip]);
-                dh[dt] = mma(dh[dt], kt_keys<KROW>(Ks, c0, ip), bdx[ip]);
-            }
-        }
-        wait_dma();
-        __syncthreads();  // chunk c done with its tiles and the score planes; c - 1 landed
-    };
-    if (c_end > c_begin) issue(c_end - 1, Ks0, Qs0, Ds0, Tb0);
-    wait_dma();
-    __syncthreads();
-    for (int c = c_end - 1; c >= c_begin; c -= 2) {
-        body(std::integral_constant<int, 0>{}, c);
-        if (c - 1 >= c_begin) body(std::integral_constant<int, 1>{}, c - 1);
-    }
-    float *dh_out = p.d_seg ? p.d_seg + ((int64_t)unit * p.n_seg + seg) * KV
-                    : c_begin == 0 && p.dh0 ? p.dh0 + unit * KV : nullptr;
-    if (dh_out) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dh_out[(slot_base(dt, g) + i) * p.V + col] = dh[dt][i];
-    }
-}
-
-
-// ----------------------------------------------------- reverse scan, role split
-// The same reverse scan with eight waves, two per SIMD, in three roles: waves
-// 0-3 keep dh (columns 16 w ..) and form each chunk's products, plus one of the
-// ten score tiles each; waves 4-5 copy the next chunk (in reverse order) into
-// LDS; waves 6-7 form the other six score tiles.  Per chunk two barriers: after
-// the score tiles (P^T dO needs all of them) and at the end.  Same arithmetic,
-// in the same order, as bwd_scan_bf16.
+// Eight waves, two per SIMD, in three roles: waves 0-3 ("chain") keep dh and
+// form each chunk's products, plus one of the ten score tiles each; waves 4-5
+// copy the next chunk (in reverse order) into LDS; waves 6-7 form the other six
+// score tiles.  Per chunk two barriers, both ordering LDS only: after the score
+// tiles (P^T dO needs all of them) and at the end (the copy waves wait for
+// their copies first).
 template <int KD>
 __device__ __forceinline__ void score_tile_t(int t, char *Pt, const char *Qs, const char *Ks, const float *gam,
                                              int n) {
