@@ -247,27 +247,43 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int iw = wv - 4;
         const char *kp = reinterpret_cast<const char *>(p.k), *qp = reinterpret_cast<const char *>(p.q);
         const char *dop = reinterpret_cast<const char *>(p.dout);
-        auto issue = [&](int c, char *K_, char *Q_, char *D_, char *T_) {
+        // the K and Q tiles of a chunk (part 0) and its dO tile and T block (part 1)
+        auto issue = [&](int part, int c, char *K_, char *Q_, char *D_, char *T_) {
             const int64_t ts = bos + (int64_t)c * CH;
             const int n = (int)min<int64_t>(CH, eos - ts);
-            copy_rows<KROW>(K_, kp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, iw, NCP);
-            copy_rows<KROW>(Q_, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, iw, NCP);
-            copy_rows<DROW>(D_, dop + ((ts * p.Hv + hv) * p.V + vt * 64) * 2, p.Hv * p.V * 2, n - 1, iw, NCP);
-            copy_bytes(T_, p.tblk + ((int64_t)(cb + c) * p.Hv + hv) * TB::BYTES, TB::BYTES, iw, NCP);
+            if (part == 0) {
+                copy_rows<KROW>(K_, kp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, iw, NCP);
+                copy_rows<KROW>(Q_, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, iw, NCP);
+            } else {
+                copy_rows<DROW>(D_, dop + ((ts * p.Hv + hv) * p.V + vt * 64) * 2, p.Hv * p.V * 2, n - 1, iw, NCP);
+                copy_bytes(T_, p.tblk + ((int64_t)(cb + c) * p.Hv + hv) * TB::BYTES, TB::BYTES, iw, NCP);
+            }
         };
+        // the next chunk's copies are issued half before the mid-chunk barrier and half
+        // after it, so that these waves reach it as early as the others
         auto body = [&](auto cur, int c) {
             constexpr bool ONE = decltype(cur)::value == 1;
-            if (c - 1 >= c_begin) {
+            const bool more = c - 1 >= c_begin;
+            if (more) {
                 if constexpr (ONE)
-                    issue(c - 1, Ks0, Qs0, Ds0, Tb0);
+                    issue(0, c - 1, Ks0, Qs0, Ds0, Tb0);
                 else
-                    issue(c - 1, Ks1, Qs1, Ds1, Tb1);
+                    issue(0, c - 1, Ks1, Qs1, Ds1, Tb1);
             }
             lds_barrier();  // score planes complete
+            if (more) {
+                if constexpr (ONE)
+                    issue(1, c - 1, Ks0, Qs0, Ds0, Tb0);
+                else
+                    issue(1, c - 1, Ks1, Qs1, Ds1, Tb1);
+            }
             wait_dma();
             lds_barrier();  // chunk c done with its tiles and the score planes; c - 1 landed
         };
-        if (c_end > c_begin) issue(c_end - 1, Ks0, Qs0, Ds0, Tb0);
+        if (c_end > c_begin) {
+            issue(0, c_end - 1, Ks0, Qs0, Ds0, Tb0);
+            issue(1, c_end - 1, Ks0, Qs0, Ds0, Tb0);
+        }
         wait_dma();
         __syncthreads();  // first chunk landed
         for (int c = c_end - 1; c >= c_begin; c -= 2) {
