@@ -125,19 +125,6 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))
             const float *eg = sc + CH, *rr = sc + 2 * CH, *bet = sc + 3 * CH;
             const int64_t ts = bos + (int64_t)c * CH;
             const int n = (int)min<int64_t>(CH, eos - ts);
-            if (!p.d_seg) {  // gradient of this chunk's end state, for the chunk-local stage: hi, lo planes of dh'^T
-                char *o = reinterpret_cast<char *>(p.dhs + ((int64_t)(cb + c) * p.Hv + hv) * KV);
-                const int plane = KD * p.V * 2;
-#pragma unroll
-                for (int dp = 0; dp < DP; ++dp) {
-                    bf16x4 hi0, lo0, hi1, lo1;
-                    split4(dh[2 * dp], hi0, lo0);
-                    split4(dh[2 * dp + 1], hi1, lo1);
-                    const uint32_t off = (uint32_t)((col * KD + slot_base(2 * dp, g)) * 2);
-                    *reinterpret_cast<bf16x8 *>(o + off) = cat(hi0, hi1);
-                    *reinterpret_cast<bf16x8 *>(o + plane + off) = cat(lo0, lo1);
-                }
-            }
             score_tile_t<KD>(w, Pt, Qs, Ks, sc, n);
             // dU~ = diag(r) K dh' + s P^T dO  (rows = tokens, this wave's columns)
             f32x4 du[4];
@@ -164,6 +151,21 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
             const OpX dob0 = kt_operand<bf16, DROW>(Ds, 16 * w, 0), dob1 = kt_operand<bf16, DROW>(Ds, 16 * w, 1);
             lds_barrier();  // score planes complete
+            // gradient of this chunk's end state, for the chunk-local stage: hi, lo planes
+            // of dh'^T (stored after the barrier: before it the copy waves use the memory path)
+            if (!p.d_seg) {
+                char *o = reinterpret_cast<char *>(p.dhs + ((int64_t)(cb + c) * p.Hv + hv) * KV);
+                const int plane = KD * p.V * 2;
+#pragma unroll
+                for (int dp = 0; dp < DP; ++dp) {
+                    bf16x4 hi0, lo0, hi1, lo1;
+                    split4(dh[2 * dp], hi0, lo0);
+                    split4(dh[2 * dp + 1], hi1, lo1);
+                    const uint32_t off = (uint32_t)((col * KD + slot_base(2 * dp, g)) * 2);
+                    *reinterpret_cast<bf16x8 *>(o + off) = cat(hi0, hi1);
+                    *reinterpret_cast<bf16x8 *>(o + plane + off) = cat(lo0, lo1);
+                }
+            }
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 f32x4 pd = zero4();
@@ -247,19 +249,19 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int iw = wv - 4;
         const char *kp = reinterpret_cast<const char *>(p.k), *qp = reinterpret_cast<const char *>(p.q);
         const char *dop = reinterpret_cast<const char *>(p.dout);
-        // the K and Q tiles of a chunk (part 0) and its dO tile and T block (part 1)
+        // the K tile of a chunk (part 0), then its Q and dO tiles and T block (part 1)
         auto issue = [&](int part, int c, char *K_, char *Q_, char *D_, char *T_) {
             const int64_t ts = bos + (int64_t)c * CH;
             const int n = (int)min<int64_t>(CH, eos - ts);
             if (part == 0) {
                 copy_rows<KROW>(K_, kp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, iw, NCP);
-                copy_rows<KROW>(Q_, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, iw, NCP);
             } else {
+                copy_rows<KROW>(Q_, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, iw, NCP);
                 copy_rows<DROW>(D_, dop + ((ts * p.Hv + hv) * p.V + vt * 64) * 2, p.Hv * p.V * 2, n - 1, iw, NCP);
                 copy_bytes(T_, p.tblk + ((int64_t)(cb + c) * p.Hv + hv) * TB::BYTES, TB::BYTES, iw, NCP);
             }
         };
-        // the next chunk's copies are issued half before the mid-chunk barrier and half
+        // the next chunk's K tile is issued before the mid-chunk barrier and the rest
         // after it, so that these waves reach it as early as the others
         auto body = [&](auto cur, int c) {
             constexpr bool ONE = decltype(cur)::value == 1;
