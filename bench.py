@@ -5,9 +5,10 @@ One step is one gdr_fwd call (gdr_chunk_prep + the fused scan/output kernel)
 over the full-width prefill shard: B=4, T=4096, H_q=16, H_v=32, K=V=128,
 bf16 q/k/v, fp32 g/beta/initial and final state, fp32 o (inference forward:
 the A and g_cum tensors a backward would need are not written).  Inputs are seeded
-synthetic tensors already resident in HBM; W untimed warm-up steps, a
-breakdown pass (up to 20 steps recording HIP events around every kernel:
-kernel_ms, breakdown_step_ms and the dominant kernel), then K timed steps between
+synthetic tensors already resident in HBM; W untimed warm-up steps,
+breakdown passes (up to 20 steps per stage recording only that stage's two HIP
+events: kernel_ms and the dominant kernel; one more pass recording every event:
+breakdown_step_ms), then K timed steps between
 stream synchronisations, in which only the dominant kernel's two events are
 recorded (on the library's stream; each event record costs the stream a few
 microseconds).  That kernel's average duration over the timed steps gives the
@@ -443,9 +444,21 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # stage breakdown (every stage's events; not part of the timed region): per-stage
-    # averages, the median step and the dominant kernel
+    # stage breakdown (not part of the timed region).  Each stage is timed in a pass
+    # of its own that records only that stage's two events: a recorded event costs the
+    # stream a few microseconds, so events around every stage would inflate each
+    # stage's time.  One more pass records every event, for the median step.
     nbk = min(steps, 20)
+    stage_ms = {}
+    for key, names, n_ev in (("f", STAGES, _lib.FWD_STAGES),) + ((("b", BWD_STAGES, _lib.BWD_STAGES),) if train else ()):
+        for s_i, name in enumerate(names):
+            ev = Events(nbk, 2 * n_ev, keep={2 * s_i, 2 * s_i + 1})
+            evs["f"], evs["b"] = (ev, None) if key == "f" else (None, ev)
+            for i in range(nbk):
+                step(i)
+            torch.cuda.synchronize()
+            stage_ms[name] = ev.stage_ms(names, only=name)[name]
+            ev.close()
     evs["f"] = Events(nbk, 2 * _lib.FWD_STAGES)
     evs["b"] = Events(nbk, 2 * _lib.BWD_STAGES) if train else None
     for i in range(nbk):
@@ -460,10 +473,8 @@ def main():
             raise RuntimeError("hipEventElapsedTime failed")
         per_step.append(f.value)
     median_ms = sorted(per_step)[len(per_step) // 2]
-    stage_ms = evs["f"].stage_ms(STAGES)
     evs["f"].close()
     if train:
-        stage_ms.update(evs["b"].stage_ms(BWD_STAGES))
         evs["b"].close()
     model = bwd_algorithmic_flops(dict(cfg, B=B, T=T)) if train else \
         algorithmic_bytes(dict(cfg, B=B, T=T), out_bytes=4)
@@ -526,7 +537,7 @@ def main():
                                      if train else ""),
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "kernel_ms": stage_ms,
-        "breakdown_step_ms": median_ms,  # median step of the breakdown pass (every event recorded)
+        "breakdown_step_ms": median_ms,  # median step of a pass that records every stage's events
         "wall_ms_per_step": t_wall * 1e3 / steps,
     }
     if cold:
