@@ -111,10 +111,16 @@ BWD_LOCAL_SOURCES = ("gdr_bwd_mfma.hip", "gdr_bwd_ops.hpp", "gdr_device.hpp", "g
 
 
 def source_hash(files=FWD_SOURCES):
+    """Hash of the code of the given kernel sources: line comments and blank
+    lines are dropped (the sources hold no block comments and no "//" inside
+    a string), so a change to the comments alone keeps the hash."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "gated_delta_rule_85_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "gated_delta_rule_85_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
