@@ -16,19 +16,22 @@
 //
 // T (split into bf16 hi/lo planes) and the gate scalars come from
 // gdr_chunk_prep as one LDS image per (chunk, v head).  Columns of h evolve
-// independently, so waves never exchange state; the four waves share the
-// decayed scores P through LDS (waves 2 and 3 form the ten 16x16 tiles as
-// K Q^T, whose accumulator layout is P's A operand, while waves 0 and 1 issue
-// the next chunk's copies).  Products with fp32 operands use split-bf16 MFMA
+// independently, so waves never exchange state; the waves share the decayed
+// scores P through LDS, formed as ten 16x16 K Q^T tiles, whose accumulator
+// layout is P's A operand.  Two forms: scan_output_kernel (four waves, each
+// owning 16 state columns; waves 2 and 3 form the score tiles while waves 0
+// and 1 issue the next chunk's copies) serves fp32 inputs and the states
+// pass, and scan_output_roles_kernel (eight waves, the role split below)
+// serves the bf16 forward.  Products with fp32 operands use split-bf16 MFMA
 // (gdr_device.hpp); accumulation is fp32.
 //
 // Data movement: K, Q, the V columns and the T block of the next chunk are
 // copied global -> LDS by the waves' direct-to-LDS loads while the current
 // chunk computes (two LDS buffers, bf16 inputs), into XOR-swizzled rows
 // (gdr_layout.hpp).  The K^T operand of the state update and the V columns
-// are read with the gfx950 transposing LDS read.  Each wave keeps its output
-// tiles in registers and stores them (16 bytes per lane and row) at the start
-// of the next chunk.
+// are read with the gfx950 transposing LDS read.  In the four-wave form each
+// wave keeps its output tiles in registers and stores them (16 bytes per lane
+// and row) at the start of the next chunk.
 //
 // Sequence split (the pages' AutoCP with its sliding-window warm-up): with
 // seg_chunks smaller than the sequence, segment s > 0 starts from a zero
@@ -509,11 +512,14 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
 // ------------------------------------------------------------------ role split
 // The bf16 forward with eight waves, two per SIMD: waves 0-3 ("chain") own the
 // state columns [16w, 16w+16) of the block and form K h, Q h, X, U~, h' and the
-// output tiles, with no global memory traffic inside the chunk loop; waves 4-7
-// ("io") copy the next chunk into LDS, form the ten decayed score tiles, and
-// store each chunk's output, which the chain waves leave in an LDS plane, one
-// chunk later as whole 256-byte token rows.  Same work items, chunk order and
-// arithmetic as scan_output_kernel, so the results are bit-identical to it.
+// output tiles, with no global memory traffic inside the chunk loop.  Waves 4-7
+// ("io") serve them: waves 4-5 ("copy") issue the next chunk's direct-to-LDS
+// copies and store each chunk's output, which the chain waves leave in an LDS
+// plane, one chunk later as whole 256-byte token rows; waves 6-7 ("score") form
+// the ten decayed score tiles.  Same work items, chunk order and split
+// products as scan_output_kernel: the states are bit-identical to it, the
+// output within a few fp32 ulps (the compiler contracts the score exponent
+// differently in the two kernels).
 template <typename In, typename Out, int KD> struct ScanRS {
     using C = Cfg<In, KD, false>;
     using O = Ops<In>;
