@@ -6,13 +6,14 @@ over the full-width prefill shard: B=4, T=4096, H_q=16, H_v=32, K=V=128,
 bf16 q/k/v, fp32 g/beta/initial and final state, fp32 o (inference forward:
 the A and g_cum tensors a backward would need are not written).  Inputs are seeded
 synthetic tensors already resident in HBM; W untimed warm-up steps,
-breakdown passes (up to 20 steps per stage recording only that stage's two HIP
-events: kernel_ms and the dominant kernel; one more pass recording every event:
-breakdown_step_ms), then K timed steps between
-stream synchronisations, in which only the dominant kernel's two events are
-recorded (on the library's stream; each event record costs the stream a few
-microseconds).  That kernel's average duration over the timed steps gives the
-roofline entry.  The fp64 CPU oracle is timed on a bounded
+breakdown passes (K steps per stage, handing the library only that stage's
+two HIP events: kernel_ms and the dominant kernel; one more pass with every
+event: breakdown_step_ms), then K timed steps between stream
+synchronisations, in which only the dominant kernel's two events are handed
+over.  The library binds a stage's events to its kernel launches, so they
+time the kernels themselves; a stage that launches nothing records both on
+the stream, which costs it a few microseconds.  The dominant kernel's average
+duration over the timed steps gives the roofline entry.  The fp64 CPU oracle is timed on a bounded
 sample of the same workload for the cpu_baseline entry.
 
 ``--workload training`` instead times one training step of the operator:
@@ -202,7 +203,7 @@ def cpu_baseline(x, seconds, train=False):
 class Events:
     """HIP events handed to the library's timing hooks, one array per step.
     With `keep`, only those entries hold events; the others are NULL, which
-    the library skips (each record costs the stream a few microseconds)."""
+    the library skips."""
 
     def __init__(self, steps, n, keep=None):
         self.hip = hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
@@ -451,10 +452,11 @@ def main():
     torch.cuda.synchronize()
 
     # stage breakdown (not part of the timed region).  Each stage is timed in a pass
-    # of its own that records only that stage's two events: a recorded event costs the
-    # stream a few microseconds, so events around every stage would inflate each
-    # stage's time.  One more pass records every event, for the median step.
-    nbk = min(steps, 20)
+    # of its own, of as many steps as the timed region, that hands over only that
+    # stage's two events: a stage that launches no kernel records its events as
+    # markers on the stream, which would slow the stages next to it.  One more pass
+    # hands over every event, for the median step.
+    nbk = steps
     stage_ms = {}
     for key, names, n_ev in (("f", STAGES, _lib.FWD_STAGES),) + ((("b", BWD_STAGES, _lib.BWD_STAGES),) if train else ()):
         for s_i, name in enumerate(names):

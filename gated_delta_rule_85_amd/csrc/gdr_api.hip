@@ -11,7 +11,19 @@
 
 using namespace gdr;
 
+namespace gdr {
+StageEvents &stage_events() {
+    static thread_local StageEvents e = {nullptr, nullptr, false};
+    return e;
+}
+}  // namespace gdr
+
 namespace {
+
+// leaves no timing stage open on this thread when an entry point returns
+struct StageGuard {
+    ~StageGuard() { stage_events() = {nullptr, nullptr, false}; }
+};
 
 constexpr size_t ALIGN = 256;
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -333,14 +345,13 @@ int gdr::fwd_impl(const gdr_fwd_args *a, hipStream_t stream, void *(*scratch_for
     const Dt ot = a->out_dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
     const SeqMap sm = make_map(a->cu_seqlens != nullptr, a->T, pl.n_seq, pl.nct, chunk_off);
 
-    auto mark = [&](int i) {
-        return !a->events || !a->events[i] || hipEventRecord(a->events[i], stream) == hipSuccess;
-    };
+    auto ev = [&](int i) { return a->events ? a->events[i] : nullptr; };
+    StageGuard stage_guard;
     if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, const_cast<int32_t *>(sm.cu), chunk_off,
                                               const_cast<int32_t *>(sm.order), (int)pl.n_seq, a->T,
                                               stream) != hipSuccess)
         return GDR_ELAUNCH;
-    if (!mark(0)) return GDR_ELAUNCH;
+    open_stage(ev(0), ev(1));
     if (pl.tokens > 0) {
         PrepParams pp;
         pp.k = a->k;
@@ -355,7 +366,8 @@ int gdr::fwd_impl(const gdr_fwd_args *a, hipStream_t stream, void *(*scratch_for
         pp.Hv = (int)a->H_v;
         if (launch_prep(dt, (int)a->K, pp, (int)pl.nt_ub, stream) != hipSuccess) return GDR_ELAUNCH;
     }
-    if (!mark(1) || !mark(2)) return GDR_ELAUNCH;
+    if (close_stage(stream) != hipSuccess) return GDR_ELAUNCH;
+    open_stage(ev(2), ev(3));
     ScanParams sp;
     sp.q = a->q;
     sp.k = a->k;
@@ -423,7 +435,8 @@ int gdr::fwd_impl(const gdr_fwd_args *a, hipStream_t stream, void *(*scratch_for
         sp.h0_seg = hseg;
     }
     if (launch_scan_output(dt, ot, (int)a->K, (int)a->V, sp, stream) != hipSuccess) return GDR_ELAUNCH;
-    if (!mark(3) || !mark(4)) return GDR_ELAUNCH;
+    if (close_stage(stream) != hipSuccess) return GDR_ELAUNCH;
+    open_stage(ev(4), ev(5));
     if ((a->w_out || a->u_out) && pl.tokens > 0) {
         if (!a->w_out || !a->u_out) return GDR_EINVAL;
         WUParams wp;
@@ -440,7 +453,7 @@ int gdr::fwd_impl(const gdr_fwd_args *a, hipStream_t stream, void *(*scratch_for
         wp.V = (int)a->V;
         if (launch_wu(dt, wp, (int)pl.nt_ub, stream) != hipSuccess) return GDR_ELAUNCH;
     }
-    if (!mark(5)) return GDR_ELAUNCH;
+    if (close_stage(stream) != hipSuccess) return GDR_ELAUNCH;
     return GDR_OK;
 }
 
@@ -516,17 +529,17 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
     bp.dh_seg = nullptr;
     bp.d_seg = nullptr;
 
-    auto mark = [&](int i) {
-        return !a->events || !a->events[i] || hipEventRecord(a->events[i], stream) == hipSuccess;
-    };
+    auto ev = [&](int i) { return a->events ? a->events[i] : nullptr; };
+    StageGuard stage_guard;
     if (a->cu_seqlens && launch_chunk_offsets(a->cu_seqlens, const_cast<int32_t *>(sm.cu), chunk_off,
                                               const_cast<int32_t *>(sm.order), (int)pl.n_seq, a->T,
                                               stream) != hipSuccess)
         return GDR_ELAUNCH;
-    if (!mark(0)) return GDR_ELAUNCH;
+    open_stage(ev(0), ev(1));
     if (pl.tokens > 0 && !a->tblk_bwd && launch_tblocks(dt, bp, (int)pl.nt_ub, stream) != hipSuccess)
         return GDR_ELAUNCH;
-    if (!mark(1) || !mark(2)) return GDR_ELAUNCH;
+    if (close_stage(stream) != hipSuccess) return GDR_ELAUNCH;
+    open_stage(ev(2), ev(3));
     if (pl.tokens > 0 && !a->h_bwd) {
         // chunk-start states: the exact forward scan without its output
         ScanParams sp;
@@ -619,7 +632,8 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
         if (launch_fill_zero(ws + pl.off_zero, 512, stream) != hipSuccess) return GDR_ELAUNCH;
         if (launch_scan_states(dt, (int)a->K, tp, stream) != hipSuccess) return GDR_ELAUNCH;
     }
-    if (!mark(3) || !mark(4)) return GDR_ELAUNCH;
+    if (close_stage(stream) != hipSuccess) return GDR_ELAUNCH;
+    open_stage(ev(4), ev(5));  // closed by launch_bwd after the reverse scan
     if (pl.split) {
         // reverse scan: every segment's start gradient from a zero end gradient (the last
         // segment from dht), the reverse carry with the transposed transitions, then the
@@ -642,8 +656,8 @@ int gdr_bwd(const gdr_bwd_args *a, hipStream_t stream) {
         bp.dh_seg = cp.h0_seg;
     }
     const Dt gt = a->grad_dtype == GDR_BF16 ? Dt::BF16 : Dt::F32;
-    const hipEvent_t *ev = a->events ? a->events + 5 : nullptr;  // reverse scan end, local start/end
-    if (launch_bwd(dt, gt, (int)a->K, bp, pl.tokens > 0 ? (int)pl.nt_ub : 0, n_units, ev, stream) != hipSuccess)
+    const hipEvent_t *lev = a->events ? a->events + 6 : nullptr;  // the chunk-local stage
+    if (launch_bwd(dt, gt, (int)a->K, bp, pl.tokens > 0 ? (int)pl.nt_ub : 0, n_units, lev, stream) != hipSuccess)
         return GDR_ELAUNCH;
     return GDR_OK;
 }

@@ -560,26 +560,25 @@ hipError_t launch_bwd_t(const BwdParams &p, int n_chunks_ub, int n_units, const 
     if constexpr (sizeof(In) == 2) {
         e = launch_bwd_scan_bf16(KD, p, n_units, s);
     } else {
-        hipLaunchKernelGGL((bwd_scan_kernel<In, KD>),
+        launch_k((bwd_scan_kernel<In, KD>),
                            dim3(p.sm.order && p.n_seg == 1 ? lpt_blocks(p.sm.n_seq, p.Hq, p.Hv, p.V / 64)
                                                            : n_units * (p.V / 64) * p.n_seg),
                            dim3(NTHR), 0, s, p, n_units);
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
-    if (ev && ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
-    if (ev && ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return e;
+    if ((e = close_stage(s)) != hipSuccess) return e;  // the reverse scan's stage
+    open_stage(ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
     if (n_chunks_ub > 0) {
         if constexpr (sizeof(In) == 2) {
             e = launch_bwd_local_bf16(sizeof(Gt) == 2 ? Dt::BF16 : Dt::F32, KD, p, n_chunks_ub, s);
         } else {
-            hipLaunchKernelGGL((bwd_local_kernel<In, Gt, KD>), dim3(n_chunks_ub, p.Hq), dim3(NTHR), 0, s, p);
+            launch_k((bwd_local_kernel<In, Gt, KD>), dim3(n_chunks_ub, p.Hq), dim3(NTHR), 0, s, p);
             e = hipGetLastError();
         }
         if (e != hipSuccess) return e;
     }
-    if (ev && ev[2]) e = hipEventRecord(ev[2], s);
-    return e;
+    return close_stage(s);
 }
 
 template <typename In, typename Gt>
@@ -594,9 +593,9 @@ hipError_t launch_bwd_k(int K, const BwdParams &p, int n_chunks_ub, int n_units,
 hipError_t launch_tblocks(Dt dt, const BwdParams &p, int n_chunks_ub, hipStream_t s) {
     const dim3 grid(n_chunks_ub, p.Hv);
     if (dt == Dt::BF16)
-        hipLaunchKernelGGL(tblock_kernel<bf16>, grid, dim3(NTHR), 0, s, p);
+        launch_k(tblock_kernel<bf16>, grid, dim3(NTHR), 0, s, p);
     else
-        hipLaunchKernelGGL(tblock_kernel<float>, grid, dim3(NTHR), 0, s, p);
+        launch_k(tblock_kernel<float>, grid, dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
 
@@ -605,9 +604,9 @@ hipError_t launch_bwd_reverse(Dt dt, int K, const BwdParams &p, int n_units, hip
     const dim3 grid(p.sm.order && p.n_seg == 1 ? lpt_blocks(p.sm.n_seq, p.Hq, p.Hv, p.V / 64)
                                                : n_units * (p.V / 64) * p.n_seg);
     if (K == 128)
-        hipLaunchKernelGGL((bwd_scan_kernel<float, 128>), grid, dim3(NTHR), 0, s, p, n_units);
+        launch_k((bwd_scan_kernel<float, 128>), grid, dim3(NTHR), 0, s, p, n_units);
     else
-        hipLaunchKernelGGL((bwd_scan_kernel<float, 64>), grid, dim3(NTHR), 0, s, p, n_units);
+        launch_k((bwd_scan_kernel<float, 64>), grid, dim3(NTHR), 0, s, p, n_units);
     return hipGetLastError();
 }
 

@@ -415,14 +415,14 @@ hipError_t launch_bwd_local_bf16(Dt gt, int K, const BwdParams &p, int n_chunks_
     const dim3 grid(n_chunks_ub, p.Hq);
     if (gt == Dt::BF16) {
         if (K == 128)
-            hipLaunchKernelGGL((bwd_local_bf16<bf16, 128>), grid, dim3(NTHR), 0, s, p);
+            launch_k((bwd_local_bf16<bf16, 128>), grid, dim3(NTHR), 0, s, p);
         else
-            hipLaunchKernelGGL((bwd_local_bf16<bf16, 64>), grid, dim3(NTHR), 0, s, p);
+            launch_k((bwd_local_bf16<bf16, 64>), grid, dim3(NTHR), 0, s, p);
     } else {
         if (K == 128)
-            hipLaunchKernelGGL((bwd_local_bf16<float, 128>), grid, dim3(NTHR), 0, s, p);
+            launch_k((bwd_local_bf16<float, 128>), grid, dim3(NTHR), 0, s, p);
         else
-            hipLaunchKernelGGL((bwd_local_bf16<float, 64>), grid, dim3(NTHR), 0, s, p);
+            launch_k((bwd_local_bf16<float, 64>), grid, dim3(NTHR), 0, s, p);
     }
     return hipGetLastError();
 }

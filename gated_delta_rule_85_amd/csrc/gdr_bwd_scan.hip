@@ -320,9 +320,9 @@ hipError_t launch_bwd_scan_bf16(int K, const BwdParams &p, int n_units, hipStrea
     const dim3 grid(p.sm.order && p.n_seg == 1 ? lpt_blocks(p.sm.n_seq, p.Hq, p.Hv, p.V / 64)
                                                : n_units * (p.V / 64) * p.n_seg);
     if (K == 128)
-        hipLaunchKernelGGL((bwd_scan_roles_bf16<128>), grid, dim3(2 * NTHR), 0, s, p, n_units);
+        launch_k((bwd_scan_roles_bf16<128>), grid, dim3(2 * NTHR), 0, s, p, n_units);
     else
-        hipLaunchKernelGGL((bwd_scan_roles_bf16<64>), grid, dim3(2 * NTHR), 0, s, p, n_units);
+        launch_k((bwd_scan_roles_bf16<64>), grid, dim3(2 * NTHR), 0, s, p, n_units);
     return hipGetLastError();
 }
 

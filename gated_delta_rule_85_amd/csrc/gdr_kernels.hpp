@@ -1,6 +1,7 @@
 // Kernel parameter blocks and host-side launchers of libgdr (internal).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -11,6 +12,36 @@
 namespace gdr {
 
 enum class Dt : int { BF16 = 0, F32 = 1 };
+
+// Stage timing for the callers' event hooks.  The events of a stage are bound
+// to its kernel launches (hipExtLaunchKernel), so they carry the kernels' own
+// start and end times, with no marker packets on the stream between kernels:
+// the stage's first launch takes the start event, and every launch takes the
+// stop event, so the last launch's end stands.  A stage that launches nothing
+// records both events at once when it closes.  One open stage per host thread.
+struct StageEvents {
+    hipEvent_t start, stop;
+    bool launched;
+};
+StageEvents &stage_events();  // this thread's (gdr_api.hip)
+inline void open_stage(hipEvent_t start, hipEvent_t stop) { stage_events() = {start, stop, false}; }
+inline hipError_t close_stage(hipStream_t s) {
+    StageEvents &e = stage_events();
+    hipError_t r = hipSuccess;
+    if (!e.launched) {
+        if (e.start) r = hipEventRecord(e.start, s);
+        if (r == hipSuccess && e.stop) r = hipEventRecord(e.stop, s);
+    }
+    e = {nullptr, nullptr, false};
+    return r;
+}
+// every kernel of the library is launched through this (errors: hipGetLastError)
+template <typename F, typename... Args>
+inline void launch_k(F kernel, dim3 grid, dim3 block, uint32_t smem, hipStream_t s, Args... args) {
+    StageEvents &e = stage_events();
+    hipExtLaunchKernelGGL(kernel, grid, block, smem, s, e.launched ? nullptr : e.start, e.stop, 0, args...);
+    e.launched = true;
+}
 
 // gdr_chunk_prep: per (chunk, q/k head): in-chunk cumulative log-gate,
 // decayed strictly lower beta K K^T, T = (I + A)^{-1}.
@@ -117,7 +148,9 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_tblocks(Dt dt, const BwdParams &p, int n_chunks_ub, hipStream_t s);
 // the reverse scan alone (the exact split's pass from zero end gradients)
 hipError_t launch_bwd_reverse(Dt dt, int K, const BwdParams &p, int n_units, hipStream_t s);
-// ev: null or 3 events: after the reverse scan, before and after the local stage
+// Closes the timing stage open on this thread (the reverse scan, opened by the
+// caller) after the reverse scan; ev: null or 2 events, the start and stop of
+// the chunk-local stage.
 hipError_t launch_bwd(Dt dt, Dt gt, int K, const BwdParams &p, int n_chunks_ub, int n_units,
                       const hipEvent_t *ev, hipStream_t s);
 hipError_t launch_bwd_scan_bf16(int K, const BwdParams &p, int n_units, hipStream_t s);

@@ -225,7 +225,7 @@ hipError_t launch_prep_t(const PrepParams &p, int n_chunks_ub, hipStream_t s) {
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     (void)attr;  // a refusal shows up as a launch error below
     dim3 grid(n_chunks_ub, p.Hq);
-    hipLaunchKernelGGL((prep_kernel<In, KD>), grid, dim3(NTHR), smem, s, p);
+    launch_k((prep_kernel<In, KD>), grid, dim3(NTHR), smem, s, p);
     return hipGetLastError();
 }
 
@@ -316,8 +316,8 @@ __global__ void seq_order_kernel(const int32_t *cu, int32_t *order, int n_seq) {
 
 hipError_t launch_chunk_offsets(const int32_t *cu, int32_t *cuc, int32_t *chunk_off, int32_t *order, int n_seq,
                                int64_t T, hipStream_t s) {
-    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, s, cu, cuc, chunk_off, n_seq, (int32_t)T);
-    if (order) hipLaunchKernelGGL(seq_order_kernel, dim3((n_seq + 255) / 256), dim3(256), 0, s, cuc, order, n_seq);
+    launch_k(chunk_offsets_kernel, dim3(1), dim3(64), 0, s, cu, cuc, chunk_off, n_seq, (int32_t)T);
+    if (order) launch_k(seq_order_kernel, dim3((n_seq + 255) / 256), dim3(256), 0, s, cuc, order, n_seq);
     return hipGetLastError();
 }
 
@@ -333,9 +333,9 @@ size_t tblock_bytes_fwd(Dt dt) { return dt == Dt::BF16 ? TBlockF<bf16>::BYTES : 
 hipError_t launch_wu(Dt dt, const WUParams &p, int n_chunks_ub, hipStream_t s) {
     dim3 grid(n_chunks_ub, p.Hv);
     if (dt == Dt::BF16)
-        hipLaunchKernelGGL(wu_kernel<bf16>, grid, dim3(NTHR), 0, s, p);
+        launch_k(wu_kernel<bf16>, grid, dim3(NTHR), 0, s, p);
     else
-        hipLaunchKernelGGL(wu_kernel<float>, grid, dim3(NTHR), 0, s, p);
+        launch_k(wu_kernel<float>, grid, dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
 

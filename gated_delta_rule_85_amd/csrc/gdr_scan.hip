@@ -877,9 +877,9 @@ hipError_t launch_scan_t(const ScanParams &p, hipStream_t s) {
     const int nb = p.sm.order && p.n_seg == 1 ? lpt_blocks(p.sm.n_seq, p.Hq, p.Hv, p.n_vt)
                                               : p.n_vt * p.n_units * p.n_seg;
     if constexpr (sizeof(In) == 2 && !STATES)
-        hipLaunchKernelGGL((scan_output_roles_kernel<In, Out, KD>), dim3(nb), dim3(2 * NTHR), 0, s, p);
+        launch_k((scan_output_roles_kernel<In, Out, KD>), dim3(nb), dim3(2 * NTHR), 0, s, p);
     else
-        hipLaunchKernelGGL((scan_output_kernel<In, Out, KD, STATES>), dim3(nb), dim3(NTHR), 0, s, p);
+        launch_k((scan_output_kernel<In, Out, KD, STATES>), dim3(nb), dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
 
@@ -990,14 +990,14 @@ __global__ void fill_zero_kernel(uint32_t *p, size_t n) {
 
 hipError_t launch_carry(const CarryParams &p, int n_units, hipStream_t s) {
     if (p.K == 128)
-        hipLaunchKernelGGL(carry_kernel<128>, dim3(n_units, p.V / 16), dim3(NTHR), 0, s, p);
+        launch_k(carry_kernel<128>, dim3(n_units, p.V / 16), dim3(NTHR), 0, s, p);
     else
-        hipLaunchKernelGGL(carry_kernel<64>, dim3(n_units, p.V / 16), dim3(NTHR), 0, s, p);
+        launch_k(carry_kernel<64>, dim3(n_units, p.V / 16), dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(256), 0, s, static_cast<uint32_t *>(p), bytes / 4);
+    launch_k(fill_zero_kernel, dim3(1), dim3(256), 0, s, static_cast<uint32_t *>(p), bytes / 4);
     return hipGetLastError();
 }
 

@@ -143,11 +143,14 @@ typedef struct {
                                    rebuild of them from A and g_cum */
     float *w_out;               /* [B,T,H_v,K] W = T diag(beta e^g_cum) K, NULL = not computed */
     float *u_out;               /* [B,T,H_v,V] U = T diag(beta) V, NULL = not computed */
-    /* timing hook: NULL, or a HOST array of 2*GDR_FWD_STAGES events that are
-       recorded on the stream before and after each stage (chunk prep, scan
-       with output, W/U); a stage that does not run records both at once.  A
-       NULL entry is skipped (each record costs the stream a few microseconds,
-       so a caller timing one stage passes only that stage's pair) */
+    /* timing hook: NULL, or a HOST array of 2*GDR_FWD_STAGES events, a start
+       and a stop per stage (chunk prep, scan with output, W/U).  They are bound
+       to the stage's kernel launches (hipExtLaunchKernel): the start event
+       takes the start of the stage's first kernel, the stop event the end of
+       its last, with no marker packets between kernels.  A stage that launches
+       nothing records both on the stream at once.  A NULL entry is skipped.
+       Not for concurrent calls from one host thread (the binding is per
+       thread) */
     hipEvent_t *events;
     /* scratch */
     void *workspace;
@@ -183,10 +186,10 @@ typedef struct {
     float *dg;                  /* [B,T,H_v] gradient w.r.t. the raw per-token g */
     float *dh0;                 /* [N,H_v,K,V] gradient of initial_state (NULL initial_state
                                    means zeros); NULL = not wanted */
-    /* timing hook: NULL, or a HOST array of 2*GDR_BWD_STAGES events recorded
-       before and after each stage (T-block rebuild, chunk-start state
-       recompute, reverse scan, chunk-local gradients); NULL entries are
-       skipped */
+    /* timing hook: NULL, or a HOST array of 2*GDR_BWD_STAGES events, a start
+       and a stop per stage (T-block rebuild, chunk-start state recompute,
+       reverse scan, chunk-local gradients), bound to the stages' kernel
+       launches as in gdr_fwd_args; NULL entries are skipped */
     hipEvent_t *events;
     void *workspace;
     size_t workspace_bytes;
