@@ -249,7 +249,9 @@ int gdr_fwd(const gdr_fwd_args *args, hipStream_t stream);
    one GPU uses that GPU's one buffer: calls that overlap in time on one GPU
    (other streams, other host threads) race and must be serialised by the
    caller; consecutive calls on one stream are ordered.  Nothing in the buffer
-   needs to start at zero: each call writes what it reads. */
+   needs to start at zero: each call writes what it reads.  The first call on a
+   device takes the buffer's address and must not be captured; later calls
+   (with args->events NULL) may be captured into a HIP graph and replayed. */
 int gdr_fwd_noalloc(const gdr_fwd_args *args, hipStream_t stream);
 
 /* Bytes of the T blocks of gdr_fwd_args.tblk_bwd for these sizes: one block
