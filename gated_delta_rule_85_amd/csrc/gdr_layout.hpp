@@ -141,7 +141,8 @@ __device__ __forceinline__ void write_tblock_scalars(char *blk, const float *gam
 
 // Write one T block from an fp32 row-major T (row r, column i at T[r * ld + i])
 // and the chunk's 64 gate values (gam padded with its last value, bet zero
-// past the chunk end); rows r >= n are written as zero.  All threads of the
+// past the chunk end); rows r >= n and the 16 x 16 blocks above the diagonal
+// (zero in T) are written as zero without being read.  All threads of the
 // workgroup take part; gam/bet/T are read, never written.
 template <typename In, typename SW = Swz<TBlock<In>::ROWB>>
 __device__ __forceinline__ void write_tblock(char *blk, const float *T, int ld, const float *gam,
@@ -151,7 +152,7 @@ __device__ __forceinline__ void write_tblock(char *blk, const float *T, int ld, 
     for (int idx = tid; idx < CH * SW::CPR; idx += nthr) {
         const int r = idx / SW::CPR, pc = idx % SW::CPR, lc = SW::chunk(r, pc);
         f32x4 x0 = zero4(), x1 = zero4();
-        if (r < n) {
+        if (r < n && ((EPC * lc) >> 4) <= (r >> 4)) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) x0[e] = T[r * ld + EPC * lc + e];
             if constexpr (TB::BF) {
@@ -172,7 +173,8 @@ __device__ __forceinline__ void write_tblock(char *blk, const float *T, int ld, 
     write_tblock_scalars<TB>(blk, gam, bet, n, tid);
 }
 
-// The forward's T block (TBlockF) from the same fp32 T and gates.
+// The forward's T block (TBlockF) from the same fp32 T and gates (the same
+// rows and blocks written as zero).
 template <typename In>
 __device__ __forceinline__ void write_tblock_f(char *blk, const float *T, int ld, const float *gam,
                                                const float *bet, int n, int tid, int nthr) {
@@ -185,7 +187,7 @@ __device__ __forceinline__ void write_tblock_f(char *blk, const float *T, int ld
             const int r = idx < 128 ? idx >> 2 : 32 + ((idx - 128) >> 3);
             const int lc = idx < 128 ? idx & 3 : (idx - 128) & 7;
             f32x4 x0 = zero4(), x1 = zero4();
-            if (r < n) {
+            if (r < n && ((8 * lc) >> 4) <= (r >> 4)) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     x0[e] = T[r * ld + 8 * lc + e];

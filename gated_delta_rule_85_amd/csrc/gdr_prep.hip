@@ -1,6 +1,7 @@
 // gdr_chunk_prep — the chunk-parallel part of the chunked forward.
 //
-// For one chunk of one q/k head (and each of the v heads sharing it):
+// For one chunk of one q/k head (and each of the v heads sharing it, two at a
+// time):
 //   gam = in-chunk running sum of the log-gate g          (returned as g_cum)
 //   A   = strictly lower part of diag(beta) (K K^T) * exp(gam_r - gam_i)
 //   T   = (I + A)^{-1}                                     (returned as A)
@@ -15,9 +16,11 @@
 // K K^T depends only on the q/k head, so it is formed once per workgroup on
 // MFMA and reused by the H_v/H_q v heads.  The inverse of the unit lower
 // triangular 64x64 matrix is blocked in 16x16 tiles: the four diagonal tiles
-// by forward substitution (one wave, one lane per column), the off-diagonal
-// tiles by T_ab = -D_a sum_{m=b}^{a-1} A_am T_mb on fp32 MFMA, one block
-// diagonal at a time.
+// by forward substitution (one wave per head, one lane per column), the
+// off-diagonal tiles by T_ab = -D_a sum_{m=b}^{a-1} A_am T_mb on fp32 MFMA, one
+// block diagonal at a time.  The v heads are taken two at a time so that the
+// one-wave phases (the gates' prefix sum, the substitution) run for both heads
+// at once.
 #include "gdr_kernels.hpp"
 #include "gdr_lds.hpp"
 
@@ -27,16 +30,23 @@ namespace {
 
 constexpr int LDF = 68;  // fp32 64x64 tiles in LDS: row pitch (floats)
 
-// acc += X[16x16] * Y[16x16], X and Y fp32 in LDS with pitch LDF
-__device__ __forceinline__ f32x4 blk_mm(f32x4 acc, const float *X, const float *Y) {
+// Each v head's 64 x 64 matrices share one LDS tile M: T (lower triangular) in
+// its lower part with the diagonal, A (strictly lower) transposed in its
+// strict upper part, M[i][r] = A[r][i] for i < r.  The diagonal blocks of A
+// are read only by the substitution, which then overwrites the upper part of
+// each diagonal block with the zeros of T; T's blocks above the diagonal are
+// never stored (they are zero) and readers mask them.
+
+// acc += A_am T_mb (block rows of A from the transposed store, T block rows)
+__device__ __forceinline__ f32x4 blk_mm_at(f32x4 acc, const float *M, int a, int m, int b) {
     const int n = ln16(), g = lg4();
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(X + n * LDF + 4 * g);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], Y[(4 * g + j) * LDF + n], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(M[(16 * m + 4 * g + j) * LDF + 16 * a + n],
+                                                   M[(16 * m + 4 * g + j) * LDF + 16 * b + n], acc, 0, 0, 0);
     return acc;
 }
-// acc += X[16x16] * Y where Y is an accumulator tile in registers
+// acc += T_aa * Y where Y is an accumulator tile in registers
 __device__ __forceinline__ f32x4 blk_mm_reg(f32x4 acc, const float *X, f32x4 y) {
     const int n = ln16(), g = lg4();
     const f32x4 a = *reinterpret_cast<const f32x4 *>(X + n * LDF + 4 * g);
@@ -45,31 +55,35 @@ __device__ __forceinline__ f32x4 blk_mm_reg(f32x4 acc, const float *X, f32x4 y) 
     return acc;
 }
 
-// T_ab (a > b) from the diagonal inverses and the lower blocks already done
-__device__ __forceinline__ void offdiag_tile(const float *A, float *Tm, int a, int b) {
+// T_ab (a > b) = -T_aa sum_{m=b}^{a-1} A_am T_mb, from the diagonal inverses and
+// the lower blocks already done
+__device__ __forceinline__ void offdiag_tile(float *M, int a, int b) {
     f32x4 P = zero4();
-    for (int m = b; m < a; ++m) P = blk_mm(P, A + 16 * a * LDF + 16 * m, Tm + 16 * m * LDF + 16 * b);
-    const f32x4 R = blk_mm_reg(zero4(), Tm + 16 * a * LDF + 16 * a, P);
+    for (int m = b; m < a; ++m) P = blk_mm_at(P, M, a, m, b);
+    const f32x4 R = blk_mm_reg(zero4(), M + 16 * a * LDF + 16 * a, P);
     const int n = ln16(), g = lg4();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) Tm[(16 * a + 4 * g + j) * LDF + 16 * b + n] = -R[j];
+    for (int j = 0; j < 4; ++j) M[(16 * a + 4 * g + j) * LDF + 16 * b + n] = -R[j];
 }
 
+// The v heads of the q/k head are taken two at a time, in step: every phase
+// below serves both heads of a pair, so a pair costs the phases of one head.
 template <typename In, int KD>
 __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
     using O = Ops<In>;
     using V16 = typename Vec16<In>::type;
     constexpr int EV = Vec16<In>::n;
     constexpr int LDK = KD + EV;  // 16-byte row padding
-    // K (until S = K K^T is in registers), then A, share the first region
-    constexpr int KBYTES = sizeof(In) * CH * LDK, ABYTES = sizeof(float) * CH * LDF;
-    constexpr int R0 = KBYTES > ABYTES ? KBYTES : ABYTES;
+    // K (until S = K K^T is in registers), then the first head's tile, share the first region
+    constexpr int KBYTES = sizeof(In) * CH * LDK, MBYTES = sizeof(float) * CH * LDF;
+    constexpr int R0 = KBYTES > MBYTES ? KBYTES : MBYTES;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     In *Ks = reinterpret_cast<In *>(smem);
-    float *A = reinterpret_cast<float *>(smem);
-    float *Tm = reinterpret_cast<float *>(smem + R0);
-    float *gam = Tm + CH * LDF;
-    float *bet = gam + CH;
+    float *const M0 = reinterpret_cast<float *>(smem), *const M1 = reinterpret_cast<float *>(smem + R0);
+    auto tile = [&](int h) { return h ? M1 : M0; };  // head h of the pair
+    float *gb = reinterpret_cast<float *>(smem + R0 + MBYTES);  // gam, bet of the two heads
+    auto gam_of = [&](int h) { return gb + 2 * CH * h; };
+    auto bet_of = [&](int h) { return gb + 2 * CH * h + CH; };
 
     const int gid = blockIdx.x, hq = blockIdx.y;
     int j, c;
@@ -81,16 +95,16 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
     const int tid = threadIdx.x, w = wave_id(), l = lane_id();
     const int G = p.Hv / p.Hq;
 
-    // wave 0 holds the log-gate and beta of the v head being processed, one token
-    // per lane; each head's pair is loaded one head ahead, the first before the
-    // K tile, so their latency overlaps other work
+    // waves 0 and 1 hold the log-gate and beta of the pair's two v heads, one token
+    // per lane; each pair's are loaded one pair ahead, the first before the K tile,
+    // so their latency overlaps other work
     float g_nx = 0.f, b_nx = 0.f;
-    if (w == 0 && l < n) {
-        g_nx = p.g[(ts + l) * p.Hv + hq * G];
-        b_nx = p.beta[(ts + l) * p.Hv + hq * G];
+    if (w < 2 && w < G && l < n) {
+        g_nx = p.g[(ts + l) * p.Hv + hq * G + w];
+        b_nx = p.beta[(ts + l) * p.Hv + hq * G + w];
     }
 
-    // K rows of the chunk (zero past its end); upper off-diagonal T tiles = 0
+    // K rows of the chunk (zero past its end)
     const In *kp = reinterpret_cast<const In *>(p.k);
     {
         // all of this thread's loads first, then the LDS writes (one memory round trip)
@@ -114,14 +128,13 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
             *reinterpret_cast<V16 *>(Ks + r * LDK + cv * EV) = val[it];
         }
     }
-    for (int idx = tid; idx < CH * CH; idx += NTHR) {
-        const int r = idx >> 6, i = idx & 63;
-        if ((i >> 4) > (r >> 4)) Tm[r * LDF + i] = 0.f;
-    }
     __syncthreads();
 
-    // S = K K^T, the ten tiles on or below the diagonal, kept in registers:
-    // wave w holds tiles w, w + 4 and (waves 0, 1) w + 8
+    // S = K K^T, the ten tiles (str, sti) on or below the diagonal, kept in
+    // registers as their transposes (S is symmetric: the product with the operands
+    // swapped), so that lane (n16, g) holds S[16 str + n16][16 sti + 4 g + jj]:
+    // one row r per lane, the layout in which A^T is stored without bank
+    // conflicts.  Wave w holds tiles w, w + 4 and (waves 0, 1) w + 8
     const int n16 = ln16(), g = lg4();
     f32x4 sS[3];
     int str[3], sti[3];
@@ -134,87 +147,103 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
         if (t < 10) {
 #pragma unroll
             for (int dp = 0; dp < KD / 32; ++dp) {
-                const In *ar = Ks + (16 * str[k] + n16) * LDK + 32 * dp + 4 * g;
-                const In *br = Ks + (16 * sti[k] + n16) * LDK + 32 * dp + 4 * g;
+                const In *ar = Ks + (16 * sti[k] + n16) * LDK + 32 * dp + 4 * g;
+                const In *br = Ks + (16 * str[k] + n16) * LDK + 32 * dp + 4 * g;
                 sS[k] = mma(sS[k], O::load(ar, ar + 16), O::load(br, br + 16));
             }
         }
     }
-    __syncthreads();  // K is no longer read: its region becomes A
+    __syncthreads();  // K is no longer read: its region becomes the first head's tile
 
-    for (int rr = 0; rr < G; ++rr) {
-        const int hv = hq * G + rr;
-        if (w == 0) {
+    for (int r0 = 0; r0 < G; r0 += 2) {
+        const int np = min(2, G - r0);  // heads in this pair
+        if (w < np) {
             // inclusive running sum of g over the chunk (zero past its end)
+            const int hv = hq * G + r0 + w;
             const float x = wave_prefix_sum(g_nx);
-            gam[l] = x;
-            bet[l] = b_nx;
+            gam_of(w)[l] = x;
+            bet_of(w)[l] = b_nx;
             if (l < n && p.g_cum) p.g_cum[(ts + l) * p.Hv + hv] = x;
-            if (rr + 1 < G && l < n) {
-                g_nx = p.g[(ts + l) * p.Hv + hv + 1];
-                b_nx = p.beta[(ts + l) * p.Hv + hv + 1];
+            if (r0 + 2 + w < G && l < n) {
+                g_nx = p.g[(ts + l) * p.Hv + hv + 2];
+                b_nx = p.beta[(ts + l) * p.Hv + hv + 2];
             }
         }
         __syncthreads();
-        // A = diag(beta) S * exp(gam_r - gam_i) below the diagonal, from the S tiles in registers
-        // (entries on and above the diagonal of a diagonal tile are never read)
+        // A = diag(beta) S * exp(gam_r - gam_i) below the diagonal, from the S tiles in
+        // registers, stored transposed: M[i][r] = A[r][i], i < r
+#pragma unroll 1
+        for (int h = 0; h < np; ++h) {
+            float *M = tile(h);
+            const float *gam = gam_of(h), *bet = bet_of(h);
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            if (w + 4 * k >= 10) break;
+            for (int k = 0; k < 3; ++k) {
+                if (w + 4 * k >= 10) break;
+                const int r = 16 * str[k] + n16, i0 = 16 * sti[k] + 4 * g;
+                const float br = bet[r], gr = gam[r];
+                const f32x4 gi = *reinterpret_cast<const f32x4 *>(gam + i0);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int r = 16 * str[k] + 4 * g + jj, i = 16 * sti[k] + n16;
-                A[r * LDF + i] = i < r ? bet[r] * fast_exp(gam[r] - gam[i]) * sS[k][jj] : 0.f;
+                for (int jj = 0; jj < 4; ++jj)
+                    if (i0 + jj < r) M[(i0 + jj) * LDF + r] = br * fast_exp(gr - gi[jj]) * sS[k][jj];
             }
         }
         __syncthreads();
-        if (w == 0) {
-            // diagonal tiles: lane = (tile b, column cc); forward substitution
+        if (w < np) {
+            // diagonal tiles of head w: lane = (tile b, column cc); forward substitution,
+            // then column cc of T_bb over the (no longer needed) block of A
+            float *M = tile(w);
             const int b = l >> 4, cc = l & 15;
-            const float *Ab = A + 16 * b * LDF + 16 * b;
+            float *Mb = M + 16 * b * LDF + 16 * b;
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float s = (r == cc) ? 1.f : 0.f;
 #pragma unroll
-                for (int i = 0; i < r; ++i) s -= Ab[r * LDF + i] * x[i];
+                for (int i = 0; i < r; ++i) s -= Mb[i * LDF + r] * x[i];
                 x[r] = s;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Tm[(16 * b + r) * LDF + 16 * b + cc] = x[r];
+            for (int r = 0; r < 16; ++r) Mb[r * LDF + cc] = x[r];
         }
         __syncthreads();
-        if (w < 3) offdiag_tile(A, Tm, w + 1, w);
+        // off-diagonal blocks, one block diagonal at a time: 3, 2, 1 blocks per head
+        if (w + 4 * 0 < 3 * np) offdiag_tile(tile(w / 3), w % 3 + 1, w % 3);
+        if (w + 4 < 3 * np) offdiag_tile(M1, (w + 4) % 3 + 1, (w + 4) % 3);
         __syncthreads();
-        if (w < 2) offdiag_tile(A, Tm, w + 2, w);
+        if (w < 2 * np) offdiag_tile(tile(w / 2), w % 2 + 2, w % 2);
         __syncthreads();
-        if (w == 0) offdiag_tile(A, Tm, 3, 0);
+        if (w < np) offdiag_tile(tile(w), 3, 0);
         __syncthreads();
-        if (p.Tm) {
-            for (int idx = tid; idx < CH * 16; idx += NTHR) {
-                const int r = idx >> 4, c4 = idx & 15;
-                if (r < n)
-                    *reinterpret_cast<f32x4 *>(p.Tm + ((ts + r) * p.Hv + hv) * CH + 4 * c4) =
-                        *reinterpret_cast<const f32x4 *>(Tm + r * LDF + 4 * c4);
+#pragma unroll 1
+        for (int h = 0; h < np; ++h) {
+            const int hv = hq * G + r0 + h;
+            const float *T = tile(h);
+            if (p.Tm) {
+                for (int idx = tid; idx < CH * 16; idx += NTHR) {
+                    const int r = idx >> 4, c4 = idx & 15;
+                    if (r < n)
+                        *reinterpret_cast<f32x4 *>(p.Tm + ((ts + r) * p.Hv + hv) * CH + 4 * c4) =
+                            (c4 >> 2) > (r >> 4) ? zero4() : *reinterpret_cast<const f32x4 *>(T + r * LDF + 4 * c4);
+                }
             }
+            // T block for the scan: swizzled planes (rows past the chunk end zero) + scalars
+            write_tblock_f<In>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlockF<In>::BYTES, T, LDF, gam_of(h),
+                               bet_of(h), n, tid, NTHR);
+            // and, for the backward of fp32 inputs, in the layout its kernels copy (plain
+            // 16-byte-chunk order); the bf16 backward reads the blocks above
+            if constexpr (sizeof(In) == 4)
+                if (p.tblk_bwd)
+                    write_tblock<In>(p.tblk_bwd + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, T, LDF,
+                                     gam_of(h), bet_of(h), n, tid, NTHR);
         }
-        // T block for the scan: swizzled planes (rows past the chunk end zero) + scalars
-        write_tblock_f<In>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlockF<In>::BYTES, Tm, LDF, gam, bet, n, tid,
-                           NTHR);
-        // and, for the backward of fp32 inputs, in the layout its kernels copy (plain
-        // 16-byte-chunk order); the bf16 backward reads the blocks above
-        if constexpr (sizeof(In) == 4)
-            if (p.tblk_bwd)
-                write_tblock<In>(p.tblk_bwd + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, Tm, LDF, gam, bet, n,
-                                 tid, NTHR);
-        lds_barrier();  // Tm, A, gam, bet free again; the block's stores drain meanwhile
+        lds_barrier();  // the tiles and gates free again; the blocks' stores drain meanwhile
     }
 }
 
 template <typename In, int KD>
 size_t prep_smem() {
-    const size_t kb = sizeof(In) * CH * (KD + Vec16<In>::n), ab = sizeof(float) * CH * LDF;
-    return (kb > ab ? kb : ab) + sizeof(float) * (CH * LDF + 2 * CH);
+    const size_t kb = sizeof(In) * CH * (KD + Vec16<In>::n), mb = sizeof(float) * CH * LDF;
+    return (kb > mb ? kb : mb) + mb + sizeof(float) * 4 * CH;
 }
 
 template <typename In, int KD>
