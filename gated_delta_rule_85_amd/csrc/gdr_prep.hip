@@ -182,9 +182,10 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
                 const int r = 16 * str[k] + n16, i0 = 16 * sti[k] + 4 * g;
                 const float br = bet[r], gr = gam[r];
                 const f32x4 gi = *reinterpret_cast<const f32x4 *>(gam + i0);
+                // no branch: in a diagonal tile the entries i >= r land in the lower
+                // part of the block, which the substitution overwrites with T
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    if (i0 + jj < r) M[(i0 + jj) * LDF + r] = br * fast_exp(gr - gi[jj]) * sS[k][jj];
+                for (int jj = 0; jj < 4; ++jj) M[(i0 + jj) * LDF + r] = br * fast_exp(gr - gi[jj]) * sS[k][jj];
             }
         }
         __syncthreads();
