@@ -174,8 +174,11 @@ __device__ __forceinline__ void write_tblock(char *blk, const float *T, int ld, 
 }
 
 // The forward's T block (TBlockF) from the same fp32 T and gates (the same
-// rows and blocks written as zero).
-template <typename In>
+// rows and blocks written as zero).  VEC: T is 16-byte aligned and ld a
+// multiple of 4, so each 8-column piece is read as two 16-byte vectors, and
+// every piece is read (rows and blocks that are written as zero included, all
+// inside the 64-row tile) and then selected, without a branch.
+template <typename In, bool VEC = false>
 __device__ __forceinline__ void write_tblock_f(char *blk, const float *T, int ld, const float *gam,
                                                const float *bet, int n, int tid, int nthr) {
     if constexpr (sizeof(In) == 4) {
@@ -187,7 +190,13 @@ __device__ __forceinline__ void write_tblock_f(char *blk, const float *T, int ld
             const int r = idx < 128 ? idx >> 2 : 32 + ((idx - 128) >> 3);
             const int lc = idx < 128 ? idx & 3 : (idx - 128) & 7;
             f32x4 x0 = zero4(), x1 = zero4();
-            if (r < n && ((8 * lc) >> 4) <= (r >> 4)) {
+            const bool ok = r < n && ((8 * lc) >> 4) <= (r >> 4);
+            if constexpr (VEC) {
+                const f32x4 *src = reinterpret_cast<const f32x4 *>(T + r * ld + 8 * lc);
+                const f32x4 a = src[0], b = src[1];
+                x0 = ok ? a : x0;
+                x1 = ok ? b : x1;
+            } else if (ok) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     x0[e] = T[r * ld + 8 * lc + e];

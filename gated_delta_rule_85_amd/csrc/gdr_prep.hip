@@ -29,6 +29,7 @@ namespace gdr {
 namespace {
 
 constexpr int LDF = 68;  // fp32 64x64 tiles in LDS: row pitch (floats)
+static_assert(LDF % 4 == 0, "rows of the tiles are read as 16-byte vectors");
 
 // Each v head's 64 x 64 matrices share one LDS tile M: T (lower triangular) in
 // its lower part with the diagonal, A (strictly lower) transposed in its
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
                 }
             }
             // T block for the scan: swizzled planes (rows past the chunk end zero) + scalars
-            write_tblock_f<In>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlockF<In>::BYTES, T, LDF, gam_of(h),
+            write_tblock_f<In, true>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlockF<In>::BYTES, T, LDF, gam_of(h),
                                bet_of(h), n, tid, NTHR);
             // and, for the backward of fp32 inputs, in the layout its kernels copy (plain
             // 16-byte-chunk order); the bf16 backward reads the blocks above
