@@ -17,8 +17,8 @@
 // MFMA and reused by the H_v/H_q v heads.  The inverse of the unit lower
 // triangular 64x64 matrix is blocked in 16x16 tiles: the four diagonal tiles
 // by forward substitution (one wave per head, one lane per column), the
-// off-diagonal tiles by T_ab = -D_a sum_{m=b}^{a-1} A_am T_mb on fp32 MFMA, one
-// block diagonal at a time.  The v heads are taken two at a time so that the
+// off-diagonal tiles by T_ab = -D_a sum_{m=b}^{a-1} A_am T_mb on fp32 MFMA, block
+// column by block column.  The v heads are taken two at a time so that the
 // one-wave phases (the gates' prefix sum, the substitution) run for both heads
 // at once.
 #include "gdr_kernels.hpp"
@@ -208,13 +208,23 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
             for (int r = 0; r < 16; ++r) Mb[r * LDF + cc] = x[r];
         }
         __syncthreads();
-        // off-diagonal blocks, one block diagonal at a time: 3, 2, 1 blocks per head
-        if (w + 4 * 0 < 3 * np) offdiag_tile(tile(w / 3), w % 3 + 1, w % 3);
-        if (w + 4 < 3 * np) offdiag_tile(M1, (w + 4) % 3 + 1, (w + 4) % 3);
-        __syncthreads();
-        if (w < 2 * np) offdiag_tile(tile(w / 2), w % 2 + 2, w % 2);
-        __syncthreads();
-        if (w < np) offdiag_tile(tile(w), 3, 0);
+        // off-diagonal blocks by block column, with no barrier inside a column: T_ab
+        // needs the diagonal inverses and the blocks T_mb above it in its own column
+        // only.  Wave w takes head w & 1: column 0 (waves 0, 1) or columns 1 and 2
+        // (waves 2, 3); each wave reads back the blocks it wrote (LDS keeps a wave's
+        // accesses in order)
+        if ((w & 1) < np) {
+            float *M = tile(w & 1);
+            if (w < 2) {
+                offdiag_tile(M, 1, 0);
+                offdiag_tile(M, 2, 0);
+                offdiag_tile(M, 3, 0);
+            } else {
+                offdiag_tile(M, 2, 1);
+                offdiag_tile(M, 3, 1);
+                offdiag_tile(M, 3, 2);
+            }
+        }
         __syncthreads();
 #pragma unroll 1
         for (int h = 0; h < np; ++h) {
