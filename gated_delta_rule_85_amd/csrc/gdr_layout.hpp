@@ -173,44 +173,50 @@ __device__ __forceinline__ void write_tblock(char *blk, const float *T, int ld, 
     write_tblock_scalars<TB>(blk, gam, bet, n, tid);
 }
 
+// One 16-byte piece (0 <= idx < TBF_PIECES) of both planes of the forward's
+// T block of bf16 inputs (TBlockF<bf16>), from an fp32 row-major T: pieces 0-127
+// are rows 0-31 (4 each), 128-383 rows 32-63 (8 each).  Rows r >= n and the
+// 16 x 16 blocks above the diagonal are written as zero.  VEC: T is 16-byte
+// aligned and ld a multiple of 4, so the piece is read as two 16-byte vectors,
+// always (inside the 64-row tile) and then selected, without a branch.
+constexpr int TBF_PIECES = 32 * 4 + 32 * 8;
+template <bool VEC>
+__device__ __forceinline__ void write_tblock_f_piece(char *blk, const float *T, int ld, int n, int idx) {
+    using TB = TBlockF<bf16>;
+    const int r = idx < 128 ? idx >> 2 : 32 + ((idx - 128) >> 3);
+    const int lc = idx < 128 ? idx & 3 : (idx - 128) & 7;
+    f32x4 x0 = zero4(), x1 = zero4();
+    const bool ok = r < n && ((8 * lc) >> 4) <= (r >> 4);
+    if constexpr (VEC) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(T + r * ld + 8 * lc);
+        const f32x4 a = src[0], b = src[1];
+        x0 = ok ? a : x0;
+        x1 = ok ? b : x1;
+    } else if (ok) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x0[e] = T[r * ld + 8 * lc + e];
+            x1[e] = T[r * ld + 8 * lc + 4 + e];
+        }
+    }
+    bf16x4 h0, l0, h1, l1;
+    split4(x0, h0, l0);
+    split4(x1, h1, l1);
+    const int off = TB::off(r, 16 * lc);
+    *reinterpret_cast<bf16x8 *>(blk + off) = cat(h0, h1);
+    *reinterpret_cast<bf16x8 *>(blk + TB::PLANE + off) = cat(l0, l1);
+}
+
 // The forward's T block (TBlockF) from the same fp32 T and gates (the same
-// rows and blocks written as zero).  VEC: T is 16-byte aligned and ld a
-// multiple of 4, so each 8-column piece is read as two 16-byte vectors, and
-// every piece is read (rows and blocks that are written as zero included, all
-// inside the 64-row tile) and then selected, without a branch.
+// rows and blocks written as zero; VEC as in write_tblock_f_piece).
 template <typename In, bool VEC = false>
 __device__ __forceinline__ void write_tblock_f(char *blk, const float *T, int ld, const float *gam,
                                                const float *bet, int n, int tid, int nthr) {
     if constexpr (sizeof(In) == 4) {
         write_tblock<float, SwzTF<float>>(blk, T, ld, gam, bet, n, tid, nthr);
     } else {
-        using TB = TBlockF<bf16>;
-        // 16-byte chunks of a plane: 4 in each of rows 0-31, 8 in each of rows 32-63
-        for (int idx = tid; idx < 32 * 4 + 32 * 8; idx += nthr) {
-            const int r = idx < 128 ? idx >> 2 : 32 + ((idx - 128) >> 3);
-            const int lc = idx < 128 ? idx & 3 : (idx - 128) & 7;
-            f32x4 x0 = zero4(), x1 = zero4();
-            const bool ok = r < n && ((8 * lc) >> 4) <= (r >> 4);
-            if constexpr (VEC) {
-                const f32x4 *src = reinterpret_cast<const f32x4 *>(T + r * ld + 8 * lc);
-                const f32x4 a = src[0], b = src[1];
-                x0 = ok ? a : x0;
-                x1 = ok ? b : x1;
-            } else if (ok) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x0[e] = T[r * ld + 8 * lc + e];
-                    x1[e] = T[r * ld + 8 * lc + 4 + e];
-                }
-            }
-            bf16x4 h0, l0, h1, l1;
-            split4(x0, h0, l0);
-            split4(x1, h1, l1);
-            const int off = TB::off(r, 16 * lc);
-            *reinterpret_cast<bf16x8 *>(blk + off) = cat(h0, h1);
-            *reinterpret_cast<bf16x8 *>(blk + TB::PLANE + off) = cat(l0, l1);
-        }
-        write_tblock_scalars<TB>(blk, gam, bet, n, tid);
+        for (int idx = tid; idx < TBF_PIECES; idx += nthr) write_tblock_f_piece<VEC>(blk, T, ld, n, idx);
+        write_tblock_scalars<TBlockF<bf16>>(blk, gam, bet, n, tid);
     }
 }
 

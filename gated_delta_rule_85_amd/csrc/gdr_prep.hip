@@ -226,6 +226,19 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
             }
         }
         __syncthreads();
+        if constexpr (sizeof(In) == 2) {
+            // the T blocks of the pair's heads as one list of pieces (an even share per
+            // thread), then the scalars, 64 threads per head
+            char *blk0 = p.tblk + ((int64_t)gid * p.Hv + hq * G + r0) * TBlockF<In>::BYTES;
+            for (int idx = tid; idx < np * TBF_PIECES; idx += NTHR) {
+                const int h = idx >= TBF_PIECES;
+                write_tblock_f_piece<true>(blk0 + h * TBlockF<In>::BYTES, tile(h), LDF, n, idx - h * TBF_PIECES);
+            }
+            if (tid < np * CH) {
+                const int h = tid >> 6;
+                write_tblock_scalars<TBlockF<In>>(blk0 + h * TBlockF<In>::BYTES, gam_of(h), bet_of(h), n, tid & 63);
+            }
+        }
 #pragma unroll 1
         for (int h = 0; h < np; ++h) {
             const int hv = hq * G + r0 + h;
@@ -238,15 +251,17 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
                             (c4 >> 2) > (r >> 4) ? zero4() : *reinterpret_cast<const f32x4 *>(T + r * LDF + 4 * c4);
                 }
             }
-            // T block for the scan: swizzled planes (rows past the chunk end zero) + scalars
-            write_tblock_f<In, true>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlockF<In>::BYTES, T, LDF, gam_of(h),
-                               bet_of(h), n, tid, NTHR);
-            // and, for the backward of fp32 inputs, in the layout its kernels copy (plain
-            // 16-byte-chunk order); the bf16 backward reads the blocks above
-            if constexpr (sizeof(In) == 4)
+            if constexpr (sizeof(In) == 4) {
+                // T block for the scan: fp32 rows, swizzled (rows past the chunk end zero)
+                // + scalars, and for the backward of fp32 inputs the same in the layout its
+                // kernels copy (plain 16-byte-chunk order); the bf16 backward reads the
+                // blocks written above
+                write_tblock_f<In>(p.tblk + ((int64_t)gid * p.Hv + hv) * TBlockF<In>::BYTES, T, LDF, gam_of(h),
+                                   bet_of(h), n, tid, NTHR);
                 if (p.tblk_bwd)
                     write_tblock<In>(p.tblk_bwd + ((int64_t)gid * p.Hv + hv) * TBlock<In>::BYTES, T, LDF,
                                      gam_of(h), bet_of(h), n, tid, NTHR);
+            }
         }
         lds_barrier();  // the tiles and gates free again; the blocks' stores drain meanwhile
     }
