@@ -24,10 +24,11 @@ using namespace bwd;
 //   dh  = e_last dh' + Q^T diag(s e) dO - K^T diag(beta e) dX.
 // A operand of M^T for a K x V tile in the contiguous-slot key order: row n is
 // key c0 + 8 (n / 4) + n % 4, k = tokens 32 ip + 4g + j and 32 ip + 16 + 4g + j
-// (the accumulator order of the token tiles it multiplies)
+// (the accumulator order of the token tiles it multiplies).  M is a K or Q tile
+// of this kernel, swizzled with KeyBK (gdr_layout.hpp)
 template <int ROWB>
 __device__ __forceinline__ OpX kt_keys(const char *M, int c0, int ip) {
-    using S = Swz<ROWB>;
+    using S = Swz<ROWB, KeyBK>;
     const int n = ln16(), g = lg4();
     const int row = 32 * ip + 4 * g + (n >> 2), byte = 2 * (c0 + 8 * (n & 3));
     OpX r;
@@ -53,8 +54,8 @@ __device__ __forceinline__ void score_tile_t(int t, char *Pt, const char *Qs, co
     f32x4 acc = zero4();
 #pragma unroll
     for (int dp = 0; dp < DP; ++dp)
-        acc = mma(acc, frag<bf16, KROW>(Qs, 16 * ti + n16, (32 * dp + 4 * g) * 2),
-                  frag<bf16, KROW>(Ks, 16 * tr + n16, (32 * dp + 4 * g) * 2));
+        acc = mma(acc, frag<bf16, KROW, KeyBK>(Qs, 16 * ti + n16, (32 * dp + 4 * g) * 2),
+                  frag<bf16, KROW, KeyBK>(Ks, 16 * tr + n16, (32 * dp + 4 * g) * 2));
     const int r = 16 * tr + n16;
     const float gr = gam[r];
     f32x4 v;
@@ -135,13 +136,13 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))
             {
                 OpX kf[2][4];
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) kf[0][rt] = frag8<bf16, Swz<KROW>>(Ks, 16 * rt + n16, 8 * g * 2);
+                for (int rt = 0; rt < 4; ++rt) kf[0][rt] = frag8<bf16, Swz<KROW, KeyBK>>(Ks, 16 * rt + n16, 8 * g * 2);
 #pragma unroll
                 for (int dp = 0; dp < DP; ++dp) {
                     if (dp + 1 < DP)
 #pragma unroll
                         for (int rt = 0; rt < 4; ++rt)
-                            kf[(dp + 1) & 1][rt] = frag8<bf16, Swz<KROW>>(Ks, 16 * rt + n16, (32 * (dp + 1) + 8 * g) * 2);
+                            kf[(dp + 1) & 1][rt] = frag8<bf16, Swz<KROW, KeyBK>>(Ks, 16 * rt + n16, (32 * (dp + 1) + 8 * g) * 2);
                     __builtin_amdgcn_sched_barrier(0);
                     const OpS hb = Ops<bf16>::split(dh[2 * dp], dh[2 * dp + 1]);
 #pragma unroll
@@ -254,9 +255,9 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))
             const int64_t ts = bos + (int64_t)c * CH;
             const int n = (int)min<int64_t>(CH, eos - ts);
             if (part == 0) {
-                copy_rows<KROW>(K_, kp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, iw, NCP);
+                copy_rows<KROW, KeyBK>(K_, kp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, iw, NCP);
             } else {
-                copy_rows<KROW>(Q_, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, iw, NCP);
+                copy_rows<KROW, KeyBK>(Q_, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, iw, NCP);
                 copy_rows<DROW>(D_, dop + ((ts * p.Hv + hv) * p.V + vt * 64) * 2, p.Hv * p.V * 2, n - 1, iw, NCP);
                 copy_bytes(T_, p.tblk + ((int64_t)(cb + c) * p.Hv + hv) * TB::BYTES, TB::BYTES, iw, NCP);
             }

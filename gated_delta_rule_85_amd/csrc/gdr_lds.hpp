@@ -48,9 +48,9 @@ __device__ __forceinline__ bf16x4 lds_tr4(const char *p) {
 // Copy the 64 rows of a row-major global tile (row r at src + r * stride,
 // ROWB bytes each) into a swizzled LDS tile, rows past nm1 repeating row nm1.
 // The 1 KB pieces are spread over nw waves; this wave is number wi of them.
-template <int ROWB>
+template <int ROWB, typename KEY = typename DefaultKey<ROWB>::type>
 __device__ __forceinline__ void copy_rows(char *dst, const char *src, int stride, int nm1, int wi, int nw) {
-    using S = Swz<ROWB>;
+    using S = Swz<ROWB, KEY>;
     constexpr int PIECES = CH * ROWB / 1024;
     const int l = lane_id();
     for (int i = wi; i < PIECES; i += nw) {
@@ -65,9 +65,9 @@ __device__ __forceinline__ void copy_bytes(char *dst, const char *src, int bytes
 }
 
 // A-operand fragment rows (row0 + lane16, bytes off..off+7 and off+32..) of a swizzled tile
-template <typename In, int ROWB>
+template <typename In, int ROWB, typename KEY = typename DefaultKey<ROWB>::type>
 __device__ __forceinline__ typename Ops<In>::X frag(const char *tile, int row, int byte) {
-    using S = Swz<ROWB>;
+    using S = Swz<ROWB, KEY>;
     return Ops<In>::load(reinterpret_cast<const In *>(tile + S::off(row, byte)),
                          reinterpret_cast<const In *>(tile + S::off(row, byte + 16 * sizeof(In))));
 }

@@ -113,6 +113,25 @@ int main() {
                const int rt = i & 3, ip = (i >> 2) <= rt / 2 ? (i >> 2) : 0;
                return TF::off(slot_row(rt, n), (32 * ip + 8 * g) * 2); }));
 
+    // ---- reverse scan (bf16, K = 128): K and Q tiles under KeyBK
+    using SB = Swz<256, KeyBK>;
+    // transposing reads of K^T, Q^T: rows 32 ip + 4 g + n / 4 (+16), keys c0 + 8 (n % 4)
+    // (all lanes in one 8-byte half of their 16-byte column: 2-way at best)
+    printf("bwd_KT_tr %.2f\n", worst(32, false, [](int i, int n, int g) {
+               const int dt = i & 7, ip = (i >> 3) & 1, h = (i >> 4) & 1;
+               const int c0 = 32 * (dt >> 1) + 4 * (dt & 1);
+               return SB::off(32 * ip + 4 * g + (n >> 2) + 16 * h, 2 * (c0 + 8 * (n & 3))); }));
+    printf("bwd_KT_tr_rowkey %.2f\n", worst(32, false, [](int i, int n, int g) {
+               const int dt = i & 7, ip = (i >> 3) & 1, h = (i >> 4) & 1;
+               const int c0 = 32 * (dt >> 1) + 4 * (dt & 1);
+               return Swz<256>::off(32 * ip + 4 * g + (n >> 2) + 16 * h, 2 * (c0 + 8 * (n & 3))); }));
+    // K rows for K dh': 16-byte reads of rows 16 rt + n at keys 32 dp + 8 g
+    printf("bwd_K_rows16 %.2f\n", worst(16, true, [](int i, int n, int g) {
+               return SB::off(16 * (i & 3) + n, 2 * (32 * (i >> 2) + 8 * g)); }));
+    // score tiles: 8-byte reads of rows 16 t + n at keys 32 dp + 4 g and 16 more
+    printf("bwd_KQ_rows8 %.2f\n", worst(32, false, [](int i, int n, int g) {
+               return SB::off(16 * (i & 3) + n, 2 * (32 * ((i >> 2) & 3) + 4 * g) + 32 * ((i >> 4) & 1)); }));
+
     // ---- every row's chunk map is a permutation (no two logical chunks share a slot)
     bool ok = true;
     auto perm = [&](auto S, int rows) {
@@ -128,6 +147,7 @@ int main() {
     perm(SP{}, 64);
     perm(S128{}, 64);
     perm(Swz<256>{}, 64);
+    perm(SB{}, 64);
     {
         std::set<int> seen;  // compact T block: every (row, column chunk) at its own 16 bytes, inside a plane
         for (int r = 0; r < 64; ++r)

@@ -6,8 +6,9 @@ swizzled tile under the bank model measured on gfx950 with an LDS probe (LDS
 cycles per instruction from SQ_LDS_IDX_ACTIVE / SQ_INSTS_LDS): 16-byte reads
 in 16-lane passes that pair lanes 0-3/12-15 of one 16-lane group with lanes
 4-11 of its neighbour, 8-byte accesses in 32-lane passes.  Every read must be
-conflict-free except the transposing K^T read of the forward scan, whose 32
-lanes all read the same half of their 16-byte columns (2-way by construction).
+conflict-free except the transposing K^T reads of the forward scan and the
+reverse scan's K^T and Q^T reads, whose 32 lanes all read the same half of
+their 16-byte columns (2-way by construction).
 """
 import os
 import shutil
@@ -37,7 +38,8 @@ def layout_costs(tmp_path_factory):
 
 
 CONFLICT_FREE = ["fwd_Kh", "fwd_KQ_rows", "fwd_T", "fwd_P_read", "fwd_P_write", "fwd_V_tr",
-                 "bwd_rows_b64", "bwd_tr", "bwd_put4", "bwd_T_rows", "bwd_T_tr", "bwd_states_T"]
+                 "bwd_rows_b64", "bwd_tr", "bwd_put4", "bwd_T_rows", "bwd_T_tr", "bwd_states_T",
+                 "bwd_K_rows16", "bwd_KQ_rows8"]
 
 
 @pytest.mark.parametrize("name", CONFLICT_FREE)
@@ -47,6 +49,12 @@ def test_operand_reads_are_conflict_free(layout_costs, name):
 
 def test_transposed_key_read_is_two_way(layout_costs):
     assert float(layout_costs["fwd_KT_tr"]) == 2.0
+
+
+def test_reverse_scan_transposed_key_reads_are_two_way(layout_costs):
+    # the reverse scan's K^T and Q^T reads: 2-way under its key, 4-way under the row key
+    assert float(layout_costs["bwd_KT_tr"]) == 2.0
+    assert float(layout_costs["bwd_KT_tr_rowkey"]) == 4.0
 
 
 def test_chunk_maps_are_permutations(layout_costs):
