@@ -146,11 +146,13 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
         sti[k] = t - str[k] * (str[k] + 1) / 2;
         sS[k] = zero4();
         if (t < 10) {
+            // operand slot j of lane group g is k = 8 g + j in each 32-deep block (both
+            // operands alike): 8 consecutive elements of a row per lane
 #pragma unroll
             for (int dp = 0; dp < KD / 32; ++dp) {
-                const In *ar = Ks + (16 * sti[k] + n16) * LDK + 32 * dp + 4 * g;
-                const In *br = Ks + (16 * str[k] + n16) * LDK + 32 * dp + 4 * g;
-                sS[k] = mma(sS[k], O::load(ar, ar + 16), O::load(br, br + 16));
+                const In *ar = Ks + (16 * sti[k] + n16) * LDK + 32 * dp + 8 * g;
+                const In *br = Ks + (16 * str[k] + n16) * LDK + 32 * dp + 8 * g;
+                sS[k] = mma(sS[k], O::load(ar, ar + 4), O::load(br, br + 4));
             }
         }
     }
@@ -193,16 +195,23 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
         if (w < np) {
             // diagonal tiles of head w: lane = (tile b, column cc); forward substitution,
             // then column cc of T_bb over the (no longer needed) block of A
+            // (right-looking: once x_i is final, row i of the transposed store, A's
+            // column i, is read as 16-byte vectors and taken off the rows below)
             float *M = tile(w);
             const int b = l >> 4, cc = l & 15;
             float *Mb = M + 16 * b * LDF + 16 * b;
             float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = (r == cc) ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) x[r] = (r == cc) ? 1.f : 0.f;
 #pragma unroll
-                for (int i = 0; i < r; ++i) s -= Mb[i * LDF + r] * x[i];
-                x[r] = s;
+            for (int i = 0; i < 15; ++i) {
+#pragma unroll
+                for (int q = (i + 1) / 4; q < 4; ++q) {
+                    const f32x4 a = *reinterpret_cast<const f32x4 *>(Mb + i * LDF + 4 * q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * q + e > i) x[4 * q + e] -= a[e] * x[i];
+                }
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) Mb[r * LDF + cc] = x[r];
