@@ -70,8 +70,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
     const float *gam = sc, *eg = sc + CH, *rr = sc + 2 * CH, *bet = sc + 3 * CH;
     const int ci = 16 * w + n16;  // this lane's column in a 64-wide strip
 
-    copy_tile<KROW>(Ks, kp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
-    copy_tile<KROW>(Qs, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
+    copy_tile<KROW, KeyBK>(Ks, kp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
+    copy_tile<KROW, KeyBK>(Qs, qp + (ts * p.Hq + hq) * KROW, p.Hq * KROW, n - 1, w);
     zero_lower_pt(Pt);
     f32x4 dqt[TD][4], dkt[TD][4];  // dq, dk tiles (key tile w + 4 s, token tile tr)
 #pragma unroll
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
                     const OpS db = frag_s<128>(B[1], PPL, 16 * w + n16, (32 * ip + 4 * g) * 2);
 #pragma unroll
                     for (int rt = 0; rt < 4; ++rt) {
-                        const OpX kf = frag<bf16, KROW>(Ks, 16 * rt + n16, (64 * hf + 32 * ip + 4 * g) * 2);
+                        const OpX kf = frag<bf16, KROW, KeyBK>(Ks, 16 * rt + n16, (64 * hf + 32 * ip + 4 * g) * 2);
                         kh[rt] = mma(kh[rt], kf, hb);
                         kd[rt] = mma(kd[rt], kf, db);
                     }
@@ -264,9 +264,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
                     dqt[s][tr] += (p.scale * er) * aQ[tr];
                     dkt[s][tr] += rr[r] * aKa[tr] - (bet[r] * er) * aKe[tr];
                     const f32x4 q4 = __builtin_convertvector(
-                        *reinterpret_cast<const bf16x4 *>(Qs + Swz<KROW>::off(r, 2 * (16 * td + 4 * g))), f32x4);
+                        *reinterpret_cast<const bf16x4 *>(Qs + Swz<KROW, KeyBK>::off(r, 2 * (16 * td + 4 * g))), f32x4);
                     const f32x4 k4 = __builtin_convertvector(
-                        *reinterpret_cast<const bf16x4 *>(Ks + Swz<KROW>::off(r, 2 * (16 * td + 4 * g))), f32x4);
+                        *reinterpret_cast<const bf16x4 *>(Ks + Swz<KROW, KeyBK>::off(r, 2 * (16 * td + 4 * g))), f32x4);
                     const f32x4 a = q4 * aQ[tr], b = k4 * aKe[tr], cc = k4 * aKa[tr];
                     rsum[0][tr] += a[0] + a[1] + a[2] + a[3];
                     rsum[1][tr] += b[0] + b[1] + b[2] + b[3];
@@ -299,8 +299,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
             f32x4 sS = zero4();  // S[r][i] (S = K K^T is symmetric)
 #pragma unroll
             for (int dp = 0; dp < DP; ++dp)
-                sS = mma(sS, frag<bf16, KROW>(Ks, 16 * w + n16, (32 * dp + 4 * g) * 2),
-                         frag<bf16, KROW>(Ks, r, (32 * dp + 4 * g) * 2));
+                sS = mma(sS, frag<bf16, KROW, KeyBK>(Ks, 16 * w + n16, (32 * dp + 4 * g) * 2),
+                         frag<bf16, KROW, KeyBK>(Ks, r, (32 * dp + 4 * g) * 2));
             // P[r][i] = P^T[i][r]: four rows of P^T at column r (only i <= r is stored)
             const f32x4 pr = rows4<bf16, 128>(Pt, 16 * w, 16 * tr) + rows4<bf16, 128>(Pt + PPL, 16 * w, 16 * tr);
             const float gr = gam[r], br = bet[r];
@@ -346,8 +346,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
 #pragma unroll
         for (int s = 0; s < TD; ++s) {
             const int td = w + 4 * s;
-            const OpX k0 = kt_operand<bf16, KROW>(Ks, 16 * td, 0), k1 = kt_operand<bf16, KROW>(Ks, 16 * td, 1);
-            const OpX q0 = kt_operand<bf16, KROW>(Qs, 16 * td, 0), q1 = kt_operand<bf16, KROW>(Qs, 16 * td, 1);
+            const OpX k0 = kt_operand<bf16, KROW, KeyBK>(Ks, 16 * td, 0), k1 = kt_operand<bf16, KROW, KeyBK>(Ks, 16 * td, 1);
+            const OpX q0 = kt_operand<bf16, KROW, KeyBK>(Qs, 16 * td, 0), q1 = kt_operand<bf16, KROW, KeyBK>(Qs, 16 * td, 1);
 #pragma unroll
             for (int tr = 0; tr < 4; ++tr) {
 #pragma unroll

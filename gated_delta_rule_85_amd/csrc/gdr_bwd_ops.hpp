@@ -51,9 +51,9 @@ __device__ __forceinline__ OpS kt_s(const char *hi, int plane, int c0, int ip) {
     return kt_s_in<Swz<ROWB>>(hi, plane, c0, ip);
 }
 
-template <int ROWB>
+template <int ROWB, typename KEY = typename DefaultKey<ROWB>::type>
 __device__ __forceinline__ void copy_tile(char *dst, const char *src, int stride, int nm1, int w) {
-    copy_rows<ROWB>(dst, src, stride, nm1, w, NTHR / 64);
+    copy_rows<ROWB, KEY>(dst, src, stride, nm1, w, NTHR / 64);
 }
 __device__ __forceinline__ void copy_flat(char *dst, const char *src, int bytes, int w) {
     copy_bytes(dst, src, bytes, w, NTHR / 64);
@@ -82,8 +82,8 @@ __device__ __forceinline__ void scores_t(char *Pt, const char *Qs, const char *K
         f32x4 acc = zero4();
 #pragma unroll
         for (int dp = 0; dp < DP; ++dp)
-            acc = mma(acc, frag<bf16, KROW>(Qs, 16 * ti + n16, (32 * dp + 4 * g) * 2),
-                      frag<bf16, KROW>(Ks, 16 * tr + n16, (32 * dp + 4 * g) * 2));
+            acc = mma(acc, frag<bf16, KROW, KeyBK>(Qs, 16 * ti + n16, (32 * dp + 4 * g) * 2),
+                      frag<bf16, KROW, KeyBK>(Ks, 16 * tr + n16, (32 * dp + 4 * g) * 2));
         const int r = 16 * tr + n16;
         const float gr = gam[r];
         f32x4 v;

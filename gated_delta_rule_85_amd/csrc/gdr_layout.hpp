@@ -64,12 +64,14 @@ struct KeyP {
 struct KeyB {
     static __host__ __device__ __forceinline__ int key(int r) { return (r & 6) ^ (((r >> 3) & 1) * 5); }
 };
-// K and Q tiles of the reverse scan (256-byte rows): the row index with key
-// bits 2 and 3 flipped on odd rows.  Its transposing 8-byte reads of K^T and
-// Q^T take rows 8-row groups at four consecutive 16-byte columns, all in the
-// same 8-byte half; this key spreads them over all 16 columns, twice each (the
-// floor for reads confined to one half; the plain row key gives 4-way), and
-// keeps its 16-byte and 8-byte reads of 16 consecutive rows conflict-free.
+// K and Q tiles of the backward's bf16 kernels (256-byte rows): the row index
+// with key bits 2 and 3 flipped on odd rows.  The reverse scan's transposing
+// 8-byte reads of K^T and Q^T take 8-row groups at four consecutive 16-byte
+// columns, all in the same 8-byte half; this key spreads them over all 16
+// columns, twice each (the floor for reads confined to one half; the plain row
+// key gives 4-way).  The chunk-local kernel's transposing reads (two 8-byte
+// halves of two columns) become conflict-free (2-way under the plain key).
+// The 16-byte and 8-byte reads of 16 consecutive rows stay conflict-free.
 struct KeyBK {
     static __host__ __device__ __forceinline__ int key(int r) { return r ^ ((r & 1) * 12); }
 };

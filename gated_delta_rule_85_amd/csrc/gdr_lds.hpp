@@ -91,11 +91,11 @@ __device__ __forceinline__ f32x4 rows4(const char *tile, int r0, int c0) {
 }
 
 // A operand of K^T: rows = key dims d0 + lane16, k = tokens 32 ip .. 32 ip + 31
-template <typename In, int ROWB>
+template <typename In, int ROWB, typename KEY = typename DefaultKey<ROWB>::type>
 __device__ __forceinline__ typename Ops<In>::X kt_operand(const char *Ks, int d0, int ip) {
     typename Ops<In>::X r;
     if constexpr (sizeof(In) == 2) {
-        using S = Swz<ROWB>;
+        using S = Swz<ROWB, KEY>;
         const int n = ln16(), g = lg4();
         const int row = 32 * ip + 4 * g + (n >> 2), byte = 2 * (d0 + 4 * (n & 3));
         r.b0 = lds_tr4(Ks + S::off(row, byte));

@@ -132,6 +132,14 @@ int main() {
     printf("bwd_KQ_rows8 %.2f\n", worst(32, false, [](int i, int n, int g) {
                return SB::off(16 * (i & 3) + n, 2 * (32 * ((i >> 2) & 3) + 4 * g) + 32 * ((i >> 4) & 1)); }));
 
+    // chunk-local backward: transposing reads of K^T, Q^T at rows 32 ip + 4 g + n / 4
+    // (+16), keys 16 td + 4 (n % 4), and 8-byte reads of rows 16 tr + n at keys 16 td + 4 g
+    printf("bwd_local_KT_tr %.2f\n", worst(32, false, [](int i, int n, int g) {
+               const int td = i & 7, ip = (i >> 3) & 1, h = (i >> 4) & 1;
+               return SB::off(32 * ip + 4 * g + (n >> 2) + 16 * h, 2 * (16 * td + 4 * (n & 3))); }));
+    printf("bwd_local_KQ_rows4 %.2f\n", worst(32, false, [](int i, int n, int g) {
+               return SB::off(16 * (i & 3) + n, 2 * (16 * (i >> 2) + 4 * g)); }));
+
     // ---- every row's chunk map is a permutation (no two logical chunks share a slot)
     bool ok = true;
     auto perm = [&](auto S, int rows) {

@@ -8,7 +8,8 @@ in 16-lane passes that pair lanes 0-3/12-15 of one 16-lane group with lanes
 4-11 of its neighbour, 8-byte accesses in 32-lane passes.  Every read must be
 conflict-free except the transposing K^T reads of the forward scan and the
 reverse scan's K^T and Q^T reads, whose 32 lanes all read the same half of
-their 16-byte columns (2-way by construction).
+their 16-byte columns (2-way by construction); the chunk-local backward's
+transposing reads, which use both halves, are conflict-free.
 """
 import os
 import shutil
@@ -39,7 +40,7 @@ def layout_costs(tmp_path_factory):
 
 CONFLICT_FREE = ["fwd_Kh", "fwd_KQ_rows", "fwd_T", "fwd_P_read", "fwd_P_write", "fwd_V_tr",
                  "bwd_rows_b64", "bwd_tr", "bwd_put4", "bwd_T_rows", "bwd_T_tr", "bwd_states_T",
-                 "bwd_K_rows16", "bwd_KQ_rows8"]
+                 "bwd_K_rows16", "bwd_KQ_rows8", "bwd_local_KT_tr", "bwd_local_KQ_rows4"]
 
 
 @pytest.mark.parametrize("name", CONFLICT_FREE)
