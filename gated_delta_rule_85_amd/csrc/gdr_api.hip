@@ -111,6 +111,10 @@ int plan_fwd(const gdr_fwd_args *a, FwdPlan &pl, int64_t slots = 0) {
     pl.tokens = a->B * a->T;
     pl.nct = cdiv(a->T, GDR_CHUNK);
     pl.nt_ub = varlen ? pl.nct + pl.n_seq : a->B * pl.nct;
+    // the chunk-parallel kernels run one-dimensional grids of (chunk, q/k head)
+    // workgroups of 256 threads (the chunks rounded up to a multiple of 8), at most
+    // 2^32 work-items
+    if ((pl.nt_ub + 7) * a->H_q >= (int64_t)1 << 24) return GDR_EINVAL;
     size_t off = 0;
     pl.off_chunk = off;
     off += seq_table_bytes(varlen, pl.n_seq);
@@ -200,6 +204,10 @@ int plan_bwd(const gdr_bwd_args *a, BwdPlan &pl, int64_t slots = 0) {
     pl.tokens = a->B * a->T;
     pl.nct = cdiv(a->T, GDR_CHUNK);
     pl.nt_ub = varlen ? pl.nct + pl.n_seq : a->B * pl.nct;
+    // the chunk-parallel kernels run one-dimensional grids of (chunk, q/k head)
+    // workgroups of 256 threads (the chunks rounded up to a multiple of 8), at most
+    // 2^32 work-items
+    if ((pl.nt_ub + 7) * a->H_q >= (int64_t)1 << 24) return GDR_EINVAL;
     const size_t nb = (size_t)(pl.nt_ub * a->H_v);
     size_t off = 0;
     pl.off_chunk = off;

@@ -52,7 +52,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
     __shared__ float cs[2][CH];
     __shared__ float red[4];
 
-    const int gid = blockIdx.x, hq = blockIdx.y;
+    // the q/k head runs fastest over the workgroups (neighbours read adjacent pieces
+    // of the same q, k, v and dO rows)
+    const int gid = blockIdx.x / p.Hq, hq = blockIdx.x % p.Hq;
     int j, c;
     if (!p.sm.locate(gid, j, c)) return;
     int64_t bos, eos;
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
 }  // namespace
 
 hipError_t launch_bwd_local_bf16(Dt gt, int K, const BwdParams &p, int n_chunks_ub, hipStream_t s) {
-    const dim3 grid(n_chunks_ub, p.Hq);
+    const dim3 grid(n_chunks_ub * p.Hq);  // (chunk, q/k head), the head fastest
     if (gt == Dt::BF16) {
         if (K == 128)
             launch_k((bwd_local_bf16<bf16, 128>), grid, dim3(NTHR), 0, s, p);

@@ -86,7 +86,13 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const PrepParams p) {
     auto gam_of = [&](int h) { return gb + 2 * CH * h; };
     auto bet_of = [&](int h) { return gb + 2 * CH * h + CH; };
 
-    const int gid = blockIdx.x, hq = blockIdx.y;
+    // Workgroup b runs on XCD b % 8.  The chunks are dealt to the XCDs in turn, so that
+    // the log-gate and beta rows of a chunk, which all its q/k heads read, are fetched
+    // into one L2; within an XCD the q/k head runs fastest, so that neighbours read
+    // adjacent 256-byte pieces of the same key rows and write adjacent T blocks.
+    // Chunks past the last (the grid rounds them up to a multiple of 8) have no work.
+    const int slot = blockIdx.x >> 3;
+    const int hq = slot % p.Hq, gid = (slot / p.Hq) * 8 + (blockIdx.x & 7);
     int j, c;
     if (!p.sm.locate(gid, j, c)) return;
     int64_t bos, eos;
@@ -289,7 +295,7 @@ hipError_t launch_prep_t(const PrepParams &p, int n_chunks_ub, hipStream_t s) {
         reinterpret_cast<const void *>(&prep_kernel<In, KD>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     (void)attr;  // a refusal shows up as a launch error below
-    dim3 grid(n_chunks_ub, p.Hq);
+    dim3 grid((n_chunks_ub + 7) / 8 * 8 * p.Hq);  // (chunk, q/k head)
     launch_k((prep_kernel<In, KD>), grid, dim3(NTHR), smem, s, p);
     return hipGetLastError();
 }

@@ -137,6 +137,18 @@ def test_segment_count_is_bounded(L):
     assert rc_ws(L, fwd_args(L, cp_mode=L.CP_EXACT, **dict(many, cp_segment_chunks=64)))[0] == 0
 
 
+def test_chunk_grid_is_bounded(L):
+    """Prep and the chunk-local backward launch one workgroup of 256 threads per
+    (chunk, q/k head) in a one-dimensional grid of at most 2^32 work-items; the plan
+    refuses shapes past it instead of launching a wrapped grid."""
+    big = dict(B=1, T=1 << 27, H_v=8)  # 2^21 chunks
+    n = ctypes.c_size_t(0)
+    assert rc_ws(L, fwd_args(L, H_q=8, **big))[0] == L.EINVAL  # 2^24 workgroups
+    assert L.lib.gdr_bwd_workspace(ctypes.byref(bwd_args(L, H_q=8, **big)), ctypes.byref(n)) == L.EINVAL
+    assert rc_ws(L, fwd_args(L, H_q=4, cp_mode=L.CP_OFF, **big))[0] == 0
+    assert L.lib.gdr_bwd_workspace(ctypes.byref(bwd_args(L, H_q=4, cp_mode=L.CP_OFF, **big)), ctypes.byref(n)) == 0
+
+
 def test_fwd_host_errors_before_any_launch(L):
     a = fwd_args(L)  # all pointers null
     assert L.lib.gdr_fwd(ctypes.byref(a), None) == L.EINVAL
