@@ -10,9 +10,12 @@ breakdown passes (K steps per stage, handing the library only that stage's
 two HIP events: kernel_ms and the dominant kernel; one more pass with every
 event: breakdown_step_ms), then K timed steps between stream
 synchronisations, in which only the dominant kernel's two events are handed
-over.  The library binds a stage's events to its kernel launches, so they
-time the kernels themselves; a stage that launches nothing records both on
-the stream, which costs it a few microseconds.  The dominant kernel's average
+over.  The library binds a stage's events to its kernel launches.  The start
+event is taken when the stream reaches the stage's first launch, so a stage's
+time also holds the gap before that kernel starts (about 2-5 microseconds on
+MI355X; rocprofv3's kernel statistics give the kernels' own durations); a
+stage that launches nothing records both on the stream, which costs it a few
+microseconds.  The dominant kernel's average
 duration over the timed steps gives the roofline entry.  The fp64 CPU oracle is timed on a bounded
 sample of the same workload for the cpu_baseline entry.
 
