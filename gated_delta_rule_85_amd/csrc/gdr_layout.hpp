@@ -214,8 +214,9 @@ __device__ __forceinline__ void write_tblock_f_piece(char *blk, const float *T, 
     split4(x0, h0, l0);
     split4(x1, h1, l1);
     const int off = TB::off(r, 16 * lc);
-    *reinterpret_cast<bf16x8 *>(blk + off) = cat(h0, h1);
-    *reinterpret_cast<bf16x8 *>(blk + TB::PLANE + off) = cat(l0, l1);
+    // nontemporal: the scan reads the block from another workgroup, after this kernel
+    __builtin_nontemporal_store(cat(h0, h1), reinterpret_cast<bf16x8 *>(blk + off));
+    __builtin_nontemporal_store(cat(l0, l1), reinterpret_cast<bf16x8 *>(blk + TB::PLANE + off));
 }
 
 // The forward's T block (TBlockF) from the same fp32 T and gates (the same

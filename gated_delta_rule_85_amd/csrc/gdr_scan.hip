@@ -73,13 +73,17 @@ template <typename In, int KD, bool FULLT = false> struct Cfg {
     static constexpr int DT = KD / 16, DP = KD / 32;
 };
 
+// o is written with nontemporal stores: nothing in the kernel reads it back, and
+// lines streamed past L2 leave less to write back when the kernel ends
 template <typename T> struct OutVec;
 template <> struct OutVec<float> {
-    static __device__ __forceinline__ void put(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
+    static __device__ __forceinline__ void put(float *p, f32x4 x) {
+        __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p));
+    }
 };
 template <> struct OutVec<bf16> {
     static __device__ __forceinline__ void put(bf16 *p, f32x4 x) {
-        *reinterpret_cast<bf16x4 *>(p) = __builtin_convertvector(x, bf16x4);
+        __builtin_nontemporal_store(__builtin_convertvector(x, bf16x4), reinterpret_cast<bf16x4 *>(p));
     }
 };
 
@@ -613,8 +617,9 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))
                         split4(h[2 * dp], hi0, lo0);
                         split4(h[2 * dp + 1], hi1, lo1);
                         const uint32_t off = (uint32_t)(((colw + n16) * KD + slot_base(2 * dp, g)) * 2);
-                        *reinterpret_cast<bf16x8 *>(hb + off) = cat(hi0, hi1);
-                        *reinterpret_cast<bf16x8 *>(hb + plane + off) = cat(lo0, lo1);
+                        // streamed past L2: nothing reads them before the backward
+                        __builtin_nontemporal_store(cat(hi0, hi1), reinterpret_cast<bf16x8 *>(hb + off));
+                        __builtin_nontemporal_store(cat(lo0, lo1), reinterpret_cast<bf16x8 *>(hb + plane + off));
                     }
                 } else {
                     int rs = p.V;
