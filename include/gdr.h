@@ -27,8 +27,9 @@
  *  - Every pointer in an args struct is a DEVICE pointer unless stated; all
  *    tensors are contiguous row-major in the layouts given, 16-byte aligned.
  *  - The caller allocates and owns every buffer, including the workspace.
- *    The library allocates nothing, holds no state between calls, never
- *    synchronises the stream and never reads device memory on the host.
+ *    The library allocates nothing, holds no state between calls (but for
+ *    the static scratch buffer of gdr_fwd_noalloc), never synchronises the
+ *    stream and never reads device memory on the host.
  *    Calls on different streams may run concurrently if their buffers do
  *    not overlap.
  *  - Validation happens on the host before any launch.  A non-zero return
@@ -54,7 +55,9 @@ extern "C" {
 
 /* return codes */
 #define GDR_OK 0
-#define GDR_EINVAL -1     /* null required pointer, bad size, misalignment, H_v % H_q != 0, B != 1 with cu_seqlens */
+#define GDR_EINVAL -1     /* null required pointer, bad size, misalignment, H_v % H_q != 0, B != 1 with cu_seqlens,
+                             a shape past the launch grids: B T >= 2^31 tokens, or (N + 7) H_q >= 2^24 for
+                             the chunk-count bound N of gdr_tblocks_bytes */
 #define GDR_ENOTSUP -2    /* K or V not in {64, 128}; unsupported dtype */
 #define GDR_EWORKSPACE -3 /* workspace_bytes below what gdr_*_workspace reports */
 #define GDR_ELAUNCH -4    /* a HIP launch failed */
