@@ -52,9 +52,13 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
     __shared__ float cs[2][CH];
     __shared__ float red[4];
 
-    // the q/k head runs fastest over the workgroups (neighbours read adjacent pieces
-    // of the same q, k, v and dO rows)
-    const int gid = blockIdx.x / p.Hq, hq = blockIdx.x % p.Hq;
+    // Workgroup b runs on XCD b % 8.  The chunks are dealt to the XCDs in turn, so that
+    // the rows of dbeta and dg that a chunk's q/k heads all write meet in one L2; within
+    // an XCD the q/k head runs fastest (neighbours read adjacent pieces of the same q,
+    // k, v and dO rows).  Chunks past the last (the grid rounds them up to a multiple
+    // of 8) have no work.
+    const int slot = blockIdx.x >> 3;
+    const int hq = slot % p.Hq, gid = (slot / p.Hq) * 8 + (blockIdx.x & 7);
     int j, c;
     if (!p.sm.locate(gid, j, c)) return;
     int64_t bos, eos;
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_bf16(const BwdParams p) {
 }  // namespace
 
 hipError_t launch_bwd_local_bf16(Dt gt, int K, const BwdParams &p, int n_chunks_ub, hipStream_t s) {
-    const dim3 grid(n_chunks_ub * p.Hq);  // (chunk, q/k head), the head fastest
+    const dim3 grid((n_chunks_ub + 7) / 8 * 8 * p.Hq);  // (chunk, q/k head)
     if (gt == Dt::BF16) {
         if (K == 128)
             launch_k((bwd_local_bf16<bf16, 128>), grid, dim3(NTHR), 0, s, p);
